@@ -1,0 +1,169 @@
+"""fp64 token-by-token CPU oracle for the Kimi Delta Attention recurrence.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` import this package.  It shares no code with
+the HIP path and never imports it.
+
+The arithmetic lives in ``kda_oracle.c`` (plain C, fp64); this module only
+compiles it with gcc and marshals numpy arrays through ctypes.  What is
+computed, and the passages it follows, are stated in the header of
+``kda_oracle.c``:
+
+* "Kimi K3 technical FAQ", question "What is KDA, and why does a serving
+  engineer care?": delta-rule recurrence with a per-channel forget gate and a
+  dk x dv state per head, read as
+  ``S_t = (I - b_t k_t k_t^T) Diag(a_t) S_{t-1} + b_t k_t v_t^T``,
+  ``o_t = dk^-1/2 S_t^T q_t``.
+* "Day-0 vLLM support for Kimi K3", section "Kimi K3's architecture, and how
+  vLLM serves it": state snapshots at block boundaries for prefix reuse.
+
+Parity pins for every function here are in ``tests/test_oracle_pins.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "kda_oracle.c")
+LIBRARY = os.path.join(_HERE, "libkda_oracle.so")
+
+
+def build(src: str = SOURCE, out: str = LIBRARY) -> str:
+    """Compile the oracle with gcc (-O2, no fast-math, no SIMD intrinsics)."""
+    tmp = out + ".tmp"
+    cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-pthread",
+           "-fno-fast-math", "-o", tmp, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
+    P = ctypes.c_void_p
+    i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+    lib.kda_oracle_prefill.restype = ctypes.c_int
+    lib.kda_oracle_prefill.argtypes = [i32, P, i32, i32, i32, P, P, P, P, P,
+                                       P, f64, i64, P, P, P, i32]
+    lib.kda_oracle_decode.restype = ctypes.c_int
+    lib.kda_oracle_decode.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P,
+                                      P, P, f64, P, i32]
+    lib.kda_oracle_snapshot_count.restype = i64
+    lib.kda_oracle_snapshot_count.argtypes = [i32, P, i64]
+    return lib
+
+
+class Oracle:
+    """ctypes handle on one compiled oracle library (the real one, or a
+    deliberately mutated copy built by the mutation tests)."""
+
+    def __init__(self, path: str = LIBRARY):
+        if not os.path.exists(path):
+            if path != LIBRARY:
+                raise FileNotFoundError(path)
+            build()
+        self.path = path
+        self.lib = _bind(ctypes.CDLL(path))
+
+    @staticmethod
+    def _threads(nthreads: Optional[int]) -> int:
+        if nthreads:
+            return int(nthreads)
+        try:
+            return max(1, len(os.sched_getaffinity(0)))
+        except AttributeError:  # pragma: no cover
+            return max(1, os.cpu_count() or 1)
+
+    @staticmethod
+    def _f32(x) -> np.ndarray:
+        return np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+
+    def snapshot_count(self, cu_seqlens, interval: int) -> int:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+        return int(self.lib.kda_oracle_snapshot_count(
+            len(cu) - 1, cu.ctypes.data, int(interval)))
+
+    def prefill(self, q, k, v, g, beta, cu_seqlens, initial_state=None,
+                scale: float = 0.0, snapshot_interval: int = 0,
+                nthreads: Optional[int] = None):
+        """Run every (sequence, head) token by token in fp64.
+
+        q, k, g: [T, H, dk]; v: [T, H, dv]; beta: [T, H] (any float dtype,
+        converted exactly to fp32).  initial_state: [N, H, dk, dv] or None,
+        converted to fp64.  Returns (out [T,H,dv], final [N,H,dk,dv],
+        snapshots [count,H,dk,dv]) as fp64 arrays.
+        """
+        q, k, v, g, beta = (self._f32(a) for a in (q, k, v, g, beta))
+        T, H, dk = q.shape
+        dv = v.shape[2]
+        assert k.shape == (T, H, dk) and g.shape == (T, H, dk)
+        assert v.shape == (T, H, dv) and beta.shape == (T, H)
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+        N = len(cu) - 1
+        assert cu[0] == 0 and cu[-1] == T
+        init = None
+        if initial_state is not None:
+            init = np.ascontiguousarray(np.asarray(initial_state, dtype=np.float64))
+            assert init.shape == (N, H, dk, dv)
+        out = np.zeros((T, H, dv), dtype=np.float64)
+        final = np.zeros((N, H, dk, dv), dtype=np.float64)
+        count = self.snapshot_count(cu, snapshot_interval)
+        snaps = np.zeros((count, H, dk, dv), dtype=np.float64)
+        rc = self.lib.kda_oracle_prefill(
+            N, cu.ctypes.data, H, dk, dv, q.ctypes.data, k.ctypes.data,
+            v.ctypes.data, g.ctypes.data, beta.ctypes.data,
+            None if init is None else init.ctypes.data, float(scale),
+            int(snapshot_interval), out.ctypes.data, final.ctypes.data,
+            snaps.ctypes.data if count else None, self._threads(nthreads))
+        if rc != 0:
+            raise ValueError("kda_oracle_prefill rejected its arguments")
+        return out, final, snaps
+
+    def decode(self, q, k, v, g, beta, state, slots=None, scale: float = 0.0,
+               nthreads: Optional[int] = None):
+        """``steps`` chained single-token steps.
+
+        q, k, g: [steps, N, H, dk]; v: [steps, N, H, dv]; beta: [steps, N, H];
+        state: [S, H, dk, dv] (copied to fp64; the updated copy is returned).
+        Returns (out [steps, N, H, dv], state).
+        """
+        q, k, v, g, beta = (self._f32(a) for a in (q, k, v, g, beta))
+        steps, N, H, dk = q.shape
+        dv = v.shape[3]
+        st = np.array(state, dtype=np.float64, order="C", copy=True)
+        sl = None
+        if slots is not None:
+            sl = np.ascontiguousarray(np.asarray(slots, dtype=np.int32))
+            assert sl.shape == (N,)
+        out = np.zeros((steps, N, H, dv), dtype=np.float64)
+        rc = self.lib.kda_oracle_decode(
+            steps, N, H, dk, dv, q.ctypes.data, k.ctypes.data, v.ctypes.data,
+            g.ctypes.data, beta.ctypes.data, st.ctypes.data,
+            None if sl is None else sl.ctypes.data, float(scale),
+            out.ctypes.data, self._threads(nthreads))
+        if rc != 0:
+            raise ValueError("kda_oracle_decode rejected its arguments")
+        return out, st
+
+
+_DEFAULT: Optional[Oracle] = None
+
+
+def get() -> Oracle:
+    """The oracle built from ``kda_oracle.c`` (compiled on first use)."""
+    global _DEFAULT
+    if _DEFAULT is None:
+        _DEFAULT = Oracle()
+    return _DEFAULT
+
+
+def prefill(*args, **kwargs):
+    return get().prefill(*args, **kwargs)
+
+
+def decode(*args, **kwargs):
+    return get().decode(*args, **kwargs)
