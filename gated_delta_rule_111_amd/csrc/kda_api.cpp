@@ -1,0 +1,231 @@
+// kda_api.cpp -- the C ABI of libkda (declared in include/kda.h): argument
+// validation, problem planning and kernel launches.  Every check runs before
+// anything is enqueued, so an error return has launched and written nothing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+thread_local char g_detail[512] = "";
+
+kda_status fail(kda_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_detail, sizeof(g_detail), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+kda_status ok() {
+    g_detail[0] = '\0';
+    return KDA_OK;
+}
+
+bool aligned(const void* p, uintptr_t bytes) {
+    return (reinterpret_cast<uintptr_t>(p) & (bytes - 1)) == 0;
+}
+
+kda_status check_config(const kda_config* cfg) {
+    if (!cfg) return fail(KDA_ERR_INVALID_ARG, "cfg is NULL");
+    if (cfg->num_heads <= 0) return fail(KDA_ERR_INVALID_ARG, "num_heads must be > 0");
+    if (cfg->dk != cfg->dv)
+        return fail(KDA_ERR_UNSUPPORTED, "dk (%d) != dv (%d) is not provided", cfg->dk, cfg->dv);
+    if (cfg->dk != 16 && cfg->dk != 32 && cfg->dk != 64 && cfg->dk != 128)
+        return fail(KDA_ERR_UNSUPPORTED, "head dim %d not in {16, 32, 64, 128}", cfg->dk);
+    if (cfg->in_dtype != KDA_BF16 && cfg->in_dtype != KDA_F32)
+        return fail(KDA_ERR_UNSUPPORTED, "in_dtype %d unknown", (int)cfg->in_dtype);
+    if (cfg->out_dtype != KDA_BF16 && cfg->out_dtype != KDA_F32)
+        return fail(KDA_ERR_UNSUPPORTED, "out_dtype %d unknown", (int)cfg->out_dtype);
+    if (!std::isfinite(cfg->scale) || cfg->scale < 0.f)
+        return fail(KDA_ERR_INVALID_ARG, "scale must be finite and >= 0");
+    return KDA_OK;
+}
+
+float effective_scale(const kda_config* cfg) {
+    return cfg->scale > 0.f ? cfg->scale : (float)(1.0 / std::sqrt((double)cfg->dk));
+}
+
+struct PtrCheck {
+    const char* name;
+    const void* p;
+    bool required;
+    uintptr_t align;  // tensors read with 128-bit accesses need 16; scalar arrays 4
+};
+
+kda_status check_ptrs(const PtrCheck* list, int n) {
+    for (int i = 0; i < n; ++i) {
+        if (!list[i].p) {
+            if (list[i].required)
+                return fail(KDA_ERR_INVALID_ARG, "%s is NULL", list[i].name);
+            continue;
+        }
+        if (!aligned(list[i].p, list[i].align))
+            return fail(KDA_ERR_ALIGNMENT, "%s is not %d-byte aligned", list[i].name,
+                        (int)list[i].align);
+    }
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kda_version(void) { return KDA_VERSION; }
+
+const char* kda_status_string(kda_status status) {
+    switch (status) {
+        case KDA_OK: return "KDA_OK";
+        case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+        case KDA_ERR_ALIGNMENT: return "KDA_ERR_ALIGNMENT";
+        case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE";
+        case KDA_ERR_HIP: return "KDA_ERR_HIP";
+    }
+    return "KDA_ERR_UNKNOWN";
+}
+
+const char* kda_last_error_detail(void) { return g_detail; }
+
+int64_t kda_snapshot_count(const int32_t* cu, int32_t num_seqs, int32_t interval) {
+    if (!cu || num_seqs < 0) return -1;
+    if (interval <= 0) return 0;
+    int64_t n = 0;
+    for (int32_t b = 0; b < num_seqs; ++b) {
+        if (cu[b + 1] < cu[b]) return -1;
+        n += (int64_t)(cu[b + 1] - cu[b]) / interval;
+    }
+    return n;
+}
+
+size_t kda_prefill_workspace_size(const kda_config* cfg, int32_t num_seqs, int64_t total_tokens) {
+    if (check_config(cfg) != KDA_OK || num_seqs < 0 || total_tokens < 0) return 0;
+    return kda::prefill_workspace_bytes(cfg->dk, cfg->dv, cfg->num_heads, num_seqs, total_tokens);
+}
+
+kda_status kda_prefill(const kda_config* cfg, int32_t num_seqs, const int32_t* cu_host,
+                       const int32_t* cu_dev, const void* q, const void* k, const void* v,
+                       const float* g, const float* beta, const float* initial_state, void* out,
+                       float* final_state, int32_t snapshot_interval, float* snapshots,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    kda_status st = check_config(cfg);
+    if (st != KDA_OK) return st;
+    if (num_seqs < 0) return fail(KDA_ERR_INVALID_ARG, "num_seqs must be >= 0");
+    if (num_seqs == 0) return ok();
+    if (!cu_host) return fail(KDA_ERR_INVALID_ARG, "cu_seqlens_host is NULL");
+    if (cu_host[0] != 0) return fail(KDA_ERR_INVALID_ARG, "cu_seqlens[0] must be 0");
+    int32_t max_len = 0;
+    for (int32_t b = 0; b < num_seqs; ++b) {
+        if (cu_host[b + 1] < cu_host[b])
+            return fail(KDA_ERR_INVALID_ARG, "cu_seqlens decreases at index %d", b + 1);
+        if (cu_host[b + 1] - cu_host[b] > max_len) max_len = cu_host[b + 1] - cu_host[b];
+    }
+    const int64_t T = cu_host[num_seqs];
+    if (snapshot_interval < 0 || snapshot_interval % 64 != 0)
+        return fail(KDA_ERR_INVALID_ARG, "snapshot_interval %d is not a non-negative multiple of 64",
+                    snapshot_interval);
+    const int64_t nsnap = kda_snapshot_count(cu_host, num_seqs, snapshot_interval);
+    const bool tok = T > 0;
+    const PtrCheck ptrs[] = {
+        {"cu_seqlens_dev", cu_dev, true, 4},
+        {"q", q, tok, 16},
+        {"k", k, tok, 16},
+        {"v", v, tok, 16},
+        {"g", g, tok, 16},
+        {"beta", beta, tok, 4},
+        {"initial_state", initial_state, false, 16},
+        {"out", out, tok, 16},
+        {"final_state", final_state, true, 16},
+        {"snapshots", snapshots, nsnap > 0, 16},
+        {"workspace", workspace, false, 16},
+    };
+    st = check_ptrs(ptrs, (int)(sizeof(ptrs) / sizeof(ptrs[0])));
+    if (st != KDA_OK) return st;
+    const size_t need = kda::prefill_workspace_bytes(cfg->dk, cfg->dv, cfg->num_heads, num_seqs, T);
+    if (workspace_bytes < need || (need > 0 && !workspace))
+        return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required",
+                    workspace_bytes, need);
+    if (initial_state && initial_state != final_state) {
+        // final_state may alias initial_state exactly; partial overlap is not allowed
+        const size_t bytes = (size_t)num_seqs * cfg->num_heads * cfg->dk * cfg->dv * sizeof(float);
+        const char* a = reinterpret_cast<const char*>(initial_state);
+        const char* b = reinterpret_cast<const char*>(final_state);
+        if (a < b + bytes && b < a + bytes)
+            return fail(KDA_ERR_INVALID_ARG, "final_state partially overlaps initial_state");
+    }
+
+    kda::PrefillArgs a{};
+    a.dk = cfg->dk;
+    a.dv = cfg->dv;
+    a.H = cfg->num_heads;
+    a.num_seqs = num_seqs;
+    a.in_bf16 = cfg->in_dtype == KDA_BF16;
+    a.out_bf16 = cfg->out_dtype == KDA_BF16;
+    a.total_tokens = T;
+    a.max_len = max_len;
+    a.cu_dev = cu_dev;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.init = initial_state;
+    a.out = out;
+    a.final_state = final_state;
+    a.interval = snapshot_interval;
+    a.snapshots = snapshots;
+    a.workspace = workspace;
+    a.workspace_bytes = workspace_bytes;
+    a.scale = effective_scale(cfg);
+    a.stream = static_cast<hipStream_t>(stream);
+    hipError_t e = kda::launch_prefill(a);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+kda_status kda_decode(const kda_config* cfg, int32_t num_seqs, const void* q, const void* k,
+                      const void* v, const float* g, const float* beta, float* state,
+                      const int32_t* slots, void* out, void* stream) {
+    kda_status st = check_config(cfg);
+    if (st != KDA_OK) return st;
+    if (num_seqs < 0) return fail(KDA_ERR_INVALID_ARG, "num_seqs must be >= 0");
+    if (num_seqs == 0) return ok();
+    if ((int64_t)num_seqs * cfg->num_heads > 0x7fffffffLL)
+        return fail(KDA_ERR_UNSUPPORTED, "num_seqs * num_heads exceeds the grid limit");
+    const PtrCheck ptrs[] = {
+        {"q", q, true, 16},     {"k", k, true, 16},         {"v", v, true, 16},
+        {"g", g, true, 16},     {"beta", beta, true, 4},    {"state", state, true, 16},
+        {"state_slots_dev", slots, false, 4},               {"out", out, true, 16},
+    };
+    st = check_ptrs(ptrs, (int)(sizeof(ptrs) / sizeof(ptrs[0])));
+    if (st != KDA_OK) return st;
+
+    kda::DecodeArgs a{};
+    a.dk = cfg->dk;
+    a.dv = cfg->dv;
+    a.H = cfg->num_heads;
+    a.num_seqs = num_seqs;
+    a.in_bf16 = cfg->in_dtype == KDA_BF16;
+    a.out_bf16 = cfg->out_dtype == KDA_BF16;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.state = state;
+    a.slots = slots;
+    a.out = out;
+    a.scale = effective_scale(cfg);
+    a.stream = static_cast<hipStream_t>(stream);
+    hipError_t e = kda::launch_decode(a);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // extern "C"

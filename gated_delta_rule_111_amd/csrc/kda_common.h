@@ -1,0 +1,92 @@
+// kda_common.h -- small device helpers shared by the libkda kernels
+// (dtype conversion and vector loads).  gfx950 only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+// bf16 is carried as its 16-bit pattern; widening to fp32 is exact.
+struct bf16_t {
+    uint16_t bits;
+};
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// fp32 -> bf16 with round-to-nearest-even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+template <typename T> struct io;
+
+template <> struct io<float> {
+    // load N consecutive values (N*4 bytes, 16-byte aligned when N % 4 == 0)
+    template <int N>
+    __device__ __forceinline__ static void load(const float* __restrict__ p, float (&x)[N]) {
+        if constexpr (N % 4 == 0) {
+#pragma unroll
+            for (int i = 0; i < N; i += 4) {
+                float4 t = *reinterpret_cast<const float4*>(p + i);
+                x[i] = t.x; x[i + 1] = t.y; x[i + 2] = t.z; x[i + 3] = t.w;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < N; ++i) x[i] = p[i];
+        }
+    }
+    __device__ __forceinline__ static void store4(float* __restrict__ p, float a, float b,
+                                                  float c, float d) {
+        *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+    }
+};
+
+template <> struct io<bf16_t> {
+    template <int N>
+    __device__ __forceinline__ static void load(const bf16_t* __restrict__ p, float (&x)[N]) {
+        if constexpr (N % 8 == 0) {
+#pragma unroll
+            for (int i = 0; i < N; i += 8) {
+                uint4 t = *reinterpret_cast<const uint4*>(p + i);
+                uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    x[i + 2 * j] = bf16_bits_to_f32(w[j] & 0xffffu);
+                    x[i + 2 * j + 1] = bf16_bits_to_f32(w[j] >> 16);
+                }
+            }
+        } else if constexpr (N % 4 == 0) {
+#pragma unroll
+            for (int i = 0; i < N; i += 4) {
+                uint2 t = *reinterpret_cast<const uint2*>(p + i);
+                x[i] = bf16_bits_to_f32(t.x & 0xffffu);
+                x[i + 1] = bf16_bits_to_f32(t.x >> 16);
+                x[i + 2] = bf16_bits_to_f32(t.y & 0xffffu);
+                x[i + 3] = bf16_bits_to_f32(t.y >> 16);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < N; ++i) x[i] = bf16_bits_to_f32(p[i].bits);
+        }
+    }
+    __device__ __forceinline__ static void store4(bf16_t* __restrict__ p, float a, float b,
+                                                  float c, float d) {
+        uint2 t;
+        t.x = (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
+        t.y = (uint32_t)f32_to_bf16_bits(c) | ((uint32_t)f32_to_bf16_bits(d) << 16);
+        *reinterpret_cast<uint2*>(p) = t;
+    }
+};
+
+// alpha = exp(g) through the hardware base-2 exponential.
+__device__ __forceinline__ float exp_gate(float g) {
+    return __builtin_amdgcn_exp2f(g * 1.4426950408889634f);
+}
+
+}  // namespace kda

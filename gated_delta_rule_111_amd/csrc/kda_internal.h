@@ -1,0 +1,47 @@
+// kda_internal.h -- launch descriptors shared by the host API (kda_api.cpp)
+// and the kernel translation units.  Arguments are validated by the host
+// API before any launcher is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct DecodeArgs {
+    int dk, dv, H, num_seqs;
+    bool in_bf16, out_bf16;
+    const void *q, *k, *v;
+    const float *g, *beta;
+    float* state;
+    const int32_t* slots;
+    void* out;
+    float scale;
+    hipStream_t stream;
+};
+
+struct PrefillArgs {
+    int dk, dv, H, num_seqs;
+    bool in_bf16, out_bf16;
+    int64_t total_tokens;
+    int32_t max_len;              // longest sequence (host-side planning)
+    const int32_t* cu_dev;        // [num_seqs + 1] device offsets
+    const void *q, *k, *v;
+    const float *g, *beta;
+    const float* init;            // nullable
+    void* out;
+    float* final_state;
+    int32_t interval;             // 0 = no snapshots
+    float* snapshots;             // nullable when no snapshot is due
+    void* workspace;
+    size_t workspace_bytes;
+    float scale;
+    hipStream_t stream;
+};
+
+hipError_t launch_decode(const DecodeArgs& a);
+hipError_t launch_prefill(const PrefillArgs& a);
+size_t prefill_workspace_bytes(int dk, int dv, int H, int num_seqs, int64_t total_tokens);
+
+}  // namespace kda

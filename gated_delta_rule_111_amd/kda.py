@@ -1,0 +1,209 @@
+"""Thin Python binding of libkda (include/kda.h).
+
+Argument marshalling only: this module checks dtypes, shapes, devices and
+contiguity of torch tensors, allocates outputs with torch when the caller
+does not pass them, and hands raw device pointers plus the current HIP stream
+to the C ABI.  Every step of the computation runs in the HIP kernels.  If the
+shared library has not been built the first call raises; there is no other
+path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_PKG, "libkda.so")
+
+KDA_BF16, KDA_F32 = 0, 1
+_STATUS = {0: "KDA_OK", 1: "KDA_ERR_INVALID_ARG", 2: "KDA_ERR_UNSUPPORTED",
+           3: "KDA_ERR_ALIGNMENT", 4: "KDA_ERR_WORKSPACE", 5: "KDA_ERR_HIP"}
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("dk", ctypes.c_int32),
+                ("dv", ctypes.c_int32), ("in_dtype", ctypes.c_int),
+                ("out_dtype", ctypes.c_int), ("scale", ctypes.c_float)]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load(path: str = LIBRARY) -> ctypes.CDLL:
+    """Load libkda.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m gated_delta_rule_111_amd.build` "
+            "(libkda has no fallback path)")
+    lib = ctypes.CDLL(path)
+    P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    CP = ctypes.POINTER(Config)
+    lib.kda_version.restype = i32
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_status_string.argtypes = [ctypes.c_int]
+    lib.kda_last_error_detail.restype = ctypes.c_char_p
+    lib.kda_snapshot_count.restype = i64
+    lib.kda_snapshot_count.argtypes = [P, i32, i32]
+    lib.kda_prefill_workspace_size.restype = sz
+    lib.kda_prefill_workspace_size.argtypes = [CP, i32, i64]
+    lib.kda_prefill.restype = ctypes.c_int
+    lib.kda_prefill.argtypes = [CP, i32, P, P, P, P, P, P, P, P, P, P, i32, P, P, sz, P]
+    lib.kda_decode.restype = ctypes.c_int
+    lib.kda_decode.argtypes = [CP, i32, P, P, P, P, P, P, P, P, P]
+    _lib = lib
+    return lib
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return KDA_BF16
+    if dt == torch.float32:
+        return KDA_F32
+    raise TypeError(f"unsupported dtype {dt}; use torch.bfloat16 or torch.float32")
+
+
+def _check(status: int):
+    if status != 0:
+        raise KdaError(status, load().kda_last_error_detail().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, name: str, shape, dtype, device):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)} != {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype} != {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def config(H: int, dk: int, dv: int, in_dtype: torch.dtype,
+           out_dtype: torch.dtype = torch.float32, scale: float = 0.0) -> Config:
+    return Config(H, dk, dv, _dtype_code(in_dtype), _dtype_code(out_dtype), float(scale))
+
+
+def snapshot_count(cu_seqlens_host: Sequence[int], interval: int) -> int:
+    cu = (ctypes.c_int32 * len(cu_seqlens_host))(*cu_seqlens_host)
+    n = load().kda_snapshot_count(cu, len(cu_seqlens_host) - 1, int(interval))
+    if n < 0:
+        raise ValueError("cu_seqlens must be non-decreasing")
+    return int(n)
+
+
+def workspace_size(cfg: Config, num_seqs: int, total_tokens: int) -> int:
+    return int(load().kda_prefill_workspace_size(ctypes.byref(cfg), num_seqs, total_tokens))
+
+
+def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+            beta: torch.Tensor, cu_seqlens: torch.Tensor,
+            initial_state: Optional[torch.Tensor] = None, snapshot_interval: int = 0,
+            out_dtype: Optional[torch.dtype] = None, scale: float = 0.0,
+            cu_seqlens_host: Optional[Sequence[int]] = None,
+            out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+            snapshots: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+            stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """kda_prefill on packed varlen sequences; returns (out, final_state, snapshots).
+
+    q, k: [T, H, dk]; v: [T, H, dv] (bf16 or fp32, same dtype); g: [T, H, dk]
+    fp32 log-gates; beta: [T, H] fp32; cu_seqlens: [N+1] int32 on the device
+    (cu_seqlens_host, if given, must hold the same offsets and avoids a copy).
+    """
+    lib = load()
+    dev = q.device
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    if cu_seqlens_host is None:
+        cu_seqlens_host = cu_seqlens.cpu().tolist()
+    cu_list = [int(x) for x in cu_seqlens_host]
+    N = len(cu_list) - 1
+    _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    for name, t, shp, dt in (("q", q, (T, H, dk), q.dtype), ("k", k, (T, H, dk), q.dtype),
+                             ("v", v, (T, H, dv), q.dtype), ("g", g, (T, H, dk), torch.float32),
+                             ("beta", beta, (T, H), torch.float32)):
+        _need(t, name, shp, dt, dev)
+    if cu_list[-1] != T:
+        raise ValueError(f"cu_seqlens ends at {cu_list[-1]} but q has {T} tokens")
+    if initial_state is not None:
+        _need(initial_state, "initial_state", (N, H, dk, dv), torch.float32, dev)
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else torch.float32
+    cfg = config(H, dk, dv, q.dtype, out_dtype, scale)
+    nsnap = snapshot_count(cu_list, snapshot_interval) if snapshot_interval > 0 else 0
+    if out is None:
+        out = torch.empty(T, H, dv, dtype=out_dtype, device=dev)
+    _need(out, "out", (T, H, dv), out_dtype, dev)
+    if final_state is None:
+        final_state = torch.empty(N, H, dk, dv, dtype=torch.float32, device=dev)
+    _need(final_state, "final_state", (N, H, dk, dv), torch.float32, dev)
+    if snapshots is None:
+        snapshots = torch.empty(nsnap, H, dk, dv, dtype=torch.float32, device=dev)
+    _need(snapshots, "snapshots", (nsnap, H, dk, dv), torch.float32, dev)
+    ws_bytes = workspace_size(cfg, N, T)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    cu_arr = (ctypes.c_int32 * len(cu_list))(*cu_list)
+    _check(lib.kda_prefill(
+        ctypes.byref(cfg), N, cu_arr, cu_seqlens.data_ptr(), q.data_ptr(), k.data_ptr(),
+        v.data_ptr(), g.data_ptr(), beta.data_ptr(), _ptr(initial_state), out.data_ptr(),
+        final_state.data_ptr(), int(snapshot_interval),
+        snapshots.data_ptr() if nsnap > 0 else None, _ptr(workspace),
+        workspace.numel() if workspace is not None else 0, _stream(stream)))
+    return out, final_state, snapshots
+
+
+def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+           beta: torch.Tensor, state: torch.Tensor, slots: Optional[torch.Tensor] = None,
+           out_dtype: Optional[torch.dtype] = None, scale: float = 0.0,
+           out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """kda_decode: one token per sequence; ``state`` [S, H, dk, dv] fp32 is
+    updated in place.  q, k: [N, H, dk]; v: [N, H, dv]; g: [N, H, dk];
+    beta: [N, H]; slots: [N] int32 device tensor or None (identity)."""
+    lib = load()
+    dev = q.device
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    for name, t, shp, dt in (("q", q, (N, H, dk), q.dtype), ("k", k, (N, H, dk), q.dtype),
+                             ("v", v, (N, H, dv), q.dtype), ("g", g, (N, H, dk), torch.float32),
+                             ("beta", beta, (N, H), torch.float32)):
+        _need(t, name, shp, dt, dev)
+    if state.dim() != 4 or tuple(state.shape[1:]) != (H, dk, dv):
+        raise ValueError(f"state: shape {tuple(state.shape)} != [S, {H}, {dk}, {dv}]")
+    _need(state, "state", tuple(state.shape), torch.float32, dev)
+    if slots is None and state.shape[0] < N:
+        raise ValueError("state has fewer rows than sequences")
+    if slots is not None:
+        _need(slots, "slots", (N,), torch.int32, dev)
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else torch.float32
+    cfg = config(H, dk, dv, q.dtype, out_dtype, scale)
+    if out is None:
+        out = torch.empty(N, H, dv, dtype=out_dtype, device=dev)
+    _need(out, "out", (N, H, dv), out_dtype, dev)
+    _check(lib.kda_decode(ctypes.byref(cfg), N, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                          g.data_ptr(), beta.data_ptr(), state.data_ptr(), _ptr(slots),
+                          out.data_ptr(), _stream(stream)))
+    return out

@@ -1,0 +1,166 @@
+/*
+ * kda.h -- C ABI of libkda: the Kimi Delta Attention (KDA) layer on one
+ * AMD MI355X (gfx950).
+ *
+ * The operation
+ * -------------
+ * "Kimi K3 technical FAQ" (Runpod guide), question "What is KDA, and why does
+ * a serving engineer care?": KDA is the delta-rule linear-attention
+ * recurrence with a per-channel forget gate; each layer keeps, per head, a
+ * recurrent state of shape dk x dv that is updated per chunk, parallel
+ * within a chunk and recurrent across chunks.  The question "What does the
+ * architecture actually look like?" on the same page adds that the state is
+ * fixed-size (it replaces a growing KV cache).  This library reads the
+ * recurrence as
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,
+ *     o_t = scale * S_t^T q_t,     scale = dk^(-1/2) unless given,
+ *
+ * with alpha_t = exp(g_t) in (0,1]^dk (one forget factor per key channel)
+ * and beta_t in [0,1].  The gate crosses this boundary in log space, g <= 0,
+ * because chunked evaluation needs sums of log-gates and products of alpha
+ * underflow fp32 within a chunk.
+ *
+ * "Day-0 vLLM support for Kimi K3" (vLLM blog), section "Kimi K3's
+ * architecture, and how vLLM serves it": prefix caching over recurrent state
+ * reuses state snapshots taken at block boundaries.  kda_prefill therefore
+ * writes the fp32 state after every `snapshot_interval` tokens of each
+ * sequence; passing snapshot j back as `initial_state` with the remaining
+ * tokens reproduces the uninterrupted run bit for bit.
+ *
+ * Conventions for every call
+ * --------------------------
+ * - All tensors are caller-owned device memory, row-major and contiguous.
+ *   The library allocates no device memory and keeps no pointer after a call
+ *   returns.
+ * - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *   stream).  KDA_OK means "validated and enqueued"; results are visible
+ *   after the stream is synchronised.
+ * - Every argument check happens before anything is enqueued: a call that
+ *   returns an error has launched nothing and written nothing.
+ *   kda_last_error_detail() then describes the failure (thread-local).
+ * - Device tensors of head vectors and states (q, k, v, g, out, states,
+ *   snapshots, workspace) must be 16-byte aligned; beta, cu_seqlens_dev and
+ *   state_slots_dev 4-byte aligned (KDA_ERR_ALIGNMENT otherwise).
+ * - Supported shapes: dk == dv in {16, 32, 64, 128}; anything else returns
+ *   KDA_ERR_UNSUPPORTED.  q/k/v are bf16 or fp32 (in_dtype); g, beta, states
+ *   and snapshots are fp32; out is fp32 or bf16 (out_dtype).
+ * - No call prints, throws across the ABI or exits.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_VERSION 1
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = 1, /* null pointer, bad size, bad cu_seqlens ...  */
+    KDA_ERR_UNSUPPORTED = 2, /* shape or dtype this build does not provide  */
+    KDA_ERR_ALIGNMENT = 3,   /* a device pointer is under-aligned           */
+    KDA_ERR_WORKSPACE = 4,   /* workspace smaller than the size required    */
+    KDA_ERR_HIP = 5          /* the HIP runtime reported a launch error     */
+} kda_status;
+
+typedef enum { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
+
+typedef struct {
+    int32_t num_heads; /* H                                                 */
+    int32_t dk;        /* key/query head dim (rows of the state)            */
+    int32_t dv;        /* value head dim (columns of the state)             */
+    kda_dtype in_dtype;  /* dtype of q, k, v                                */
+    kda_dtype out_dtype; /* dtype of out                                    */
+    float scale;       /* output scale; 0 selects dk^(-1/2)                 */
+} kda_config;
+
+/* Library version (KDA_VERSION of the build). */
+int32_t kda_version(void);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *kda_status_string(kda_status status);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char *kda_last_error_detail(void);
+
+/*
+ * Number of snapshot rows kda_prefill writes for these sequences:
+ * sum_b floor(L_b / interval), L_b = cu_seqlens_host[b+1] - cu_seqlens_host[b].
+ * Sequence b's snapshots occupy rows starting at sum_{b'<b} floor(L_b'/interval),
+ * in order j = 1 .. floor(L_b/interval).  Returns 0 when interval <= 0 and
+ * -1 when cu_seqlens_host is NULL or decreasing.
+ */
+int64_t kda_snapshot_count(const int32_t *cu_seqlens_host, int32_t num_seqs,
+                           int32_t interval);
+
+/*
+ * Bytes of device workspace kda_prefill needs for this problem (may be 0;
+ * then `workspace` may be NULL).  Returns 0 for unsupported configs too;
+ * kda_prefill reports those.
+ */
+size_t kda_prefill_workspace_size(const kda_config *cfg, int32_t num_seqs,
+                                  int64_t total_tokens);
+
+/*
+ * Chunked prefill over packed variable-length sequences.
+ *
+ * Sequence b owns tokens [cu[b], cu[b+1]) of every token-major tensor
+ * (T = cu[num_seqs] tokens in all):
+ *   q, k : [T, H, dk]  in_dtype       v    : [T, H, dv]  in_dtype
+ *   g    : [T, H, dk]  fp32, log of the forget gate, every entry <= 0
+ *   beta : [T, H]      fp32, in [0, 1]
+ *   initial_state : [num_seqs, H, dk, dv] fp32, or NULL for zero states
+ *   out  : [T, H, dv]  out_dtype      (written)
+ *   final_state : [num_seqs, H, dk, dv] fp32 (written; may alias
+ *                 initial_state exactly, no other aliasing allowed)
+ *   snapshots : [kda_snapshot_count(...), H, dk, dv] fp32 (written); may be
+ *               NULL when that count is 0
+ * cu_seqlens_host and cu_seqlens_dev hold the same num_seqs+1 offsets
+ * (host memory and device memory): cu[0] == 0, non-decreasing.  Empty
+ * sequences are allowed (their final state is their initial state).
+ * snapshot_interval: 0 for none, otherwise a positive multiple of 64 (the
+ * chunk length); chunks restart at every sequence start.
+ * Errors: KDA_ERR_INVALID_ARG (null required pointer, num_seqs < 0, bad
+ * offsets, interval not a multiple of 64, snapshots NULL while some are
+ * due), KDA_ERR_UNSUPPORTED, KDA_ERR_ALIGNMENT, KDA_ERR_WORKSPACE, KDA_ERR_HIP.
+ */
+kda_status kda_prefill(const kda_config *cfg, int32_t num_seqs,
+                       const int32_t *cu_seqlens_host,
+                       const int32_t *cu_seqlens_dev, const void *q,
+                       const void *k, const void *v, const float *g,
+                       const float *beta, const float *initial_state,
+                       void *out, float *final_state,
+                       int32_t snapshot_interval, float *snapshots,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One decode step: one new token for each of num_seqs sequences against
+ * states resident on the device, updated in place.
+ *   q, k : [num_seqs, H, dk] in_dtype    v : [num_seqs, H, dv] in_dtype
+ *   g    : [num_seqs, H, dk] fp32 (<= 0) beta : [num_seqs, H] fp32
+ *   state : [num_slots, H, dk, dv] fp32, read and written in place
+ *   state_slots_dev : [num_seqs] int32 device array mapping sequence n to
+ *                     its state row, or NULL for the identity; entries must
+ *                     be distinct and < num_slots (not checked on device)
+ *   out  : [num_seqs, H, dv] out_dtype (written)
+ * "Moonshot releases Kimi K3 report" (runtimewire), section "The
+ * architecture is built around inference cost": the state is fixed-size, so
+ * each step reads and writes exactly H*dk*dv*4 bytes of state per sequence.
+ * Errors: KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_ALIGNMENT,
+ * KDA_ERR_HIP.  num_seqs == 0 is a no-op.
+ */
+kda_status kda_decode(const kda_config *cfg, int32_t num_seqs, const void *q,
+                      const void *k, const void *v, const float *g,
+                      const float *beta, float *state,
+                      const int32_t *state_slots_dev, void *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -1,0 +1,135 @@
+"""The C ABI on the CPU: the library loads, exports every function that
+include/kda.h declares, and rejects bad arguments before touching the GPU
+(every call here fails validation, so no HIP call is ever made)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from gated_delta_rule_111_amd import kda as libkda
+    if not os.path.exists(libkda.LIBRARY):
+        from gated_delta_rule_111_amd import build
+        build.build()
+    return libkda.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_calls():
+    names = declared_functions()
+    for required in ("kda_prefill", "kda_decode", "kda_snapshot_count",
+                     "kda_prefill_workspace_size", "kda_status_string",
+                     "kda_last_error_detail", "kda_version"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from gated_delta_rule_111_amd import kda as libkda
+    out = subprocess.run(["nm", "-D", "--defined-only", libkda.LIBRARY],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (kda_\w+)", out))
+    for name in declared_functions():
+        assert name in exported, f"{name} declared in kda.h but not exported"
+        assert hasattr(lib, name)
+
+
+def test_header_compiles_as_c(tmp_path):
+    src = tmp_path / "use.c"
+    src.write_text('#include "kda.h"\nint main(void){return kda_version()==0;}\n')
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-c", f"-I{ROOT}/include",
+                    str(src), "-o", str(tmp_path / "use.o")], check=True)
+
+
+def test_version_and_strings(lib):
+    assert lib.kda_version() == 1
+    assert lib.kda_status_string(0) == b"KDA_OK"
+    assert lib.kda_status_string(4) == b"KDA_ERR_WORKSPACE"
+
+
+def test_snapshot_count(lib):
+    from gated_delta_rule_111_amd import kda as libkda
+    assert libkda.snapshot_count([0, 100, 4196, 4196, 12288], 1024) == 0 + 4 + 0 + 7
+    assert libkda.snapshot_count([0, 64], 0) == 0
+    with pytest.raises(ValueError):
+        libkda.snapshot_count([0, 10, 5], 64)
+
+
+# fake, never-dereferenced device addresses: 16-byte aligned and misaligned
+A = 0x10000
+MIS = 0x10008
+
+
+def _cfg(H=2, d=128, ind=0, outd=1, scale=0.0):
+    from gated_delta_rule_111_amd import kda as libkda
+    return libkda.Config(H, d, d, ind, outd, scale)
+
+
+def _prefill(lib, cfg, cu, ptr=A, interval=0, snaps=A, final=A, ws=None, ws_bytes=0, cu_dev=A,
+             init=None):
+    arr = (ctypes.c_int32 * len(cu))(*cu) if cu is not None else None
+    cfgp = ctypes.byref(cfg) if cfg is not None else None
+    return lib.kda_prefill(cfgp, len(cu) - 1 if cu else 1, arr, cu_dev, ptr, ptr, ptr, ptr, ptr,
+                           init, ptr, final, interval, snaps, ws, ws_bytes, None)
+
+
+def test_prefill_rejects_bad_arguments(lib):
+    E_ARG, E_UNS, E_ALN = 1, 2, 3
+    assert _prefill(lib, None, [0, 64]) == E_ARG
+    assert _prefill(lib, _cfg(d=96), [0, 64]) == E_UNS
+    from gated_delta_rule_111_amd import kda as libkda
+    bad = libkda.Config(2, 128, 64, 0, 1, 0.0)
+    assert _prefill(lib, bad, [0, 64]) == E_UNS
+    assert _prefill(lib, _cfg(ind=7), [0, 64]) == E_UNS
+    assert _prefill(lib, _cfg(scale=-1.0), [0, 64]) == E_ARG
+    assert _prefill(lib, _cfg(H=0), [0, 64]) == E_ARG
+    assert _prefill(lib, _cfg(), [1, 64]) == E_ARG            # cu[0] != 0
+    assert _prefill(lib, _cfg(), [0, 64, 32]) == E_ARG        # decreasing
+    assert _prefill(lib, _cfg(), [0, 64], interval=100) == E_ARG
+    assert _prefill(lib, _cfg(), [0, 128], interval=64, snaps=None) == E_ARG
+    assert _prefill(lib, _cfg(), [0, 64], ptr=MIS) == E_ALN
+    assert _prefill(lib, _cfg(), [0, 64], ptr=None) == E_ARG
+    assert _prefill(lib, _cfg(), [0, 64], final=None) == E_ARG
+    assert _prefill(lib, _cfg(), [0, 64], cu_dev=None) == E_ARG
+    assert _prefill(lib, _cfg(), [0, 64], init=A + 64) == E_ARG  # partial overlap
+    detail = lib.kda_last_error_detail().decode()
+    assert "overlap" in detail
+
+
+def test_prefill_zero_sequences_is_noop(lib):
+    from gated_delta_rule_111_amd import kda as libkda
+    cfg = _cfg()
+    assert lib.kda_prefill(ctypes.byref(cfg), 0, None, None, None, None, None, None, None, None,
+                           None, None, 0, None, None, 0, None) == 0
+
+
+def test_decode_rejects_bad_arguments(lib):
+    cfg = _cfg()
+    p = ctypes.byref(cfg)
+    assert lib.kda_decode(None, 4, A, A, A, A, A, A, None, A, None) == 1
+    assert lib.kda_decode(p, -1, A, A, A, A, A, A, None, A, None) == 1
+    assert lib.kda_decode(p, 4, A, A, A, A, A, None, None, A, None) == 1
+    assert lib.kda_decode(p, 4, A, MIS, A, A, A, A, None, A, None) == 3
+    assert lib.kda_decode(p, 4, A, A, A, A, A, A, A + 2, A, None) == 3  # slots: 4-byte
+    assert lib.kda_decode(p, 4, A, A, A, A, A + 2, A, None, A, None) == 3  # beta: 4-byte
+    c2 = _cfg(d=48)
+    assert lib.kda_decode(ctypes.byref(c2), 4, A, A, A, A, A, A, None, A, None) == 2
+    assert lib.kda_decode(p, 0, None, None, None, None, None, None, None, None, None) == 0
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    from gated_delta_rule_111_amd import kda as libkda
+    monkeypatch.setattr(libkda, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        libkda.load(str(tmp_path / "nope.so"))
