@@ -1,0 +1,328 @@
+"""libkda benchmark: KDA decode seq-steps/s and chunked-prefill tokens/s on
+one MI355X, each with its roofline fraction, and the fp64 oracle timed on the
+host beside them.
+
+    python bench.py [--steps K] [--warmup W] [--prefill-reps R] [--long]
+
+One JSON line is printed.  Its ``value`` is the decode rate on the workload
+256 sequences x 32 heads, dk = dv = 128, bf16 q/k/v, fp32 states resident in
+HBM, chained steps (a "step" advances every sequence by one token through
+one KDA layer, all 32 heads).  ``prefill`` holds the chunked-prefill rate on
+B=1, H=32, T=8192 with snapshots every 1024 tokens (``prefill_long``, with
+--long, the same at T=1,048,576 with snapshots every 65,536).  All inputs are
+seeded synthetic tensors generated on the device before timing starts.
+
+Kernel durations come from HIP events recorded on the stream the kernels are
+launched on (torch's current stream, which the binding passes to the C ABI).
+``--copy-calibration MiB`` instead times a plain device copy of that size;
+run under ``rocprofv3 --pmc FETCH_SIZE`` / ``WRITE_SIZE`` it gives the factor
+that turns those counters into bytes.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/s + decode seq-steps/s; % of MFMA / HBM roofline, 1 GPU"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+
+# Algorithmic work per unit (the bytes a kernel must move and the flops the
+# chunked method must do, independent of how the kernels are written).
+#   decode, per (sequence, head, step): fp32 state read + written
+#   (2 * dk * dv * 4 B) + q, k, v bf16 (3 * 256 B) + g fp32 (512 B)
+#   + beta (4 B) + out fp32 (512 B)
+#   prefill, per (token, head): q, k, v bf16 768 B + g 512 B + beta 4 B +
+#   out fp32 512 B = 1796 B, plus snapshot and final-state bytes per call;
+#   140,757 flop for the chunked form (C = 64 accounting: A, B Gram
+#   triangles, the triangular solve, W and U~, the three state products, B U)
+DECODE_STATE_BYTES = 2 * 128 * 128 * 4
+DECODE_IO_BYTES = 3 * 128 * 2 + 128 * 4 + 4 + 128 * 4
+PREFILL_BYTES_PER_TOKEN_HEAD = 1796
+PREFILL_FLOP_PER_TOKEN_HEAD = 140757
+STATE_BYTES = 128 * 128 * 4
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "decode": os.path.join(ROOT, "gated_delta_rule_111_amd", "csrc", "kda_decode.hip"),
+    "prefill": os.path.join(ROOT, "gated_delta_rule_111_amd", "csrc", "kda_prefill.hip"),
+}
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash(kind: str) -> str:
+    with open(KERNEL_SOURCES[kind], "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kind: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    runs, or None when they were taken on another version of the kernel."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(kind)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256_16") != source_hash(kind) or rec.get("workload") != workload:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:
+        return max(1, os.cpu_count() or 1)
+
+
+# ---------------------------------------------------------------------------
+def bench_decode(args, torch, kda, inputs):
+    w = inputs.DECODE
+    dev = "cuda:0"
+    log(f"[bench] decode: generating {w.decode_steps} x {w.decode_N} x {w.H} tokens")
+    inp = inputs.make_decode(w, device=dev)
+    state = inp.state.clone()
+    out = torch.empty(w.decode_N, w.H, w.dv, dtype=torch.float32, device=dev)
+    nin = inp.q.shape[0]
+
+    def step(i):
+        j = i % nin
+        kda.decode(inp.q[j], inp.k[j], inp.v[j], inp.g[j], inp.beta[j], state, out=out)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = e0.elapsed_time(e1)
+    per_launch_s = gpu_ms / 1e3 / args.steps
+    units = w.decode_N * w.H
+    bytes_per_launch = units * (DECODE_STATE_BYTES + DECODE_IO_BYTES)
+    achieved = bytes_per_launch / per_launch_s / 1e9
+    log(f"[bench] decode: {args.steps} steps wall {wall * 1e3:.1f} ms, "
+        f"events {gpu_ms:.1f} ms, {per_launch_s * 1e6:.1f} us/step, {achieved:.0f} GB/s")
+    res = {
+        "workload": w.name,
+        "seq_steps_per_s": w.decode_N * args.steps / wall,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "kernel_us": per_launch_s * 1e6,
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic("decode", w.name),
+            "kernel": "decode_kernel<128,128,4,bf16,f32>",
+            "bytes_per_launch": bytes_per_launch,
+        },
+    }
+    return res, inp
+
+
+def cpu_decode_baseline(inp, args):
+    import numpy as np
+    import oracle
+    n_seq, n_steps = args.cpu_decode_seqs, args.cpu_decode_steps
+    f = lambda t: t[:n_steps, :n_seq].float().cpu().numpy()
+    st = inp.state[:n_seq].cpu().numpy().astype(np.float64)
+    q, k, v, g, b = f(inp.q), f(inp.k), f(inp.v), f(inp.g), f(inp.beta)
+    threads = cpu_threads()
+    log(f"[bench] cpu oracle: decode {n_seq} seqs x {n_steps} steps on {threads} threads")
+    t0 = time.perf_counter()
+    oracle.decode(q, k, v, g, b, st, nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": round(n_seq * n_steps / dt, 2), "unit": "seq-steps/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"first {n_steps} chained steps of the first {n_seq} of 256 sequences, "
+                      "all 32 heads, fp64 token-by-token"}
+
+
+# ---------------------------------------------------------------------------
+def bench_prefill(torch, kda, inputs, w, reps, warmup):
+    dev = "cuda:0"
+    log(f"[bench] prefill {w.name}: generating inputs")
+    inp = inputs.make_prefill(w, device=dev)
+    T = int(inp.q.shape[0])
+    cu_host = inp.cu_seqlens.cpu().tolist()
+    N = len(cu_host) - 1
+    nsnap = kda.snapshot_count(cu_host, w.snapshot_interval)
+    out = torch.empty(T, w.H, w.dv, dtype=torch.float32, device=dev)
+    fin = torch.empty(N, w.H, w.dk, w.dv, dtype=torch.float32, device=dev)
+    snaps = torch.empty(nsnap, w.H, w.dk, w.dv, dtype=torch.float32, device=dev)
+
+    def call():
+        kda.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens,
+                    initial_state=inp.initial_state, snapshot_interval=w.snapshot_interval,
+                    cu_seqlens_host=cu_host, out=out, final_state=fin, snapshots=snaps)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call = e0.elapsed_time(e1) / 1e3 / reps
+    th = T * w.H
+    nbytes = th * PREFILL_BYTES_PER_TOKEN_HEAD + (nsnap + N) * w.H * STATE_BYTES
+    if inp.initial_state is not None:
+        nbytes += N * w.H * STATE_BYTES
+    flops = th * PREFILL_FLOP_PER_TOKEN_HEAD
+    gbs = nbytes / per_call / 1e9
+    tflops = flops / per_call / 1e12
+    log(f"[bench] prefill {w.name}: {per_call * 1e3:.3f} ms/call, {T / per_call:.3e} tok/s, "
+        f"{gbs:.0f} GB/s, {tflops:.1f} TFLOP/s")
+    res = {
+        "workload": w.name,
+        "value": round(T / (wall / reps), 1),
+        "unit": "tokens/s",
+        "ms_per_call": round(wall * 1e3 / reps, 4),
+        "kernel_ms": round(per_call * 1e3, 4),
+        "reps": reps,
+        "dtype": "bf16 MFMA (hi/lo split operands) + f32 state",
+        "roofline": {
+            "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic("prefill", w.name),
+            "kernel": "prefill_kernel<128,DVT,bf16>",
+            "bytes_per_launch": nbytes,
+        },
+        "mfma": {
+            "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+            "flop_per_launch": flops,
+            "attainable_frac": round(
+                tflops / min(BF16_MFMA_PEAK_TFLOPS, flops / nbytes * HBM_PEAK_GBS / 1e3), 4),
+        },
+    }
+    return res, inp
+
+
+def cpu_prefill_baseline(inp, tokens: int):
+    import oracle
+    T = min(tokens, int(inp.q.shape[0]))
+    f = lambda t: t[:T].float().cpu().numpy()
+    threads = cpu_threads()
+    log(f"[bench] cpu oracle: prefill first {T} tokens on {threads} threads")
+    t0 = time.perf_counter()
+    oracle.prefill(f(inp.q), f(inp.k), f(inp.v), f(inp.g), f(inp.beta), [0, T],
+                   nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": round(T / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"first {T} tokens of the sequence, all heads, fp64 token-by-token "
+                      "(parallel over the heads only)"}
+
+
+# ---------------------------------------------------------------------------
+def copy_calibration(torch, mib: int):
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4,
+                      "launches": 10}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000, help="timed chained decode steps")
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--prefill-reps", type=int, default=20)
+    ap.add_argument("--long", action="store_true", help="also time the 1,048,576-token prefill")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-decode-seqs", type=int, default=64)
+    ap.add_argument("--cpu-decode-steps", type=int, default=100)
+    ap.add_argument("--cpu-prefill-tokens", type=int, default=8192)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE {world}); the KDA layer shards by sequence or head with no "
+              "exchange, so a multi-GPU figure is N times the one-GPU one and is not "
+              "measured here.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible; libkda runs on an MI355X only", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration(torch, args.copy_calibration)
+        return
+
+    from gated_delta_rule_111_amd import inputs, kda
+    kda.load()
+
+    dec, dinp = bench_decode(args, torch, kda, inputs)
+    pre = pre_long = None
+    pinp = None
+    if not args.no_prefill:
+        pre, pinp = bench_prefill(torch, kda, inputs, inputs.PREFILL_8K, args.prefill_reps,
+                                  max(2, args.warmup // 10))
+    if args.long:
+        pre_long, _ = bench_prefill(torch, kda, inputs, inputs.LONG, 3, 1)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_decode_baseline(dinp, args)
+        if pre is not None:
+            pre["cpu_baseline"] = cpu_prefill_baseline(pinp, args.cpu_prefill_tokens)
+
+    line = {
+        "metric": METRIC,
+        "value": round(dec["seq_steps_per_s"], 1),
+        "unit": "seq-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": dec["workload"], "num_seqs": 256, "heads": 32, "dk": 128,
+                   "dv": 128, "in_dtype": "bf16", "state_dtype": "f32", "out_dtype": "f32",
+                   "parallelism": "none (1 GPU)"},
+        "roofline": dec["roofline"],
+        "cpu_baseline": cpu,
+        "decode_kernel_us": round(dec["kernel_us"], 2),
+        "prefill": pre,
+    }
+    if pre_long is not None:
+        line["prefill_long"] = pre_long
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
