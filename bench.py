@@ -166,11 +166,14 @@ def bench_prefill(torch, kda, inputs, w, reps, warmup):
     out = torch.empty(T, w.H, w.dv, dtype=torch.float32, device=dev)
     fin = torch.empty(N, w.H, w.dk, w.dv, dtype=torch.float32, device=dev)
     snaps = torch.empty(nsnap, w.H, w.dk, w.dv, dtype=torch.float32, device=dev)
+    cfg = kda.config(w.H, w.dk, w.dv, inp.q.dtype)
+    ws = torch.empty(kda.workspace_size(cfg, N, T), dtype=torch.uint8, device=dev)
 
     def call():
         kda.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens,
                     initial_state=inp.initial_state, snapshot_interval=w.snapshot_interval,
-                    cu_seqlens_host=cu_host, out=out, final_state=fin, snapshots=snaps)
+                    cu_seqlens_host=cu_host, out=out, final_state=fin, snapshots=snaps,
+                    workspace=ws)
 
     for _ in range(warmup):
         call()
@@ -206,7 +209,7 @@ def bench_prefill(torch, kda, inputs, w, reps, warmup):
             "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic("prefill", w.name),
-            "kernel": "prefill_kernel<128,DVT,bf16>",
+            "kernel": "plan + prep_kernel<bf16> + scan_kernel<bf16> (whole call)",
             "bytes_per_launch": nbytes,
         },
         "mfma": {

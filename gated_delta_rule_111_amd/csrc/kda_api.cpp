@@ -120,11 +120,14 @@ kda_status kda_prefill(const kda_config* cfg, int32_t num_seqs, const int32_t* c
     if (num_seqs == 0) return ok();
     if (!cu_host) return fail(KDA_ERR_INVALID_ARG, "cu_seqlens_host is NULL");
     if (cu_host[0] != 0) return fail(KDA_ERR_INVALID_ARG, "cu_seqlens[0] must be 0");
-    int32_t max_len = 0;
+    if (cfg->num_heads > 65535)
+        return fail(KDA_ERR_UNSUPPORTED, "num_heads %d exceeds 65535", cfg->num_heads);
+    const int64_t crow = kda::prefill_chunk_rows();
+    int64_t total_chunks = 0;
     for (int32_t b = 0; b < num_seqs; ++b) {
         if (cu_host[b + 1] < cu_host[b])
             return fail(KDA_ERR_INVALID_ARG, "cu_seqlens decreases at index %d", b + 1);
-        if (cu_host[b + 1] - cu_host[b] > max_len) max_len = cu_host[b + 1] - cu_host[b];
+        total_chunks += (cu_host[b + 1] - cu_host[b] + crow - 1) / crow;
     }
     const int64_t T = cu_host[num_seqs];
     if (snapshot_interval < 0 || snapshot_interval % 64 != 0)
@@ -147,10 +150,6 @@ kda_status kda_prefill(const kda_config* cfg, int32_t num_seqs, const int32_t* c
     };
     st = check_ptrs(ptrs, (int)(sizeof(ptrs) / sizeof(ptrs[0])));
     if (st != KDA_OK) return st;
-    const size_t need = kda::prefill_workspace_bytes(cfg->dk, cfg->dv, cfg->num_heads, num_seqs, T);
-    if (workspace_bytes < need || (need > 0 && !workspace))
-        return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required",
-                    workspace_bytes, need);
     if (initial_state && initial_state != final_state) {
         // final_state may alias initial_state exactly; partial overlap is not allowed
         const size_t bytes = (size_t)num_seqs * cfg->num_heads * cfg->dk * cfg->dv * sizeof(float);
@@ -159,6 +158,10 @@ kda_status kda_prefill(const kda_config* cfg, int32_t num_seqs, const int32_t* c
         if (a < b + bytes && b < a + bytes)
             return fail(KDA_ERR_INVALID_ARG, "final_state partially overlaps initial_state");
     }
+    const size_t need = kda::prefill_workspace_bytes(cfg->dk, cfg->dv, cfg->num_heads, num_seqs, T);
+    if (workspace_bytes < need || (need > 0 && !workspace))
+        return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required",
+                    workspace_bytes, need);
 
     kda::PrefillArgs a{};
     a.dk = cfg->dk;
@@ -168,7 +171,7 @@ kda_status kda_prefill(const kda_config* cfg, int32_t num_seqs, const int32_t* c
     a.in_bf16 = cfg->in_dtype == KDA_BF16;
     a.out_bf16 = cfg->out_dtype == KDA_BF16;
     a.total_tokens = T;
-    a.max_len = max_len;
+    a.total_chunks = total_chunks;
     a.cu_dev = cu_dev;
     a.q = q;
     a.k = k;

@@ -25,7 +25,7 @@ struct PrefillArgs {
     int dk, dv, H, num_seqs;
     bool in_bf16, out_bf16;
     int64_t total_tokens;
-    int32_t max_len;              // longest sequence (host-side planning)
+    int64_t total_chunks;         // sum over sequences of ceil(L_b / chunk rows)
     const int32_t* cu_dev;        // [num_seqs + 1] device offsets
     const void *q, *k, *v;
     const float *g, *beta;
@@ -43,5 +43,6 @@ struct PrefillArgs {
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);
 size_t prefill_workspace_bytes(int dk, int dv, int H, int num_seqs, int64_t total_tokens);
+int prefill_chunk_rows();  // tokens per chunk; snapshot intervals are multiples of 64
 
 }  // namespace kda

@@ -13,39 +13,41 @@
 // "Day-0 vLLM support for Kimi K3", section "Kimi K3's architecture, and how
 // vLLM serves it": state snapshots at block boundaries feed a prefix cache.
 //
-// Chunked form (derived from the recurrence; C = 32 rows per chunk, G = the
-// inclusive cumulative sum of g inside the chunk, S = state at chunk start):
+// Chunked form (C = 64 rows per chunk; G = inclusive cumulative sum of g
+// inside the chunk, G_C its last row; S = state at the chunk start):
 //   A_ts = b_t sum_c k_t[c] k_s[c] e^{G_t[c]-G_s[c]}   (s < t)
 //   B_ts =     sum_c q_t[c] k_s[c] e^{G_t[c]-G_s[c]}   (s <= t)
-//   T    = (I + A)^-1                                   (unit lower triangular)
-//   W    = T (b . K . e^G),   U~ = T (b . V)           (the UT / WY transform)
-//   U    = U~ - W S                                     (delta-rule targets)
+//   T    = (I + A)^-1,   TB = T Diag(b)                 (the UT transform)
+//   U    = TB (V - (K . e^G) S)                         (delta-rule targets)
 //   O    = scale ((Q . e^G) S + B U)
 //   S'   = Diag(e^{G_C}) S + (K . e^{G_C - G})^T U
-// The Gram matrices A, B are contractions over channels with a per-channel
-// decay between rows t and s; they are factorised per 16-row sub-chunk with
-// a reference r so that both factors e^{G_t - r}, e^{r - G_s} stay within
-// fp32 range (off-diagonal blocks: r = G at the end of the earlier
-// sub-chunk, both factors <= 1; diagonal blocks: r = G at the sub-chunk's
-// middle row, factors within e^{+-80}).  When a sub-chunk's decay span is
-// too large for that, its diagonal blocks are evaluated pairwise instead.
+// Substituting the recurrence into itself inside a chunk gives
+// (I + A) U = Diag(b) (V - (K . e^G) S); the rest follows by unrolling.
 //
-// Precision: MFMA v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  Operands
-// that are not exact bf16 values are split into hi + lo bf16 and multiplied
-// in two or three passes (hi*hi + hi*lo + lo*hi), which keeps ~16 bits; the
-// KK^T Gram, b.K.e^G and W tolerate a single bf16 pass.  The state S is kept
-// and carried in fp32 registers; snapshots are exact copies of it.
+// Three launches on the caller's stream:
+//   plan  -- one workgroup: per-sequence offsets of chunks and snapshots;
+//   prep  -- one workgroup per (chunk, head), all chunks in parallel: the
+//            Gram matrices A and B on MFMA, T by block forward substitution,
+//            then TB and B written to the workspace as hi/lo bf16 MFMA
+//            operands (everything here is independent of the state);
+//   scan  -- one workgroup per (sequence, head, 16 value columns), walking
+//            the sequence chunk by chunk with the fp32 state in registers.
+//            Wave w owns 32 state rows.  Per chunk each wave builds its
+//            decay-scaled operands from the cumulative log-decay, forms its
+//            partial (K e^G) S and (Q e^G) S, and the four waves exchange
+//            them through LDS with one barrier; then every wave forms U,
+//            its rows of O and its rows of the next state.
 //
-// Work decomposition: one workgroup (4 wavefronts) per (sequence, head,
-// dv-tile of DVT columns).  Value columns evolve independently, so dv-tiles
-// need no communication; each recomputes the dv-independent chunk quantities
-// (A, B, T, W).  Inside the workgroup the S-dependent products are split over
-// waves either by state rows (small DVT; partial sums combined through LDS)
-// or by state columns (large DVT).  The contraction over state rows is always
-// evaluated as one MFMA chain per 32-row K-step, started from zero, summed in
-// K-step order, so results do not depend on DVT or on the wave split; with
-// chunks aligned to each sequence start this makes snapshot resumption
-// bit-exact.
+// Precision: v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  Operands that
+// are not exact bf16 values are split into hi + lo bf16 and multiplied in
+// three passes (hi*hi + hi*lo + lo*hi, ~16 bits); the K K^T Gram and the
+// (K e^G) S product use one bf16 rounding of the decay-scaled keys.  State,
+// snapshots, outputs and every accumulation are fp32.
+//
+// Determinism: every reduction has a fixed order that depends neither on the
+// number of value tiles nor on where a sequence sits in the packed batch,
+// and chunks restart at every sequence start, so resuming from a snapshot
+// reproduces the uninterrupted run bit for bit.
 #include "kda_common.h"
 #include "kda_internal.h"
 
@@ -55,52 +57,35 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int C = 32;                 // chunk rows
-constexpr int NT = 256;               // threads per workgroup (4 waves)
-constexpr float SPAN_LIMIT = 80.0f;   // |exponent| bound for the diagonal-block factors
-constexpr int AP = 33;                // padded row stride of the fp32 32x32 tiles
+constexpr int C = 64;                // chunk rows
+constexpr int NT = 256;              // threads per workgroup (4 waves)
+constexpr int DKP = 128;             // state rows, zero-padded above dk
+constexpr int SL = 32;               // state rows per wave
+constexpr float SPAN_LIMIT = 80.0f;  // |exponent| bound for the diagonal Gram factors
+constexpr int PLANE = 512;           // uint4 per operand plane (4 row tiles x 2 K-steps x 64 lanes)
+constexpr int CHUNK_OPS = 4 * PLANE; // TB hi, TB lo, B hi, B lo
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8_t& a, const bf16x8_t& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Workgroup barrier that waits only for this wave's LDS traffic.  The
+// generic barrier also drains outstanding global loads and stores, which
+// would stall every prefetch issued ahead of it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+// LDS writes of this wave are complete (and visible to its other lanes).
+__device__ __forceinline__ void lds_wave_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 __device__ __forceinline__ uint16_t bfb(float x) { return f32_to_bf16_bits(x); }
-__device__ __forceinline__ float bff(uint16_t b) { return bf16_bits_to_f32(b); }
+__device__ __forceinline__ float bff(uint32_t b) { return bf16_bits_to_f32(b); }
+__device__ __forceinline__ float ex(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
 
 // x = hi + lo with hi = bf16(x), lo = bf16(x - hi) (x - hi is exact in fp32)
 __device__ __forceinline__ void split(float x, uint16_t& hi, uint16_t& lo) {
     hi = bfb(x);
     lo = bfb(x - bff(hi));
-}
-
-// 8 consecutive bf16 (16 bytes) as an MFMA operand
-__device__ __forceinline__ bf16x8_t ld8(const uint16_t* p) {
-    return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p));
-}
-// operand in the permuted K order used by the state products: elements 0..3
-// are p[0..3], elements 4..7 are p[16..19]
-__device__ __forceinline__ bf16x8_t ld4x2(const uint16_t* p) {
-    const uint2 a = *reinterpret_cast<const uint2*>(p);
-    const uint2 b = *reinterpret_cast<const uint2*>(p + 16);
-    return __builtin_bit_cast(bf16x8_t, make_uint4(a.x, a.y, b.x, b.y));
-}
-// two accumulator tiles (rows 4g..4g+3 and 16+4g..16+4g+3 of a 32-row block)
-// packed as one operand in the same permuted K order, hi and lo parts
-__device__ __forceinline__ void pack_split(const f32x4& x0, const f32x4& x1, bf16x8_t& hi,
-                                           bf16x8_t& lo) {
-    uint16_t h[8], l[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        split(x0[e], h[e], l[e]);
-        split(x1[e], h[4 + e], l[4 + e]);
-    }
-    uint4 uh, ul;
-    uh.x = h[0] | ((uint32_t)h[1] << 16); uh.y = h[2] | ((uint32_t)h[3] << 16);
-    uh.z = h[4] | ((uint32_t)h[5] << 16); uh.w = h[6] | ((uint32_t)h[7] << 16);
-    ul.x = l[0] | ((uint32_t)l[1] << 16); ul.y = l[2] | ((uint32_t)l[3] << 16);
-    ul.z = l[4] | ((uint32_t)l[5] << 16); ul.w = l[6] | ((uint32_t)l[7] << 16);
-    hi = __builtin_bit_cast(bf16x8_t, uh);
-    lo = __builtin_bit_cast(bf16x8_t, ul);
 }
 
 __device__ __forceinline__ uint4 pack8(const uint16_t (&x)[8]) {
@@ -109,768 +94,841 @@ __device__ __forceinline__ uint4 pack8(const uint16_t (&x)[8]) {
     u.z = x[4] | ((uint32_t)x[5] << 16); u.w = x[6] | ((uint32_t)x[7] << 16);
     return u;
 }
+__device__ __forceinline__ bf16x8_t as_op(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
 
-__device__ __forceinline__ float ex(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+// Two accumulator tiles (row blocks 0 and 1 of a 32-row K-step) as one MFMA
+// operand: elements 0..3 come from tile 0, 4..7 from tile 1, split hi / lo.
+__device__ __forceinline__ void pack_split(const f32x4& x0, const f32x4& x1, bf16x8_t& hi,
+                                           bf16x8_t& lo) {
+    uint16_t h[8], l[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        split(x0[e], h[e], l[e]);
+        split(x1[e], h[4 + e], l[4 + e]);
+    }
+    hi = as_op(pack8(h));
+    lo = as_op(pack8(l));
+}
+
+// Row orders inside a chunk.  An accumulator tile holds rows 4*(lane/16)+e;
+// two tiles packed as one operand give a lane K positions 4*(lane/16)+e of
+// each.  Numbering the chunk's tokens and the wave's state rows so that
+// those 8 positions are 8 consecutive tokens (channels) lets every operand
+// that comes from memory be one contiguous 8-element vector.
+//   token of row r in token tile mt (mt = 0..3, r = 0..15):
+__device__ __forceinline__ int tok_of(int mt, int r) {
+    return ((mt >> 1) << 5) + ((r >> 2) << 3) + ((mt & 1) << 2) + (r & 3);
+}
+//   state row (within the wave's 32) of row r in row tile m (m = 0, 1):
+__device__ __forceinline__ int chan_of(int m, int r) { return ((r >> 2) << 3) + (m << 2) + (r & 3); }
 
 // ---------------------------------------------------------------------------
-// Compile-time geometry
+// Input access (bf16 or fp32 q, k, v)
 // ---------------------------------------------------------------------------
-template <int DK, int DVT, typename TIn>
-struct Geo {
-    static constexpr int DKP = DK < 32 ? 32 : DK;      // channels padded to one K-step
-    static constexpr int NKS = DKP / 32;               // K-steps over state rows
-    static constexpr int RW = DVT >= 64 ? 1 : NKS;     // waves splitting state rows
-    static constexpr int CWr = 4 / RW;
-    static constexpr int CW = CWr < DVT / 16 ? CWr : DVT / 16;  // waves splitting columns
-    static constexpr int NSW = RW * CW;                // waves holding state
-    static constexpr int KSP = NKS / RW;               // K-steps per state wave
-    static constexpr int JT = DVT / CW / 16;           // 16-column tiles per state wave
-    static constexpr int NJ = DVT / 16;                // 16-column tiles per workgroup
-    static constexpr bool F32IN = sizeof(TIn) == 4;
-    static constexpr int VPL = F32IN ? 2 : 1;          // V planes (fp32 inputs are split)
-    static constexpr int VEC = 16 / sizeof(TIn);       // elements per 16-byte vector
-    static_assert(NSW <= 4 && NSW >= 1 && JT >= 1, "wave geometry");
-    static_assert(DKP * 2 <= NT, "one prep thread per 8 channels x 2 rows");
+template <typename TIn> struct In;
+template <> struct In<bf16_t> {
+    using V8 = uint4;  // 8 values
+    __device__ __forceinline__ static V8 load8(const void* base, int64_t idx) {
+        return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
+    }
+    __device__ __forceinline__ static V8 zero8() { return make_uint4(0, 0, 0, 0); }
+    __device__ __forceinline__ static void f32x8(const V8& u, float (&x)[8]) {
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x[2 * j] = bff(w[j] & 0xffffu);
+            x[2 * j + 1] = bff(w[j] >> 16);
+        }
+    }
+    using V1 = uint32_t;
+    __device__ __forceinline__ static V1 load1(const void* base, int64_t idx) {
+        return static_cast<const uint16_t*>(base)[idx];
+    }
+    __device__ __forceinline__ static float f32(V1 x) { return bff(x); }
+};
+template <> struct In<float> {
+    struct V8 { float4 a, b; };
+    __device__ __forceinline__ static V8 load8(const void* base, int64_t idx) {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
+        return V8{p[0], p[1]};
+    }
+    __device__ __forceinline__ static V8 zero8() {
+        return V8{make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)};
+    }
+    __device__ __forceinline__ static void f32x8(const V8& u, float (&x)[8]) {
+        x[0] = u.a.x; x[1] = u.a.y; x[2] = u.a.z; x[3] = u.a.w;
+        x[4] = u.b.x; x[5] = u.b.y; x[6] = u.b.z; x[7] = u.b.w;
+    }
+    using V1 = float;
+    __device__ __forceinline__ static V1 load1(const void* base, int64_t idx) {
+        return static_cast<const float*>(base)[idx];
+    }
+    __device__ __forceinline__ static float f32(V1 x) { return x; }
 };
 
-template <int DK, int DVT, typename TIn>
-struct Smem {
-    using G_ = Geo<DK, DVT, TIn>;
-    static constexpr int DKP = G_::DKP;
-    float G[C][DKP];           // cumulative log-decay inside the chunk
-    float decay[DKP];          // e^{G_C}
-    float beta[C];
+// ---------------------------------------------------------------------------
+// plan: chunk_start[b] = sum_{b' < b} ceil(L_b' / C), snap_base[b] =
+// sum_{b' < b} floor(L_b' / interval), for b = 0 .. num_seqs.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(NT) void plan_kernel(const int32_t* __restrict__ cu, int num_seqs,
+                                                  int interval, int32_t* __restrict__ chunk_start,
+                                                  int32_t* __restrict__ snap_base) {
+    __shared__ int32_t wtot[2][4];
+    __shared__ int32_t carry[2];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid == 0) carry[0] = carry[1] = 0;
+    __syncthreads();
+    for (int base = 0; base <= num_seqs; base += NT) {
+        const int b = base + tid;
+        int vc = 0, vs = 0;
+        if (b < num_seqs) {
+            const int L = cu[b + 1] - cu[b];
+            vc = (L + C - 1) / C;
+            vs = interval > 0 ? L / interval : 0;
+        }
+        int ic = vc, is = vs;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int yc = __shfl_up(ic, off, 64), ys = __shfl_up(is, off, 64);
+            if (lane >= off) { ic += yc; is += ys; }
+        }
+        if (lane == 63) { wtot[0][wave] = ic; wtot[1][wave] = is; }
+        __syncthreads();
+        int pc = carry[0], ps = carry[1];
+        for (int w = 0; w < wave; ++w) { pc += wtot[0][w]; ps += wtot[1][w]; }
+        if (b <= num_seqs) {
+            chunk_start[b] = pc + ic - vc;
+            snap_base[b] = ps + is - vs;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            for (int w = 0; w < 4; ++w) { carry[0] += wtot[0][w]; carry[1] += wtot[1][w]; }
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// prep: per (chunk, head) the state-independent chunk quantities.
+// ---------------------------------------------------------------------------
+struct PrepSmem {
     union {
-        struct {               // Gram operands (dead after the Gram products)
-            uint16_t XKd[C][DKP];        // k_t e^{G_t - r_diag}          hi
-            uint16_t XK1[16][DKP];       // k_t e^{G_t - G_15}, t >= 16   hi
-            uint16_t XQd[2][C][DKP];     // q_t e^{G_t - r_diag}          hi, lo
-            uint16_t XQ1[2][16][DKP];    // q_t e^{G_t - G_15}, t >= 16   hi, lo
-            uint16_t YKd[2][C][DKP];     // k_s e^{r_diag - G_s}          hi, lo
-            uint16_t YK1[2][16][DKP];    // k_s e^{G_15 - G_s}, s < 16    hi, lo
-        } gram;
-        struct {               // state-phase buffers
-            uint16_t W[C][DKP];                               // W (bf16)
-            f32x4 PW[G_::RW > 1 ? G_::NKS : 1][2][G_::NJ][64];  // per-K-step partials of W S
-            f32x4 PQ[G_::RW > 1 ? G_::NKS : 1][2][G_::NJ][64];  // ... of (Q e^G) S
-        } st;
+        float G[C][DKP + 4];  // cumulative log-decay (dead after the Gram matrices)
+        float T[C][C + 4];    // (I + A)^-1, lower block triangle
     } u;
-    uint16_t KgT[DKP][C];      // (b_s k_s e^{G_s})^T                       hi
-    uint16_t Qg[2][C][DKP];    // q_t e^{G_t}                               hi, lo
-    uint16_t KdT[2][DKP][C];   // (k_t e^{G_C - G_t})^T                     hi, lo
-    uint16_t VT[G_::VPL][DVT][C];  // V^T                                   (hi, lo)
-    float A[C][AP];
-    float B[C][AP];
-    float Tf[C][AP];
-    float M1[16][17];
-    uint16_t Bhl[2][C][C];
-    uint16_t Thl[2][C][C];
-    uint16_t TBhl[2][C][C];
-    int extreme;
+    float A[C][C + 1];
+    float B[C][C + 1];
+    float M[3][16][17];
+    float beta[C];
 };
 
-struct Params {
+struct PrepParams {
+    const void* q;
+    const void* k;
+    const float* g;
+    const float* beta;
+    const int32_t* cu;
+    const int32_t* chunk_start;
+    uint4* ops;  // [chunks][H][CHUNK_OPS]
+    int H, dk, num_seqs;
+};
+
+template <typename TIn>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prep_kernel(PrepParams p) {
+    using IO = In<TIn>;
+    __shared__ PrepSmem sm;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int g4 = lane >> 4, i16 = lane & 15;
+    const int gc = blockIdx.x, h = blockIdx.y;
+
+    // sequence of this chunk: the last b with chunk_start[b] <= gc
+    int lo = 0, hi = p.num_seqs;  // invariant: chunk_start[lo] <= gc < chunk_start[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (p.chunk_start[mid] <= gc) lo = mid; else hi = mid;
+    }
+    const int b = lo;
+    const int ci = gc - p.chunk_start[b];
+    const int64_t row0 = (int64_t)p.cu[b] + (int64_t)ci * C;
+    const int len = p.cu[b + 1] - p.cu[b];
+    const int n = min(C, len - ci * C);
+    const int dk = p.dk;
+
+    // ---- cumulative log-decay per channel (rows past n count as g = 0) ----
+    {
+        const int c = tid & 127, half = tid >> 7;
+        float run = 0.f;
+#pragma unroll 8
+        for (int r = 0; r < 32; ++r) {
+            const int t = half * 32 + r;
+            run += (t < n && c < dk) ? p.g[((row0 + t) * p.H + h) * (int64_t)dk + c] : 0.f;
+            sm.u.G[t][c] = run;
+        }
+        if (tid < C) sm.beta[tid] = tid < n ? p.beta[(row0 + tid) * p.H + h] : 0.f;
+        __syncthreads();
+        if (half == 1) {
+            const float base = sm.u.G[31][c];
+#pragma unroll 8
+            for (int r = 32; r < 64; ++r) sm.u.G[r][c] += base;
+        }
+        __syncthreads();
+    }
+
+    // ---- Gram matrices: wave w computes row tile w (rows 16w .. 16w+15) ----
+    // Off-diagonal blocks (column tile ts < w) use the reference r = G at row
+    // 16w - 1, so both factors e^{G_t - r} and e^{r - G_s} are <= 1.  The
+    // diagonal block uses r = G at row 16w + 7, keeping both factors within
+    // e^{+-span/2} of the block; spans beyond SPAN_LIMIT take the pairwise path.
+    int extreme = 0;
+    {
+        f32x4 accA[4], accB[4];
+#pragma unroll
+        for (int ts = 0; ts < 4; ++ts) {
+            accA[ts] = f32x4{0.f, 0.f, 0.f, 0.f};
+            accB[ts] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        const int t = 16 * w + i16;
+#pragma unroll 1
+        for (int ks = 0; ks < 4; ++ks) {
+            const int c0 = 32 * ks + 8 * g4;
+            const bool cok = c0 < dk;
+            float kt[8], qt[8];
+            {
+                const int64_t idx = ((row0 + t) * p.H + h) * (int64_t)dk + c0;
+                const bool ok = cok && t < n;
+                IO::f32x8(ok ? IO::load8(p.k, idx) : IO::zero8(), kt);
+                IO::f32x8(ok ? IO::load8(p.q, idx) : IO::zero8(), qt);
+            }
+            float Gt[8], rw[8], rm[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                Gt[e] = sm.u.G[t][c0 + e];
+                rw[e] = sm.u.G[w > 0 ? 16 * w - 1 : 0][c0 + e];
+                rm[e] = sm.u.G[16 * w + 7][c0 + e];
+                extreme |= (sm.u.G[16 * w][c0 + e] - rm[e] > SPAN_LIMIT) |
+                           (rm[e] - sm.u.G[16 * w + 15][c0 + e] > SPAN_LIMIT);
+            }
+            // diagonal block
+            {
+                uint16_t xk[8], xqh[8], xql[8], yh[8], yl[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float xd = ex(Gt[e] - rm[e]);
+                    const float yd = ex(rm[e] - Gt[e]);
+                    xk[e] = bfb(kt[e] * xd);
+                    split(qt[e] * xd, xqh[e], xql[e]);
+                    split(kt[e] * yd, yh[e], yl[e]);
+                }
+                const bf16x8_t XK = as_op(pack8(xk)), XQH = as_op(pack8(xqh)),
+                               XQL = as_op(pack8(xql)), YH = as_op(pack8(yh)),
+                               YL = as_op(pack8(yl));
+#pragma unroll
+                for (int ts = 0; ts < 4; ++ts) {
+                    if (ts == w) {
+                        accA[ts] = mfma(XK, YH, accA[ts]);
+                        accB[ts] = mfma(XQH, YH, accB[ts]);
+                        accB[ts] = mfma(XQH, YL, accB[ts]);
+                        accB[ts] = mfma(XQL, YH, accB[ts]);
+                    }
+                }
+            }
+            // off-diagonal blocks
+            if (w > 0) {
+                uint16_t xk[8], xqh[8], xql[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float xo = ex(Gt[e] - rw[e]);
+                    xk[e] = bfb(kt[e] * xo);
+                    split(qt[e] * xo, xqh[e], xql[e]);
+                }
+                const bf16x8_t XK = as_op(pack8(xk)), XQH = as_op(pack8(xqh)),
+                               XQL = as_op(pack8(xql));
+#pragma unroll
+                for (int ts = 0; ts < 3; ++ts) {
+                    if (ts < w) {
+                        const int s = 16 * ts + i16;
+                        float ksv[8];
+                        const int64_t idx = ((row0 + s) * p.H + h) * (int64_t)dk + c0;
+                        IO::f32x8((cok && s < n) ? IO::load8(p.k, idx) : IO::zero8(), ksv);
+                        uint16_t yh[8], yl[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            split(ksv[e] * ex(rw[e] - sm.u.G[s][c0 + e]), yh[e], yl[e]);
+                        const bf16x8_t YH = as_op(pack8(yh)), YL = as_op(pack8(yl));
+                        accA[ts] = mfma(XK, YH, accA[ts]);
+                        accB[ts] = mfma(XQH, YH, accB[ts]);
+                        accB[ts] = mfma(XQH, YL, accB[ts]);
+                        accB[ts] = mfma(XQL, YH, accB[ts]);
+                    }
+                }
+            }
+        }
+        // accumulator (row 4*g4+e, column i16) of block (w, ts); masked entries
+        // are selected away, never multiplied (they may hold inf)
+#pragma unroll
+        for (int ts = 0; ts < 4; ++ts)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int tr = 16 * w + 4 * g4 + e, sc = 16 * ts + i16;
+                sm.A[tr][sc] = (sc < tr) ? accA[ts][e] * sm.beta[tr] : 0.f;
+                sm.B[tr][sc] = (sc <= tr) ? accB[ts][e] : 0.f;
+            }
+    }
+    const int any_extreme = __syncthreads_or(extreme);
+
+    if (any_extreme) {
+        // a diagonal block spans more decay than fp32 factors can carry:
+        // evaluate the four diagonal blocks pair by pair
+        for (int idx = tid; idx < 4 * 256; idx += NT) {
+            const int blk = idx >> 8, tl = (idx >> 4) & 15, sl = idx & 15;
+            if (sl > tl) continue;
+            const int t = 16 * blk + tl, s = 16 * blk + sl;
+            float sa = 0.f, sb = 0.f;
+            if (t < n) {
+                const int64_t bt = ((row0 + t) * p.H + h) * (int64_t)dk;
+                const int64_t bs = ((row0 + s) * p.H + h) * (int64_t)dk;
+                for (int c = 0; c < dk; ++c) {
+                    const float kt = IO::f32(IO::load1(p.k, bt + c));
+                    const float kv = IO::f32(IO::load1(p.k, bs + c));
+                    const float qt = IO::f32(IO::load1(p.q, bt + c));
+                    const float e = ex(sm.u.G[t][c] - sm.u.G[s][c]);
+                    sa = fmaf(kt * kv, e, sa);
+                    sb = fmaf(qt * kv, e, sb);
+                }
+            }
+            sm.A[t][s] = (s < t) ? sa * sm.beta[t] : 0.f;
+            sm.B[t][s] = sb;
+        }
+        __syncthreads();
+    }
+
+    // ---- T = (I + A)^-1 by block forward substitution (G is dead now) ----
+    if (lane < 16) {
+        // diagonal block w, column j = lane
+        const int bo = 16 * w, j = lane;
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float acc = 0.f;
+#pragma unroll
+            for (int m = 0; m < r; ++m) acc = fmaf(sm.A[bo + r][bo + m], x[m], acc);
+            x[r] = (r == j) ? 1.f : -acc;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sm.u.T[bo + r][bo + j] = x[r];
+    }
+    __syncthreads();
+    {
+        const int r = tid >> 4, cc = tid & 15;
+#pragma unroll
+        for (int d = 1; d < 4; ++d) {
+            // blocks (I, J = I - d): M = sum_{K=J}^{I-1} A_IK T_KJ ; T_IJ = -T_II M
+            for (int I = d; I < 4; ++I) {
+                const int J = I - d;
+                float acc = 0.f;
+                for (int K = J; K < I; ++K)
+#pragma unroll
+                    for (int m = 0; m < 16; ++m)
+                        acc = fmaf(sm.A[16 * I + r][16 * K + m], sm.u.T[16 * K + m][16 * J + cc], acc);
+                sm.M[I - d][r][cc] = acc;
+            }
+            __syncthreads();
+            for (int I = d; I < 4; ++I) {
+                const int J = I - d;
+                float acc = 0.f;
+#pragma unroll
+                for (int m = 0; m < 16; ++m)
+                    acc = fmaf(sm.u.T[16 * I + r][16 * I + m], sm.M[I - d][m][cc], acc);
+                sm.u.T[16 * I + r][16 * J + cc] = -acc;
+            }
+            __syncthreads();
+        }
+    }
+
+    // ---- TB = T Diag(beta) and B as hi/lo MFMA operands in scan order ----
+    uint4* __restrict__ dst = p.ops + ((int64_t)gc * p.H + h) * CHUNK_OPS;
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+        const int idx = tid + NT * rr;           // 0 .. 511
+        const int mt = idx >> 7, ks = (idx >> 6) & 1, ln = idx & 63;
+        const int t = tok_of(mt, ln & 15);
+        const int s0 = 32 * ks + 8 * (ln >> 4);
+        uint16_t th[8], tl[8], bh[8], bl[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int s = s0 + e;
+            const float tb = (s <= t) ? sm.u.T[t][s] * sm.beta[s] : 0.f;
+            split(tb, th[e], tl[e]);
+            split(sm.B[t][s], bh[e], bl[e]);
+        }
+        dst[0 * PLANE + idx] = pack8(th);
+        dst[1 * PLANE + idx] = pack8(tl);
+        dst[2 * PLANE + idx] = pack8(bh);
+        dst[3 * PLANE + idx] = pack8(bl);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// scan: per (sequence, head, 16 value columns) the recurrence over chunks.
+// ---------------------------------------------------------------------------
+// LDS of the scan workgroup.  Staging areas are private to a wave and reused
+// every chunk; the exchange area and TB alternate between two parities so
+// that one barrier per chunk suffices.
+template <typename TIn>
+struct ScanSmem {
+    static constexpr bool KSTAGE = sizeof(TIn) == 2;  // bf16 keys are staged for the transpose
+    float G[4][C][SL + 4];                      // per wave: cumulative log-decay of its 32 rows
+    uint16_t K[KSTAGE ? 4 : 1][C][SL + 8];      // per wave: its 32 key channels (bf16)
+    struct Ex { f32x4 X[4][64]; f32x4 P[4][64]; } ex[2][4];  // partial (K e^G) S, (Q e^G) S
+    uint4 tb[2][2 * PLANE];                     // TB hi, lo of the chunk
+};
+
+struct ScanParams {
     const void* q;
     const void* k;
     const void* v;
     const float* g;
-    const float* beta;
     const int32_t* cu;
+    const int32_t* chunk_start;
+    const int32_t* snap_base;
+    const uint4* ops;
     const float* init;
     void* out;
     float* final_state;
     float* snapshots;
-    int32_t interval;
-    int H;
-    int num_seqs;
-    int ntiles;
-    int nwg;
-    float scale;
+    int interval;
+    int H, dk, dv;
+    int ntiles, nwg;
     int out_bf16;
+    float scale;
 };
 
-// Prefetch registers of one chunk for one prep thread: 2 rows x 8 channels of
-// g, k, q, the two betas, and this thread's share of V.
-template <int DK, int DVT, typename TIn>
-struct Prefetch {
-    using G_ = Geo<DK, DVT, TIn>;
-    static constexpr int VV = C * DVT / G_::VEC;                 // 16-byte V vectors per chunk
-    static constexpr int VPT = (VV + NT - 1) / NT;              // per thread
-    float4 g[2][2];
-    uint4 k[2][sizeof(TIn) / 2];   // 8 elements = 16 B (bf16) or 32 B (fp32)
-    uint4 q[2][sizeof(TIn) / 2];
-    float b[2];
-    uint4 v[VPT];
+// One chunk's inputs for one lane, loaded a chunk ahead.
+template <typename TIn>
+struct ScanPrefetch {
+    using IO = In<TIn>;
+    uint4 bo[2][2];                // B rows of this wave's token tile: [ks][hi, lo]
+    float4 g[8];                   // g of tokens 8*(lane/8)+r, channels 4*(lane%8)..+3
+    typename IO::V8 ka[4];         // k at (tok_of(mt, lane%16), channels 8*(lane/16)..+7)
+    typename IO::V8 qa[4];         // q at the same positions
+    typename IO::V1 v[4][4];       // v at (tok_of(mt, 4*(lane/16)+e), column j)
 };
 
-template <int DK, int DVT, typename TIn>
-__device__ __forceinline__ void load_chunk(Prefetch<DK, DVT, TIn>& pf, const Params& p, int64_t row0,
-                                           int n, int h, int tile, int tid) {
-    using G_ = Geo<DK, DVT, TIn>;
-    const int cg = tid >> 4, tb = tid & 15;
-    const int c0 = cg * 8;
-    const bool chan_ok = c0 < DK;
-    const TIn* __restrict__ kp = static_cast<const TIn*>(p.k);
-    const TIn* __restrict__ qp = static_cast<const TIn*>(p.q);
+template <typename TIn>
+__device__ __forceinline__ void scan_load(ScanPrefetch<TIn>& pf, const ScanParams& p, int64_t gc,
+                                          int64_t row0, int n, int h, int j, int w, int lane) {
+    using IO = In<TIn>;
+    const int g4 = lane >> 4, i16 = lane & 15;
+    const int dk = p.dk;
+    const uint4* __restrict__ blk = p.ops + (gc * p.H + h) * CHUNK_OPS;
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int t = 2 * tb + r;
-        const bool ok = chan_ok && t < n;
-        const int64_t base = ((row0 + t) * p.H + h) * (int64_t)DK + c0;
-        if (ok) {
-            pf.g[r][0] = *reinterpret_cast<const float4*>(p.g + base);
-            pf.g[r][1] = *reinterpret_cast<const float4*>(p.g + base + 4);
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int i = 0; i < (int)(sizeof(TIn) / 2); ++i) {
-                pf.k[r][i] = *reinterpret_cast<const uint4*>(kp + base + i * G_::VEC);
-                pf.q[r][i] = *reinterpret_cast<const uint4*>(qp + base + i * G_::VEC);
-            }
-        } else {
-            pf.g[r][0] = pf.g[r][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int pl = 0; pl < 2; ++pl)
+            pf.bo[ks][pl] = blk[(2 + pl) * PLANE + (w * 2 + ks) * 64 + lane];
+    {
+        const int cg = SL * w + 4 * (lane & 7), tq = 8 * (lane >> 3);
 #pragma unroll
-            for (int i = 0; i < (int)(sizeof(TIn) / 2); ++i) {
-                pf.k[r][i] = make_uint4(0, 0, 0, 0);
-                pf.q[r][i] = make_uint4(0, 0, 0, 0);
-            }
+        for (int r = 0; r < 8; ++r) {
+            const int t = tq + r;
+            pf.g[r] = (t < n && cg < dk)
+                          ? *reinterpret_cast<const float4*>(p.g + ((row0 + t) * p.H + h) * (int64_t)dk + cg)
+                          : make_float4(0.f, 0.f, 0.f, 0.f);
         }
-        pf.b[r] = (t < n) ? p.beta[(row0 + t) * p.H + h] : 0.f;
     }
-    // V: rows t, 16-byte vectors of VEC columns of this dv-tile
-    constexpr int VPR = DVT / G_::VEC;  // vectors per row
-    const TIn* __restrict__ vp = static_cast<const TIn*>(p.v);
-    const int DVfull = p.ntiles * DVT;
+    {
+        const int c = SL * w + 8 * g4;
 #pragma unroll
-    for (int i = 0; i < Prefetch<DK, DVT, TIn>::VPT; ++i) {
-        const int vi = tid + i * NT;
-        const int t = vi / VPR, cv = vi % VPR;
-        if (vi < Prefetch<DK, DVT, TIn>::VV && t < n)
-            pf.v[i] = *reinterpret_cast<const uint4*>(
-                vp + ((row0 + t) * p.H + h) * (int64_t)DVfull + tile * DVT + cv * G_::VEC);
-        else
-            pf.v[i] = make_uint4(0, 0, 0, 0);
+        for (int mt = 0; mt < 4; ++mt) {
+            const int t = tok_of(mt, i16);
+            const bool ok = t < n && c < dk;
+            const int64_t idx = ((row0 + t) * p.H + h) * (int64_t)dk + c;
+            pf.ka[mt] = ok ? IO::load8(p.k, idx) : IO::zero8();
+            pf.qa[mt] = ok ? IO::load8(p.q, idx) : IO::zero8();
+        }
     }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int t = tok_of(mt, 4 * g4 + e);
+            pf.v[mt][e] = t < n ? IO::load1(p.v, ((row0 + t) * p.H + h) * (int64_t)p.dv + j)
+                                : typename IO::V1(0);
+        }
+}
+
+// This thread's share (4 x 16 bytes) of a chunk's TB hi and lo planes.
+struct TbShare {
+    uint4 a, b, c, d;
+};
+__device__ __forceinline__ TbShare load_tb(const ScanParams& p, int64_t gc, int h, int tid) {
+    const uint4* __restrict__ blk = p.ops + (gc * p.H + h) * CHUNK_OPS;
+    return TbShare{blk[tid], blk[tid + NT], blk[tid + 2 * NT], blk[tid + 3 * NT]};
+}
+__device__ __forceinline__ void store_tb(uint4* dst, const TbShare& s, int tid) {
+    dst[tid] = s.a;
+    dst[tid + NT] = s.b;
+    dst[tid + 2 * NT] = s.c;
+    dst[tid + 3 * NT] = s.d;
 }
 
 template <typename TIn>
-__device__ __forceinline__ void decode8(const uint4* src, float (&x)[8]) {
-    if constexpr (sizeof(TIn) == 2) {
-        const uint4 u = src[0];
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            x[2 * j] = bff((uint16_t)(w[j] & 0xffffu));
-            x[2 * j + 1] = bff((uint16_t)(w[j] >> 16));
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const uint4 u = src[i];
-            x[4 * i + 0] = __uint_as_float(u.x); x[4 * i + 1] = __uint_as_float(u.y);
-            x[4 * i + 2] = __uint_as_float(u.z); x[4 * i + 3] = __uint_as_float(u.w);
-        }
-    }
-}
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void scan_kernel(ScanParams p) {
+    using IO = In<TIn>;
+    using SM = ScanSmem<TIn>;
+    __shared__ SM sm;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int g4 = lane >> 4, i16 = lane & 15;
 
-// ---------------------------------------------------------------------------
-// The kernel
-// ---------------------------------------------------------------------------
-template <int DK, int DVT, typename TIn>
-__global__ __launch_bounds__(NT) void prefill_kernel(Params p) {
-    using G_ = Geo<DK, DVT, TIn>;
-    constexpr int DKP = G_::DKP, NKS = G_::NKS, RW = G_::RW, KSP = G_::KSP, JT = G_::JT;
-    __shared__ Smem<DK, DVT, TIn> sm;
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int g4 = lane >> 4, l16 = lane & 15;
-
-    // workgroup -> (sequence, head, dv-tile); dv-tiles of one head are given
-    // consecutive logical ids, and consecutive logical ids are placed on one
-    // XCD (workgroups are dealt round-robin over the 8 XCDs), so the tiles of
-    // a head share K, Q, g through that XCD's L2.
+    // workgroup -> (sequence, head, value tile).  Workgroups are dealt
+    // round-robin over the 8 XCDs; the remap gives each XCD a contiguous
+    // range of logical ids, so the tiles of one head share its L2.
     int L = blockIdx.x;
     if ((p.nwg & 7) == 0) L = (blockIdx.x & 7) * (p.nwg >> 3) + (blockIdx.x >> 3);
     const int tile = L % p.ntiles;
     const int chain = L / p.ntiles;
-    const int b = chain / p.H, h = chain % p.H;
-    const int DV = p.ntiles * DVT;
+    const int b = chain / p.H, h = chain - b * p.H;
+    const int dk = p.dk, dv = p.dv;
+    const int j = 16 * tile + i16;
     const int64_t seq0 = p.cu[b];
     const int len = p.cu[b + 1] - p.cu[b];
-    int64_t snap_base = 0;
-    if (p.interval > 0)
-        for (int i = 0; i < b; ++i) snap_base += (p.cu[i + 1] - p.cu[i]) / p.interval;
+    const int nch = (len + C - 1) / C;
+    const int64_t cbase = p.chunk_start[b];
+    const int64_t sbase = p.snap_base[b];
+    float (*Gs)[SL + 4] = sm.G[w];
 
-    // ---- state registers (state waves only) ------------------------------
-    const bool swave = wave < G_::NSW;
-    const int rw = wave % RW, cw = wave / RW;
-    f32x4 S[KSP][2][JT];
-    const int64_t sbase = ((int64_t)b * p.H + h) * DK;  // state row base
+    // state rows of this lane: 32w + chan_of(m, 4*g4 + e) = 32w + 8*g4 + 4m + e
+    f32x4 S[2];
+    const int64_t srow = ((int64_t)b * p.H + h) * dk;
 #pragma unroll
-    for (int kk = 0; kk < KSP; ++kk)
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-            for (int jt = 0; jt < JT; ++jt) {
-                const int c = 16 * (2 * (rw * KSP + kk) + m) + 4 * g4;
-                const int j = tile * DVT + 16 * (cw * JT + jt) + l16;
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    S[kk][m][jt][e] = (swave && p.init && c + e < DK)
-                                          ? p.init[(sbase + c + e) * DV + j] : 0.f;
-            }
-
-    const int nchunks = (len + C - 1) / C;
-    Prefetch<DK, DVT, TIn> pf;
-    if (nchunks > 0) load_chunk<DK, DVT, TIn>(pf, p, seq0, len < C ? len : C, h, tile, tid);
-
-    for (int ci = 0; ci < nchunks; ++ci) {
-        const int64_t row0 = seq0 + (int64_t)ci * C;
-        const int n = (len - ci * C) < C ? (len - ci * C) : C;
-
-        // ================= prep: cumulative decay and all operands =================
-        {
-            const int cg = tid >> 4, tb = tid & 15;
-            const int c0 = cg * 8, t0 = 2 * tb;
-            const bool active = cg < DKP / 8;
-            float gf[2][8], kf[2][8], qf[2][8];
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                gf[r][0] = pf.g[r][0].x; gf[r][1] = pf.g[r][0].y; gf[r][2] = pf.g[r][0].z;
-                gf[r][3] = pf.g[r][0].w; gf[r][4] = pf.g[r][1].x; gf[r][5] = pf.g[r][1].y;
-                gf[r][6] = pf.g[r][1].z; gf[r][7] = pf.g[r][1].w;
-                decode8<TIn>(pf.k[r], kf[r]);
-                decode8<TIn>(pf.q[r], qf[r]);
-            }
-            const float b0 = pf.b[0], b1 = pf.b[1];
-            // inclusive scan of the row-pair sums over the 16 lanes of this channel group
-            float G0[8], G1[8];
-            int ext = 0;
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const float pair = gf[0][c] + gf[1][c];
-                float incl = pair;
-#pragma unroll
-                for (int off = 1; off < 16; off <<= 1) {
-                    const float y = __shfl_up(incl, off, 16);
-                    if (tb >= off) incl += y;
-                }
-                float excl = __shfl_up(incl, 1, 16);
-                if (tb == 0) excl = 0.f;
-                G0[c] = excl + gf[0][c];
-                G1[c] = G0[c] + gf[1][c];
-            }
-            // references: G_7 (row 7), G_15, G_23, G_31 = G_C; and G_0, G_16
-            const int lb = lane & ~15;
-            float r0[8], r01[8], r1[8], GC[8];
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                r0[c] = __shfl(G1[c], lb + 3, 64);
-                r01[c] = __shfl(G1[c], lb + 7, 64);
-                r1[c] = __shfl(G1[c], lb + 11, 64);
-                GC[c] = __shfl(G1[c], lb + 15, 64);
-                const float Gfirst0 = __shfl(G0[c], lb + 0, 64);
-                const float Gfirst1 = __shfl(G0[c], lb + 8, 64);
-                ext |= (Gfirst0 - r0[c] > SPAN_LIMIT) | (r0[c] - r01[c] > SPAN_LIMIT) |
-                       (Gfirst1 - r1[c] > SPAN_LIMIT) | (r1[c] - GC[c] > SPAN_LIMIT);
-            }
-            if (active) {
-#pragma unroll
-                for (int r = 0; r < 2; ++r) {
-                    const int t = t0 + r;
-                    const float* Gr = r == 0 ? G0 : G1;
-                    const float bt = r == 0 ? b0 : b1;
-                    uint16_t xk[8], xqh[8], xql[8], ykh[8], ykl[8], x1h[8], x1l[8], x1k[8];
-                    uint16_t qgh[8], qgl[8];
-                    uint16_t kg[8], kdh[8], kdl[8];
-#pragma unroll
-                    for (int c = 0; c < 8; ++c) {
-                        const float rd = t < 16 ? r0[c] : r1[c];
-                        const float xe = ex(Gr[c] - rd);
-                        const float ye = ex(rd - Gr[c]);
-                        xk[c] = bfb(kf[r][c] * xe);
-                        split(qf[r][c] * xe, xqh[c], xql[c]);
-                        split(kf[r][c] * ye, ykh[c], ykl[c]);
-                        if (t >= 16) {
-                            const float e1 = ex(Gr[c] - r01[c]);
-                            x1k[c] = bfb(kf[r][c] * e1);
-                            split(qf[r][c] * e1, x1h[c], x1l[c]);
-                        } else {
-                            const float e1 = ex(r01[c] - Gr[c]);
-                            split(kf[r][c] * e1, x1h[c], x1l[c]);
-                        }
-                        const float eg = ex(Gr[c]);
-                        kg[c] = bfb(bt * kf[r][c] * eg);
-                        split(qf[r][c] * eg, qgh[c], qgl[c]);
-                        split(kf[r][c] * ex(GC[c] - Gr[c]), kdh[c], kdl[c]);
-                    }
-                    *reinterpret_cast<uint4*>(&sm.u.gram.XKd[t][c0]) = pack8(xk);
-                    *reinterpret_cast<uint4*>(&sm.u.gram.XQd[0][t][c0]) = pack8(xqh);
-                    *reinterpret_cast<uint4*>(&sm.u.gram.XQd[1][t][c0]) = pack8(xql);
-                    *reinterpret_cast<uint4*>(&sm.u.gram.YKd[0][t][c0]) = pack8(ykh);
-                    *reinterpret_cast<uint4*>(&sm.u.gram.YKd[1][t][c0]) = pack8(ykl);
-                    if (t >= 16) {
-                        *reinterpret_cast<uint4*>(&sm.u.gram.XK1[t - 16][c0]) = pack8(x1k);
-                        *reinterpret_cast<uint4*>(&sm.u.gram.XQ1[0][t - 16][c0]) = pack8(x1h);
-                        *reinterpret_cast<uint4*>(&sm.u.gram.XQ1[1][t - 16][c0]) = pack8(x1l);
-                    } else {
-                        *reinterpret_cast<uint4*>(&sm.u.gram.YK1[0][t][c0]) = pack8(x1h);
-                        *reinterpret_cast<uint4*>(&sm.u.gram.YK1[1][t][c0]) = pack8(x1l);
-                    }
-                    *reinterpret_cast<uint4*>(&sm.Qg[0][t][c0]) = pack8(qgh);
-                    *reinterpret_cast<uint4*>(&sm.Qg[1][t][c0]) = pack8(qgl);
-                    *reinterpret_cast<float4*>(&sm.G[t][c0]) =
-                        make_float4(Gr[0], Gr[1], Gr[2], Gr[3]);
-                    *reinterpret_cast<float4*>(&sm.G[t][c0 + 4]) =
-                        make_float4(Gr[4], Gr[5], Gr[6], Gr[7]);
-                    // transposed buffers [channel][row]
-#pragma unroll
-                    for (int c = 0; c < 8; ++c) {
-                        sm.KgT[c0 + c][t] = kg[c];
-                        sm.KdT[0][c0 + c][t] = kdh[c];
-                        sm.KdT[1][c0 + c][t] = kdl[c];
-                    }
-                }
-                if (tb == 15) {
-#pragma unroll
-                    for (int c = 0; c < 8; ++c) sm.decay[c0 + c] = ex(GC[c]);
-                }
-                if (cg == 0) {
-                    sm.beta[t0] = b0;
-                    sm.beta[t0 + 1] = b1;
-                }
-            }
-            // V^T (split for fp32 inputs)
-            constexpr int VPR = DVT / G_::VEC;
-#pragma unroll
-            for (int i = 0; i < Prefetch<DK, DVT, TIn>::VPT; ++i) {
-                const int vi = tid + i * NT;
-                if (vi < Prefetch<DK, DVT, TIn>::VV) {
-                    const int t = vi / VPR, cv = vi % VPR;
-                    if constexpr (!G_::F32IN) {
-                        const uint4 u = pf.v[i];
-                        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-                        for (int jj = 0; jj < 4; ++jj) {
-                            sm.VT[0][cv * 8 + 2 * jj][t] = (uint16_t)(w[jj] & 0xffffu);
-                            sm.VT[0][cv * 8 + 2 * jj + 1][t] = (uint16_t)(w[jj] >> 16);
-                        }
-                    } else {
-                        const uint4 u = pf.v[i];
-                        const float x[4] = {__uint_as_float(u.x), __uint_as_float(u.y),
-                                            __uint_as_float(u.z), __uint_as_float(u.w)};
-#pragma unroll
-                        for (int jj = 0; jj < 4; ++jj) {
-                            uint16_t hh, ll;
-                            split(x[jj], hh, ll);
-                            sm.VT[0][cv * 4 + jj][t] = hh;
-                            sm.VT[G_::VPL - 1][cv * 4 + jj][t] = ll;
-                        }
-                    }
-                }
-            }
-            const int any_ext = __syncthreads_or(ext);
-            if (tid == 0) sm.extreme = any_ext;
-        }
-        // the prefetch registers are free: start loading the next chunk
-        if (ci + 1 < nchunks) {
-            const int n2 = (len - (ci + 1) * C) < C ? (len - (ci + 1) * C) : C;
-            load_chunk<DK, DVT, TIn>(pf, p, row0 + C, n2, h, tile, tid);
+        for (int e = 0; e < 4; ++e) {
+            const int c = SL * w + 8 * g4 + 4 * m + e;
+            S[m][e] = (p.init && c < dk) ? p.init[(srow + c) * dv + j] : 0.f;
         }
 
-        // ================= Gram matrices A (wave 0) and B (waves 1-3) ================
-        {
-            const int blk = wave == 0 ? 0 : wave - 1;  // 0: (0,0)  1: (1,1)  2: (1,0)
-            const int rb = blk == 0 ? 0 : 16;          // row block start
-            const int cb = blk == 1 ? 16 : 0;          // column block start
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            if (wave == 0) {
-#pragma unroll
-                for (int bb = 0; bb < 3; ++bb) {
-                    const uint16_t* X = bb == 2 ? &sm.u.gram.XK1[0][0] : &sm.u.gram.XKd[bb * 16][0];
-                    const uint16_t* Y = bb == 2 ? &sm.u.gram.YK1[0][0][0] : &sm.u.gram.YKd[0][bb * 16][0];
-                    f32x4 a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int ks = 0; ks < NKS; ++ks)
-                        a = mfma(ld8(X + l16 * DKP + 32 * ks + 8 * g4),
-                                 ld8(Y + l16 * DKP + 32 * ks + 8 * g4), a);
-                    const int rb2 = bb == 0 ? 0 : 16, cb2 = bb == 1 ? 16 : 0;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int t = rb2 + 4 * g4 + e, s = cb2 + l16;
-                        sm.A[t][s] = (s < t) ? a[e] * sm.beta[t] : 0.f;
-                    }
-                }
-            } else {
-                const uint16_t* X0 = blk == 2 ? &sm.u.gram.XQ1[0][0][0] : &sm.u.gram.XQd[0][rb][0];
-                const uint16_t* X1 = blk == 2 ? &sm.u.gram.XQ1[1][0][0] : &sm.u.gram.XQd[1][rb][0];
-                const uint16_t* Y0 = blk == 2 ? &sm.u.gram.YK1[0][0][0] : &sm.u.gram.YKd[0][cb][0];
-                const uint16_t* Y1 = blk == 2 ? &sm.u.gram.YK1[1][0][0] : &sm.u.gram.YKd[1][cb][0];
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    const int off = l16 * DKP + 32 * ks + 8 * g4;
-                    const bf16x8_t xh = ld8(X0 + off), xl = ld8(X1 + off);
-                    const bf16x8_t yh = ld8(Y0 + off), yl = ld8(Y1 + off);
-                    acc = mfma(xh, yh, acc);
-                    acc = mfma(xh, yl, acc);
-                    acc = mfma(xl, yh, acc);
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int t = rb + 4 * g4 + e, s = cb + l16;
-                    sm.B[t][s] = (s <= t) ? acc[e] : 0.f;
-                }
-            }
-        }
-        __syncthreads();
-
-        // extreme decay inside a sub-chunk: diagonal blocks pairwise in fp32
-        if (sm.extreme) {
-            const TIn* __restrict__ kp = static_cast<const TIn*>(p.k);
-            const TIn* __restrict__ qp = static_cast<const TIn*>(p.q);
-            for (int idx = tid; idx < 512; idx += NT) {
-                const int blk = idx >> 8, tl = (idx >> 4) & 15, sl = idx & 15;
-                if (sl > tl) continue;
-                const int t = blk * 16 + tl, s = blk * 16 + sl;
-                float sa = 0.f, sb = 0.f;
-                if (t < n) {
-                    const int64_t bt = ((row0 + t) * p.H + h) * (int64_t)DK;
-                    const int64_t bs = ((row0 + s) * p.H + h) * (int64_t)DK;
-                    for (int c = 0; c < DK; ++c) {
-                        float kt, ks_, qt;
-                        if constexpr (G_::F32IN) {
-                            kt = kp[bt + c]; ks_ = kp[bs + c]; qt = qp[bt + c];
-                        } else {
-                            kt = bff(reinterpret_cast<const uint16_t*>(kp)[bt + c]);
-                            ks_ = bff(reinterpret_cast<const uint16_t*>(kp)[bs + c]);
-                            qt = bff(reinterpret_cast<const uint16_t*>(qp)[bt + c]);
-                        }
-                        const float e = ex(sm.G[t][c] - sm.G[s][c]);
-                        sa = fmaf(kt * ks_, e, sa);
-                        sb = fmaf(qt * ks_, e, sb);
-                    }
-                }
-                sm.A[t][s] = (s < t) ? sa * sm.beta[t] : 0.f;
-                sm.B[t][s] = sb;
-            }
-            __syncthreads();
-        }
-
-        // ================= T = (I + A)^-1 ===============================================
-        if (wave == 0 && lane < 32) {
-            // diagonal 16x16 blocks by forward substitution, one column per lane
-            const int bo = (lane >> 4) * 16, j = lane & 15;
-            float x[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float acc = 0.f;
-#pragma unroll
-                for (int m = 0; m < i; ++m) acc = fmaf(sm.A[bo + i][bo + m], x[m], acc);
-                x[i] = (i == j) ? 1.f : (i > j ? -acc : 0.f);
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sm.Tf[bo + i][bo + j] = x[i];
-        }
-        __syncthreads();
-        {
-            const int i = tid >> 4, j = tid & 15;
-            float acc = 0.f;
-#pragma unroll
-            for (int m = 0; m < 16; ++m) acc = fmaf(sm.A[16 + i][m], sm.Tf[m][j], acc);
-            sm.M1[i][j] = acc;
-        }
-        __syncthreads();
-        {
-            const int i = tid >> 4, j = tid & 15;
-            float acc = 0.f;
-#pragma unroll
-            for (int m = 0; m < 16; ++m) acc = fmaf(sm.Tf[16 + i][16 + m], sm.M1[m][j], acc);
-            sm.Tf[16 + i][j] = -acc;
-            sm.Tf[i][16 + j] = 0.f;
-        }
-        __syncthreads();
-        {
-            const int t = tid >> 3, s0 = (tid & 7) * 4;
-            uint16_t th[4], tl[4], bh[4], bl[4], qh[4], ql[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int s = s0 + e;
-                const float tv = sm.Tf[t][s];
-                split(tv, th[e], tl[e]);
-                split(tv * sm.beta[s], bh[e], bl[e]);
-                split(s <= t ? sm.B[t][s] : 0.f, qh[e], ql[e]);
-            }
-            auto p4 = [](const uint16_t (&x)[4]) {
-                return make_uint2(x[0] | ((uint32_t)x[1] << 16), x[2] | ((uint32_t)x[3] << 16));
-            };
-            *reinterpret_cast<uint2*>(&sm.Thl[0][t][s0]) = p4(th);
-            *reinterpret_cast<uint2*>(&sm.Thl[1][t][s0]) = p4(tl);
-            *reinterpret_cast<uint2*>(&sm.TBhl[0][t][s0]) = p4(bh);
-            *reinterpret_cast<uint2*>(&sm.TBhl[1][t][s0]) = p4(bl);
-            *reinterpret_cast<uint2*>(&sm.Bhl[0][t][s0]) = p4(qh);
-            *reinterpret_cast<uint2*>(&sm.Bhl[1][t][s0]) = p4(ql);
-        }
-        __syncthreads();
-
-        // ================= W = T (b K e^G), computed as W^T = KgT T^T ==================
-        {
-            constexpr int NTILE = DKP / 8;  // (DKP/16 channel tiles) x (2 row tiles)
-            for (int ti = wave; ti < NTILE; ti += 4) {
-                const int mc = ti >> 1, nt = ti & 1;
-                const bf16x8_t a = ld8(&sm.KgT[mc * 16 + l16][8 * g4]);
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                acc = mfma(a, ld8(&sm.Thl[0][nt * 16 + l16][8 * g4]), acc);
-                acc = mfma(a, ld8(&sm.Thl[1][nt * 16 + l16][8 * g4]), acc);
-                uint16_t w4[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) w4[e] = bfb(acc[e]);
-                *reinterpret_cast<uint2*>(&sm.u.st.W[nt * 16 + l16][mc * 16 + 4 * g4]) =
-                    make_uint2(w4[0] | ((uint32_t)w4[1] << 16), w4[2] | ((uint32_t)w4[3] << 16));
-            }
-        }
-        __syncthreads();
-
-        // ================= state products ===============================================
-        f32x4 sumW[2][JT], sumQ[2][JT];
-        if (swave) {
-#pragma unroll
-            for (int kk = 0; kk < KSP; ++kk) {
-                const int ks = rw * KSP + kk;
-#pragma unroll
-                for (int jt = 0; jt < JT; ++jt) {
-                    bf16x8_t sh, sl;
-                    pack_split(S[kk][0][jt], S[kk][1][jt], sh, sl);
-#pragma unroll
-                    for (int mt = 0; mt < 2; ++mt) {
-                        const int roff = (mt * 16 + l16) * DKP + 32 * ks + 4 * g4;
-                        const bf16x8_t w = ld4x2(&sm.u.st.W[0][0] + roff);
-                        const bf16x8_t qh = ld4x2(&sm.Qg[0][0][0] + roff);
-                        const bf16x8_t ql = ld4x2(&sm.Qg[1][0][0] + roff);
-                        f32x4 pw = {0.f, 0.f, 0.f, 0.f}, pq = {0.f, 0.f, 0.f, 0.f};
-                        pw = mfma(w, sh, pw);
-                        pw = mfma(w, sl, pw);
-                        pq = mfma(qh, sh, pq);
-                        pq = mfma(qh, sl, pq);
-                        pq = mfma(ql, sh, pq);
-                        if constexpr (RW > 1) {
-                            sm.u.st.PW[ks][mt][cw * JT + jt][lane] = pw;
-                            sm.u.st.PQ[ks][mt][cw * JT + jt][lane] = pq;
-                        } else {
-                            if (kk == 0) {
-                                sumW[mt][jt] = pw;
-                                sumQ[mt][jt] = pq;
-                            } else {
-                                sumW[mt][jt] += pw;
-                                sumQ[mt][jt] += pq;
-                            }
-                        }
-                    }
-                }
-            }
-        }
-        if constexpr (RW > 1) {
-            __syncthreads();
-            if (swave) {
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                    for (int jt = 0; jt < JT; ++jt) {
-                        const int nj = cw * JT + jt;
-                        sumW[mt][jt] = sm.u.st.PW[0][mt][nj][lane];
-                        sumQ[mt][jt] = sm.u.st.PQ[0][mt][nj][lane];
-#pragma unroll
-                        for (int ks = 1; ks < NKS; ++ks) {
-                            sumW[mt][jt] += sm.u.st.PW[ks][mt][nj][lane];
-                            sumQ[mt][jt] += sm.u.st.PQ[ks][mt][nj][lane];
-                        }
-                    }
-            }
-        }
-        if (swave) {
-            // U = T (b V) - W S, in accumulator layout [t][j]
-            bf16x8_t uh[JT], ul[JT];
-            f32x4 U[2][JT];
-#pragma unroll
-            for (int jt = 0; jt < JT; ++jt) {
-                const int nj = cw * JT + jt;
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt) {
-                    const bf16x8_t th = ld8(&sm.TBhl[0][mt * 16 + l16][8 * g4]);
-                    const bf16x8_t tl = ld8(&sm.TBhl[1][mt * 16 + l16][8 * g4]);
-                    const bf16x8_t vh = ld8(&sm.VT[0][nj * 16 + l16][8 * g4]);
-                    f32x4 ut = {0.f, 0.f, 0.f, 0.f};
-                    ut = mfma(th, vh, ut);
-                    if constexpr (G_::F32IN) {
-                        const bf16x8_t vl = ld8(&sm.VT[G_::VPL - 1][nj * 16 + l16][8 * g4]);
-                        ut = mfma(th, vl, ut);
-                    }
-                    ut = mfma(tl, vh, ut);
-                    U[mt][jt] = ut - sumW[mt][jt];
-                }
-                pack_split(U[0][jt], U[1][jt], uh[jt], ul[jt]);
-            }
-            // O = scale ((Q e^G) S + B U), written by the first row-wave of each column group
-            if (rw == 0) {
-                const bool ob = p.out_bf16 != 0;
-#pragma unroll
-                for (int jt = 0; jt < JT; ++jt) {
-                    const int j = tile * DVT + 16 * (cw * JT + jt) + l16;
-#pragma unroll
-                    for (int mt = 0; mt < 2; ++mt) {
-                        const int roff = (mt * 16 + l16) * C + 4 * g4;
-                        const bf16x8_t bh = ld4x2(&sm.Bhl[0][0][0] + roff);
-                        const bf16x8_t bl = ld4x2(&sm.Bhl[1][0][0] + roff);
-                        f32x4 bu = {0.f, 0.f, 0.f, 0.f};
-                        bu = mfma(bh, uh[jt], bu);
-                        bu = mfma(bh, ul[jt], bu);
-                        bu = mfma(bl, uh[jt], bu);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int t = mt * 16 + 4 * g4 + e;
-                            if (t < n) {
-                                const float o = p.scale * (sumQ[mt][jt][e] + bu[e]);
-                                const int64_t oi = ((row0 + t) * p.H + h) * (int64_t)DV + j;
-                                if (ob)
-                                    static_cast<uint16_t*>(p.out)[oi] = bfb(o);
-                                else
-                                    static_cast<float*>(p.out)[oi] = o;
-                            }
-                        }
-                    }
-                }
-            }
-            // S <- Diag(e^{G_C}) S + (K e^{G_C - G})^T U
-#pragma unroll
-            for (int kk = 0; kk < KSP; ++kk)
-#pragma unroll
-                for (int m = 0; m < 2; ++m) {
-                    const int crow = 16 * (2 * (rw * KSP + kk) + m);
-                    const bf16x8_t kh = ld4x2(&sm.KdT[0][crow + l16][4 * g4]);
-                    const bf16x8_t kl = ld4x2(&sm.KdT[1][crow + l16][4 * g4]);
-                    const float d0 = sm.decay[crow + 4 * g4 + 0], d1 = sm.decay[crow + 4 * g4 + 1];
-                    const float d2 = sm.decay[crow + 4 * g4 + 2], d3 = sm.decay[crow + 4 * g4 + 3];
-#pragma unroll
-                    for (int jt = 0; jt < JT; ++jt) {
-                        f32x4 s = S[kk][m][jt];
-                        s[0] *= d0; s[1] *= d1; s[2] *= d2; s[3] *= d3;
-                        s = mfma(kh, uh[jt], s);
-                        s = mfma(kh, ul[jt], s);
-                        s = mfma(kl, uh[jt], s);
-                        S[kk][m][jt] = s;
-                    }
-                }
-            // snapshot at block boundaries of this sequence
-            const int done = ci * C + n;
-            if (p.interval > 0 && done % p.interval == 0) {
-                const int64_t jsnap = done / p.interval - 1;
-                float* __restrict__ dst = p.snapshots + ((snap_base + jsnap) * p.H + h) * (int64_t)DK * DV;
-#pragma unroll
-                for (int kk = 0; kk < KSP; ++kk)
-#pragma unroll
-                    for (int m = 0; m < 2; ++m)
-#pragma unroll
-                        for (int jt = 0; jt < JT; ++jt) {
-                            const int c = 16 * (2 * (rw * KSP + kk) + m) + 4 * g4;
-                            const int j = tile * DVT + 16 * (cw * JT + jt) + l16;
-#pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                if (c + e < DK) dst[(int64_t)(c + e) * DV + j] = S[kk][m][jt][e];
-                        }
-            }
-        }
-        __syncthreads();
+    ScanPrefetch<TIn> pf;
+    if (nch > 0) {
+        store_tb(sm.tb[0], load_tb(p, cbase, h, tid), tid);
+        scan_load<TIn>(pf, p, cbase, seq0, min(C, len), h, j, w, lane);
+        lds_barrier();
     }
 
-    // final state
-    if (swave) {
+    for (int ci = 0; ci < nch; ++ci) {
+        const int par = ci & 1;
+        const int64_t row0 = seq0 + (int64_t)ci * C;
+        const int n = min(C, len - ci * C);
+
+        // ---- (a) stage the cumulative log-decay (and bf16 keys) of this chunk ----
+        typename IO::V1 vcur[4][4];
+        uint4 bcur[2][2];
 #pragma unroll
-        for (int kk = 0; kk < KSP; ++kk)
+        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) vcur[mt][e] = pf.v[mt][e];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) { bcur[ks][0] = pf.bo[ks][0]; bcur[ks][1] = pf.bo[ks][1]; }
+        {
+            // lane scan over its 8 tokens, then an exclusive scan over the 8 token groups
+            float4 run = pf.g[0];
+            float4 Gl[8];
+            Gl[0] = run;
+#pragma unroll
+            for (int r = 1; r < 8; ++r) {
+                run.x += pf.g[r].x; run.y += pf.g[r].y; run.z += pf.g[r].z; run.w += pf.g[r].w;
+                Gl[r] = run;
+            }
+            float4 incl = run;
+#pragma unroll
+            for (int off = 8; off < 64; off <<= 1) {
+                float4 y;
+                y.x = __shfl_up(incl.x, off, 64); y.y = __shfl_up(incl.y, off, 64);
+                y.z = __shfl_up(incl.z, off, 64); y.w = __shfl_up(incl.w, off, 64);
+                if (lane >= off) { incl.x += y.x; incl.y += y.y; incl.z += y.z; incl.w += y.w; }
+            }
+            const float4 excl = make_float4(incl.x - run.x, incl.y - run.y, incl.z - run.z, incl.w - run.w);
+            const int cq = 4 * (lane & 7), tq = 8 * (lane >> 3);
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                *reinterpret_cast<float4*>(&Gs[tq + r][cq]) =
+                    make_float4(Gl[r].x + excl.x, Gl[r].y + excl.y, Gl[r].z + excl.z, Gl[r].w + excl.w);
+        }
+        if constexpr (SM::KSTAGE) {
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+                *reinterpret_cast<uint4*>(&sm.K[w][tok_of(mt, i16)][8 * g4]) = pf.ka[mt];
+        }
+        lds_wave_sync();
+
+        // ---- (b) decay-scaled operands of the products with the old state ----
+        bf16x8_t Kg[4], Qh[4], Ql[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            const int t = tok_of(mt, i16);
+            const float4 ga = *reinterpret_cast<const float4*>(&Gs[t][8 * g4]);
+            const float4 gb = *reinterpret_cast<const float4*>(&Gs[t][8 * g4 + 4]);
+            const float Gv[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
+            float kv[8], qv[8];
+            IO::f32x8(pf.ka[mt], kv);
+            IO::f32x8(pf.qa[mt], qv);
+            uint16_t xk[8], xh[8], xl[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float eg = ex(Gv[e]);
+                xk[e] = bfb(kv[e] * eg);
+                split(qv[e] * eg, xh[e], xl[e]);
+            }
+            Kg[mt] = as_op(pack8(xk));
+            Qh[mt] = as_op(pack8(xh));
+            Ql[mt] = as_op(pack8(xl));
+        }
+
+        // ---- (c) prefetch the next chunk ----
+        TbShare tbn{};
+        if (ci + 1 < nch) {
+            tbn = load_tb(p, cbase + ci + 1, h, tid);
+            scan_load<TIn>(pf, p, cbase + ci + 1, row0 + C, min(C, len - (ci + 1) * C), h, j, w,
+                           lane);
+        }
+
+        // ---- (d) partial (K e^G) S and (Q e^G) S over this wave's 32 rows ----
+        {
+            bf16x8_t Sh, Sl;
+            pack_split(S[0], S[1], Sh, Sl);
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            typename SM::Ex& E = sm.ex[par][w];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                f32x4 x = mfma(Kg[mt], Sh, z);
+                x = mfma(Kg[mt], Sl, x);
+                f32x4 pq = mfma(Qh[mt], Sh, z);
+                pq = mfma(Qh[mt], Sl, pq);
+                pq = mfma(Ql[mt], Sh, pq);
+                E.X[mt][lane] = x;
+                E.P[mt][lane] = pq;
+            }
+        }
+        lds_barrier();
+
+        // ---- (e) U = TB (V - (K e^G) S) for all tokens of the chunk ----
+        bf16x8_t Uh[2], Ul[2];
+        {
+            f32x4 D[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                f32x4 xs = sm.ex[par][0].X[mt][lane];
+                xs += sm.ex[par][1].X[mt][lane];
+                xs += sm.ex[par][2].X[mt][lane];
+                xs += sm.ex[par][3].X[mt][lane];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) D[mt][e] = IO::f32(vcur[mt][e]) - xs[e];
+            }
+            bf16x8_t Dh[2], Dl[2];
+            pack_split(D[0], D[1], Dh[0], Dl[0]);
+            pack_split(D[2], D[3], Dh[1], Dl[1]);
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            f32x4 U[4];
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt) {
+                f32x4 u = z;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const bf16x8_t th = as_op(sm.tb[par][(mt * 2 + ks) * 64 + lane]);
+                    const bf16x8_t tl = as_op(sm.tb[par][PLANE + (mt * 2 + ks) * 64 + lane]);
+                    u = mfma(th, Dh[ks], u);
+                    u = mfma(th, Dl[ks], u);
+                    u = mfma(tl, Dh[ks], u);
+                }
+                U[mt] = u;
+            }
+            pack_split(U[0], U[1], Uh[0], Ul[0]);
+            pack_split(U[2], U[3], Uh[1], Ul[1]);
+        }
+
+        // ---- (f) this wave's token tile of O = scale ((Q e^G) S + B U) ----
+        {
+            f32x4 po = sm.ex[par][0].P[w][lane];
+            po += sm.ex[par][1].P[w][lane];
+            po += sm.ex[par][2].P[w][lane];
+            po += sm.ex[par][3].P[w][lane];
+            f32x4 bu = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const bf16x8_t bh = as_op(bcur[ks][0]), bl = as_op(bcur[ks][1]);
+                bu = mfma(bh, Uh[ks], bu);
+                bu = mfma(bh, Ul[ks], bu);
+                bu = mfma(bl, Uh[ks], bu);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = tok_of(w, 4 * g4 + e);
+                if (t < n) {
+                    const float o = p.scale * (po[e] + bu[e]);
+                    const int64_t oi = ((row0 + t) * p.H + h) * (int64_t)dv + j;
+                    if (p.out_bf16)
+                        static_cast<uint16_t*>(p.out)[oi] = bfb(o);
+                    else
+                        static_cast<float*>(p.out)[oi] = o;
+                }
+            }
+        }
+
+        // ---- (g) S <- Diag(e^{G_C}) S + (K e^{G_C - G})^T U ----
+        {
+            const float4 gca = *reinterpret_cast<const float4*>(&Gs[C - 1][8 * g4]);
+            const float4 gcb = *reinterpret_cast<const float4*>(&Gs[C - 1][8 * g4 + 4]);
+            const f32x4 dec[2] = {f32x4{ex(gca.x), ex(gca.y), ex(gca.z), ex(gca.w)},
+                                  f32x4{ex(gcb.x), ex(gcb.y), ex(gcb.z), ex(gcb.w)}};
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const int cl = chan_of(m, i16);
+                const float gcl = Gs[C - 1][cl];
+                f32x4 s = S[m] * dec[m];
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    uint16_t hh[8], ll[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int t = 32 * ks + 8 * g4 + e;
+                        float kv;
+                        if constexpr (SM::KSTAGE) {
+                            kv = bff(sm.K[w][t][cl]);
+                        } else {
+                            kv = (t < n && SL * w + cl < dk)
+                                     ? IO::f32(IO::load1(p.k, ((row0 + t) * p.H + h) * (int64_t)dk + SL * w + cl))
+                                     : 0.f;
+                        }
+                        split(kv * ex(gcl - Gs[t][cl]), hh[e], ll[e]);
+                    }
+                    const bf16x8_t kh = as_op(pack8(hh)), kl = as_op(pack8(ll));
+                    s = mfma(kh, Uh[ks], s);
+                    s = mfma(kh, Ul[ks], s);
+                    s = mfma(kl, Uh[ks], s);
+                }
+                S[m] = s;
+            }
+        }
+        const int done = ci * C + n;
+        if (p.interval > 0 && done % p.interval == 0) {
+            float* __restrict__ dst =
+                p.snapshots + ((sbase + done / p.interval - 1) * p.H + h) * (int64_t)dk * dv;
 #pragma unroll
             for (int m = 0; m < 2; ++m)
 #pragma unroll
-                for (int jt = 0; jt < JT; ++jt) {
-                    const int c = 16 * (2 * (rw * KSP + kk) + m) + 4 * g4;
-                    const int j = tile * DVT + 16 * (cw * JT + jt) + l16;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (c + e < DK) p.final_state[(sbase + c + e) * DV + j] = S[kk][m][jt][e];
+                for (int e = 0; e < 4; ++e) {
+                    const int c = SL * w + 8 * g4 + 4 * m + e;
+                    if (c < dk) dst[(int64_t)c * dv + j] = S[m][e];
                 }
-    }
-}
-
-template <int DK, int DVT, typename TIn>
-hipError_t launch_t(const PrefillArgs& a, Params p) {
-    p.ntiles = a.dv / DVT;
-    const int64_t nwg = (int64_t)a.num_seqs * a.H * p.ntiles;
-    if (nwg > 0x7fffffffLL) return hipErrorInvalidValue;
-    p.nwg = (int)nwg;
-    hipLaunchKernelGGL((prefill_kernel<DK, DVT, TIn>), dim3((unsigned)nwg), dim3(NT), 0, a.stream, p);
-    return hipGetLastError();
-}
-
-// dv-tile width: the widest tile that still gives every CU a workgroup
-// (each dv-tile recomputes the dv-independent chunk work, so wider is cheaper
-// whenever the chip is already full).
-int pick_dvt(int dv, int64_t chains, bool f32in) {
-    int dvt = dv;
-    const int cap = f32in ? 16 : 128;
-    while (dvt > cap) dvt /= 2;
-    while (dvt > 16 && chains * (dv / dvt) < 256) dvt /= 2;
-    return dvt;
-}
-
-template <int DK, typename TIn>
-hipError_t launch_dk(const PrefillArgs& a, const Params& p) {
-    const int dvt = pick_dvt(a.dv, (int64_t)a.num_seqs * a.H, sizeof(TIn) == 4);
-    if constexpr (sizeof(TIn) == 4) {
-        return launch_t<DK, 16, TIn>(a, p);
-    } else {
-        switch (dvt) {
-            case 16: return launch_t<DK, 16, TIn>(a, p);
-            case 32: if constexpr (DK >= 32) return launch_t<DK, 32, TIn>(a, p); break;
-            case 64: if constexpr (DK >= 64) return launch_t<DK, 64, TIn>(a, p); break;
-            case 128: if constexpr (DK >= 128) return launch_t<DK, 128, TIn>(a, p); break;
         }
-        return hipErrorInvalidValue;
+
+        // ---- (h) TB of the next chunk into the other parity ----
+        if (ci + 1 < nch) store_tb(sm.tb[par ^ 1], tbn, tid);
     }
+
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int c = SL * w + 8 * g4 + 4 * m + e;
+            if (c < dk) p.final_state[(srow + c) * dv + j] = S[m][e];
+        }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+constexpr size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct WsLayout {
+    size_t chunk_start, snap_base, ops, total;
+};
+
+WsLayout ws_layout(int H, int num_seqs, int64_t max_chunks) {
+    WsLayout l;
+    l.chunk_start = 0;
+    l.snap_base = align_up((size_t)(num_seqs + 1) * 4, 256);
+    l.ops = l.snap_base + align_up((size_t)(num_seqs + 1) * 4, 256);
+    l.total = l.ops + (size_t)max_chunks * H * CHUNK_OPS * sizeof(uint4);
+    return l;
+}
+
+template <typename TIn>
+hipError_t launch_t(const PrefillArgs& a) {
+    const WsLayout l = ws_layout(a.H, a.num_seqs, a.total_chunks);
+    char* ws = static_cast<char*>(a.workspace);
+    int32_t* chunk_start = reinterpret_cast<int32_t*>(ws + l.chunk_start);
+    int32_t* snap_base = reinterpret_cast<int32_t*>(ws + l.snap_base);
+    uint4* ops = reinterpret_cast<uint4*>(ws + l.ops);
+
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(NT), 0, a.stream, a.cu_dev, a.num_seqs, a.interval,
+                       chunk_start, snap_base);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+
+    if (a.total_chunks > 0) {
+        PrepParams pp{};
+        pp.q = a.q;
+        pp.k = a.k;
+        pp.g = a.g;
+        pp.beta = a.beta;
+        pp.cu = a.cu_dev;
+        pp.chunk_start = chunk_start;
+        pp.ops = ops;
+        pp.H = a.H;
+        pp.dk = a.dk;
+        pp.num_seqs = a.num_seqs;
+        hipLaunchKernelGGL((prep_kernel<TIn>), dim3((unsigned)a.total_chunks, (unsigned)a.H), dim3(NT),
+                           0, a.stream, pp);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+
+    ScanParams sp{};
+    sp.q = a.q;
+    sp.k = a.k;
+    sp.v = a.v;
+    sp.g = a.g;
+    sp.cu = a.cu_dev;
+    sp.chunk_start = chunk_start;
+    sp.snap_base = snap_base;
+    sp.ops = ops;
+    sp.init = a.init;
+    sp.out = a.out;
+    sp.final_state = a.final_state;
+    sp.snapshots = a.snapshots;
+    sp.interval = a.interval;
+    sp.H = a.H;
+    sp.dk = a.dk;
+    sp.dv = a.dv;
+    sp.ntiles = a.dv / 16;
+    sp.out_bf16 = a.out_bf16 ? 1 : 0;
+    sp.scale = a.scale;
+    const int64_t nwg = (int64_t)a.num_seqs * a.H * sp.ntiles;
+    sp.nwg = (int)nwg;
+    hipLaunchKernelGGL((scan_kernel<TIn>), dim3((unsigned)nwg), dim3(NT), 0, a.stream, sp);
+    return hipGetLastError();
 }
 
 }  // namespace
 
-size_t prefill_workspace_bytes(int, int, int, int, int64_t) { return 0; }
+int64_t prefill_max_chunks(int num_seqs, int64_t total_tokens) {
+    // sum_b ceil(L_b / C) <= floor(T / C) + num_seqs
+    return total_tokens / C + num_seqs;
+}
+
+int prefill_chunk_rows() { return C; }
+
+size_t prefill_workspace_bytes(int, int, int H, int num_seqs, int64_t total_tokens) {
+    return ws_layout(H, num_seqs, prefill_max_chunks(num_seqs, total_tokens)).total;
+}
 
 hipError_t launch_prefill(const PrefillArgs& a) {
-    Params p{};
-    p.q = a.q;
-    p.k = a.k;
-    p.v = a.v;
-    p.g = a.g;
-    p.beta = a.beta;
-    p.cu = a.cu_dev;
-    p.init = a.init;
-    p.out = a.out;
-    p.final_state = a.final_state;
-    p.snapshots = a.snapshots;
-    p.interval = a.interval;
-    p.H = a.H;
-    p.num_seqs = a.num_seqs;
-    p.scale = a.scale;
-    p.out_bf16 = a.out_bf16 ? 1 : 0;
-    if (a.in_bf16) {
-        switch (a.dk) {
-            case 16: return launch_dk<16, bf16_t>(a, p);
-            case 32: return launch_dk<32, bf16_t>(a, p);
-            case 64: return launch_dk<64, bf16_t>(a, p);
-            case 128: return launch_dk<128, bf16_t>(a, p);
-        }
-    } else {
-        switch (a.dk) {
-            case 16: return launch_dk<16, float>(a, p);
-            case 32: return launch_dk<32, float>(a, p);
-            case 64: return launch_dk<64, float>(a, p);
-            case 128: return launch_dk<128, float>(a, p);
-        }
-    }
-    return hipErrorInvalidValue;
+    if (a.dk > DKP || a.dv % 16 != 0) return hipErrorInvalidValue;
+    if ((int64_t)a.num_seqs * a.H * (a.dv / 16) > 0x7fffffffLL) return hipErrorInvalidValue;
+    return a.in_bf16 ? launch_t<bf16_t>(a) : launch_t<float>(a);
 }
 
 }  // namespace kda
