@@ -63,7 +63,6 @@ constexpr int DKP = 128;             // state rows, zero-padded above dk
 constexpr int SL = 32;               // state rows per wave
 constexpr float SPAN_LIMIT = 80.0f;  // |exponent| bound for the diagonal Gram factors
 constexpr int PLANE = 512;           // uint4 per operand plane (4 row tiles x 2 K-steps x 64 lanes)
-constexpr int CHUNK_OPS = 4 * PLANE; // TB hi, TB lo, B hi, B lo
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8_t& a, const bf16x8_t& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -95,6 +94,20 @@ __device__ __forceinline__ uint4 pack8(const uint16_t (&x)[8]) {
     return u;
 }
 __device__ __forceinline__ bf16x8_t as_op(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+// Returns x unchanged, but the compiler cannot move arithmetic on x across
+// this point.  Applied to prefetched values where they are consumed, it keeps
+// the compiler from hoisting that arithmetic back next to the loads (which
+// would make the loads' issuer wait for their data).
+__device__ __forceinline__ uint32_t pin(uint16_t x16) {
+    uint32_t x = x16;
+    asm volatile("" : "+v"(x));
+    return x;
+}
+__device__ __forceinline__ float pin(float x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
 
 // Two accumulator tiles (row blocks 0 and 1 of a 32-row K-step) as one MFMA
 // operand: elements 0..3 come from tile 0, 4..7 from tile 1, split hi / lo.
@@ -140,7 +153,7 @@ template <> struct In<bf16_t> {
             x[2 * j + 1] = bff(w[j] >> 16);
         }
     }
-    using V1 = uint32_t;
+    using V1 = uint16_t;
     __device__ __forceinline__ static V1 load1(const void* base, int64_t idx) {
         return static_cast<const uint16_t*>(base)[idx];
     }
@@ -209,15 +222,38 @@ __global__ __launch_bounds__(NT) void plan_kernel(const int32_t* __restrict__ cu
 }
 
 // ---------------------------------------------------------------------------
-// prep: per (chunk, head) the state-independent chunk quantities.
+// prep: per (chunk, head) every state-independent quantity of the chunk,
+// written to the workspace as MFMA operands in the order the scan reads them.
 // ---------------------------------------------------------------------------
+// Operand block of one (chunk, head), in 16-byte units (8 bf16 = one MFMA
+// operand of one lane).  Scan lane (g = lane/16, i = lane%16) of wave w reads
+// index [...][lane] of:
+//   TB, B   [mt][ks]     row tok_of(mt, i), columns 32ks + 8g .. +7
+//   W, Qd   [w][mt]      row tok_of(mt, i), channels 32w + 8g .. +7
+//   Kd      [w][m][ks]   channel 32w + chan_of(m, i), tokens 32ks + 8g .. +7
+//   dec     128 floats, e^{G_C} per channel
+// with W = TB (K . e^G), Qd = Q . e^G, Kd = (K . e^{G_C - G})^T, each as a hi
+// plane followed by a lo plane.
+constexpr int OP_TB = 0;
+constexpr int OP_B = 2 * PLANE;
+constexpr int OP_W = 4 * PLANE;
+constexpr int OP_Q = 8 * PLANE;
+constexpr int OP_K = 12 * PLANE;
+constexpr int OP_DEC = 16 * PLANE;
+constexpr int CHUNK_OPS = 16 * PLANE + 32;
+
 struct PrepSmem {
     union {
-        float G[C][DKP + 4];  // cumulative log-decay (dead after the Gram matrices)
-        float T[C][C + 4];    // (I + A)^-1, lower block triangle
+        float G[C][DKP + 4];   // cumulative log-decay
+        float T[C][C + 4];     // (I + A)^-1, once the decay-scaled operands are out
+        float W[C][DKP + 4];   // W, for the transpose into operand order
     } u;
-    float A[C][C + 1];
-    float B[C][C + 1];
+    union {
+        float A[C][C + 1];     // strictly lower b_t sum_c k_t k_s e^{G_t - G_s}
+        float B[C][C + 1];     // lower sum_c q_t k_s e^{G_t - G_s}, once T is formed
+    } ab;
+    uint16_t KgT[DKP][C + 8];  // (K . e^G)^T in bf16, [channel][token]
+    float Bd[4][16][17];       // diagonal blocks of B from the pairwise path
     float M[3][16][17];
     float beta[C];
 };
@@ -254,22 +290,37 @@ void prep_kernel(PrepParams p) {
     const int len = p.cu[b + 1] - p.cu[b];
     const int n = min(C, len - ci * C);
     const int dk = p.dk;
+    uint4* __restrict__ dst = p.ops + ((int64_t)gc * p.H + h) * CHUNK_OPS;
+    // row t (clamped into the chunk), channel c (clamped below dk) of a [T, H, dk] tensor
+    auto at = [&](int t, int c) -> int64_t {
+        return ((row0 + min(t, n - 1)) * p.H + h) * (int64_t)dk + (c < dk ? c : 0);
+    };
 
     // ---- cumulative log-decay per channel (rows past n count as g = 0) ----
     {
         const int c = tid & 127, half = tid >> 7;
+        const bool cok = c < dk;
         float run = 0.f;
-#pragma unroll 8
+        float gv[32];
+#pragma unroll
         for (int r = 0; r < 32; ++r) {
             const int t = half * 32 + r;
-            run += (t < n && c < dk) ? p.g[((row0 + t) * p.H + h) * (int64_t)dk + c] : 0.f;
-            sm.u.G[t][c] = run;
+            const float x = p.g[at(t, c)];
+            gv[r] = (t < n && cok) ? x : 0.f;
         }
-        if (tid < C) sm.beta[tid] = tid < n ? p.beta[(row0 + tid) * p.H + h] : 0.f;
+#pragma unroll
+        for (int r = 0; r < 32; ++r) {
+            run += gv[r];
+            sm.u.G[half * 32 + r][c] = run;
+        }
+        if (tid < C) {
+            const float x = p.beta[(row0 + min(tid, n - 1)) * p.H + h];
+            sm.beta[tid] = tid < n ? x : 0.f;
+        }
         __syncthreads();
         if (half == 1) {
             const float base = sm.u.G[31][c];
-#pragma unroll 8
+#pragma unroll
             for (int r = 32; r < 64; ++r) sm.u.G[r][c] += base;
         }
         __syncthreads();
@@ -281,8 +332,9 @@ void prep_kernel(PrepParams p) {
     // diagonal block uses r = G at row 16w + 7, keeping both factors within
     // e^{+-span/2} of the block; spans beyond SPAN_LIMIT take the pairwise path.
     int extreme = 0;
+    f32x4 accB[4];
     {
-        f32x4 accA[4], accB[4];
+        f32x4 accA[4];
 #pragma unroll
         for (int ts = 0; ts < 4; ++ts) {
             accA[ts] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -295,10 +347,10 @@ void prep_kernel(PrepParams p) {
             const bool cok = c0 < dk;
             float kt[8], qt[8];
             {
-                const int64_t idx = ((row0 + t) * p.H + h) * (int64_t)dk + c0;
                 const bool ok = cok && t < n;
-                IO::f32x8(ok ? IO::load8(p.k, idx) : IO::zero8(), kt);
-                IO::f32x8(ok ? IO::load8(p.q, idx) : IO::zero8(), qt);
+                const typename IO::V8 kx = IO::load8(p.k, at(t, c0)), qx = IO::load8(p.q, at(t, c0));
+                IO::f32x8(ok ? kx : IO::zero8(), kt);
+                IO::f32x8(ok ? qx : IO::zero8(), qt);
             }
             float Gt[8], rw[8], rm[8];
 #pragma unroll
@@ -349,8 +401,8 @@ void prep_kernel(PrepParams p) {
                     if (ts < w) {
                         const int s = 16 * ts + i16;
                         float ksv[8];
-                        const int64_t idx = ((row0 + s) * p.H + h) * (int64_t)dk + c0;
-                        IO::f32x8((cok && s < n) ? IO::load8(p.k, idx) : IO::zero8(), ksv);
+                        const typename IO::V8 kx = IO::load8(p.k, at(s, c0));
+                        IO::f32x8((cok && s < n) ? kx : IO::zero8(), ksv);
                         uint16_t yh[8], yl[8];
 #pragma unroll
                         for (int e = 0; e < 8; ++e)
@@ -371,8 +423,7 @@ void prep_kernel(PrepParams p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int tr = 16 * w + 4 * g4 + e, sc = 16 * ts + i16;
-                sm.A[tr][sc] = (sc < tr) ? accA[ts][e] * sm.beta[tr] : 0.f;
-                sm.B[tr][sc] = (sc <= tr) ? accB[ts][e] : 0.f;
+                sm.ab.A[tr][sc] = (sc < tr) ? accA[ts][e] * sm.beta[tr] : 0.f;
             }
     }
     const int any_extreme = __syncthreads_or(extreme);
@@ -386,22 +437,61 @@ void prep_kernel(PrepParams p) {
             const int t = 16 * blk + tl, s = 16 * blk + sl;
             float sa = 0.f, sb = 0.f;
             if (t < n) {
-                const int64_t bt = ((row0 + t) * p.H + h) * (int64_t)dk;
-                const int64_t bs = ((row0 + s) * p.H + h) * (int64_t)dk;
                 for (int c = 0; c < dk; ++c) {
-                    const float kt = IO::f32(IO::load1(p.k, bt + c));
-                    const float kv = IO::f32(IO::load1(p.k, bs + c));
-                    const float qt = IO::f32(IO::load1(p.q, bt + c));
+                    const float kt = IO::f32(IO::load1(p.k, at(t, c)));
+                    const float kv = IO::f32(IO::load1(p.k, at(s, c)));
+                    const float qt = IO::f32(IO::load1(p.q, at(t, c)));
                     const float e = ex(sm.u.G[t][c] - sm.u.G[s][c]);
                     sa = fmaf(kt * kv, e, sa);
                     sb = fmaf(qt * kv, e, sb);
                 }
             }
-            sm.A[t][s] = (s < t) ? sa * sm.beta[t] : 0.f;
-            sm.B[t][s] = sb;
+            sm.ab.A[t][s] = (s < t) ? sa * sm.beta[t] : 0.f;
+            sm.Bd[blk][tl][sl] = sb;
         }
         __syncthreads();
     }
+
+    // ---- decay-scaled operands: Qd planes, Kd planes, dec, and (K e^G)^T ----
+#pragma unroll 1
+    for (int r = 0; r < 4; ++r) {
+        const int idx = tid + NT * r;  // (w', mt, lane)
+        const int ws = idx >> 8, mt = (idx >> 6) & 3, ln = idx & 63;
+        const int t = tok_of(mt, ln & 15), c0 = SL * ws + 8 * (ln >> 4);
+        const bool ok = t < n && c0 < dk;
+        float qv[8], kv[8];
+        const typename IO::V8 qx = IO::load8(p.q, at(t, c0)), kx = IO::load8(p.k, at(t, c0));
+        IO::f32x8(ok ? qx : IO::zero8(), qv);
+        IO::f32x8(ok ? kx : IO::zero8(), kv);
+        uint16_t qh[8], ql[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float eg = ex(sm.u.G[t][c0 + e]);
+            split(qv[e] * eg, qh[e], ql[e]);
+            sm.KgT[c0 + e][t] = bfb(kv[e] * eg);
+        }
+        dst[OP_Q + idx] = pack8(qh);
+        dst[OP_Q + 2 * PLANE + idx] = pack8(ql);
+    }
+#pragma unroll 1
+    for (int r = 0; r < 4; ++r) {
+        const int idx = tid + NT * r;  // (w', m, ks, lane)
+        const int ws = idx >> 8, m = (idx >> 7) & 1, ks = (idx >> 6) & 1, ln = idx & 63;
+        const int c = SL * ws + chan_of(m, ln & 15), t0 = 32 * ks + 8 * (ln >> 4);
+        const float gcc = sm.u.G[C - 1][c];
+        uint16_t kh[8], kl[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int t = t0 + e;
+            const float x = IO::f32(IO::load1(p.k, at(t, c)));
+            const float kv = (t < n && c < dk) ? x : 0.f;
+            split(kv * ex(gcc - sm.u.G[t][c]), kh[e], kl[e]);
+        }
+        dst[OP_K + idx] = pack8(kh);
+        dst[OP_K + 2 * PLANE + idx] = pack8(kl);
+    }
+    if (tid < DKP) reinterpret_cast<float*>(dst + OP_DEC)[tid] = ex(sm.u.G[C - 1][tid]);
+    __syncthreads();
 
     // ---- T = (I + A)^-1 by block forward substitution (G is dead now) ----
     if (lane < 16) {
@@ -412,7 +502,7 @@ void prep_kernel(PrepParams p) {
         for (int r = 0; r < 16; ++r) {
             float acc = 0.f;
 #pragma unroll
-            for (int m = 0; m < r; ++m) acc = fmaf(sm.A[bo + r][bo + m], x[m], acc);
+            for (int m = 0; m < r; ++m) acc = fmaf(sm.ab.A[bo + r][bo + m], x[m], acc);
             x[r] = (r == j) ? 1.f : -acc;
         }
 #pragma unroll
@@ -430,7 +520,7 @@ void prep_kernel(PrepParams p) {
                 for (int K = J; K < I; ++K)
 #pragma unroll
                     for (int m = 0; m < 16; ++m)
-                        acc = fmaf(sm.A[16 * I + r][16 * K + m], sm.u.T[16 * K + m][16 * J + cc], acc);
+                        acc = fmaf(sm.ab.A[16 * I + r][16 * K + m], sm.u.T[16 * K + m][16 * J + cc], acc);
                 sm.M[I - d][r][cc] = acc;
             }
             __syncthreads();
@@ -446,11 +536,20 @@ void prep_kernel(PrepParams p) {
         }
     }
 
-    // ---- TB = T Diag(beta) and B as hi/lo MFMA operands in scan order ----
-    uint4* __restrict__ dst = p.ops + ((int64_t)gc * p.H + h) * CHUNK_OPS;
+    // ---- B (A is dead now), then TB and B as operand planes ----
+#pragma unroll
+    for (int ts = 0; ts < 4; ++ts)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int tr = 16 * w + 4 * g4 + e, sc = 16 * ts + i16;
+            float v = accB[ts][e];
+            if (any_extreme && ts == w) v = sm.Bd[w][4 * g4 + e][i16];
+            sm.ab.B[tr][sc] = (sc <= tr) ? v : 0.f;
+        }
+    __syncthreads();
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
-        const int idx = tid + NT * rr;           // 0 .. 511
+        const int idx = tid + NT * rr;  // (mt, ks, lane)
         const int mt = idx >> 7, ks = (idx >> 6) & 1, ln = idx & 63;
         const int t = tok_of(mt, ln & 15);
         const int s0 = 32 * ks + 8 * (ln >> 4);
@@ -460,35 +559,77 @@ void prep_kernel(PrepParams p) {
             const int s = s0 + e;
             const float tb = (s <= t) ? sm.u.T[t][s] * sm.beta[s] : 0.f;
             split(tb, th[e], tl[e]);
-            split(sm.B[t][s], bh[e], bl[e]);
+            split(sm.ab.B[t][s], bh[e], bl[e]);
         }
-        dst[0 * PLANE + idx] = pack8(th);
-        dst[1 * PLANE + idx] = pack8(tl);
-        dst[2 * PLANE + idx] = pack8(bh);
-        dst[3 * PLANE + idx] = pack8(bl);
+        dst[OP_TB + idx] = pack8(th);
+        dst[OP_TB + PLANE + idx] = pack8(tl);
+        dst[OP_B + idx] = pack8(bh);
+        dst[OP_B + PLANE + idx] = pack8(bl);
+    }
+
+    // ---- W = TB (K e^G): wave w forms token tile w for all 128 channels ----
+    {
+        bf16x8_t TBh[2], TBl[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int t = tok_of(w, i16), s0 = 32 * ks + 8 * g4;
+            uint16_t th[8], tl[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int s = s0 + e;
+                split((s <= t) ? sm.u.T[t][s] * sm.beta[s] : 0.f, th[e], tl[e]);
+            }
+            TBh[ks] = as_op(pack8(th));
+            TBl[ks] = as_op(pack8(tl));
+        }
+        f32x4 acc[8];
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct) {
+            acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const bf16x8_t kg = as_op(*reinterpret_cast<const uint4*>(&sm.KgT[16 * ct + i16][32 * ks + 8 * g4]));
+                acc[ct] = mfma(TBh[ks], kg, acc[ct]);
+                acc[ct] = mfma(TBl[ks], kg, acc[ct]);
+            }
+        }
+        __syncthreads();  // every read of T is done: its storage becomes W
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sm.u.W[tok_of(w, 4 * g4 + e)][16 * ct + i16] = acc[ct][e];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int idx = tid + NT * r;  // (w', mt, lane)
+        const int ws = idx >> 8, mt = (idx >> 6) & 3, ln = idx & 63;
+        const int t = tok_of(mt, ln & 15), c0 = SL * ws + 8 * (ln >> 4);
+        const float4 a = *reinterpret_cast<const float4*>(&sm.u.W[t][c0]);
+        const float4 bq = *reinterpret_cast<const float4*>(&sm.u.W[t][c0 + 4]);
+        const float x[8] = {a.x, a.y, a.z, a.w, bq.x, bq.y, bq.z, bq.w};
+        uint16_t wh[8], wl[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) split(x[e], wh[e], wl[e]);
+        dst[OP_W + idx] = pack8(wh);
+        dst[OP_W + 2 * PLANE + idx] = pack8(wl);
     }
 }
 
 // ---------------------------------------------------------------------------
 // scan: per (sequence, head, 16 value columns) the recurrence over chunks.
+// Wave w owns state rows 32w .. 32w+31.  Per chunk it forms its partial
+// W S and (Q e^G) S over those rows (and TB V for its token tile), the four
+// waves exchange the partials through LDS with one barrier, then each wave
+// forms U = TB V - W S for the whole chunk, its token tile of O and its rows
+// of the next state.
 // ---------------------------------------------------------------------------
-// LDS of the scan workgroup.  Staging areas are private to a wave and reused
-// every chunk; the exchange area and TB alternate between two parities so
-// that one barrier per chunk suffices.
-template <typename TIn>
 struct ScanSmem {
-    static constexpr bool KSTAGE = sizeof(TIn) == 2;  // bf16 keys are staged for the transpose
-    float G[4][C][SL + 4];                      // per wave: cumulative log-decay of its 32 rows
-    uint16_t K[KSTAGE ? 4 : 1][C][SL + 8];      // per wave: its 32 key channels (bf16)
-    struct Ex { f32x4 X[4][64]; f32x4 P[4][64]; } ex[2][4];  // partial (K e^G) S, (Q e^G) S
-    uint4 tb[2][2 * PLANE];                     // TB hi, lo of the chunk
+    struct Ex { f32x4 Y[4][64]; f32x4 P[4][64]; } ex[2][4];  // by chunk parity, wave
 };
 
 struct ScanParams {
-    const void* q;
-    const void* k;
     const void* v;
-    const float* g;
     const int32_t* cu;
     const int32_t* chunk_start;
     const int32_t* snap_base;
@@ -500,87 +641,73 @@ struct ScanParams {
     int interval;
     int H, dk, dv;
     int ntiles, nwg;
-    int out_bf16;
     float scale;
 };
 
-// One chunk's inputs for one lane, loaded a chunk ahead.
+// One chunk's operands for one lane, loaded a chunk ahead.
 template <typename TIn>
-struct ScanPrefetch {
-    using IO = In<TIn>;
-    uint4 bo[2][2];                // B rows of this wave's token tile: [ks][hi, lo]
-    float4 g[8];                   // g of tokens 8*(lane/8)+r, channels 4*(lane%8)..+3
-    typename IO::V8 ka[4];         // k at (tok_of(mt, lane%16), channels 8*(lane/16)..+7)
-    typename IO::V8 qa[4];         // q at the same positions
-    typename IO::V1 v[4][4];       // v at (tok_of(mt, 4*(lane/16)+e), column j)
+struct ScanOps {
+    uint4 w[4][2];        // W       [mt][hi, lo]
+    uint4 q[4][2];        // Qd      [mt][hi, lo]
+    uint4 kd[2][2][2];    // Kd      [m][ks][hi, lo]
+    uint4 tb[2][2];       // TB rows of this wave's token tile [ks][hi, lo]
+    uint4 b[2][2];        // B  rows of this wave's token tile [ks][hi, lo]
+    float4 dec[2];        // e^{G_C} of the lane's state rows
+    typename In<TIn>::V1 v[2][8];  // v at tokens 32ks + 8*(lane/16) + e, column j
 };
 
 template <typename TIn>
-__device__ __forceinline__ void scan_load(ScanPrefetch<TIn>& pf, const ScanParams& p, int64_t gc,
+__device__ __forceinline__ void scan_load(ScanOps<TIn>& o, const ScanParams& p, int64_t gc,
                                           int64_t row0, int n, int h, int j, int w, int lane) {
     using IO = In<TIn>;
-    const int g4 = lane >> 4, i16 = lane & 15;
-    const int dk = p.dk;
+    const int g4 = lane >> 4;
     const uint4* __restrict__ blk = p.ops + (gc * p.H + h) * CHUNK_OPS;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        const int x = (w * 4 + mt) * 64 + lane;
+        o.w[mt][0] = blk[OP_W + x];
+        o.w[mt][1] = blk[OP_W + 2 * PLANE + x];
+        o.q[mt][0] = blk[OP_Q + x];
+        o.q[mt][1] = blk[OP_Q + 2 * PLANE + x];
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int x = ((w * 2 + m) * 2 + ks) * 64 + lane;
+            o.kd[m][ks][0] = blk[OP_K + x];
+            o.kd[m][ks][1] = blk[OP_K + 2 * PLANE + x];
+        }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        const int x = (w * 2 + ks) * 64 + lane;
+        o.tb[ks][0] = blk[OP_TB + x];
+        o.tb[ks][1] = blk[OP_TB + PLANE + x];
+        o.b[ks][0] = blk[OP_B + x];
+        o.b[ks][1] = blk[OP_B + PLANE + x];
+    }
+    const float4* dec = reinterpret_cast<const float4*>(blk + OP_DEC);
+    o.dec[0] = dec[8 * w + 2 * g4];
+    o.dec[1] = dec[8 * w + 2 * g4 + 1];
+    // v rows past the chunk end are read from its last row; TB has zero
+    // columns there, so they never reach U
+    const int64_t vrow = (int64_t)p.H * p.dv;
+    const int64_t vbase = (row0 * p.H + h) * (int64_t)p.dv + j;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int pl = 0; pl < 2; ++pl)
-            pf.bo[ks][pl] = blk[(2 + pl) * PLANE + (w * 2 + ks) * 64 + lane];
-    {
-        const int cg = SL * w + 4 * (lane & 7), tq = 8 * (lane >> 3);
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int t = tq + r;
-            pf.g[r] = (t < n && cg < dk)
-                          ? *reinterpret_cast<const float4*>(p.g + ((row0 + t) * p.H + h) * (int64_t)dk + cg)
-                          : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-    }
-    {
-        const int c = SL * w + 8 * g4;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            const int t = tok_of(mt, i16);
-            const bool ok = t < n && c < dk;
-            const int64_t idx = ((row0 + t) * p.H + h) * (int64_t)dk + c;
-            pf.ka[mt] = ok ? IO::load8(p.k, idx) : IO::zero8();
-            pf.qa[mt] = ok ? IO::load8(p.q, idx) : IO::zero8();
-        }
-    }
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int t = tok_of(mt, 4 * g4 + e);
-            pf.v[mt][e] = t < n ? IO::load1(p.v, ((row0 + t) * p.H + h) * (int64_t)p.dv + j)
-                                : typename IO::V1(0);
-        }
+        for (int e = 0; e < 8; ++e)
+            o.v[ks][e] = IO::load1(p.v, vbase + (int64_t)min(32 * ks + 8 * g4 + e, n - 1) * vrow);
 }
 
-// This thread's share (4 x 16 bytes) of a chunk's TB hi and lo planes.
-struct TbShare {
-    uint4 a, b, c, d;
-};
-__device__ __forceinline__ TbShare load_tb(const ScanParams& p, int64_t gc, int h, int tid) {
-    const uint4* __restrict__ blk = p.ops + (gc * p.H + h) * CHUNK_OPS;
-    return TbShare{blk[tid], blk[tid + NT], blk[tid + 2 * NT], blk[tid + 3 * NT]};
-}
-__device__ __forceinline__ void store_tb(uint4* dst, const TbShare& s, int tid) {
-    dst[tid] = s.a;
-    dst[tid + NT] = s.b;
-    dst[tid + 2 * NT] = s.c;
-    dst[tid + 3 * NT] = s.d;
-}
-
-template <typename TIn>
+template <typename TIn, bool OUT_BF16>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void scan_kernel(ScanParams p) {
     using IO = In<TIn>;
-    using SM = ScanSmem<TIn>;
-    __shared__ SM sm;
+    __shared__ ScanSmem sm;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int g4 = lane >> 4, i16 = lane & 15;
+    (void)tid;
 
     // workgroup -> (sequence, head, value tile).  Workgroups are dealt
     // round-robin over the 8 XCDs; the remap gives each XCD a contiguous
@@ -597,7 +724,6 @@ void scan_kernel(ScanParams p) {
     const int nch = (len + C - 1) / C;
     const int64_t cbase = p.chunk_start[b];
     const int64_t sbase = p.snap_base[b];
-    float (*Gs)[SL + 4] = sm.G[w];
 
     // state rows of this lane: 32w + chan_of(m, 4*g4 + e) = 32w + 8*g4 + 4m + e
     f32x4 S[2];
@@ -607,148 +733,92 @@ void scan_kernel(ScanParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int c = SL * w + 8 * g4 + 4 * m + e;
-            S[m][e] = (p.init && c < dk) ? p.init[(srow + c) * dv + j] : 0.f;
+            S[m][e] = 0.f;
+            if (p.init) {
+                const float x = p.init[(srow + (c < dk ? c : 0)) * dv + j];
+                S[m][e] = c < dk ? x : 0.f;
+            }
         }
 
-    ScanPrefetch<TIn> pf;
-    if (nch > 0) {
-        store_tb(sm.tb[0], load_tb(p, cbase, h, tid), tid);
-        scan_load<TIn>(pf, p, cbase, seq0, min(C, len), h, j, w, lane);
-        lds_barrier();
-    }
+    // Operands are prefetched one chunk ahead into two register sets used in
+    // turn (the loop body is instantiated twice with the roles swapped), so
+    // no loaded value is copied and nothing waits early for the next chunk.
+    ScanOps<TIn> opA, opB;
+    if (nch > 0) scan_load<TIn>(opA, p, cbase, seq0, min(C, len), h, j, w, lane);
 
-    for (int ci = 0; ci < nch; ++ci) {
+    auto chunk = [&](const int ci, ScanOps<TIn>& o, ScanOps<TIn>& nx) {
         const int par = ci & 1;
         const int64_t row0 = seq0 + (int64_t)ci * C;
         const int n = min(C, len - ci * C);
 
-        // ---- (a) stage the cumulative log-decay (and bf16 keys) of this chunk ----
-        typename IO::V1 vcur[4][4];
-        uint4 bcur[2][2];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) vcur[mt][e] = pf.v[mt][e];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) { bcur[ks][0] = pf.bo[ks][0]; bcur[ks][1] = pf.bo[ks][1]; }
-        {
-            // lane scan over its 8 tokens, then an exclusive scan over the 8 token groups
-            float4 run = pf.g[0];
-            float4 Gl[8];
-            Gl[0] = run;
-#pragma unroll
-            for (int r = 1; r < 8; ++r) {
-                run.x += pf.g[r].x; run.y += pf.g[r].y; run.z += pf.g[r].z; run.w += pf.g[r].w;
-                Gl[r] = run;
-            }
-            float4 incl = run;
-#pragma unroll
-            for (int off = 8; off < 64; off <<= 1) {
-                float4 y;
-                y.x = __shfl_up(incl.x, off, 64); y.y = __shfl_up(incl.y, off, 64);
-                y.z = __shfl_up(incl.z, off, 64); y.w = __shfl_up(incl.w, off, 64);
-                if (lane >= off) { incl.x += y.x; incl.y += y.y; incl.z += y.z; incl.w += y.w; }
-            }
-            const float4 excl = make_float4(incl.x - run.x, incl.y - run.y, incl.z - run.z, incl.w - run.w);
-            const int cq = 4 * (lane & 7), tq = 8 * (lane >> 3);
-#pragma unroll
-            for (int r = 0; r < 8; ++r)
-                *reinterpret_cast<float4*>(&Gs[tq + r][cq]) =
-                    make_float4(Gl[r].x + excl.x, Gl[r].y + excl.y, Gl[r].z + excl.z, Gl[r].w + excl.w);
-        }
-        if constexpr (SM::KSTAGE) {
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-                *reinterpret_cast<uint4*>(&sm.K[w][tok_of(mt, i16)][8 * g4]) = pf.ka[mt];
-        }
-        lds_wave_sync();
+        // ---- prefetch the next chunk (the last chunk reloads itself, so the
+        // same loads are issued on every path; that data is unused) ----
+        const int cn = min(ci + 1, nch - 1);
+        scan_load<TIn>(nx, p, cbase + cn, seq0 + (int64_t)cn * C, min(C, len - cn * C), h, j, w, lane);
 
-        // ---- (b) decay-scaled operands of the products with the old state ----
-        bf16x8_t Kg[4], Qh[4], Ql[4];
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-            const int t = tok_of(mt, i16);
-            const float4 ga = *reinterpret_cast<const float4*>(&Gs[t][8 * g4]);
-            const float4 gb = *reinterpret_cast<const float4*>(&Gs[t][8 * g4 + 4]);
-            const float Gv[8] = {ga.x, ga.y, ga.z, ga.w, gb.x, gb.y, gb.z, gb.w};
-            float kv[8], qv[8];
-            IO::f32x8(pf.ka[mt], kv);
-            IO::f32x8(pf.qa[mt], qv);
-            uint16_t xk[8], xh[8], xl[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float eg = ex(Gv[e]);
-                xk[e] = bfb(kv[e] * eg);
-                split(qv[e] * eg, xh[e], xl[e]);
-            }
-            Kg[mt] = as_op(pack8(xk));
-            Qh[mt] = as_op(pack8(xh));
-            Ql[mt] = as_op(pack8(xl));
-        }
-
-        // ---- (c) prefetch the next chunk ----
-        TbShare tbn{};
-        if (ci + 1 < nch) {
-            tbn = load_tb(p, cbase + ci + 1, h, tid);
-            scan_load<TIn>(pf, p, cbase + ci + 1, row0 + C, min(C, len - (ci + 1) * C), h, j, w,
-                           lane);
-        }
-
-        // ---- (d) partial (K e^G) S and (Q e^G) S over this wave's 32 rows ----
+        // ---- partial W S and (Q e^G) S over this wave's rows; TB V ----
         {
             bf16x8_t Sh, Sl;
             pack_split(S[0], S[1], Sh, Sl);
+            f32x4 ut = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const bf16x8_t th = as_op(o.tb[ks][0]), tl = as_op(o.tb[ks][1]);
+                if constexpr (sizeof(TIn) == 2) {
+                    uint4 vp;  // 16-bit loads arrive zero-extended: pack the pairs
+                    vp.x = pin(o.v[ks][0]) | (pin(o.v[ks][1]) << 16);
+                    vp.y = pin(o.v[ks][2]) | (pin(o.v[ks][3]) << 16);
+                    vp.z = pin(o.v[ks][4]) | (pin(o.v[ks][5]) << 16);
+                    vp.w = pin(o.v[ks][6]) | (pin(o.v[ks][7]) << 16);
+                    const bf16x8_t vb = as_op(vp);
+                    ut = mfma(th, vb, ut);
+                    ut = mfma(tl, vb, ut);
+                } else {
+                    uint16_t vh[8], vl[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) split(pin(IO::f32(o.v[ks][e])), vh[e], vl[e]);
+                    const bf16x8_t bh = as_op(pack8(vh)), bl = as_op(pack8(vl));
+                    ut = mfma(th, bh, ut);
+                    ut = mfma(th, bl, ut);
+                    ut = mfma(tl, bh, ut);
+                }
+            }
             const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            typename SM::Ex& E = sm.ex[par][w];
+            ScanSmem::Ex& E = sm.ex[par][w];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                f32x4 x = mfma(Kg[mt], Sh, z);
-                x = mfma(Kg[mt], Sl, x);
-                f32x4 pq = mfma(Qh[mt], Sh, z);
-                pq = mfma(Qh[mt], Sl, pq);
-                pq = mfma(Ql[mt], Sh, pq);
-                E.X[mt][lane] = x;
+                const bf16x8_t wh = as_op(o.w[mt][0]), wl = as_op(o.w[mt][1]);
+                f32x4 y = mfma(wh, Sh, z);
+                y = mfma(wh, Sl, y);
+                y = mfma(wl, Sh, y);
+                if (mt == w) y -= ut;   // Y_w[w] = (W S)_w - TB V, so U = -sum_w Y_w
+                const bf16x8_t qh = as_op(o.q[mt][0]), ql = as_op(o.q[mt][1]);
+                f32x4 pq = mfma(qh, Sh, z);
+                pq = mfma(qh, Sl, pq);
+                pq = mfma(ql, Sh, pq);
+                E.Y[mt][lane] = y;
                 E.P[mt][lane] = pq;
             }
         }
         lds_barrier();
 
-        // ---- (e) U = TB (V - (K e^G) S) for all tokens of the chunk ----
+        // ---- U = TB V - W S for every token of the chunk ----
         bf16x8_t Uh[2], Ul[2];
         {
-            f32x4 D[4];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                f32x4 xs = sm.ex[par][0].X[mt][lane];
-                xs += sm.ex[par][1].X[mt][lane];
-                xs += sm.ex[par][2].X[mt][lane];
-                xs += sm.ex[par][3].X[mt][lane];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) D[mt][e] = IO::f32(vcur[mt][e]) - xs[e];
-            }
-            bf16x8_t Dh[2], Dl[2];
-            pack_split(D[0], D[1], Dh[0], Dl[0]);
-            pack_split(D[2], D[3], Dh[1], Dl[1]);
-            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
             f32x4 U[4];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                f32x4 u = z;
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const bf16x8_t th = as_op(sm.tb[par][(mt * 2 + ks) * 64 + lane]);
-                    const bf16x8_t tl = as_op(sm.tb[par][PLANE + (mt * 2 + ks) * 64 + lane]);
-                    u = mfma(th, Dh[ks], u);
-                    u = mfma(th, Dl[ks], u);
-                    u = mfma(tl, Dh[ks], u);
-                }
-                U[mt] = u;
+                f32x4 ys = sm.ex[par][0].Y[mt][lane];
+                ys += sm.ex[par][1].Y[mt][lane];
+                ys += sm.ex[par][2].Y[mt][lane];
+                ys += sm.ex[par][3].Y[mt][lane];
+                U[mt] = -ys;
             }
             pack_split(U[0], U[1], Uh[0], Ul[0]);
             pack_split(U[2], U[3], Uh[1], Ul[1]);
         }
 
-        // ---- (f) this wave's token tile of O = scale ((Q e^G) S + B U) ----
+        // ---- this wave's token tile of O = scale ((Q e^G) S + B U) ----
         {
             f32x4 po = sm.ex[par][0].P[w][lane];
             po += sm.ex[par][1].P[w][lane];
@@ -757,7 +827,7 @@ void scan_kernel(ScanParams p) {
             f32x4 bu = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8_t bh = as_op(bcur[ks][0]), bl = as_op(bcur[ks][1]);
+                const bf16x8_t bh = as_op(o.b[ks][0]), bl = as_op(o.b[ks][1]);
                 bu = mfma(bh, Uh[ks], bu);
                 bu = mfma(bh, Ul[ks], bu);
                 bu = mfma(bl, Uh[ks], bu);
@@ -766,66 +836,47 @@ void scan_kernel(ScanParams p) {
             for (int e = 0; e < 4; ++e) {
                 const int t = tok_of(w, 4 * g4 + e);
                 if (t < n) {
-                    const float o = p.scale * (po[e] + bu[e]);
+                    const float ov = p.scale * (po[e] + bu[e]);
                     const int64_t oi = ((row0 + t) * p.H + h) * (int64_t)dv + j;
-                    if (p.out_bf16)
-                        static_cast<uint16_t*>(p.out)[oi] = bfb(o);
+                    if constexpr (OUT_BF16)
+                        static_cast<uint16_t*>(p.out)[oi] = bfb(ov);
                     else
-                        static_cast<float*>(p.out)[oi] = o;
+                        static_cast<float*>(p.out)[oi] = ov;
                 }
             }
         }
 
-        // ---- (g) S <- Diag(e^{G_C}) S + (K e^{G_C - G})^T U ----
-        {
-            const float4 gca = *reinterpret_cast<const float4*>(&Gs[C - 1][8 * g4]);
-            const float4 gcb = *reinterpret_cast<const float4*>(&Gs[C - 1][8 * g4 + 4]);
-            const f32x4 dec[2] = {f32x4{ex(gca.x), ex(gca.y), ex(gca.z), ex(gca.w)},
-                                  f32x4{ex(gcb.x), ex(gcb.y), ex(gcb.z), ex(gcb.w)}};
+        // ---- S <- Diag(e^{G_C}) S + (K e^{G_C - G})^T U ----
 #pragma unroll
-            for (int m = 0; m < 2; ++m) {
-                const int cl = chan_of(m, i16);
-                const float gcl = Gs[C - 1][cl];
-                f32x4 s = S[m] * dec[m];
+        for (int m = 0; m < 2; ++m) {
+            const float4 d = o.dec[m];
+            f32x4 s = S[m] * f32x4{d.x, d.y, d.z, d.w};
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    uint16_t hh[8], ll[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int t = 32 * ks + 8 * g4 + e;
-                        float kv;
-                        if constexpr (SM::KSTAGE) {
-                            kv = bff(sm.K[w][t][cl]);
-                        } else {
-                            kv = (t < n && SL * w + cl < dk)
-                                     ? IO::f32(IO::load1(p.k, ((row0 + t) * p.H + h) * (int64_t)dk + SL * w + cl))
-                                     : 0.f;
-                        }
-                        split(kv * ex(gcl - Gs[t][cl]), hh[e], ll[e]);
-                    }
-                    const bf16x8_t kh = as_op(pack8(hh)), kl = as_op(pack8(ll));
-                    s = mfma(kh, Uh[ks], s);
-                    s = mfma(kh, Ul[ks], s);
-                    s = mfma(kl, Uh[ks], s);
-                }
-                S[m] = s;
+            for (int ks = 0; ks < 2; ++ks) {
+                const bf16x8_t kh = as_op(o.kd[m][ks][0]), kl = as_op(o.kd[m][ks][1]);
+                s = mfma(kh, Uh[ks], s);
+                s = mfma(kh, Ul[ks], s);
+                s = mfma(kl, Uh[ks], s);
             }
+            S[m] = s;
         }
         const int done = ci * C + n;
         if (p.interval > 0 && done % p.interval == 0) {
-            float* __restrict__ dst =
+            float* __restrict__ dsts =
                 p.snapshots + ((sbase + done / p.interval - 1) * p.H + h) * (int64_t)dk * dv;
 #pragma unroll
             for (int m = 0; m < 2; ++m)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int c = SL * w + 8 * g4 + 4 * m + e;
-                    if (c < dk) dst[(int64_t)c * dv + j] = S[m][e];
+                    if (c < dk) dsts[(int64_t)c * dv + j] = S[m][e];
                 }
         }
+    };
 
-        // ---- (h) TB of the next chunk into the other parity ----
-        if (ci + 1 < nch) store_tb(sm.tb[par ^ 1], tbn, tid);
+    for (int ci = 0; ci < nch; ci += 2) {
+        chunk(ci, opA, opB);
+        if (ci + 1 < nch) chunk(ci + 1, opB, opA);
     }
 
 #pragma unroll
@@ -887,10 +938,7 @@ hipError_t launch_t(const PrefillArgs& a) {
     }
 
     ScanParams sp{};
-    sp.q = a.q;
-    sp.k = a.k;
     sp.v = a.v;
-    sp.g = a.g;
     sp.cu = a.cu_dev;
     sp.chunk_start = chunk_start;
     sp.snap_base = snap_base;
@@ -904,11 +952,13 @@ hipError_t launch_t(const PrefillArgs& a) {
     sp.dk = a.dk;
     sp.dv = a.dv;
     sp.ntiles = a.dv / 16;
-    sp.out_bf16 = a.out_bf16 ? 1 : 0;
     sp.scale = a.scale;
     const int64_t nwg = (int64_t)a.num_seqs * a.H * sp.ntiles;
     sp.nwg = (int)nwg;
-    hipLaunchKernelGGL((scan_kernel<TIn>), dim3((unsigned)nwg), dim3(NT), 0, a.stream, sp);
+    if (a.out_bf16)
+        hipLaunchKernelGGL((scan_kernel<TIn, true>), dim3((unsigned)nwg), dim3(NT), 0, a.stream, sp);
+    else
+        hipLaunchKernelGGL((scan_kernel<TIn, false>), dim3((unsigned)nwg), dim3(NT), 0, a.stream, sp);
     return hipGetLastError();
 }
 
