@@ -95,20 +95,6 @@ __device__ __forceinline__ uint4 pack8(const uint16_t (&x)[8]) {
 }
 __device__ __forceinline__ bf16x8_t as_op(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
 
-// Returns x unchanged, but the compiler cannot move arithmetic on x across
-// this point.  Applied to prefetched values where they are consumed, it keeps
-// the compiler from hoisting that arithmetic back next to the loads (which
-// would make the loads' issuer wait for their data).
-__device__ __forceinline__ uint32_t pin(uint16_t x16) {
-    uint32_t x = x16;
-    asm volatile("" : "+v"(x));
-    return x;
-}
-__device__ __forceinline__ float pin(float x) {
-    asm volatile("" : "+v"(x));
-    return x;
-}
-
 // Two accumulator tiles (row blocks 0 and 1 of a 32-row K-step) as one MFMA
 // operand: elements 0..3 come from tile 0, 4..7 from tile 1, split hi / lo.
 __device__ __forceinline__ void pack_split(const f32x4& x0, const f32x4& x1, bf16x8_t& hi,
@@ -624,8 +610,10 @@ void prep_kernel(PrepParams p) {
 // forms U = TB V - W S for the whole chunk, its token tile of O and its rows
 // of the next state.
 // ---------------------------------------------------------------------------
+template <typename TIn>
 struct ScanSmem {
     struct Ex { f32x4 Y[4][64]; f32x4 P[4][64]; } ex[2][4];  // by chunk parity, wave
+    TIn vt[4][C][16 + 16 / sizeof(TIn)];                  // per wave: the v tile, row-major
 };
 
 struct ScanParams {
@@ -653,23 +641,60 @@ struct ScanOps {
     uint4 tb[2][2];       // TB rows of this wave's token tile [ks][hi, lo]
     uint4 b[2][2];        // B  rows of this wave's token tile [ks][hi, lo]
     float4 dec[2];        // e^{G_C} of the lane's state rows
-    typename In<TIn>::V1 v[2][8];  // v at tokens 32ks + 8*(lane/16) + e, column j
+    typename In<TIn>::V8 v[2];     // v rows 32r + lane/2, columns 8*(lane%2) .. +7 of the tile
 };
 
+// The next chunk's operands are loaded in three parts spread over the
+// current chunk, so the wave never stalls on a full memory queue.
 template <typename TIn>
-__device__ __forceinline__ void scan_load(ScanOps<TIn>& o, const ScanParams& p, int64_t gc,
-                                          int64_t row0, int n, int h, int j, int w, int lane) {
-    using IO = In<TIn>;
-    const int g4 = lane >> 4;
-    const uint4* __restrict__ blk = p.ops + (gc * p.H + h) * CHUNK_OPS;
+__device__ __forceinline__ const uint4* scan_block(const ScanParams& p, int64_t gc, int h) {
+    return p.ops + (gc * p.H + h) * CHUNK_OPS;
+}
+
+template <typename TIn>
+__device__ __forceinline__ void scan_load1(ScanOps<TIn>& o, const uint4* __restrict__ blk, int w,
+                                           int lane) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
         const int x = (w * 4 + mt) * 64 + lane;
         o.w[mt][0] = blk[OP_W + x];
         o.w[mt][1] = blk[OP_W + 2 * PLANE + x];
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        const int x = (w * 2 + ks) * 64 + lane;
+        o.tb[ks][0] = blk[OP_TB + x];
+        o.tb[ks][1] = blk[OP_TB + PLANE + x];
+    }
+}
+
+template <typename TIn>
+__device__ __forceinline__ void scan_load2(ScanOps<TIn>& o, const uint4* __restrict__ blk,
+                                           const ScanParams& p, int64_t row0, int n, int h, int j16,
+                                           int w, int lane) {
+    using IO = In<TIn>;
+    const int g4 = lane >> 4;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        const int x = (w * 4 + mt) * 64 + lane;
         o.q[mt][0] = blk[OP_Q + x];
         o.q[mt][1] = blk[OP_Q + 2 * PLANE + x];
     }
+    (void)g4;
+    // the wave's copy of the chunk's v tile (64 rows x 16 columns), row-major:
+    // rows past the chunk end are read from its last row; TB has zero columns
+    // there, so they never reach U
+    const int64_t vrow = (int64_t)p.H * p.dv;
+    const int64_t vbase = (row0 * p.H + h) * (int64_t)p.dv + j16 + 8 * (lane & 1);
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+        o.v[r] = IO::load8(p.v, vbase + (int64_t)min(32 * r + (lane >> 1), n - 1) * vrow);
+}
+
+template <typename TIn>
+__device__ __forceinline__ void scan_load3(ScanOps<TIn>& o, const uint4* __restrict__ blk, int w,
+                                           int lane) {
+    const int g4 = lane >> 4;
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -681,30 +706,28 @@ __device__ __forceinline__ void scan_load(ScanOps<TIn>& o, const ScanParams& p, 
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
         const int x = (w * 2 + ks) * 64 + lane;
-        o.tb[ks][0] = blk[OP_TB + x];
-        o.tb[ks][1] = blk[OP_TB + PLANE + x];
         o.b[ks][0] = blk[OP_B + x];
         o.b[ks][1] = blk[OP_B + PLANE + x];
     }
     const float4* dec = reinterpret_cast<const float4*>(blk + OP_DEC);
     o.dec[0] = dec[8 * w + 2 * g4];
     o.dec[1] = dec[8 * w + 2 * g4 + 1];
-    // v rows past the chunk end are read from its last row; TB has zero
-    // columns there, so they never reach U
-    const int64_t vrow = (int64_t)p.H * p.dv;
-    const int64_t vbase = (row0 * p.H + h) * (int64_t)p.dv + j;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            o.v[ks][e] = IO::load1(p.v, vbase + (int64_t)min(32 * ks + 8 * g4 + e, n - 1) * vrow);
+}
+
+template <typename TIn>
+__device__ __forceinline__ void scan_load(ScanOps<TIn>& o, const ScanParams& p, int64_t gc,
+                                          int64_t row0, int n, int h, int j16, int w, int lane) {
+    const uint4* blk = scan_block<TIn>(p, gc, h);
+    scan_load1<TIn>(o, blk, w, lane);
+    scan_load2<TIn>(o, blk, p, row0, n, h, j16, w, lane);
+    scan_load3<TIn>(o, blk, w, lane);
 }
 
 template <typename TIn, bool OUT_BF16>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void scan_kernel(ScanParams p) {
     using IO = In<TIn>;
-    __shared__ ScanSmem sm;
+    __shared__ ScanSmem<TIn> sm;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int g4 = lane >> 4, i16 = lane & 15;
     (void)tid;
@@ -744,7 +767,7 @@ void scan_kernel(ScanParams p) {
     // turn (the loop body is instantiated twice with the roles swapped), so
     // no loaded value is copied and nothing waits early for the next chunk.
     ScanOps<TIn> opA, opB;
-    if (nch > 0) scan_load<TIn>(opA, p, cbase, seq0, min(C, len), h, j, w, lane);
+    if (nch > 0) scan_load<TIn>(opA, p, cbase, seq0, min(C, len), h, 16 * tile, w, lane);
 
     auto chunk = [&](const int ci, ScanOps<TIn>& o, ScanOps<TIn>& nx) {
         const int par = ci & 1;
@@ -754,29 +777,43 @@ void scan_kernel(ScanParams p) {
         // ---- prefetch the next chunk (the last chunk reloads itself, so the
         // same loads are issued on every path; that data is unused) ----
         const int cn = min(ci + 1, nch - 1);
-        scan_load<TIn>(nx, p, cbase + cn, seq0 + (int64_t)cn * C, min(C, len - cn * C), h, j, w, lane);
+        const uint4* nblk = scan_block<TIn>(p, cbase + cn, h);
+        scan_load1<TIn>(nx, nblk, w, lane);
 
         // ---- partial W S and (Q e^G) S over this wave's rows; TB V ----
         {
             bf16x8_t Sh, Sl;
             pack_split(S[0], S[1], Sh, Sl);
+            // v tile through the wave's LDS area: rows in, K-ordered columns out
+            TIn (*vt)[16 + 16 / sizeof(TIn)] = sm.vt[w];
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                TIn* row = &vt[32 * r + (lane >> 1)][8 * (lane & 1)];
+                if constexpr (sizeof(TIn) == 2) {
+                    *reinterpret_cast<uint4*>(row) = o.v[r];
+                } else {
+                    reinterpret_cast<float4*>(row)[0] = o.v[r].a;
+                    reinterpret_cast<float4*>(row)[1] = o.v[r].b;
+                }
+            }
+            lds_wave_sync();
             f32x4 ut = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 const bf16x8_t th = as_op(o.tb[ks][0]), tl = as_op(o.tb[ks][1]);
                 if constexpr (sizeof(TIn) == 2) {
-                    uint4 vp;  // 16-bit loads arrive zero-extended: pack the pairs
-                    vp.x = pin(o.v[ks][0]) | (pin(o.v[ks][1]) << 16);
-                    vp.y = pin(o.v[ks][2]) | (pin(o.v[ks][3]) << 16);
-                    vp.z = pin(o.v[ks][4]) | (pin(o.v[ks][5]) << 16);
-                    vp.w = pin(o.v[ks][6]) | (pin(o.v[ks][7]) << 16);
-                    const bf16x8_t vb = as_op(vp);
+                    uint16_t vv[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        vv[e] = reinterpret_cast<const uint16_t&>(vt[32 * ks + 8 * g4 + e][i16]);
+                    const bf16x8_t vb = as_op(pack8(vv));
                     ut = mfma(th, vb, ut);
                     ut = mfma(tl, vb, ut);
                 } else {
                     uint16_t vh[8], vl[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) split(pin(IO::f32(o.v[ks][e])), vh[e], vl[e]);
+                    for (int e = 0; e < 8; ++e)
+                        split(reinterpret_cast<const float&>(vt[32 * ks + 8 * g4 + e][i16]), vh[e], vl[e]);
                     const bf16x8_t bh = as_op(pack8(vh)), bl = as_op(pack8(vl));
                     ut = mfma(th, bh, ut);
                     ut = mfma(th, bl, ut);
@@ -784,7 +821,7 @@ void scan_kernel(ScanParams p) {
                 }
             }
             const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            ScanSmem::Ex& E = sm.ex[par][w];
+            typename ScanSmem<TIn>::Ex& E = sm.ex[par][w];
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
                 const bf16x8_t wh = as_op(o.w[mt][0]), wl = as_op(o.w[mt][1]);
@@ -800,6 +837,8 @@ void scan_kernel(ScanParams p) {
                 E.P[mt][lane] = pq;
             }
         }
+        scan_load2<TIn>(nx, nblk, p, seq0 + (int64_t)cn * C, min(C, len - cn * C), h, 16 * tile, w,
+                        lane);
         lds_barrier();
 
         // ---- U = TB V - W S for every token of the chunk ----
@@ -817,6 +856,8 @@ void scan_kernel(ScanParams p) {
             pack_split(U[0], U[1], Uh[0], Ul[0]);
             pack_split(U[2], U[3], Uh[1], Ul[1]);
         }
+
+        scan_load3<TIn>(nx, nblk, w, lane);
 
         // ---- this wave's token tile of O = scale ((Q e^G) S + B U) ----
         {
