@@ -48,6 +48,8 @@
 // number of value tiles nor on where a sequence sits in the packed batch,
 // and chunks restart at every sequence start, so resuming from a snapshot
 // reproduces the uninterrupted run bit for bit.
+#include <algorithm>
+
 #include "kda_common.h"
 #include "kda_internal.h"
 
@@ -144,6 +146,7 @@ template <> struct In<bf16_t> {
         return static_cast<const uint16_t*>(base)[idx];
     }
     __device__ __forceinline__ static float f32(V1 x) { return bff(x); }
+    __device__ __forceinline__ static float f32(bf16_t x) { return bff(x.bits); }
 };
 template <> struct In<float> {
     struct V8 { float4 a, b; };
@@ -228,7 +231,9 @@ constexpr int OP_K = 12 * PLANE;
 constexpr int OP_DEC = 16 * PLANE;
 constexpr int CHUNK_OPS = 16 * PLANE + 32;
 
+template <typename TIn>
 struct PrepSmem {
+    static constexpr int KP = DKP + 16 / (int)sizeof(TIn);  // padded row of staged keys, queries
     union {
         float G[C][DKP + 4];   // cumulative log-decay
         float T[C][C + 4];     // (I + A)^-1, once the decay-scaled operands are out
@@ -238,7 +243,10 @@ struct PrepSmem {
         float A[C][C + 1];     // strictly lower b_t sum_c k_t k_s e^{G_t - G_s}
         float B[C][C + 1];     // lower sum_c q_t k_s e^{G_t - G_s}, once T is formed
     } ab;
-    uint16_t KgT[DKP][C + 8];  // (K . e^G)^T in bf16, [channel][token]
+    union {
+        TIn kS[C][KP];             // the chunk's keys (zero past n and dk)
+        uint16_t KgT[DKP][C + 8];  // (K . e^G)^T in bf16, [channel][token], once kS is read
+    } k;
     float Bd[4][16][17];       // diagonal blocks of B from the pairwise path
     float M[3][16][17];
     float beta[C];
@@ -255,350 +263,435 @@ struct PrepParams {
     int H, dk, num_seqs;
 };
 
-template <typename TIn>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void prep_kernel(PrepParams p) {
-    using IO = In<TIn>;
-    __shared__ PrepSmem sm;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int g4 = lane >> 4, i16 = lane & 15;
-    const int gc = blockIdx.x, h = blockIdx.y;
+// Location of one (chunk, head) item.
+struct PrepItem {
+    int h, n;          // head; valid rows of the chunk (1 .. C)
+    int64_t gc, row0;  // global chunk index; first packed row
+};
 
+__device__ __forceinline__ PrepItem prep_item(const PrepParams& p, int it) {
+    PrepItem r;
+    const int gc = it / p.H;
+    r.h = it - gc * p.H;
+    r.gc = gc;
     // sequence of this chunk: the last b with chunk_start[b] <= gc
     int lo = 0, hi = p.num_seqs;  // invariant: chunk_start[lo] <= gc < chunk_start[hi]
     while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
         if (p.chunk_start[mid] <= gc) lo = mid; else hi = mid;
     }
-    const int b = lo;
-    const int ci = gc - p.chunk_start[b];
-    const int64_t row0 = (int64_t)p.cu[b] + (int64_t)ci * C;
-    const int len = p.cu[b + 1] - p.cu[b];
-    const int n = min(C, len - ci * C);
+    const int ci = gc - p.chunk_start[lo];
+    r.row0 = (int64_t)p.cu[lo] + (int64_t)ci * C;
+    r.n = min(C, p.cu[lo + 1] - p.cu[lo] - ci * C);
+    return r;
+}
+
+// This thread's share of one item's raw inputs: g rows 8r + tid/32, channels
+// 4*(tid%32)..+3; k, q rows 16r + tid/16, channels 8*(tid%16)..+7; beta of
+// row tid (tid < 64).  Rows past the chunk end are read from its last row
+// and channels past dk from channel 0; the values are masked when staged.
+template <typename TIn>
+struct PrepRaw {
+    float4 g[8];
+    typename In<TIn>::V8 k[4];
+    typename In<TIn>::V8 qg[4];  // q at (16w + lane%16, 32ks + 8*(lane/16)), ks = 0..3
+    typename In<TIn>::V8 qd[4];  // q at (tok_of(mt, lane%16), 32w' + 8*(lane/16)) of unit r
+    float beta;
+};
+
+template <typename TIn>
+__device__ __forceinline__ void prep_load(PrepRaw<TIn>& r, const PrepParams& p, const PrepItem& x,
+                                          int tid) {
+    using IO = In<TIn>;
     const int dk = p.dk;
-    uint4* __restrict__ dst = p.ops + ((int64_t)gc * p.H + h) * CHUNK_OPS;
-    // row t (clamped into the chunk), channel c (clamped below dk) of a [T, H, dk] tensor
-    auto at = [&](int t, int c) -> int64_t {
-        return ((row0 + min(t, n - 1)) * p.H + h) * (int64_t)dk + (c < dk ? c : 0);
-    };
-
-    // ---- cumulative log-decay per channel (rows past n count as g = 0) ----
+    const int64_t rs = (int64_t)p.H * dk;                    // row stride
+    const int64_t base = (x.row0 * p.H + x.h) * (int64_t)dk;  // row 0, channel 0
     {
-        const int c = tid & 127, half = tid >> 7;
-        const bool cok = c < dk;
-        float run = 0.f;
-        float gv[32];
+        const int c = 4 * (tid & 31);
+        const int cl = c < dk ? c : 0;
 #pragma unroll
-        for (int r = 0; r < 32; ++r) {
-            const int t = half * 32 + r;
-            const float x = p.g[at(t, c)];
-            gv[r] = (t < n && cok) ? x : 0.f;
+        for (int i = 0; i < 8; ++i) {
+            const int t = 8 * i + (tid >> 5);
+            r.g[i] = *reinterpret_cast<const float4*>(p.g + base + min(t, x.n - 1) * rs + cl);
         }
-#pragma unroll
-        for (int r = 0; r < 32; ++r) {
-            run += gv[r];
-            sm.u.G[half * 32 + r][c] = run;
-        }
-        if (tid < C) {
-            const float x = p.beta[(row0 + min(tid, n - 1)) * p.H + h];
-            sm.beta[tid] = tid < n ? x : 0.f;
-        }
-        __syncthreads();
-        if (half == 1) {
-            const float base = sm.u.G[31][c];
-#pragma unroll
-            for (int r = 32; r < 64; ++r) sm.u.G[r][c] += base;
-        }
-        __syncthreads();
     }
-
-    // ---- Gram matrices: wave w computes row tile w (rows 16w .. 16w+15) ----
-    // Off-diagonal blocks (column tile ts < w) use the reference r = G at row
-    // 16w - 1, so both factors e^{G_t - r} and e^{r - G_s} are <= 1.  The
-    // diagonal block uses r = G at row 16w + 7, keeping both factors within
-    // e^{+-span/2} of the block; spans beyond SPAN_LIMIT take the pairwise path.
-    int extreme = 0;
-    f32x4 accB[4];
     {
-        f32x4 accA[4];
+        const int c = 8 * (tid & 15);
+        const int cl = c < dk ? c : 0;
 #pragma unroll
-        for (int ts = 0; ts < 4; ++ts) {
-            accA[ts] = f32x4{0.f, 0.f, 0.f, 0.f};
-            accB[ts] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < 4; ++i) {
+            const int t = 16 * i + (tid >> 4);
+            r.k[i] = IO::load8(p.k, base + min(t, x.n - 1) * rs + cl);
         }
-        const int t = 16 * w + i16;
-#pragma unroll 1
+    }
+    {
+        const int lane = tid & 63, w = tid >> 6;
+        const int t = 16 * w + (lane & 15);
+#pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const int c0 = 32 * ks + 8 * g4;
-            const bool cok = c0 < dk;
-            float kt[8], qt[8];
-            {
-                const bool ok = cok && t < n;
-                const typename IO::V8 kx = IO::load8(p.k, at(t, c0)), qx = IO::load8(p.q, at(t, c0));
-                IO::f32x8(ok ? kx : IO::zero8(), kt);
-                IO::f32x8(ok ? qx : IO::zero8(), qt);
+            const int c = 32 * ks + 8 * (lane >> 4);
+            r.qg[ks] = IO::load8(p.q, base + min(t, x.n - 1) * rs + (c < dk ? c : 0));
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int idx = tid + NT * u;
+            const int ws = idx >> 8, mt = (idx >> 6) & 3, ln = idx & 63;
+            const int tt = tok_of(mt, ln & 15), c = SL * ws + 8 * (ln >> 4);
+            r.qd[u] = IO::load8(p.q, base + min(tt, x.n - 1) * rs + (c < dk ? c : 0));
+        }
+    }
+    r.beta = p.beta[(x.row0 + min(tid & 63, x.n - 1)) * p.H + x.h];
+}
+
+// One workgroup per (chunk, head) item; two are resident per compute unit.
+// All of the item's global inputs are requested up front.
+template <typename TIn>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prep_kernel(PrepParams p) {
+    using IO = In<TIn>;
+    using SM = PrepSmem<TIn>;
+    __shared__ SM sm;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int g4 = lane >> 4, i16 = lane & 15;
+    const int dk = p.dk;
+
+    const PrepItem x = prep_item(p, blockIdx.x);
+    PrepRaw<TIn> raw;
+    prep_load<TIn>(raw, p, x, tid);
+    {
+        const int n = x.n;
+        uint4* __restrict__ dst = p.ops + (x.gc * p.H + x.h) * CHUNK_OPS;
+
+        // ---- stage this item's inputs (zero past n and dk) ----
+        {
+            const int c = 4 * (tid & 31);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int t = 8 * i + (tid >> 5);
+                *reinterpret_cast<float4*>(&sm.u.G[t][c]) =
+                    (t < n && c < dk) ? raw.g[i] : make_float4(0.f, 0.f, 0.f, 0.f);
             }
-            float Gt[8], rw[8], rm[8];
+        }
+        {
+            const int c = 8 * (tid & 15);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 16 * i + (tid >> 4);
+                const typename IO::V8 kz = (t < n && c < dk) ? raw.k[i] : IO::zero8();
+                *reinterpret_cast<typename IO::V8*>(&sm.k.kS[t][c]) = kz;
+            }
+        }
+        if (tid < C) sm.beta[tid] = tid < n ? raw.beta : 0.f;
+        __syncthreads();
+
+        // ---- cumulative log-decay per channel ----
+        {
+            const int c = tid & 127, half = tid >> 7;
+            float run = 0.f;
+#pragma unroll 8
+            for (int r = 0; r < 32; ++r) {
+                run += sm.u.G[half * 32 + r][c];
+                sm.u.G[half * 32 + r][c] = run;
+            }
+            __syncthreads();
+            if (half == 1) {
+                const float base = sm.u.G[31][c];
+#pragma unroll 8
+                for (int r = 32; r < 64; ++r) sm.u.G[r][c] += base;
+            }
+            __syncthreads();
+        }
+
+        // ---- Gram matrices: wave w computes row tile w (rows 16w .. 16w+15) ----
+        // Off-diagonal blocks (column tile ts < w) use the reference r = G at
+        // row 16w - 1, so both factors e^{G_t - r} and e^{r - G_s} are <= 1.
+        // The diagonal block uses r = G at row 16w + 7, keeping both factors
+        // within e^{+-span/2} of the block; spans beyond SPAN_LIMIT take the
+        // pairwise path.
+        int extreme = 0;
+        f32x4 accB[4];
+        {
+            f32x4 accA[4];
+#pragma unroll
+            for (int ts = 0; ts < 4; ++ts) {
+                accA[ts] = f32x4{0.f, 0.f, 0.f, 0.f};
+                accB[ts] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+            const int t = 16 * w + i16;
+#pragma unroll 1
+            for (int ks = 0; ks < 4; ++ks) {
+                const int c0 = 32 * ks + 8 * g4;
+                float kt[8], qt[8];
+                IO::f32x8(*reinterpret_cast<const typename IO::V8*>(&sm.k.kS[t][c0]), kt);
+                typename IO::V8 qx = raw.qg[0];
+#pragma unroll
+                for (int q = 1; q < 4; ++q)
+                    if (ks == q) qx = raw.qg[q];
+                IO::f32x8((t < n && c0 < dk) ? qx : IO::zero8(), qt);
+                float Gt[8], rw[8], rm[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    Gt[e] = sm.u.G[t][c0 + e];
+                    rw[e] = sm.u.G[w > 0 ? 16 * w - 1 : 0][c0 + e];
+                    rm[e] = sm.u.G[16 * w + 7][c0 + e];
+                    extreme |= (sm.u.G[16 * w][c0 + e] - rm[e] > SPAN_LIMIT) |
+                               (rm[e] - sm.u.G[16 * w + 15][c0 + e] > SPAN_LIMIT);
+                }
+                // diagonal block
+                {
+                    uint16_t xk[8], xqh[8], xql[8], yh[8], yl[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float xd = ex(Gt[e] - rm[e]);
+                        const float yd = ex(rm[e] - Gt[e]);
+                        xk[e] = bfb(kt[e] * xd);
+                        split(qt[e] * xd, xqh[e], xql[e]);
+                        split(kt[e] * yd, yh[e], yl[e]);
+                    }
+                    const bf16x8_t XK = as_op(pack8(xk)), XQH = as_op(pack8(xqh)),
+                                   XQL = as_op(pack8(xql)), YH = as_op(pack8(yh)),
+                                   YL = as_op(pack8(yl));
+#pragma unroll
+                    for (int ts = 0; ts < 4; ++ts) {
+                        if (ts == w) {
+                            accA[ts] = mfma(XK, YH, accA[ts]);
+                            accB[ts] = mfma(XQH, YH, accB[ts]);
+                            accB[ts] = mfma(XQH, YL, accB[ts]);
+                            accB[ts] = mfma(XQL, YH, accB[ts]);
+                        }
+                    }
+                }
+                // off-diagonal blocks
+                if (w > 0) {
+                    uint16_t xk[8], xqh[8], xql[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float xo = ex(Gt[e] - rw[e]);
+                        xk[e] = bfb(kt[e] * xo);
+                        split(qt[e] * xo, xqh[e], xql[e]);
+                    }
+                    const bf16x8_t XK = as_op(pack8(xk)), XQH = as_op(pack8(xqh)),
+                                   XQL = as_op(pack8(xql));
+#pragma unroll
+                    for (int ts = 0; ts < 3; ++ts) {
+                        if (ts < w) {
+                            const int s = 16 * ts + i16;
+                            float ksv[8];
+                            IO::f32x8(*reinterpret_cast<const typename IO::V8*>(&sm.k.kS[s][c0]), ksv);
+                            uint16_t yh[8], yl[8];
+#pragma unroll
+                            for (int e = 0; e < 8; ++e)
+                                split(ksv[e] * ex(rw[e] - sm.u.G[s][c0 + e]), yh[e], yl[e]);
+                            const bf16x8_t YH = as_op(pack8(yh)), YL = as_op(pack8(yl));
+                            accA[ts] = mfma(XK, YH, accA[ts]);
+                            accB[ts] = mfma(XQH, YH, accB[ts]);
+                            accB[ts] = mfma(XQH, YL, accB[ts]);
+                            accB[ts] = mfma(XQL, YH, accB[ts]);
+                        }
+                    }
+                }
+            }
+            // accumulator (row 4*g4+e, column i16) of block (w, ts); masked
+            // entries are selected away, never multiplied (they may hold inf)
+#pragma unroll
+            for (int ts = 0; ts < 4; ++ts)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int tr = 16 * w + 4 * g4 + e, sc = 16 * ts + i16;
+                    sm.ab.A[tr][sc] = (sc < tr) ? accA[ts][e] * sm.beta[tr] : 0.f;
+                }
+        }
+        const int any_extreme = __syncthreads_or(extreme);
+
+        if (any_extreme) {
+            // a diagonal block spans more decay than fp32 factors can carry:
+            // evaluate the four diagonal blocks pair by pair
+            for (int idx = tid; idx < 4 * 256; idx += NT) {
+                const int blk = idx >> 8, tl = (idx >> 4) & 15, sl = idx & 15;
+                if (sl > tl) continue;
+                const int t = 16 * blk + tl, s = 16 * blk + sl;
+                float sa = 0.f, sb = 0.f;
+                for (int c = 0; c < dk; ++c) {
+                    const float kt = IO::f32(sm.k.kS[t][c]), kv = IO::f32(sm.k.kS[s][c]);
+                    const float qt = t < n ? IO::f32(IO::load1(p.q, ((x.row0 + t) * p.H + x.h) * (int64_t)dk + c)) : 0.f;
+                    const float e = ex(sm.u.G[t][c] - sm.u.G[s][c]);
+                    sa = fmaf(kt * kv, e, sa);
+                    sb = fmaf(qt * kv, e, sb);
+                }
+                sm.ab.A[t][s] = (s < t) ? sa * sm.beta[t] : 0.f;
+                sm.Bd[blk][tl][sl] = sb;
+            }
+            __syncthreads();
+        }
+
+        // ---- decay-scaled operands: Kd planes, Qd planes, dec, then (K e^G)^T ----
+#pragma unroll 2
+        for (int r = 0; r < 4; ++r) {
+            const int idx = tid + NT * r;  // (w', m, ks, lane)
+            const int ws = idx >> 8, m = (idx >> 7) & 1, ks = (idx >> 6) & 1, ln = idx & 63;
+            const int c = SL * ws + chan_of(m, ln & 15), t0 = 32 * ks + 8 * (ln >> 4);
+            const float gcc = sm.u.G[C - 1][c];
+            uint16_t kh[8], kl[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                Gt[e] = sm.u.G[t][c0 + e];
-                rw[e] = sm.u.G[w > 0 ? 16 * w - 1 : 0][c0 + e];
-                rm[e] = sm.u.G[16 * w + 7][c0 + e];
-                extreme |= (sm.u.G[16 * w][c0 + e] - rm[e] > SPAN_LIMIT) |
-                           (rm[e] - sm.u.G[16 * w + 15][c0 + e] > SPAN_LIMIT);
+                const int t = t0 + e;
+                split(IO::f32(sm.k.kS[t][c]) * ex(gcc - sm.u.G[t][c]), kh[e], kl[e]);
             }
-            // diagonal block
-            {
-                uint16_t xk[8], xqh[8], xql[8], yh[8], yl[8];
+            dst[OP_K + idx] = pack8(kh);
+            dst[OP_K + 2 * PLANE + idx] = pack8(kl);
+        }
+        uint16_t kg[4][8];  // (K e^G) of this thread's Qd units, for the transposed copy
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float xd = ex(Gt[e] - rm[e]);
-                    const float yd = ex(rm[e] - Gt[e]);
-                    xk[e] = bfb(kt[e] * xd);
-                    split(qt[e] * xd, xqh[e], xql[e]);
-                    split(kt[e] * yd, yh[e], yl[e]);
-                }
-                const bf16x8_t XK = as_op(pack8(xk)), XQH = as_op(pack8(xqh)),
-                               XQL = as_op(pack8(xql)), YH = as_op(pack8(yh)),
-                               YL = as_op(pack8(yl));
+        for (int r = 0; r < 4; ++r) {
+            const int idx = tid + NT * r;  // (w', mt, lane)
+            const int ws = idx >> 8, mt = (idx >> 6) & 3, ln = idx & 63;
+            const int t = tok_of(mt, ln & 15), c0 = SL * ws + 8 * (ln >> 4);
+            float qv[8], kv[8];
+            IO::f32x8((t < n && c0 < dk) ? raw.qd[r] : IO::zero8(), qv);
+            IO::f32x8(*reinterpret_cast<const typename IO::V8*>(&sm.k.kS[t][c0]), kv);
+            uint16_t qh[8], ql[8];
 #pragma unroll
-                for (int ts = 0; ts < 4; ++ts) {
-                    if (ts == w) {
-                        accA[ts] = mfma(XK, YH, accA[ts]);
-                        accB[ts] = mfma(XQH, YH, accB[ts]);
-                        accB[ts] = mfma(XQH, YL, accB[ts]);
-                        accB[ts] = mfma(XQL, YH, accB[ts]);
-                    }
-                }
+            for (int e = 0; e < 8; ++e) {
+                const float eg = ex(sm.u.G[t][c0 + e]);
+                split(qv[e] * eg, qh[e], ql[e]);
+                kg[r][e] = bfb(kv[e] * eg);
             }
-            // off-diagonal blocks
-            if (w > 0) {
-                uint16_t xk[8], xqh[8], xql[8];
+            dst[OP_Q + idx] = pack8(qh);
+            dst[OP_Q + 2 * PLANE + idx] = pack8(ql);
+        }
+        if (tid < DKP) reinterpret_cast<float*>(dst + OP_DEC)[tid] = ex(sm.u.G[C - 1][tid]);
+        __syncthreads();  // keys are read: their storage becomes (K e^G)^T
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float xo = ex(Gt[e] - rw[e]);
-                    xk[e] = bfb(kt[e] * xo);
-                    split(qt[e] * xo, xqh[e], xql[e]);
+        for (int r = 0; r < 4; ++r) {
+            const int idx = tid + NT * r;
+            const int ws = idx >> 8, mt = (idx >> 6) & 3, ln = idx & 63;
+            const int t = tok_of(mt, ln & 15), c0 = SL * ws + 8 * (ln >> 4);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sm.k.KgT[c0 + e][t] = kg[r][e];
+        }
+        __syncthreads();
+
+        // ---- T = (I + A)^-1 by block forward substitution (G is dead now) ----
+        if (lane < 16) {
+            // diagonal block w, column j = lane
+            const int bo = 16 * w, j = lane;
+            float xs[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float acc = 0.f;
+#pragma unroll
+                for (int m = 0; m < r; ++m) acc = fmaf(sm.ab.A[bo + r][bo + m], xs[m], acc);
+                xs[r] = (r == j) ? 1.f : -acc;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sm.u.T[bo + r][bo + j] = xs[r];
+        }
+        __syncthreads();
+        {
+            const int r = tid >> 4, cc = tid & 15;
+#pragma unroll
+            for (int d = 1; d < 4; ++d) {
+                // blocks (I, J = I - d): M = sum_{K=J}^{I-1} A_IK T_KJ ; T_IJ = -T_II M
+                for (int I = d; I < 4; ++I) {
+                    const int J = I - d;
+                    float acc = 0.f;
+                    for (int K = J; K < I; ++K)
+#pragma unroll
+                        for (int m = 0; m < 16; ++m)
+                            acc = fmaf(sm.ab.A[16 * I + r][16 * K + m], sm.u.T[16 * K + m][16 * J + cc], acc);
+                    sm.M[I - d][r][cc] = acc;
                 }
-                const bf16x8_t XK = as_op(pack8(xk)), XQH = as_op(pack8(xqh)),
-                               XQL = as_op(pack8(xql));
+                __syncthreads();
+                for (int I = d; I < 4; ++I) {
+                    const int J = I - d;
+                    float acc = 0.f;
 #pragma unroll
-                for (int ts = 0; ts < 3; ++ts) {
-                    if (ts < w) {
-                        const int s = 16 * ts + i16;
-                        float ksv[8];
-                        const typename IO::V8 kx = IO::load8(p.k, at(s, c0));
-                        IO::f32x8((cok && s < n) ? kx : IO::zero8(), ksv);
-                        uint16_t yh[8], yl[8];
-#pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            split(ksv[e] * ex(rw[e] - sm.u.G[s][c0 + e]), yh[e], yl[e]);
-                        const bf16x8_t YH = as_op(pack8(yh)), YL = as_op(pack8(yl));
-                        accA[ts] = mfma(XK, YH, accA[ts]);
-                        accB[ts] = mfma(XQH, YH, accB[ts]);
-                        accB[ts] = mfma(XQH, YL, accB[ts]);
-                        accB[ts] = mfma(XQL, YH, accB[ts]);
-                    }
+                    for (int m = 0; m < 16; ++m)
+                        acc = fmaf(sm.u.T[16 * I + r][16 * I + m], sm.M[I - d][m][cc], acc);
+                    sm.u.T[16 * I + r][16 * J + cc] = -acc;
                 }
+                __syncthreads();
             }
         }
-        // accumulator (row 4*g4+e, column i16) of block (w, ts); masked entries
-        // are selected away, never multiplied (they may hold inf)
+
+        // ---- B (A is dead now), then TB and B as operand planes ----
 #pragma unroll
         for (int ts = 0; ts < 4; ++ts)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int tr = 16 * w + 4 * g4 + e, sc = 16 * ts + i16;
-                sm.ab.A[tr][sc] = (sc < tr) ? accA[ts][e] * sm.beta[tr] : 0.f;
+                float v = accB[ts][e];
+                if (any_extreme && ts == w) v = sm.Bd[w][4 * g4 + e][i16];
+                sm.ab.B[tr][sc] = (sc <= tr) ? v : 0.f;
             }
-    }
-    const int any_extreme = __syncthreads_or(extreme);
-
-    if (any_extreme) {
-        // a diagonal block spans more decay than fp32 factors can carry:
-        // evaluate the four diagonal blocks pair by pair
-        for (int idx = tid; idx < 4 * 256; idx += NT) {
-            const int blk = idx >> 8, tl = (idx >> 4) & 15, sl = idx & 15;
-            if (sl > tl) continue;
-            const int t = 16 * blk + tl, s = 16 * blk + sl;
-            float sa = 0.f, sb = 0.f;
-            if (t < n) {
-                for (int c = 0; c < dk; ++c) {
-                    const float kt = IO::f32(IO::load1(p.k, at(t, c)));
-                    const float kv = IO::f32(IO::load1(p.k, at(s, c)));
-                    const float qt = IO::f32(IO::load1(p.q, at(t, c)));
-                    const float e = ex(sm.u.G[t][c] - sm.u.G[s][c]);
-                    sa = fmaf(kt * kv, e, sa);
-                    sb = fmaf(qt * kv, e, sb);
-                }
-            }
-            sm.ab.A[t][s] = (s < t) ? sa * sm.beta[t] : 0.f;
-            sm.Bd[blk][tl][sl] = sb;
-        }
         __syncthreads();
-    }
-
-    // ---- decay-scaled operands: Qd planes, Kd planes, dec, and (K e^G)^T ----
-#pragma unroll 1
-    for (int r = 0; r < 4; ++r) {
-        const int idx = tid + NT * r;  // (w', mt, lane)
-        const int ws = idx >> 8, mt = (idx >> 6) & 3, ln = idx & 63;
-        const int t = tok_of(mt, ln & 15), c0 = SL * ws + 8 * (ln >> 4);
-        const bool ok = t < n && c0 < dk;
-        float qv[8], kv[8];
-        const typename IO::V8 qx = IO::load8(p.q, at(t, c0)), kx = IO::load8(p.k, at(t, c0));
-        IO::f32x8(ok ? qx : IO::zero8(), qv);
-        IO::f32x8(ok ? kx : IO::zero8(), kv);
-        uint16_t qh[8], ql[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float eg = ex(sm.u.G[t][c0 + e]);
-            split(qv[e] * eg, qh[e], ql[e]);
-            sm.KgT[c0 + e][t] = bfb(kv[e] * eg);
-        }
-        dst[OP_Q + idx] = pack8(qh);
-        dst[OP_Q + 2 * PLANE + idx] = pack8(ql);
-    }
-#pragma unroll 1
-    for (int r = 0; r < 4; ++r) {
-        const int idx = tid + NT * r;  // (w', m, ks, lane)
-        const int ws = idx >> 8, m = (idx >> 7) & 1, ks = (idx >> 6) & 1, ln = idx & 63;
-        const int c = SL * ws + chan_of(m, ln & 15), t0 = 32 * ks + 8 * (ln >> 4);
-        const float gcc = sm.u.G[C - 1][c];
-        uint16_t kh[8], kl[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int t = t0 + e;
-            const float x = IO::f32(IO::load1(p.k, at(t, c)));
-            const float kv = (t < n && c < dk) ? x : 0.f;
-            split(kv * ex(gcc - sm.u.G[t][c]), kh[e], kl[e]);
-        }
-        dst[OP_K + idx] = pack8(kh);
-        dst[OP_K + 2 * PLANE + idx] = pack8(kl);
-    }
-    if (tid < DKP) reinterpret_cast<float*>(dst + OP_DEC)[tid] = ex(sm.u.G[C - 1][tid]);
-    __syncthreads();
-
-    // ---- T = (I + A)^-1 by block forward substitution (G is dead now) ----
-    if (lane < 16) {
-        // diagonal block w, column j = lane
-        const int bo = 16 * w, j = lane;
-        float x[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float acc = 0.f;
-#pragma unroll
-            for (int m = 0; m < r; ++m) acc = fmaf(sm.ab.A[bo + r][bo + m], x[m], acc);
-            x[r] = (r == j) ? 1.f : -acc;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sm.u.T[bo + r][bo + j] = x[r];
-    }
-    __syncthreads();
-    {
-        const int r = tid >> 4, cc = tid & 15;
-#pragma unroll
-        for (int d = 1; d < 4; ++d) {
-            // blocks (I, J = I - d): M = sum_{K=J}^{I-1} A_IK T_KJ ; T_IJ = -T_II M
-            for (int I = d; I < 4; ++I) {
-                const int J = I - d;
-                float acc = 0.f;
-                for (int K = J; K < I; ++K)
-#pragma unroll
-                    for (int m = 0; m < 16; ++m)
-                        acc = fmaf(sm.ab.A[16 * I + r][16 * K + m], sm.u.T[16 * K + m][16 * J + cc], acc);
-                sm.M[I - d][r][cc] = acc;
-            }
-            __syncthreads();
-            for (int I = d; I < 4; ++I) {
-                const int J = I - d;
-                float acc = 0.f;
-#pragma unroll
-                for (int m = 0; m < 16; ++m)
-                    acc = fmaf(sm.u.T[16 * I + r][16 * I + m], sm.M[I - d][m][cc], acc);
-                sm.u.T[16 * I + r][16 * J + cc] = -acc;
-            }
-            __syncthreads();
-        }
-    }
-
-    // ---- B (A is dead now), then TB and B as operand planes ----
-#pragma unroll
-    for (int ts = 0; ts < 4; ++ts)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int tr = 16 * w + 4 * g4 + e, sc = 16 * ts + i16;
-            float v = accB[ts][e];
-            if (any_extreme && ts == w) v = sm.Bd[w][4 * g4 + e][i16];
-            sm.ab.B[tr][sc] = (sc <= tr) ? v : 0.f;
-        }
-    __syncthreads();
-#pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-        const int idx = tid + NT * rr;  // (mt, ks, lane)
-        const int mt = idx >> 7, ks = (idx >> 6) & 1, ln = idx & 63;
-        const int t = tok_of(mt, ln & 15);
-        const int s0 = 32 * ks + 8 * (ln >> 4);
-        uint16_t th[8], tl[8], bh[8], bl[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int s = s0 + e;
-            const float tb = (s <= t) ? sm.u.T[t][s] * sm.beta[s] : 0.f;
-            split(tb, th[e], tl[e]);
-            split(sm.ab.B[t][s], bh[e], bl[e]);
-        }
-        dst[OP_TB + idx] = pack8(th);
-        dst[OP_TB + PLANE + idx] = pack8(tl);
-        dst[OP_B + idx] = pack8(bh);
-        dst[OP_B + PLANE + idx] = pack8(bl);
-    }
-
-    // ---- W = TB (K e^G): wave w forms token tile w for all 128 channels ----
-    {
-        bf16x8_t TBh[2], TBl[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int t = tok_of(w, i16), s0 = 32 * ks + 8 * g4;
-            uint16_t th[8], tl[8];
+        for (int rr = 0; rr < 2; ++rr) {
+            const int idx = tid + NT * rr;  // (mt, ks, lane)
+            const int mt = idx >> 7, ks = (idx >> 6) & 1, ln = idx & 63;
+            const int t = tok_of(mt, ln & 15);
+            const int s0 = 32 * ks + 8 * (ln >> 4);
+            uint16_t th[8], tl[8], bh[8], bl[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int s = s0 + e;
-                split((s <= t) ? sm.u.T[t][s] * sm.beta[s] : 0.f, th[e], tl[e]);
+                const float tb = (s <= t) ? sm.u.T[t][s] * sm.beta[s] : 0.f;
+                split(tb, th[e], tl[e]);
+                split(sm.ab.B[t][s], bh[e], bl[e]);
             }
-            TBh[ks] = as_op(pack8(th));
-            TBl[ks] = as_op(pack8(tl));
+            dst[OP_TB + idx] = pack8(th);
+            dst[OP_TB + PLANE + idx] = pack8(tl);
+            dst[OP_B + idx] = pack8(bh);
+            dst[OP_B + PLANE + idx] = pack8(bl);
         }
-        f32x4 acc[8];
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct) {
-            acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        // ---- W = TB (K e^G): wave w forms token tile w for all 128 channels ----
+        {
+            bf16x8_t TBh[2], TBl[2];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8_t kg = as_op(*reinterpret_cast<const uint4*>(&sm.KgT[16 * ct + i16][32 * ks + 8 * g4]));
-                acc[ct] = mfma(TBh[ks], kg, acc[ct]);
-                acc[ct] = mfma(TBl[ks], kg, acc[ct]);
+                const int t = tok_of(w, i16), s0 = 32 * ks + 8 * g4;
+                uint16_t th[8], tl[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int s = s0 + e;
+                    split((s <= t) ? sm.u.T[t][s] * sm.beta[s] : 0.f, th[e], tl[e]);
+                }
+                TBh[ks] = as_op(pack8(th));
+                TBl[ks] = as_op(pack8(tl));
             }
+            f32x4 acc[8];
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct) {
+                acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const bf16x8_t kg = as_op(*reinterpret_cast<const uint4*>(&sm.k.KgT[16 * ct + i16][32 * ks + 8 * g4]));
+                    acc[ct] = mfma(TBh[ks], kg, acc[ct]);
+                    acc[ct] = mfma(TBl[ks], kg, acc[ct]);
+                }
+            }
+            __syncthreads();  // every read of T is done: its storage becomes W
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sm.u.W[tok_of(w, 4 * g4 + e)][16 * ct + i16] = acc[ct][e];
         }
-        __syncthreads();  // every read of T is done: its storage becomes W
+        __syncthreads();
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
+        for (int r = 0; r < 4; ++r) {
+            const int idx = tid + NT * r;  // (w', mt, lane)
+            const int ws = idx >> 8, mt = (idx >> 6) & 3, ln = idx & 63;
+            const int t = tok_of(mt, ln & 15), c0 = SL * ws + 8 * (ln >> 4);
+            const float4 a = *reinterpret_cast<const float4*>(&sm.u.W[t][c0]);
+            const float4 bq = *reinterpret_cast<const float4*>(&sm.u.W[t][c0 + 4]);
+            const float xv[8] = {a.x, a.y, a.z, a.w, bq.x, bq.y, bq.z, bq.w};
+            uint16_t wh[8], wl[8];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sm.u.W[tok_of(w, 4 * g4 + e)][16 * ct + i16] = acc[ct][e];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int idx = tid + NT * r;  // (w', mt, lane)
-        const int ws = idx >> 8, mt = (idx >> 6) & 3, ln = idx & 63;
-        const int t = tok_of(mt, ln & 15), c0 = SL * ws + 8 * (ln >> 4);
-        const float4 a = *reinterpret_cast<const float4*>(&sm.u.W[t][c0]);
-        const float4 bq = *reinterpret_cast<const float4*>(&sm.u.W[t][c0 + 4]);
-        const float x[8] = {a.x, a.y, a.z, a.w, bq.x, bq.y, bq.z, bq.w};
-        uint16_t wh[8], wl[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) split(x[e], wh[e], wl[e]);
-        dst[OP_W + idx] = pack8(wh);
-        dst[OP_W + 2 * PLANE + idx] = pack8(wl);
+            for (int e = 0; e < 8; ++e) split(xv[e], wh[e], wl[e]);
+            dst[OP_W + idx] = pack8(wh);
+            dst[OP_W + 2 * PLANE + idx] = pack8(wl);
+        }
     }
 }
 
@@ -972,8 +1065,9 @@ hipError_t launch_t(const PrefillArgs& a) {
         pp.H = a.H;
         pp.dk = a.dk;
         pp.num_seqs = a.num_seqs;
-        hipLaunchKernelGGL((prep_kernel<TIn>), dim3((unsigned)a.total_chunks, (unsigned)a.H), dim3(NT),
-                           0, a.stream, pp);
+        const int64_t items = a.total_chunks * a.H;
+        if (items > 0x7fffffffLL) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((prep_kernel<TIn>), dim3((unsigned)items), dim3(NT), 0, a.stream, pp);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
