@@ -241,14 +241,25 @@ def cpu_prefill_baseline(inp, tokens: int):
 
 # ---------------------------------------------------------------------------
 def copy_calibration(torch, mib: int):
+    """A plain device copy and an in-place scale of `mib` MiB, timed with HIP
+    events: the practical read+write bandwidth ceiling for the decode step."""
     n = mib * (1 << 20) // 4
     src = torch.ones(n, dtype=torch.float32, device="cuda:0")
     dst = torch.empty_like(src)
-    for _ in range(10):
-        dst.copy_(src)
-    torch.cuda.synchronize()
-    print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4,
-                      "launches": 10}), flush=True)
+    stream = torch.cuda.current_stream()
+    res = {"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4, "launches": 10}
+    for name, fn in (("copy", lambda: dst.copy_(src)), ("inplace_scale", lambda: src.mul_(1.0))):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) / 1e3 / 10
+        res[name + "_GBps"] = round(2 * n * 4 / sec / 1e9, 1)
+    print(json.dumps(res), flush=True)
 
 
 def main():
@@ -260,8 +271,8 @@ def main():
     ap.add_argument("--long", action="store_true", help="also time the 1,048,576-token prefill")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-decode-seqs", type=int, default=64)
-    ap.add_argument("--cpu-decode-steps", type=int, default=100)
+    ap.add_argument("--cpu-decode-seqs", type=int, default=128)
+    ap.add_argument("--cpu-decode-steps", type=int, default=1000)
     ap.add_argument("--cpu-prefill-tokens", type=int, default=8192)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB")
     args = ap.parse_args()

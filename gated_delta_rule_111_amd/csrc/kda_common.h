@@ -81,6 +81,18 @@ template <> struct io<bf16_t> {
     }
 };
 
+// 16-byte loads and stores that bypass cache retention: for data touched
+// once per kernel (the decode state streams through HBM in place).
+typedef float f32v4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 load_stream4(const float* p) {
+    const f32v4 x = __builtin_nontemporal_load(reinterpret_cast<const f32v4*>(p));
+    return make_float4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ void store_stream4(float* p, const float4& v) {
+    const f32v4 x = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(x, reinterpret_cast<f32v4*>(p));
+}
+
 // alpha = exp(g) through the hardware base-2 exponential.
 __device__ __forceinline__ float exp_gate(float g) {
     return __builtin_amdgcn_exp2f(g * 1.4426950408889634f);

@@ -20,7 +20,9 @@
 // - in a wave, lane l owns a 4-column group (16-byte accesses) and a block
 //   of dk/RG consecutive rows; the dk-reductions are a per-lane partial sum
 //   followed by a butterfly over the RG row groups;
-// - the state is loaded once into VGPRs, updated there and stored once.
+// - the state is loaded once into VGPRs, updated there and stored once, with
+//   non-temporal 16-byte accesses (each state is touched once per step, and
+//   keeping it out of the caches leaves them to the small per-token inputs).
 #include "kda_common.h"
 #include "kda_internal.h"
 
@@ -54,7 +56,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(
     // state tile: RPL rows x 4 columns, issued first so HBM latency overlaps the rest
     float4 s[RPL];
 #pragma unroll
-    for (int m = 0; m < RPL; ++m) s[m] = *reinterpret_cast<const float4*>(S + m * DV);
+    for (int m = 0; m < RPL; ++m) s[m] = load_stream4(S + m * DV);
 
     float kr[RPL], qr[RPL], gr[RPL], vv[4];
     io<TIn>::template load<RPL>(k + tok * DK + row0, kr);
@@ -95,7 +97,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(
         float4 t = s[m];
         t.x = fmaf(kr[m], u0, t.x); t.y = fmaf(kr[m], u1, t.y);
         t.z = fmaf(kr[m], u2, t.z); t.w = fmaf(kr[m], u3, t.w);
-        *reinterpret_cast<float4*>(S + m * DV) = t;
+        store_stream4(S + m * DV, t);
     }
     if (rg == 0) {
         io<TOut>::store4(out + tok * DV + col, scale * fmaf(kq, u0, b0),
