@@ -1008,10 +1008,15 @@ void scan_kernel(ScanParams p) {
         }
     };
 
-    for (int ci = 0; ci < nch; ci += 2) {
+    // The loop body always runs both halves, so the back edge is reached
+    // only after the second half has consumed what the first half loaded;
+    // an odd last chunk runs after the loop.
+    int ci = 0;
+    for (; ci + 1 < nch; ci += 2) {
         chunk(ci, opA, opB);
-        if (ci + 1 < nch) chunk(ci + 1, opB, opA);
+        chunk(ci + 1, opB, opA);
     }
+    if (ci < nch) chunk(ci, opA, opB);
 
 #pragma unroll
     for (int m = 0; m < 2; ++m)
