@@ -111,6 +111,18 @@ __device__ __forceinline__ void pack_split(const f32x4& x0, const f32x4& x1, bf1
     lo = as_op(pack8(l));
 }
 
+// -x for a bf16 operand (sign flips, exact)
+__device__ __forceinline__ bf16x8_t neg(const bf16x8_t& x) {
+    const uint4 u = __builtin_bit_cast(uint4, x);
+    return __builtin_bit_cast(bf16x8_t, make_uint4(u.x ^ 0x80008000u, u.y ^ 0x80008000u,
+                                                   u.z ^ 0x80008000u, u.w ^ 0x80008000u));
+}
+
+// Storage slot of 16-byte group g (tokens 8g .. 8g+7) in row j of V^T.  The
+// permutation differs between rows 8 apart (the transposing writes of one
+// instruction) and between neighbouring rows (the operand reads).
+__device__ __forceinline__ int vt_group(int j, int g) { return g ^ ((j ^ (j >> 3)) & 7); }
+
 // Row orders inside a chunk.  An accumulator tile holds rows 4*(lane/16)+e;
 // two tiles packed as one operand give a lane K positions 4*(lane/16)+e of
 // each.  Numbering the chunk's tokens and the wave's state rows so that
@@ -215,52 +227,61 @@ __global__ __launch_bounds__(NT) void plan_kernel(const int32_t* __restrict__ cu
 // written to the workspace as MFMA operands in the order the scan reads them.
 // ---------------------------------------------------------------------------
 // Operand block of one (chunk, head), in 16-byte units (8 bf16 = one MFMA
-// operand of one lane).  Scan lane (g = lane/16, i = lane%16) of wave w reads
-// index [...][lane] of:
-//   TB, B   [mt][ks]     row tok_of(mt, i), columns 32ks + 8g .. +7
-//   W, Qd   [w][mt]      row tok_of(mt, i), channels 32w + 8g .. +7
+// operand of one lane, or 4 fp32 accumulator values of one lane).  Scan lane
+// (g = lane/16, i = lane%16) of wave w reads index [...][lane] of:
+//   W, Q'   [r][mt]      row tok_of(mt, i), channels 32r + 8g .. +7
 //   Kd      [w][m][ks]   channel 32w + chan_of(m, i), tokens 32ks + 8g .. +7
+//   U~, O~  [jt][mt]     fp32 rows tok_of(mt, 4g .. 4g+3), column 16jt + i
 //   dec     128 floats, e^{G_C} per channel
-// with W = TB (K . e^G), Qd = Q . e^G, Kd = (K . e^{G_C - G})^T, each as a hi
-// plane followed by a lo plane.
-constexpr int OP_TB = 0;
-constexpr int OP_B = 2 * PLANE;
-constexpr int OP_W = 4 * PLANE;
-constexpr int OP_Q = 8 * PLANE;
-constexpr int OP_K = 12 * PLANE;
-constexpr int OP_DEC = 16 * PLANE;
-constexpr int CHUNK_OPS = 16 * PLANE + 32;
+// with W = TB (K . e^G), M = B TB, Q' = Q . e^G - M (K . e^G),
+// Kd = (K . e^{G_C - G})^T as a hi plane followed by a lo plane, and
+// U~ = TB V, O~ = M V in fp32.  With these the chunk step is
+//   U = U~ - W S,   O = scale (Q' S + O~),   S' = Diag(e^{G_C}) S + Kd U,
+// since B U = B TB V - B TB (K . e^G) S.
+constexpr int OP_W = 0;
+constexpr int OP_Q = 4 * PLANE;
+constexpr int OP_K = 8 * PLANE;
+constexpr int OP_U = 12 * PLANE;
+constexpr int OP_O = 16 * PLANE;
+constexpr int OP_DEC = 20 * PLANE;
+constexpr int CHUNK_OPS = 20 * PLANE + 32;
+constexpr int DVP = 128;             // value columns the operand block holds
 
 template <typename TIn>
 struct PrepSmem {
     static constexpr int KP = DKP + 16 / (int)sizeof(TIn);  // padded row of staged keys, queries
+    static constexpr int NV = sizeof(TIn) == 2 ? 1 : 2;     // bf16 planes of a value (hi[, lo])
     union {
         float G[C][DKP + 4];   // cumulative log-decay
-        float T[C][C + 4];     // (I + A)^-1, once the decay-scaled operands are out
-        float W[C][DKP + 4];   // W, for the transpose into operand order
+        struct {
+            float T[C][C + 4];             // (I + A)^-1, once the decay-scaled operands are out
+            uint16_t VT[NV][DVP][C];       // V^T in bf16 planes, 16-byte groups swizzled by column
+        } tv;
     } u;
     union {
         float A[C][C + 1];     // strictly lower b_t sum_c k_t k_s e^{G_t - G_s}
         float B[C][C + 1];     // lower sum_c q_t k_s e^{G_t - G_s}, once T is formed
+        float M[C][C + 1];     // B TB, once every wave holds its rows of B
     } ab;
     union {
         TIn kS[C][KP];             // the chunk's keys (zero past n and dk)
         uint16_t KgT[DKP][C + 8];  // (K . e^G)^T in bf16, [channel][token], once kS is read
     } k;
     float Bd[4][16][17];       // diagonal blocks of B from the pairwise path
-    float M[3][16][17];
+    float Ms[3][16][17];       // block products of the forward substitution
     float beta[C];
 };
 
 struct PrepParams {
     const void* q;
     const void* k;
+    const void* v;
     const float* g;
     const float* beta;
     const int32_t* cu;
     const int32_t* chunk_start;
     uint4* ops;  // [chunks][H][CHUNK_OPS]
-    int H, dk, num_seqs;
+    int H, dk, dv, num_seqs;
 };
 
 // Location of one (chunk, head) item.
@@ -540,38 +561,69 @@ void prep_kernel(PrepParams p) {
             dst[OP_K + idx] = pack8(kh);
             dst[OP_K + 2 * PLANE + idx] = pack8(kl);
         }
-        uint16_t kg[4][8];  // (K e^G) of this thread's Qd units, for the transposed copy
+        // Q e^G of this thread's units (token tok_of(w, i16), channels
+        // 32r + 8*g4 .. +7) stay in fp32 until Q' is formed; K e^G of the same
+        // units goes to the transposed bf16 copy
+        float qd[4][8];
+        uint16_t kg[4][8];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int idx = tid + NT * r;  // (w', mt, lane)
-            const int ws = idx >> 8, mt = (idx >> 6) & 3, ln = idx & 63;
-            const int t = tok_of(mt, ln & 15), c0 = SL * ws + 8 * (ln >> 4);
+            const int t = tok_of(w, i16), c0 = SL * r + 8 * g4;
             float qv[8], kv[8];
             IO::f32x8((t < n && c0 < dk) ? raw.qd[r] : IO::zero8(), qv);
             IO::f32x8(*reinterpret_cast<const typename IO::V8*>(&sm.k.kS[t][c0]), kv);
-            uint16_t qh[8], ql[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float eg = ex(sm.u.G[t][c0 + e]);
-                split(qv[e] * eg, qh[e], ql[e]);
+                qd[r][e] = qv[e] * eg;
                 kg[r][e] = bfb(kv[e] * eg);
             }
-            dst[OP_Q + idx] = pack8(qh);
-            dst[OP_Q + 2 * PLANE + idx] = pack8(ql);
         }
         if (tid < DKP) reinterpret_cast<float*>(dst + OP_DEC)[tid] = ex(sm.u.G[C - 1][tid]);
-        __syncthreads();  // keys are read: their storage becomes (K e^G)^T
+        __syncthreads();  // keys and G are read: their storage becomes (K e^G)^T, T and V^T
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int idx = tid + NT * r;
-            const int ws = idx >> 8, mt = (idx >> 6) & 3, ln = idx & 63;
-            const int t = tok_of(mt, ln & 15), c0 = SL * ws + 8 * (ln >> 4);
+            const int t = tok_of(w, i16), c0 = SL * r + 8 * g4;
 #pragma unroll
             for (int e = 0; e < 8; ++e) sm.k.KgT[c0 + e][t] = kg[r][e];
         }
+        // this item's v rows (16 rows x 8 columns per thread), staged as V^T
+        // while the forward substitution runs; rows past n and columns past
+        // dv are zero.  V^T rows are 64 tokens; its 16-byte groups are
+        // permuted by vt_group so that neither the transposing writes nor the
+        // operand reads collide in LDS banks.
+        {
+            typename IO::V8 vr[4];
+            const int c = 8 * (tid & 15);
+            const int64_t vs = (int64_t)p.H * p.dv;
+            const int64_t vb = (x.row0 * p.H + x.h) * (int64_t)p.dv + (c < p.dv ? c : 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) vr[i] = IO::load8(p.v, vb + min(16 * i + (tid >> 4), n - 1) * vs);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 16 * i + (tid >> 4);
+                const bool live = t < n && c < p.dv;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int j = c + e;
+                    const int off = vt_group(j, t >> 3) * 8 + (t & 7);
+                    if constexpr (sizeof(TIn) == 2) {
+                        const uint32_t wd = (&vr[i].x)[e >> 1];
+                        sm.u.tv.VT[0][j][off] = live ? (uint16_t)((e & 1) ? (wd >> 16) : (wd & 0xffffu)) : 0;
+                    } else {
+                        float xv[8];
+                        IO::f32x8(vr[i], xv);
+                        uint16_t hi, lo;
+                        split(live ? xv[e] : 0.f, hi, lo);
+                        sm.u.tv.VT[0][j][off] = hi;
+                        sm.u.tv.VT[SM::NV - 1][j][off] = lo;
+                    }
+                }
+            }
+        }
         __syncthreads();
 
-        // ---- T = (I + A)^-1 by block forward substitution (G is dead now) ----
+        // ---- T = (I + A)^-1 by block forward substitution ----
         if (lane < 16) {
             // diagonal block w, column j = lane
             const int bo = 16 * w, j = lane;
@@ -584,7 +636,7 @@ void prep_kernel(PrepParams p) {
                 xs[r] = (r == j) ? 1.f : -acc;
             }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sm.u.T[bo + r][bo + j] = xs[r];
+            for (int r = 0; r < 16; ++r) sm.u.tv.T[bo + r][bo + j] = xs[r];
         }
         __syncthreads();
         {
@@ -598,8 +650,8 @@ void prep_kernel(PrepParams p) {
                     for (int K = J; K < I; ++K)
 #pragma unroll
                         for (int m = 0; m < 16; ++m)
-                            acc = fmaf(sm.ab.A[16 * I + r][16 * K + m], sm.u.T[16 * K + m][16 * J + cc], acc);
-                    sm.M[I - d][r][cc] = acc;
+                            acc = fmaf(sm.ab.A[16 * I + r][16 * K + m], sm.u.tv.T[16 * K + m][16 * J + cc], acc);
+                    sm.Ms[I - d][r][cc] = acc;
                 }
                 __syncthreads();
                 for (int I = d; I < 4; ++I) {
@@ -607,14 +659,14 @@ void prep_kernel(PrepParams p) {
                     float acc = 0.f;
 #pragma unroll
                     for (int m = 0; m < 16; ++m)
-                        acc = fmaf(sm.u.T[16 * I + r][16 * I + m], sm.M[I - d][m][cc], acc);
-                    sm.u.T[16 * I + r][16 * J + cc] = -acc;
+                        acc = fmaf(sm.u.tv.T[16 * I + r][16 * I + m], sm.Ms[I - d][m][cc], acc);
+                    sm.u.tv.T[16 * I + r][16 * J + cc] = -acc;
                 }
                 __syncthreads();
             }
         }
 
-        // ---- B (A is dead now), then TB and B as operand planes ----
+        // ---- B (A is dead now) ----
 #pragma unroll
         for (int ts = 0; ts < 4; ++ts)
 #pragma unroll
@@ -625,92 +677,148 @@ void prep_kernel(PrepParams p) {
                 sm.ab.B[tr][sc] = (sc <= tr) ? v : 0.f;
             }
         __syncthreads();
-#pragma unroll
-        for (int rr = 0; rr < 2; ++rr) {
-            const int idx = tid + NT * rr;  // (mt, ks, lane)
-            const int mt = idx >> 7, ks = (idx >> 6) & 1, ln = idx & 63;
-            const int t = tok_of(mt, ln & 15);
-            const int s0 = 32 * ks + 8 * (ln >> 4);
-            uint16_t th[8], tl[8], bh[8], bl[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int s = s0 + e;
-                const float tb = (s <= t) ? sm.u.T[t][s] * sm.beta[s] : 0.f;
-                split(tb, th[e], tl[e]);
-                split(sm.ab.B[t][s], bh[e], bl[e]);
-            }
-            dst[OP_TB + idx] = pack8(th);
-            dst[OP_TB + PLANE + idx] = pack8(tl);
-            dst[OP_B + idx] = pack8(bh);
-            dst[OP_B + PLANE + idx] = pack8(bl);
-        }
 
-        // ---- W = TB (K e^G): wave w forms token tile w for all 128 channels ----
+        // ---- wave w from here on: token tile w.  Rows of TB and B as MFMA
+        // operands, then M = B TB (blocks that vanish by triangularity are
+        // skipped) ----
+        bf16x8_t TBh[2], TBl[2], Mh[2], Ml[2];
         {
-            bf16x8_t TBh[2], TBl[2];
+            const int t = tok_of(w, i16);
+            bf16x8_t Bh[2], Bl[2];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const int t = tok_of(w, i16), s0 = 32 * ks + 8 * g4;
-                uint16_t th[8], tl[8];
+                const int s0 = 32 * ks + 8 * g4;
+                uint16_t th[8], tl[8], bh[8], bl[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int s = s0 + e;
-                    split((s <= t) ? sm.u.T[t][s] * sm.beta[s] : 0.f, th[e], tl[e]);
+                    split((s <= t) ? sm.u.tv.T[t][s] * sm.beta[s] : 0.f, th[e], tl[e]);
+                    split(sm.ab.B[t][s], bh[e], bl[e]);
                 }
                 TBh[ks] = as_op(pack8(th));
                 TBl[ks] = as_op(pack8(tl));
+                Bh[ks] = as_op(pack8(bh));
+                Bl[ks] = as_op(pack8(bl));
             }
-            f32x4 acc[8];
+            f32x4 acc[4];
 #pragma unroll
-            for (int ct = 0; ct < 8; ++ct) {
-                acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const bf16x8_t kg = as_op(*reinterpret_cast<const uint4*>(&sm.k.KgT[16 * ct + i16][32 * ks + 8 * g4]));
-                    acc[ct] = mfma(TBh[ks], kg, acc[ct]);
-                    acc[ct] = mfma(TBl[ks], kg, acc[ct]);
+            for (int ks = 0; ks < 2; ++ks) {
+                if (ks == 1 && w < 2) continue;  // tokens of tiles 0, 1 are < 32: B[t][s >= 32] = 0
+#pragma unroll
+                for (int nt = 0; nt < 4; ++nt) {
+                    if (ks == 0 && nt >= 2) continue;  // TB[s < 32][s' >= 32] = 0
+                    // column 16nt + i16 of TB over tokens 32ks + 8*g4 .. +7
+                    const int sc = 16 * nt + i16;
+                    uint16_t ch[8], cl[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int s = 32 * ks + 8 * g4 + e;
+                        split((sc <= s) ? sm.u.tv.T[s][sc] * sm.beta[sc] : 0.f, ch[e], cl[e]);
+                    }
+                    const bf16x8_t CH = as_op(pack8(ch)), CL = as_op(pack8(cl));
+                    acc[nt] = mfma(Bh[ks], CH, acc[nt]);
+                    acc[nt] = mfma(Bh[ks], CL, acc[nt]);
+                    acc[nt] = mfma(Bl[ks], CH, acc[nt]);
                 }
             }
-            __syncthreads();  // every read of T is done: its storage becomes W
+            __syncthreads();  // every row of B is read: its storage becomes M
 #pragma unroll
-            for (int ct = 0; ct < 8; ++ct)
+            for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) sm.u.W[tok_of(w, 4 * g4 + e)][16 * ct + i16] = acc[ct][e];
+                for (int e = 0; e < 4; ++e) sm.ab.M[tok_of(w, 4 * g4 + e)][16 * nt + i16] = acc[nt][e];
         }
         __syncthreads();
+        {
+            const int t = tok_of(w, i16);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                uint16_t mh[8], ml[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) split(sm.ab.M[t][32 * ks + 8 * g4 + e], mh[e], ml[e]);
+                Mh[ks] = as_op(pack8(mh));
+                Ml[ks] = as_op(pack8(ml));
+            }
+        }
+
+        // ---- W = TB (K e^G) and Q' = Q e^G - M (K e^G) for token tile w,
+        // formed transposed: accumulator rows are channels 32r + chan_of(m, .),
+        // columns the tile's tokens, so the two row tiles of K-step r pack
+        // directly into the scan's operand ----
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int idx = tid + NT * r;  // (w', mt, lane)
-            const int ws = idx >> 8, mt = (idx >> 6) & 3, ln = idx & 63;
-            const int t = tok_of(mt, ln & 15), c0 = SL * ws + 8 * (ln >> 4);
-            const float4 a = *reinterpret_cast<const float4*>(&sm.u.W[t][c0]);
-            const float4 bq = *reinterpret_cast<const float4*>(&sm.u.W[t][c0 + 4]);
-            const float xv[8] = {a.x, a.y, a.z, a.w, bq.x, bq.y, bq.z, bq.w};
-            uint16_t wh[8], wl[8];
+            f32x4 aw[2], aq[2];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) split(xv[e], wh[e], wl[e]);
-            dst[OP_W + idx] = pack8(wh);
-            dst[OP_W + 2 * PLANE + idx] = pack8(wl);
+            for (int m = 0; m < 2; ++m) {
+                aw[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+                aq[m] = f32x4{qd[r][4 * m], qd[r][4 * m + 1], qd[r][4 * m + 2], qd[r][4 * m + 3]};
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const bf16x8_t kgo = as_op(*reinterpret_cast<const uint4*>(
+                        &sm.k.KgT[SL * r + chan_of(m, i16)][32 * ks + 8 * g4]));
+                    aw[m] = mfma(kgo, TBh[ks], aw[m]);
+                    aw[m] = mfma(kgo, TBl[ks], aw[m]);
+                    aq[m] = mfma(kgo, neg(Mh[ks]), aq[m]);
+                    aq[m] = mfma(kgo, neg(Ml[ks]), aq[m]);
+                }
+            }
+            const int idx = (r * 4 + w) * 64 + lane;
+            bf16x8_t hi, lo;
+            pack_split(aw[0], aw[1], hi, lo);
+            dst[OP_W + idx] = __builtin_bit_cast(uint4, hi);
+            dst[OP_W + 2 * PLANE + idx] = __builtin_bit_cast(uint4, lo);
+            pack_split(aq[0], aq[1], hi, lo);
+            dst[OP_Q + idx] = __builtin_bit_cast(uint4, hi);
+            dst[OP_Q + 2 * PLANE + idx] = __builtin_bit_cast(uint4, lo);
+        }
+
+        // ---- U~ = TB V and O~ = M V for token tile w, every value tile ----
+        const int ntv = p.dv >> 4;
+        float4* __restrict__ du = reinterpret_cast<float4*>(dst + OP_U);
+        float4* __restrict__ dov = reinterpret_cast<float4*>(dst + OP_O);
+#pragma unroll
+        for (int jt = 0; jt < DVP / 16; ++jt) {
+            if (jt >= ntv) break;
+            f32x4 au = {0.f, 0.f, 0.f, 0.f}, ao = {0.f, 0.f, 0.f, 0.f};
+            const int j = 16 * jt + i16;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const int off = vt_group(j, 4 * ks + g4) * 8;
+                const bf16x8_t vh = as_op(*reinterpret_cast<const uint4*>(&sm.u.tv.VT[0][j][off]));
+                au = mfma(TBh[ks], vh, au);
+                au = mfma(TBl[ks], vh, au);
+                ao = mfma(Mh[ks], vh, ao);
+                ao = mfma(Ml[ks], vh, ao);
+                if constexpr (SM::NV == 2) {
+                    const bf16x8_t vl =
+                        as_op(*reinterpret_cast<const uint4*>(&sm.u.tv.VT[SM::NV - 1][j][off]));
+                    au = mfma(TBh[ks], vl, au);
+                    ao = mfma(Mh[ks], vl, ao);
+                }
+            }
+            du[(jt * 4 + w) * 64 + lane] = make_float4(au[0], au[1], au[2], au[3]);
+            dov[(jt * 4 + w) * 64 + lane] = make_float4(ao[0], ao[1], ao[2], ao[3]);
         }
     }
 }
 
 // ---------------------------------------------------------------------------
 // scan: per (sequence, head, 16 value columns) the recurrence over chunks.
-// Wave w owns state rows 32w .. 32w+31.  Per chunk it forms its partial
-// W S and (Q e^G) S over those rows (and TB V for its token tile), the four
-// waves exchange the partials through LDS with one barrier, then each wave
-// forms U = TB V - W S for the whole chunk, its token tile of O and its rows
-// of the next state.
+// Wave w owns state rows 32w .. 32w+31 and token tile w of the chunk.  Per
+// chunk the waves publish their state rows (as hi/lo MFMA operands) through
+// LDS; each wave then forms its token tile of W S, U = TB V - W S and
+// (Q e^G) S over all 128 state rows and publishes its tile of U; after the
+// second barrier each wave updates its state rows from the whole U and
+// writes its token tile of O.  Nothing is reduced across waves, so the LDS
+// traffic per chunk is the state once and U once.
 // ---------------------------------------------------------------------------
-template <typename TIn>
 struct ScanSmem {
-    struct Ex { f32x4 Y[4][64]; f32x4 P[4][64]; } ex[2][4];  // by chunk parity, wave
-    TIn vt[4][C][16 + 16 / sizeof(TIn)];                  // per wave: the v tile, row-major
+    uint4 sx[4][64][2];                               // state rows of wave r as K-step r operands [hi, lo]
+    struct Ux { uint2 h[2]; uint2 l[2]; } ux[2][64];  // U operands per K-step, halves by token tile
 };
 
 struct ScanParams {
-    const void* v;
     const int32_t* cu;
     const int32_t* chunk_start;
     const int32_t* snap_base;
@@ -726,66 +834,45 @@ struct ScanParams {
 };
 
 // One chunk's operands for one lane, loaded a chunk ahead.
-template <typename TIn>
 struct ScanOps {
-    uint4 w[4][2];        // W       [mt][hi, lo]
-    uint4 q[4][2];        // Qd      [mt][hi, lo]
-    uint4 kd[2][2][2];    // Kd      [m][ks][hi, lo]
-    uint4 tb[2][2];       // TB rows of this wave's token tile [ks][hi, lo]
-    uint4 b[2][2];        // B  rows of this wave's token tile [ks][hi, lo]
+    uint4 w[4][2];        // W  of this wave's token tile, K-step r = state rows 32r.. [r][hi, lo]
+    uint4 q[4][2];        // Q' of this wave's token tile [r][hi, lo]
+    uint4 kd[2][2][2];    // Kd of this wave's state rows [m][ks][hi, lo]
+    float4 u, o;          // U~ and O~ of this wave's token tile, the workgroup's value tile
     float4 dec[2];        // e^{G_C} of the lane's state rows
-    typename In<TIn>::V8 v[2];     // v rows 32r + lane/2, columns 8*(lane%2) .. +7 of the tile
 };
 
 // The next chunk's operands are loaded in three parts spread over the
-// current chunk, so the wave never stalls on a full memory queue.
-template <typename TIn>
+// current chunk, so the wave never stalls on a full memory queue.  rot
+// rotates the order of the state-row blocks, so the value tiles of one head
+// do not all request the same lines at once.
 __device__ __forceinline__ const uint4* scan_block(const ScanParams& p, int64_t gc, int h) {
     return p.ops + (gc * p.H + h) * CHUNK_OPS;
 }
 
-template <typename TIn>
-__device__ __forceinline__ void scan_load1(ScanOps<TIn>& o, const uint4* __restrict__ blk, int w,
-                                           int lane) {
+__device__ __forceinline__ void scan_load1(ScanOps& o, const uint4* __restrict__ blk, int w, int tile,
+                                           int lane, int rot) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-        const int x = (w * 4 + mt) * 64 + lane;
-        o.w[mt][0] = blk[OP_W + x];
-        o.w[mt][1] = blk[OP_W + 2 * PLANE + x];
+    for (int r = 0; r < 4; ++r) {
+        const int x = (((r + rot) & 3) * 4 + w) * 64 + lane;
+        o.w[r][0] = blk[OP_W + x];
+        o.w[r][1] = blk[OP_W + 2 * PLANE + x];
     }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        const int x = (w * 2 + ks) * 64 + lane;
-        o.tb[ks][0] = blk[OP_TB + x];
-        o.tb[ks][1] = blk[OP_TB + PLANE + x];
-    }
+    o.u = reinterpret_cast<const float4*>(blk + OP_U)[(tile * 4 + w) * 64 + lane];
 }
 
-template <typename TIn>
-__device__ __forceinline__ void scan_load2(ScanOps<TIn>& o, const uint4* __restrict__ blk,
-                                           const ScanParams& p, int64_t row0, int n, int h, int j16,
-                                           int w, int lane) {
-    using IO = In<TIn>;
-    const int g4 = lane >> 4;
+__device__ __forceinline__ void scan_load2(ScanOps& o, const uint4* __restrict__ blk, int w, int tile,
+                                           int lane, int rot) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-        const int x = (w * 4 + mt) * 64 + lane;
-        o.q[mt][0] = blk[OP_Q + x];
-        o.q[mt][1] = blk[OP_Q + 2 * PLANE + x];
+    for (int r = 0; r < 4; ++r) {
+        const int x = (((r + rot) & 3) * 4 + w) * 64 + lane;
+        o.q[r][0] = blk[OP_Q + x];
+        o.q[r][1] = blk[OP_Q + 2 * PLANE + x];
     }
-    (void)g4;
-    // the wave's copy of the chunk's v tile (64 rows x 16 columns), row-major:
-    // rows past the chunk end are read from its last row; TB has zero columns
-    // there, so they never reach U
-    const int64_t vrow = (int64_t)p.H * p.dv;
-    const int64_t vbase = (row0 * p.H + h) * (int64_t)p.dv + j16 + 8 * (lane & 1);
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-        o.v[r] = IO::load8(p.v, vbase + (int64_t)min(32 * r + (lane >> 1), n - 1) * vrow);
+    o.o = reinterpret_cast<const float4*>(blk + OP_O)[(tile * 4 + w) * 64 + lane];
 }
 
-template <typename TIn>
-__device__ __forceinline__ void scan_load3(ScanOps<TIn>& o, const uint4* __restrict__ blk, int w,
+__device__ __forceinline__ void scan_load3(ScanOps& o, const uint4* __restrict__ blk, int w,
                                            int lane) {
     const int g4 = lane >> 4;
 #pragma unroll
@@ -796,31 +883,24 @@ __device__ __forceinline__ void scan_load3(ScanOps<TIn>& o, const uint4* __restr
             o.kd[m][ks][0] = blk[OP_K + x];
             o.kd[m][ks][1] = blk[OP_K + 2 * PLANE + x];
         }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-        const int x = (w * 2 + ks) * 64 + lane;
-        o.b[ks][0] = blk[OP_B + x];
-        o.b[ks][1] = blk[OP_B + PLANE + x];
-    }
     const float4* dec = reinterpret_cast<const float4*>(blk + OP_DEC);
     o.dec[0] = dec[8 * w + 2 * g4];
     o.dec[1] = dec[8 * w + 2 * g4 + 1];
 }
 
-template <typename TIn>
-__device__ __forceinline__ void scan_load(ScanOps<TIn>& o, const ScanParams& p, int64_t gc,
-                                          int64_t row0, int n, int h, int j16, int w, int lane) {
-    const uint4* blk = scan_block<TIn>(p, gc, h);
-    scan_load1<TIn>(o, blk, w, lane);
-    scan_load2<TIn>(o, blk, p, row0, n, h, j16, w, lane);
-    scan_load3<TIn>(o, blk, w, lane);
+// hi and lo bf16 of four fp32 values, as two packed 64-bit halves
+__device__ __forceinline__ void split4(const f32x4& x, uint2& hi, uint2& lo) {
+    uint16_t h[4], l[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) split(x[e], h[e], l[e]);
+    hi = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+    lo = make_uint2(l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16));
 }
 
-template <typename TIn, bool OUT_BF16>
+template <bool OUT_BF16>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void scan_kernel(ScanParams p) {
-    using IO = In<TIn>;
-    __shared__ ScanSmem<TIn> sm;
+    __shared__ ScanSmem sm;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int g4 = lane >> 4, i16 = lane & 15;
     (void)tid;
@@ -835,6 +915,7 @@ void scan_kernel(ScanParams p) {
     const int b = chain / p.H, h = chain - b * p.H;
     const int dk = p.dk, dv = p.dv;
     const int j = 16 * tile + i16;
+    const int rot = tile & 3;
     const int64_t seq0 = p.cu[b];
     const int len = p.cu[b + 1] - p.cu[b];
     const int nch = (len + C - 1) / C;
@@ -859,118 +940,72 @@ void scan_kernel(ScanParams p) {
     // Operands are prefetched one chunk ahead into two register sets used in
     // turn (the loop body is instantiated twice with the roles swapped), so
     // no loaded value is copied and nothing waits early for the next chunk.
-    ScanOps<TIn> opA, opB;
-    if (nch > 0) scan_load<TIn>(opA, p, cbase, seq0, min(C, len), h, 16 * tile, w, lane);
+    ScanOps opA, opB;
+    if (nch > 0) {
+        const uint4* blk = scan_block(p, cbase, h);
+        scan_load1(opA, blk, w, tile, lane, rot);
+        scan_load2(opA, blk, w, tile, lane, rot);
+        scan_load3(opA, blk, w, lane);
+    }
 
-    auto chunk = [&](const int ci, ScanOps<TIn>& o, ScanOps<TIn>& nx) {
-        const int par = ci & 1;
+    auto chunk = [&](const int ci, ScanOps& o, ScanOps& nx) {
         const int64_t row0 = seq0 + (int64_t)ci * C;
         const int n = min(C, len - ci * C);
+        // the next chunk (the last chunk reloads itself, so the same loads are
+        // issued on every path; that data is unused)
+        const uint4* nblk = scan_block(p, cbase + min(ci + 1, nch - 1), h);
 
-        // ---- prefetch the next chunk (the last chunk reloads itself, so the
-        // same loads are issued on every path; that data is unused) ----
-        const int cn = min(ci + 1, nch - 1);
-        const uint4* nblk = scan_block<TIn>(p, cbase + cn, h);
-        scan_load1<TIn>(nx, nblk, w, lane);
-
-        // ---- partial W S and (Q e^G) S over this wave's rows; TB V ----
+        // ---- publish this wave's state rows ----
         {
             bf16x8_t Sh, Sl;
             pack_split(S[0], S[1], Sh, Sl);
-            // v tile through the wave's LDS area: rows in, K-ordered columns out
-            TIn (*vt)[16 + 16 / sizeof(TIn)] = sm.vt[w];
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                TIn* row = &vt[32 * r + (lane >> 1)][8 * (lane & 1)];
-                if constexpr (sizeof(TIn) == 2) {
-                    *reinterpret_cast<uint4*>(row) = o.v[r];
-                } else {
-                    reinterpret_cast<float4*>(row)[0] = o.v[r].a;
-                    reinterpret_cast<float4*>(row)[1] = o.v[r].b;
-                }
-            }
-            lds_wave_sync();
-            f32x4 ut = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8_t th = as_op(o.tb[ks][0]), tl = as_op(o.tb[ks][1]);
-                if constexpr (sizeof(TIn) == 2) {
-                    uint16_t vv[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        vv[e] = reinterpret_cast<const uint16_t&>(vt[32 * ks + 8 * g4 + e][i16]);
-                    const bf16x8_t vb = as_op(pack8(vv));
-                    ut = mfma(th, vb, ut);
-                    ut = mfma(tl, vb, ut);
-                } else {
-                    uint16_t vh[8], vl[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        split(reinterpret_cast<const float&>(vt[32 * ks + 8 * g4 + e][i16]), vh[e], vl[e]);
-                    const bf16x8_t bh = as_op(pack8(vh)), bl = as_op(pack8(vl));
-                    ut = mfma(th, bh, ut);
-                    ut = mfma(th, bl, ut);
-                    ut = mfma(tl, bh, ut);
-                }
-            }
-            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            typename ScanSmem<TIn>::Ex& E = sm.ex[par][w];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                const bf16x8_t wh = as_op(o.w[mt][0]), wl = as_op(o.w[mt][1]);
-                f32x4 y = mfma(wh, Sh, z);
-                y = mfma(wh, Sl, y);
-                y = mfma(wl, Sh, y);
-                if (mt == w) y -= ut;   // Y_w[w] = (W S)_w - TB V, so U = -sum_w Y_w
-                const bf16x8_t qh = as_op(o.q[mt][0]), ql = as_op(o.q[mt][1]);
-                f32x4 pq = mfma(qh, Sh, z);
-                pq = mfma(qh, Sl, pq);
-                pq = mfma(ql, Sh, pq);
-                E.Y[mt][lane] = y;
-                E.P[mt][lane] = pq;
-            }
+            sm.sx[w][lane][0] = __builtin_bit_cast(uint4, Sh);
+            sm.sx[w][lane][1] = __builtin_bit_cast(uint4, Sl);
         }
-        scan_load2<TIn>(nx, nblk, p, seq0 + (int64_t)cn * C, min(C, len - cn * C), h, 16 * tile, w,
-                        lane);
+        scan_load1(nx, nblk, w, tile, lane, rot);
         lds_barrier();
 
-        // ---- U = TB V - W S for every token of the chunk ----
-        bf16x8_t Uh[2], Ul[2];
+        // ---- this wave's token tile: U = U~ - W S and O = scale (Q' S + O~) ----
         {
-            f32x4 U[4];
+            bf16x8_t Sh[4], Sl[4];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                f32x4 ys = sm.ex[par][0].Y[mt][lane];
-                ys += sm.ex[par][1].Y[mt][lane];
-                ys += sm.ex[par][2].Y[mt][lane];
-                ys += sm.ex[par][3].Y[mt][lane];
-                U[mt] = -ys;
+            for (int r = 0; r < 4; ++r) {
+                Sh[r] = as_op(sm.sx[(r + rot) & 3][lane][0]);
+                Sl[r] = as_op(sm.sx[(r + rot) & 3][lane][1]);
             }
-            pack_split(U[0], U[1], Uh[0], Ul[0]);
-            pack_split(U[2], U[3], Uh[1], Ul[1]);
-        }
-
-        scan_load3<TIn>(nx, nblk, w, lane);
-
-        // ---- this wave's token tile of O = scale ((Q e^G) S + B U) ----
-        {
-            f32x4 po = sm.ex[par][0].P[w][lane];
-            po += sm.ex[par][1].P[w][lane];
-            po += sm.ex[par][2].P[w][lane];
-            po += sm.ex[par][3].P[w][lane];
-            f32x4 bu = {0.f, 0.f, 0.f, 0.f};
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            f32x4 y0 = z, y1 = z, p0 = z, p1 = z;
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8_t bh = as_op(o.b[ks][0]), bl = as_op(o.b[ks][1]);
-                bu = mfma(bh, Uh[ks], bu);
-                bu = mfma(bh, Ul[ks], bu);
-                bu = mfma(bl, Uh[ks], bu);
+            for (int r = 0; r < 4; r += 2) {
+                y0 = mfma(as_op(o.w[r][0]), Sh[r], y0);
+                y1 = mfma(as_op(o.w[r + 1][0]), Sh[r + 1], y1);
+                y0 = mfma(as_op(o.w[r][0]), Sl[r], y0);
+                y1 = mfma(as_op(o.w[r + 1][0]), Sl[r + 1], y1);
+                y0 = mfma(as_op(o.w[r][1]), Sh[r], y0);
+                y1 = mfma(as_op(o.w[r + 1][1]), Sh[r + 1], y1);
             }
+            const f32x4 u = f32x4{o.u.x, o.u.y, o.u.z, o.u.w} - (y0 + y1);
+            uint2 uh, ul;
+            split4(u, uh, ul);
+            sm.ux[w >> 1][lane].h[w & 1] = uh;
+            sm.ux[w >> 1][lane].l[w & 1] = ul;
+            scan_load2(nx, nblk, w, tile, lane, rot);
+#pragma unroll
+            for (int r = 0; r < 4; r += 2) {
+                p0 = mfma(as_op(o.q[r][0]), Sh[r], p0);
+                p1 = mfma(as_op(o.q[r + 1][0]), Sh[r + 1], p1);
+                p0 = mfma(as_op(o.q[r][0]), Sl[r], p0);
+                p1 = mfma(as_op(o.q[r + 1][0]), Sl[r + 1], p1);
+                p0 = mfma(as_op(o.q[r][1]), Sh[r], p0);
+                p1 = mfma(as_op(o.q[r + 1][1]), Sh[r + 1], p1);
+            }
+            const f32x4 po = p0 + p1;
+            const float ob[4] = {o.o.x, o.o.y, o.o.z, o.o.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = tok_of(w, 4 * g4 + e);
                 if (t < n) {
-                    const float ov = p.scale * (po[e] + bu[e]);
+                    const float ov = p.scale * (po[e] + ob[e]);
                     const int64_t oi = ((row0 + t) * p.H + h) * (int64_t)dv + j;
                     if constexpr (OUT_BF16)
                         static_cast<uint16_t*>(p.out)[oi] = bfb(ov);
@@ -979,21 +1014,34 @@ void scan_kernel(ScanParams p) {
                 }
             }
         }
+        lds_barrier();
 
-        // ---- S <- Diag(e^{G_C}) S + (K e^{G_C - G})^T U ----
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const float4 d = o.dec[m];
-            f32x4 s = S[m] * f32x4{d.x, d.y, d.z, d.w};
+        // ---- the whole U: this wave's state rows ----
+        {
+            bf16x8_t Uh[2], Ul[2];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const bf16x8_t kh = as_op(o.kd[m][ks][0]), kl = as_op(o.kd[m][ks][1]);
-                s = mfma(kh, Uh[ks], s);
-                s = mfma(kh, Ul[ks], s);
-                s = mfma(kl, Uh[ks], s);
+                const ScanSmem::Ux x = sm.ux[ks][lane];
+                Uh[ks] = __builtin_bit_cast(bf16x8_t, make_uint4(x.h[0].x, x.h[0].y, x.h[1].x, x.h[1].y));
+                Ul[ks] = __builtin_bit_cast(bf16x8_t, make_uint4(x.l[0].x, x.l[0].y, x.l[1].x, x.l[1].y));
             }
-            S[m] = s;
+            scan_load3(nx, nblk, w, lane);
+            // S <- Diag(e^{G_C}) S + (K e^{G_C - G})^T U
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const float4 d = o.dec[m];
+                f32x4 sv = S[m] * f32x4{d.x, d.y, d.z, d.w};
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    const bf16x8_t kh = as_op(o.kd[m][ks][0]), kl = as_op(o.kd[m][ks][1]);
+                    sv = mfma(kh, Uh[ks], sv);
+                    sv = mfma(kh, Ul[ks], sv);
+                    sv = mfma(kl, Uh[ks], sv);
+                }
+                S[m] = sv;
+            }
         }
+
         const int done = ci * C + n;
         if (p.interval > 0 && done % p.interval == 0) {
             float* __restrict__ dsts =
@@ -1062,6 +1110,7 @@ hipError_t launch_t(const PrefillArgs& a) {
         PrepParams pp{};
         pp.q = a.q;
         pp.k = a.k;
+        pp.v = a.v;
         pp.g = a.g;
         pp.beta = a.beta;
         pp.cu = a.cu_dev;
@@ -1069,6 +1118,7 @@ hipError_t launch_t(const PrefillArgs& a) {
         pp.ops = ops;
         pp.H = a.H;
         pp.dk = a.dk;
+        pp.dv = a.dv;
         pp.num_seqs = a.num_seqs;
         const int64_t items = a.total_chunks * a.H;
         if (items > 0x7fffffffLL) return hipErrorInvalidValue;
@@ -1078,7 +1128,6 @@ hipError_t launch_t(const PrefillArgs& a) {
     }
 
     ScanParams sp{};
-    sp.v = a.v;
     sp.cu = a.cu_dev;
     sp.chunk_start = chunk_start;
     sp.snap_base = snap_base;
@@ -1096,9 +1145,9 @@ hipError_t launch_t(const PrefillArgs& a) {
     const int64_t nwg = (int64_t)a.num_seqs * a.H * sp.ntiles;
     sp.nwg = (int)nwg;
     if (a.out_bf16)
-        hipLaunchKernelGGL((scan_kernel<TIn, true>), dim3((unsigned)nwg), dim3(NT), 0, a.stream, sp);
+        hipLaunchKernelGGL((scan_kernel<true>), dim3((unsigned)nwg), dim3(NT), 0, a.stream, sp);
     else
-        hipLaunchKernelGGL((scan_kernel<TIn, false>), dim3((unsigned)nwg), dim3(NT), 0, a.stream, sp);
+        hipLaunchKernelGGL((scan_kernel<false>), dim3((unsigned)nwg), dim3(NT), 0, a.stream, sp);
     return hipGetLastError();
 }
 
@@ -1116,7 +1165,7 @@ size_t prefill_workspace_bytes(int, int, int H, int num_seqs, int64_t total_toke
 }
 
 hipError_t launch_prefill(const PrefillArgs& a) {
-    if (a.dk > DKP || a.dv % 16 != 0) return hipErrorInvalidValue;
+    if (a.dk > DKP || a.dv > DVP || a.dv % 16 != 0) return hipErrorInvalidValue;
     if ((int64_t)a.num_seqs * a.H * (a.dv / 16) > 0x7fffffffLL) return hipErrorInvalidValue;
     return a.in_bf16 ? launch_t<bf16_t>(a) : launch_t<float>(a);
 }
