@@ -89,26 +89,43 @@ __device__ __forceinline__ void split(float x, uint16_t& hi, uint16_t& lo) {
     lo = bfb(x - bff(hi));
 }
 
-__device__ __forceinline__ uint4 pack8(const uint16_t (&x)[8]) {
-    uint4 u;
-    u.x = x[0] | ((uint32_t)x[1] << 16); u.y = x[2] | ((uint32_t)x[3] << 16);
-    u.z = x[4] | ((uint32_t)x[5] << 16); u.w = x[6] | ((uint32_t)x[7] << 16);
-    return u;
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// bf16 of two values (round to nearest even, one instruction), a in the low half
+__device__ __forceinline__ uint32_t bf2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
+// split of two values at once, packed like bf2
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+    hi = bf2(a, b);
+    lo = bf2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+}
+// eight values as one operand, rounded once
+__device__ __forceinline__ uint4 bf8(const float (&x)[8]) {
+    return make_uint4(bf2(x[0], x[1]), bf2(x[2], x[3]), bf2(x[4], x[5]), bf2(x[6], x[7]));
+}
+// eight values as hi and lo operands
+__device__ __forceinline__ void split8(const float (&x)[8], uint4& hi, uint4& lo) {
+    split2(x[0], x[1], hi.x, lo.x);
+    split2(x[2], x[3], hi.y, lo.y);
+    split2(x[4], x[5], hi.z, lo.z);
+    split2(x[6], x[7], hi.w, lo.w);
+}
+
 __device__ __forceinline__ bf16x8_t as_op(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
 
 // Two accumulator tiles (row blocks 0 and 1 of a 32-row K-step) as one MFMA
 // operand: elements 0..3 come from tile 0, 4..7 from tile 1, split hi / lo.
 __device__ __forceinline__ void pack_split(const f32x4& x0, const f32x4& x1, bf16x8_t& hi,
                                            bf16x8_t& lo) {
-    uint16_t h[8], l[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        split(x0[e], h[e], l[e]);
-        split(x1[e], h[4 + e], l[4 + e]);
-    }
-    hi = as_op(pack8(h));
-    lo = as_op(pack8(l));
+    uint4 h, l;
+    split2(x0[0], x0[1], h.x, l.x);
+    split2(x0[2], x0[3], h.y, l.y);
+    split2(x1[0], x1[1], h.z, l.z);
+    split2(x1[2], x1[3], h.w, l.w);
+    hi = as_op(h);
+    lo = as_op(l);
 }
 
 // -x for a bf16 operand (sign flips, exact)
@@ -372,7 +389,9 @@ void prep_kernel(PrepParams p) {
     using IO = In<TIn>;
     using SM = PrepSmem<TIn>;
     __shared__ SM sm;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    // the wave index is uniform: kept in a scalar register, so addresses that
+    // depend on it are formed on the scalar unit
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g4 = lane >> 4, i16 = lane & 15;
     const int dk = p.dk;
 
@@ -460,18 +479,20 @@ void prep_kernel(PrepParams p) {
                 }
                 // diagonal block
                 {
-                    uint16_t xk[8], xqh[8], xql[8], yh[8], yl[8];
+                    float xk[8], xq[8], yv[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const float xd = ex(Gt[e] - rm[e]);
                         const float yd = ex(rm[e] - Gt[e]);
-                        xk[e] = bfb(kt[e] * xd);
-                        split(qt[e] * xd, xqh[e], xql[e]);
-                        split(kt[e] * yd, yh[e], yl[e]);
+                        xk[e] = kt[e] * xd;
+                        xq[e] = qt[e] * xd;
+                        yv[e] = kt[e] * yd;
                     }
-                    const bf16x8_t XK = as_op(pack8(xk)), XQH = as_op(pack8(xqh)),
-                                   XQL = as_op(pack8(xql)), YH = as_op(pack8(yh)),
-                                   YL = as_op(pack8(yl));
+                    uint4 xqh, xql, yh, yl;
+                    split8(xq, xqh, xql);
+                    split8(yv, yh, yl);
+                    const bf16x8_t XK = as_op(bf8(xk)), XQH = as_op(xqh), XQL = as_op(xql),
+                                   YH = as_op(yh), YL = as_op(yl);
 #pragma unroll
                     for (int ts = 0; ts < 4; ++ts) {
                         if (ts == w) {
@@ -484,26 +505,28 @@ void prep_kernel(PrepParams p) {
                 }
                 // off-diagonal blocks
                 if (w > 0) {
-                    uint16_t xk[8], xqh[8], xql[8];
+                    float xk[8], xq[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const float xo = ex(Gt[e] - rw[e]);
-                        xk[e] = bfb(kt[e] * xo);
-                        split(qt[e] * xo, xqh[e], xql[e]);
+                        xk[e] = kt[e] * xo;
+                        xq[e] = qt[e] * xo;
                     }
-                    const bf16x8_t XK = as_op(pack8(xk)), XQH = as_op(pack8(xqh)),
-                                   XQL = as_op(pack8(xql));
+                    uint4 xqh, xql;
+                    split8(xq, xqh, xql);
+                    const bf16x8_t XK = as_op(bf8(xk)), XQH = as_op(xqh), XQL = as_op(xql);
 #pragma unroll
                     for (int ts = 0; ts < 3; ++ts) {
                         if (ts < w) {
                             const int s = 16 * ts + i16;
                             float ksv[8];
                             IO::f32x8(*reinterpret_cast<const typename IO::V8*>(&sm.k.kS[s][c0]), ksv);
-                            uint16_t yh[8], yl[8];
+                            float yv[8];
 #pragma unroll
-                            for (int e = 0; e < 8; ++e)
-                                split(ksv[e] * ex(rw[e] - sm.u.G[s][c0 + e]), yh[e], yl[e]);
-                            const bf16x8_t YH = as_op(pack8(yh)), YL = as_op(pack8(yl));
+                            for (int e = 0; e < 8; ++e) yv[e] = ksv[e] * ex(rw[e] - sm.u.G[s][c0 + e]);
+                            uint4 yh, yl;
+                            split8(yv, yh, yl);
+                            const bf16x8_t YH = as_op(yh), YL = as_op(yl);
                             accA[ts] = mfma(XK, YH, accA[ts]);
                             accB[ts] = mfma(XQH, YH, accB[ts]);
                             accB[ts] = mfma(XQH, YL, accB[ts]);
@@ -552,14 +575,16 @@ void prep_kernel(PrepParams p) {
             const int ws = idx >> 8, m = (idx >> 7) & 1, ks = (idx >> 6) & 1, ln = idx & 63;
             const int c = SL * ws + chan_of(m, ln & 15), t0 = 32 * ks + 8 * (ln >> 4);
             const float gcc = sm.u.G[C - 1][c];
-            uint16_t kh[8], kl[8];
+            float kv[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int t = t0 + e;
-                split(IO::f32(sm.k.kS[t][c]) * ex(gcc - sm.u.G[t][c]), kh[e], kl[e]);
+                kv[e] = IO::f32(sm.k.kS[t][c]) * ex(gcc - sm.u.G[t][c]);
             }
-            dst[OP_K + idx] = pack8(kh);
-            dst[OP_K + 2 * PLANE + idx] = pack8(kl);
+            uint4 kh, kl;
+            split8(kv, kh, kl);
+            dst[OP_K + idx] = kh;
+            dst[OP_K + 2 * PLANE + idx] = kl;
         }
         // Q e^G of this thread's units (token tok_of(w, i16), channels
         // 32r + 8*g4 .. +7) stay in fp32 until Q' is formed; K e^G of the same
@@ -688,17 +713,20 @@ void prep_kernel(PrepParams p) {
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 const int s0 = 32 * ks + 8 * g4;
-                uint16_t th[8], tl[8], bh[8], bl[8];
+                float tv[8], bv[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int s = s0 + e;
-                    split((s <= t) ? sm.u.tv.T[t][s] * sm.beta[s] : 0.f, th[e], tl[e]);
-                    split(sm.ab.B[t][s], bh[e], bl[e]);
+                    tv[e] = (s <= t) ? sm.u.tv.T[t][s] * sm.beta[s] : 0.f;
+                    bv[e] = sm.ab.B[t][s];
                 }
-                TBh[ks] = as_op(pack8(th));
-                TBl[ks] = as_op(pack8(tl));
-                Bh[ks] = as_op(pack8(bh));
-                Bl[ks] = as_op(pack8(bl));
+                uint4 th, tl, bh, bl;
+                split8(tv, th, tl);
+                split8(bv, bh, bl);
+                TBh[ks] = as_op(th);
+                TBl[ks] = as_op(tl);
+                Bh[ks] = as_op(bh);
+                Bl[ks] = as_op(bl);
             }
             f32x4 acc[4];
 #pragma unroll
@@ -711,13 +739,15 @@ void prep_kernel(PrepParams p) {
                     if (ks == 0 && nt >= 2) continue;  // TB[s < 32][s' >= 32] = 0
                     // column 16nt + i16 of TB over tokens 32ks + 8*g4 .. +7
                     const int sc = 16 * nt + i16;
-                    uint16_t ch[8], cl[8];
+                    float cv[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const int s = 32 * ks + 8 * g4 + e;
-                        split((sc <= s) ? sm.u.tv.T[s][sc] * sm.beta[sc] : 0.f, ch[e], cl[e]);
+                        cv[e] = (sc <= s) ? sm.u.tv.T[s][sc] * sm.beta[sc] : 0.f;
                     }
-                    const bf16x8_t CH = as_op(pack8(ch)), CL = as_op(pack8(cl));
+                    uint4 ch, cl;
+                    split8(cv, ch, cl);
+                    const bf16x8_t CH = as_op(ch), CL = as_op(cl);
                     acc[nt] = mfma(Bh[ks], CH, acc[nt]);
                     acc[nt] = mfma(Bh[ks], CL, acc[nt]);
                     acc[nt] = mfma(Bl[ks], CH, acc[nt]);
@@ -734,11 +764,13 @@ void prep_kernel(PrepParams p) {
             const int t = tok_of(w, i16);
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                uint16_t mh[8], ml[8];
+                float mv[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) split(sm.ab.M[t][32 * ks + 8 * g4 + e], mh[e], ml[e]);
-                Mh[ks] = as_op(pack8(mh));
-                Ml[ks] = as_op(pack8(ml));
+                for (int e = 0; e < 8; ++e) mv[e] = sm.ab.M[t][32 * ks + 8 * g4 + e];
+                uint4 mh, ml;
+                split8(mv, mh, ml);
+                Mh[ks] = as_op(mh);
+                Ml[ks] = as_op(ml);
             }
         }
 
@@ -845,63 +877,72 @@ struct ScanOps {
 // The next chunk's operands are loaded in three parts spread over the
 // current chunk, so the wave never stalls on a full memory queue.  rot
 // rotates the order of the state-row blocks, so the value tiles of one head
-// do not all request the same lines at once.
-__device__ __forceinline__ const uint4* scan_block(const ScanParams& p, int64_t gc, int h) {
-    return p.ops + (gc * p.H + h) * CHUNK_OPS;
+// do not all request the same lines at once.  Loads go through a buffer
+// resource of the chunk's block: the lane's offset is one register for every
+// load, the rest of each address is a scalar.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t scan_block(const ScanParams& p, int64_t gc, int h) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(p.ops + (gc * p.H + h) * CHUNK_OPS), 0,
+                                             CHUNK_OPS * 16, 0x00020000);
+}
+__device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, int unit) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, unit * 16, 0));
+}
+__device__ __forceinline__ float4 ld16f(__amdgpu_buffer_rsrc_t r, uint32_t voff, int unit) {
+    return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, unit * 16, 0));
 }
 
-__device__ __forceinline__ void scan_load1(ScanOps& o, const uint4* __restrict__ blk, int w, int tile,
-                                           int lane, int rot) {
+// vo = 16 * lane
+__device__ __forceinline__ void scan_load1(ScanOps& o, __amdgpu_buffer_rsrc_t blk, int w, int tile,
+                                           uint32_t vo, int rot) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const int x = (((r + rot) & 3) * 4 + w) * 64 + lane;
-        o.w[r][0] = blk[OP_W + x];
-        o.w[r][1] = blk[OP_W + 2 * PLANE + x];
+        const int x = (((r + rot) & 3) * 4 + w) * 64;
+        o.w[r][0] = ld16(blk, vo, OP_W + x);
+        o.w[r][1] = ld16(blk, vo, OP_W + 2 * PLANE + x);
     }
-    o.u = reinterpret_cast<const float4*>(blk + OP_U)[(tile * 4 + w) * 64 + lane];
+    o.u = ld16f(blk, vo, OP_U + (tile * 4 + w) * 64);
 }
 
-__device__ __forceinline__ void scan_load2(ScanOps& o, const uint4* __restrict__ blk, int w, int tile,
-                                           int lane, int rot) {
+__device__ __forceinline__ void scan_load2(ScanOps& o, __amdgpu_buffer_rsrc_t blk, int w, int tile,
+                                           uint32_t vo, int rot) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const int x = (((r + rot) & 3) * 4 + w) * 64 + lane;
-        o.q[r][0] = blk[OP_Q + x];
-        o.q[r][1] = blk[OP_Q + 2 * PLANE + x];
+        const int x = (((r + rot) & 3) * 4 + w) * 64;
+        o.q[r][0] = ld16(blk, vo, OP_Q + x);
+        o.q[r][1] = ld16(blk, vo, OP_Q + 2 * PLANE + x);
     }
-    o.o = reinterpret_cast<const float4*>(blk + OP_O)[(tile * 4 + w) * 64 + lane];
+    o.o = ld16f(blk, vo, OP_O + (tile * 4 + w) * 64);
 }
 
-__device__ __forceinline__ void scan_load3(ScanOps& o, const uint4* __restrict__ blk, int w,
-                                           int lane) {
-    const int g4 = lane >> 4;
+// vd = 32 * (lane / 16)
+__device__ __forceinline__ void scan_load3(ScanOps& o, __amdgpu_buffer_rsrc_t blk, int w, uint32_t vo,
+                                           uint32_t vd) {
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            const int x = ((w * 2 + m) * 2 + ks) * 64 + lane;
-            o.kd[m][ks][0] = blk[OP_K + x];
-            o.kd[m][ks][1] = blk[OP_K + 2 * PLANE + x];
+            const int x = ((w * 2 + m) * 2 + ks) * 64;
+            o.kd[m][ks][0] = ld16(blk, vo, OP_K + x);
+            o.kd[m][ks][1] = ld16(blk, vo, OP_K + 2 * PLANE + x);
         }
-    const float4* dec = reinterpret_cast<const float4*>(blk + OP_DEC);
-    o.dec[0] = dec[8 * w + 2 * g4];
-    o.dec[1] = dec[8 * w + 2 * g4 + 1];
+    // e^{G_C} of channels 32w + 8*(lane/16) .. +7
+    o.dec[0] = ld16f(blk, vd, OP_DEC + 8 * w);
+    o.dec[1] = ld16f(blk, vd, OP_DEC + 8 * w + 1);
 }
 
 // hi and lo bf16 of four fp32 values, as two packed 64-bit halves
 __device__ __forceinline__ void split4(const f32x4& x, uint2& hi, uint2& lo) {
-    uint16_t h[4], l[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) split(x[e], h[e], l[e]);
-    hi = make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
-    lo = make_uint2(l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16));
+    split2(x[0], x[1], hi.x, lo.x);
+    split2(x[2], x[3], hi.y, lo.y);
 }
 
 template <bool OUT_BF16>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void scan_kernel(ScanParams p) {
     __shared__ ScanSmem sm;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    // the wave index is uniform: kept in a scalar register, so addresses that
+    // depend on it are formed on the scalar unit
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g4 = lane >> 4, i16 = lane & 15;
     (void)tid;
 
@@ -940,20 +981,30 @@ void scan_kernel(ScanParams p) {
     // Operands are prefetched one chunk ahead into two register sets used in
     // turn (the loop body is instantiated twice with the roles swapped), so
     // no loaded value is copied and nothing waits early for the next chunk.
+    const uint32_t vo = 16 * lane, vd = 32 * g4;
     ScanOps opA, opB;
     if (nch > 0) {
-        const uint4* blk = scan_block(p, cbase, h);
-        scan_load1(opA, blk, w, tile, lane, rot);
-        scan_load2(opA, blk, w, tile, lane, rot);
-        scan_load3(opA, blk, w, lane);
+        const __amdgpu_buffer_rsrc_t blk = scan_block(p, cbase, h);
+        scan_load1(opA, blk, w, tile, vo, rot);
+        scan_load2(opA, blk, w, tile, vo, rot);
+        scan_load3(opA, blk, w, vo, vd);
     }
+
+    // Output rows of a chunk through a buffer resource that ends at the
+    // sequence's last row: stores past it fall outside and are dropped.
+    constexpr int OB = OUT_BF16 ? 2 : 4;
+    const int64_t orow = (int64_t)p.H * dv;  // elements per token row
+    uint32_t ooff[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        ooff[e] = (uint32_t)(((int64_t)tok_of(w, 4 * g4 + e) * orow + (int64_t)h * dv + j) * OB);
 
     auto chunk = [&](const int ci, ScanOps& o, ScanOps& nx) {
         const int64_t row0 = seq0 + (int64_t)ci * C;
         const int n = min(C, len - ci * C);
         // the next chunk (the last chunk reloads itself, so the same loads are
         // issued on every path; that data is unused)
-        const uint4* nblk = scan_block(p, cbase + min(ci + 1, nch - 1), h);
+        const __amdgpu_buffer_rsrc_t nblk = scan_block(p, cbase + min(ci + 1, nch - 1), h);
 
         // ---- publish this wave's state rows ----
         {
@@ -962,7 +1013,7 @@ void scan_kernel(ScanParams p) {
             sm.sx[w][lane][0] = __builtin_bit_cast(uint4, Sh);
             sm.sx[w][lane][1] = __builtin_bit_cast(uint4, Sl);
         }
-        scan_load1(nx, nblk, w, tile, lane, rot);
+        scan_load1(nx, nblk, w, tile, vo, rot);
         lds_barrier();
 
         // ---- this wave's token tile: U = U~ - W S and O = scale (Q' S + O~) ----
@@ -989,7 +1040,7 @@ void scan_kernel(ScanParams p) {
             split4(u, uh, ul);
             sm.ux[w >> 1][lane].h[w & 1] = uh;
             sm.ux[w >> 1][lane].l[w & 1] = ul;
-            scan_load2(nx, nblk, w, tile, lane, rot);
+            scan_load2(nx, nblk, w, tile, vo, rot);
 #pragma unroll
             for (int r = 0; r < 4; r += 2) {
                 p0 = mfma(as_op(o.q[r][0]), Sh[r], p0);
@@ -1001,17 +1052,15 @@ void scan_kernel(ScanParams p) {
             }
             const f32x4 po = p0 + p1;
             const float ob[4] = {o.o.x, o.o.y, o.o.z, o.o.w};
+            const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+                static_cast<char*>(p.out) + row0 * orow * OB, 0, (int)((int64_t)n * orow * OB), 0x00020000);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int t = tok_of(w, 4 * g4 + e);
-                if (t < n) {
-                    const float ov = p.scale * (po[e] + ob[e]);
-                    const int64_t oi = ((row0 + t) * p.H + h) * (int64_t)dv + j;
-                    if constexpr (OUT_BF16)
-                        static_cast<uint16_t*>(p.out)[oi] = bfb(ov);
-                    else
-                        static_cast<float*>(p.out)[oi] = ov;
-                }
+                const float ov = p.scale * (po[e] + ob[e]);
+                if constexpr (OUT_BF16)
+                    __builtin_amdgcn_raw_buffer_store_b16(bfb(ov), orsrc, ooff[e], 0, 0);
+                else
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ov), orsrc, ooff[e], 0, 0);
             }
         }
         lds_barrier();
@@ -1025,7 +1074,7 @@ void scan_kernel(ScanParams p) {
                 Uh[ks] = __builtin_bit_cast(bf16x8_t, make_uint4(x.h[0].x, x.h[0].y, x.h[1].x, x.h[1].y));
                 Ul[ks] = __builtin_bit_cast(bf16x8_t, make_uint4(x.l[0].x, x.l[0].y, x.l[1].x, x.l[1].y));
             }
-            scan_load3(nx, nblk, w, lane);
+            scan_load3(nx, nblk, w, vo, vd);
             // S <- Diag(e^{G_C}) S + (K e^{G_C - G})^T U
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
