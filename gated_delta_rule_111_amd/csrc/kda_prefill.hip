@@ -664,31 +664,37 @@ void prep_kernel(PrepParams p) {
             for (int r = 0; r < 16; ++r) sm.u.tv.T[bo + r][bo + j] = xs[r];
         }
         __syncthreads();
-        {
-            const int r = tid >> 4, cc = tid & 15;
+        // Off-diagonal blocks band by band; wave I forms block (I, J = I - d):
+        //   M = sum_{K=J}^{I-1} A_IK T_KJ,   T_IJ = -T_II M
+        // on the fp32 MFMA (16x16x4, one fp32 value per lane and operand), so
+        // every product is exact in fp32.
 #pragma unroll
-            for (int d = 1; d < 4; ++d) {
-                // blocks (I, J = I - d): M = sum_{K=J}^{I-1} A_IK T_KJ ; T_IJ = -T_II M
-                for (int I = d; I < 4; ++I) {
-                    const int J = I - d;
-                    float acc = 0.f;
-                    for (int K = J; K < I; ++K)
+        for (int d = 1; d < 4; ++d) {
+            if (w >= d) {
+                const int I = w, J = w - d;
+                const int ar = 16 * I + i16;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                for (int K = J; K < I; ++K)
 #pragma unroll
-                        for (int m = 0; m < 16; ++m)
-                            acc = fmaf(sm.ab.A[16 * I + r][16 * K + m], sm.u.tv.T[16 * K + m][16 * J + cc], acc);
-                    sm.Ms[I - d][r][cc] = acc;
+                    for (int kk = 0; kk < 4; ++kk) {
+                        const int k = 16 * K + 4 * kk + g4;
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.ab.A[ar][k], sm.u.tv.T[k][16 * J + i16],
+                                                                 acc, 0, 0, 0);
+                    }
+                float (*Mw)[17] = sm.Ms[w - 1];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Mw[4 * g4 + e][i16] = acc[e];
+                lds_wave_sync();
+                f32x4 tm = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const int k = 4 * kk + g4;
+                    tm = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.u.tv.T[ar][16 * I + k], Mw[k][i16], tm, 0, 0, 0);
                 }
-                __syncthreads();
-                for (int I = d; I < 4; ++I) {
-                    const int J = I - d;
-                    float acc = 0.f;
 #pragma unroll
-                    for (int m = 0; m < 16; ++m)
-                        acc = fmaf(sm.u.tv.T[16 * I + r][16 * I + m], sm.Ms[I - d][m][cc], acc);
-                    sm.u.tv.T[16 * I + r][16 * J + cc] = -acc;
-                }
-                __syncthreads();
+                for (int e = 0; e < 4; ++e) sm.u.tv.T[16 * I + 4 * g4 + e][16 * J + i16] = -tm[e];
             }
+            __syncthreads();
         }
 
         // ---- B (A is dead now) ----
