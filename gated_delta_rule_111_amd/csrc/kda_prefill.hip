@@ -289,6 +289,20 @@ struct PrepSmem {
     float beta[C];
 };
 
+// Exchange slots of the Gram partial sums, one 64-lane f32x4 tile per
+// (row tile R, column tile ts <= R, A or B): row tiles 2 and 3 in the A/B
+// area, row tiles 0 and 1 in the pairwise-path scratch that follows it.
+template <typename SM>
+__device__ __forceinline__ f32x4* gram_xch(SM& sm, int R, int ts, int which) {
+    // blocks before row tile R: R (R + 1) / 2
+    if (R >= 2) {
+        const int blk = (R * (R + 1) / 2 - 3) + ts;  // row 2 -> 0..2, row 3 -> 3..6
+        return reinterpret_cast<f32x4*>(&sm.ab.A[0][0]) + (blk * 2 + which) * 64;
+    }
+    const int blk = R * (R + 1) / 2 + ts;  // row 0 -> 0, row 1 -> 1..2
+    return reinterpret_cast<f32x4*>(&sm.Bd[0][0][0]) + (blk * 2 + which) * 64;
+}
+
 struct PrepParams {
     const void* q;
     const void* k;
@@ -324,6 +338,14 @@ __device__ __forceinline__ PrepItem prep_item(const PrepParams& p, int it) {
     return r;
 }
 
+// Gram work split: waves 0 and 3 form row tiles 0 and 3, waves 1 and 2 row
+// tiles 1 and 2 (equal work per pair: a row tile w has w + 1 blocks), each
+// wave over one half of the channels (K-steps 2 (w / 2), 2 (w / 2) + 1).
+__device__ __forceinline__ int gram_row(int w, int slot) {
+    const int ra = (w == 0 || w == 3) ? 0 : 1;
+    return slot ? 3 - ra : ra;
+}
+
 // This thread's share of one item's raw inputs: g rows 8r + tid/32, channels
 // 4*(tid%32)..+3; k, q rows 16r + tid/16, channels 8*(tid%16)..+7; beta of
 // row tid (tid < 64).  Rows past the chunk end are read from its last row
@@ -332,7 +354,7 @@ template <typename TIn>
 struct PrepRaw {
     float4 g[8];
     typename In<TIn>::V8 k[4];
-    typename In<TIn>::V8 qg[4];  // q at (16w + lane%16, 32ks + 8*(lane/16)), ks = 0..3
+    typename In<TIn>::V8 qg[4];  // q of the Gram rows: [row slot][K-step of the channel half]
     typename In<TIn>::V8 qd[4];  // q at (tok_of(mt, lane%16), 32w' + 8*(lane/16)) of unit r
     float beta;
 };
@@ -364,11 +386,12 @@ __device__ __forceinline__ void prep_load(PrepRaw<TIn>& r, const PrepParams& p, 
     }
     {
         const int lane = tid & 63, w = tid >> 6;
-        const int t = 16 * w + (lane & 15);
+        const int ra = gram_row(w, 0), rb = gram_row(w, 1);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const int c = 32 * ks + 8 * (lane >> 4);
-            r.qg[ks] = IO::load8(p.q, base + min(t, x.n - 1) * rs + (c < dk ? c : 0));
+        for (int u = 0; u < 4; ++u) {
+            const int t = 16 * ((u >> 1) ? rb : ra) + (lane & 15);
+            const int c = 32 * (2 * (w >> 1) + (u & 1)) + 8 * (lane >> 4);
+            r.qg[u] = IO::load8(p.q, base + min(t, x.n - 1) * rs + (c < dk ? c : 0));
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -442,99 +465,131 @@ void prep_kernel(PrepParams p) {
             __syncthreads();
         }
 
-        // ---- Gram matrices: wave w computes row tile w (rows 16w .. 16w+15) ----
-        // Off-diagonal blocks (column tile ts < w) use the reference r = G at
-        // row 16w - 1, so both factors e^{G_t - r} and e^{r - G_s} are <= 1.
-        // The diagonal block uses r = G at row 16w + 7, keeping both factors
-        // within e^{+-span/2} of the block; spans beyond SPAN_LIMIT take the
-        // pairwise path.
+        // ---- Gram matrices A and B, 16 x 16 blocks (row tile R, column tile ts <= R) ----
+        // Off-diagonal blocks use the reference r = G at row 16R - 1, so both
+        // factors e^{G_t - r} and e^{r - G_s} are <= 1.  The diagonal block
+        // uses r = G at row 16R + 7, keeping both factors within e^{+-span/2}
+        // of the block; spans beyond SPAN_LIMIT take the pairwise path.
+        // Wave w forms row tiles gram_row(w, 0..1) over its channel half; the
+        // partial sums of the row tile it does not own go to its partner
+        // through LDS, so that wave w ends with row tile w summed over all
+        // channels.
         int extreme = 0;
         f32x4 accB[4];
         {
+            f32x4 pA[2][4], pB[2][4];  // [row slot][column tile]
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+                for (int ts = 0; ts < 4; ++ts) {
+                    pA[sl][ts] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    pB[sl][ts] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+            const int hh = w >> 1;
+#pragma unroll 1
+            for (int kk = 0; kk < 2; ++kk) {
+                const int c0 = 32 * (2 * hh + kk) + 8 * g4;
+#pragma unroll
+                for (int sl = 0; sl < 2; ++sl) {
+                    const int R = gram_row(w, sl);
+                    const int t = 16 * R + i16;
+                    float kt[8], qt[8];
+                    IO::f32x8(*reinterpret_cast<const typename IO::V8*>(&sm.k.kS[t][c0]), kt);
+                    const typename IO::V8 qx = kk ? raw.qg[2 * sl + 1] : raw.qg[2 * sl];
+                    IO::f32x8((t < n && c0 < dk) ? qx : IO::zero8(), qt);
+                    float Gt[8], rw[8], rm[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        Gt[e] = sm.u.G[t][c0 + e];
+                        rw[e] = sm.u.G[R > 0 ? 16 * R - 1 : 0][c0 + e];
+                        rm[e] = sm.u.G[16 * R + 7][c0 + e];
+                        extreme |= (sm.u.G[16 * R][c0 + e] - rm[e] > SPAN_LIMIT) |
+                                   (rm[e] - sm.u.G[16 * R + 15][c0 + e] > SPAN_LIMIT);
+                    }
+                    // diagonal block
+                    {
+                        float xk[8], xq[8], yv[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const float xd = ex(Gt[e] - rm[e]);
+                            const float yd = ex(rm[e] - Gt[e]);
+                            xk[e] = kt[e] * xd;
+                            xq[e] = qt[e] * xd;
+                            yv[e] = kt[e] * yd;
+                        }
+                        uint4 xqh, xql, yh, yl;
+                        split8(xq, xqh, xql);
+                        split8(yv, yh, yl);
+                        const bf16x8_t XK = as_op(bf8(xk)), XQH = as_op(xqh), XQL = as_op(xql),
+                                       YH = as_op(yh), YL = as_op(yl);
+#pragma unroll
+                        for (int ts = 0; ts < 4; ++ts) {
+                            if (ts == R) {
+                                pA[sl][ts] = mfma(XK, YH, pA[sl][ts]);
+                                pB[sl][ts] = mfma(XQH, YH, pB[sl][ts]);
+                                pB[sl][ts] = mfma(XQH, YL, pB[sl][ts]);
+                                pB[sl][ts] = mfma(XQL, YH, pB[sl][ts]);
+                            }
+                        }
+                    }
+                    // off-diagonal blocks
+                    if (R > 0) {
+                        float xk[8], xq[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const float xo = ex(Gt[e] - rw[e]);
+                            xk[e] = kt[e] * xo;
+                            xq[e] = qt[e] * xo;
+                        }
+                        uint4 xqh, xql;
+                        split8(xq, xqh, xql);
+                        const bf16x8_t XK = as_op(bf8(xk)), XQH = as_op(xqh), XQL = as_op(xql);
+#pragma unroll
+                        for (int ts = 0; ts < 3; ++ts) {
+                            if (ts < R) {
+                                const int s = 16 * ts + i16;
+                                float ksv[8];
+                                IO::f32x8(*reinterpret_cast<const typename IO::V8*>(&sm.k.kS[s][c0]), ksv);
+                                float yv[8];
+#pragma unroll
+                                for (int e = 0; e < 8; ++e) yv[e] = ksv[e] * ex(rw[e] - sm.u.G[s][c0 + e]);
+                                uint4 yh, yl;
+                                split8(yv, yh, yl);
+                                const bf16x8_t YH = as_op(yh), YL = as_op(yl);
+                                pA[sl][ts] = mfma(XK, YH, pA[sl][ts]);
+                                pB[sl][ts] = mfma(XQH, YH, pB[sl][ts]);
+                                pB[sl][ts] = mfma(XQH, YL, pB[sl][ts]);
+                                pB[sl][ts] = mfma(XQL, YH, pB[sl][ts]);
+                            }
+                        }
+                    }
+                }
+            }
+            // exchange: the slot this wave does not own goes to its partner
+            const int own = (gram_row(w, 0) == w) ? 0 : 1;
             f32x4 accA[4];
+            {
+                const int R = gram_row(w, 1 - own);
+#pragma unroll
+                for (int ts = 0; ts < 4; ++ts)
+                    if (ts <= R) {
+                        gram_xch(sm, R, ts, 0)[lane] = own ? pA[0][ts] : pA[1][ts];
+                        gram_xch(sm, R, ts, 1)[lane] = own ? pB[0][ts] : pB[1][ts];
+                    }
+            }
+            __syncthreads();
 #pragma unroll
             for (int ts = 0; ts < 4; ++ts) {
-                accA[ts] = f32x4{0.f, 0.f, 0.f, 0.f};
-                accB[ts] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-            const int t = 16 * w + i16;
-#pragma unroll 1
-            for (int ks = 0; ks < 4; ++ks) {
-                const int c0 = 32 * ks + 8 * g4;
-                float kt[8], qt[8];
-                IO::f32x8(*reinterpret_cast<const typename IO::V8*>(&sm.k.kS[t][c0]), kt);
-                typename IO::V8 qx = raw.qg[0];
-#pragma unroll
-                for (int q = 1; q < 4; ++q)
-                    if (ks == q) qx = raw.qg[q];
-                IO::f32x8((t < n && c0 < dk) ? qx : IO::zero8(), qt);
-                float Gt[8], rw[8], rm[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    Gt[e] = sm.u.G[t][c0 + e];
-                    rw[e] = sm.u.G[w > 0 ? 16 * w - 1 : 0][c0 + e];
-                    rm[e] = sm.u.G[16 * w + 7][c0 + e];
-                    extreme |= (sm.u.G[16 * w][c0 + e] - rm[e] > SPAN_LIMIT) |
-                               (rm[e] - sm.u.G[16 * w + 15][c0 + e] > SPAN_LIMIT);
-                }
-                // diagonal block
-                {
-                    float xk[8], xq[8], yv[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float xd = ex(Gt[e] - rm[e]);
-                        const float yd = ex(rm[e] - Gt[e]);
-                        xk[e] = kt[e] * xd;
-                        xq[e] = qt[e] * xd;
-                        yv[e] = kt[e] * yd;
-                    }
-                    uint4 xqh, xql, yh, yl;
-                    split8(xq, xqh, xql);
-                    split8(yv, yh, yl);
-                    const bf16x8_t XK = as_op(bf8(xk)), XQH = as_op(xqh), XQL = as_op(xql),
-                                   YH = as_op(yh), YL = as_op(yl);
-#pragma unroll
-                    for (int ts = 0; ts < 4; ++ts) {
-                        if (ts == w) {
-                            accA[ts] = mfma(XK, YH, accA[ts]);
-                            accB[ts] = mfma(XQH, YH, accB[ts]);
-                            accB[ts] = mfma(XQH, YL, accB[ts]);
-                            accB[ts] = mfma(XQL, YH, accB[ts]);
-                        }
-                    }
-                }
-                // off-diagonal blocks
-                if (w > 0) {
-                    float xk[8], xq[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const float xo = ex(Gt[e] - rw[e]);
-                        xk[e] = kt[e] * xo;
-                        xq[e] = qt[e] * xo;
-                    }
-                    uint4 xqh, xql;
-                    split8(xq, xqh, xql);
-                    const bf16x8_t XK = as_op(bf8(xk)), XQH = as_op(xqh), XQL = as_op(xql);
-#pragma unroll
-                    for (int ts = 0; ts < 3; ++ts) {
-                        if (ts < w) {
-                            const int s = 16 * ts + i16;
-                            float ksv[8];
-                            IO::f32x8(*reinterpret_cast<const typename IO::V8*>(&sm.k.kS[s][c0]), ksv);
-                            float yv[8];
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) yv[e] = ksv[e] * ex(rw[e] - sm.u.G[s][c0 + e]);
-                            uint4 yh, yl;
-                            split8(yv, yh, yl);
-                            const bf16x8_t YH = as_op(yh), YL = as_op(yl);
-                            accA[ts] = mfma(XK, YH, accA[ts]);
-                            accB[ts] = mfma(XQH, YH, accB[ts]);
-                            accB[ts] = mfma(XQH, YL, accB[ts]);
-                            accB[ts] = mfma(XQL, YH, accB[ts]);
-                        }
-                    }
+                const f32x4 a = own ? pA[1][ts] : pA[0][ts], bb = own ? pB[1][ts] : pB[0][ts];
+                if (ts <= w) {
+                    accA[ts] = a + gram_xch(sm, w, ts, 0)[lane];
+                    accB[ts] = bb + gram_xch(sm, w, ts, 1)[lane];
+                } else {
+                    accA[ts] = a;
+                    accB[ts] = bb;
                 }
             }
+            __syncthreads();  // the exchange area overlaps A
             // accumulator (row 4*g4+e, column i16) of block (w, ts); masked
             // entries are selected away, never multiplied (they may hold inf)
 #pragma unroll
