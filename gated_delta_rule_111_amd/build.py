@@ -23,9 +23,12 @@ ARCH = "gfx950"
 SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_prefill.hip"]
 
 # Packed fp32 VALU ops are switched off for every device pass; the host pass
-# warns that it does not know the feature, which is harmless.
+# warns that it does not know the feature, which is harmless.  MFMA
+# accumulators are kept in ordinary VGPRs (no copies between register files
+# where results feed vector ALU work).
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-mfma-vgpr-form",
           "-Wno-unused-command-line-argument", f"-I{os.path.join(ROOT, 'include')}"]
 
 
