@@ -209,7 +209,7 @@ def bench_prefill(torch, kda, inputs, w, reps, warmup):
             "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic("prefill", w.name),
-            "kernel": "plan + prep_kernel<bf16> + scan_kernel<bf16> (whole call)",
+            "kernel": "plan + prep_kernel<bf16> + scan_kernel (whole call)",
             "bytes_per_launch": nbytes,
         },
         "mfma": {

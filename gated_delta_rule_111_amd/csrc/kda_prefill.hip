@@ -23,25 +23,29 @@
 //   S'   = Diag(e^{G_C}) S + (K . e^{G_C - G})^T U
 // Substituting the recurrence into itself inside a chunk gives
 // (I + A) U = Diag(b) (V - (K . e^G) S); the rest follows by unrolling.
+// With W = TB (K . e^G), M = B TB, U~ = TB V, O~ = M V and
+// Q' = Q . e^G - M (K . e^G) the step becomes
+//   U = U~ - W S,   O = scale (Q' S + O~),   S' = Diag(e^{G_C}) S + Kd U
+// (Kd = (K . e^{G_C - G})^T), so everything but three products with S is
+// independent of the state.
 //
 // Three launches on the caller's stream:
 //   plan  -- one workgroup: per-sequence offsets of chunks and snapshots;
 //   prep  -- one workgroup per (chunk, head), all chunks in parallel: the
-//            Gram matrices A and B on MFMA, T by block forward substitution,
-//            then TB and B written to the workspace as hi/lo bf16 MFMA
-//            operands (everything here is independent of the state);
+//            Gram matrices A and B, T, W, M, Q', U~ and O~ (MFMA wherever
+//            the step is a product), written to the workspace as the
+//            scan's per-lane operands;
 //   scan  -- one workgroup per (sequence, head, 16 value columns), walking
 //            the sequence chunk by chunk with the fp32 state in registers.
-//            Wave w owns 32 state rows.  Per chunk each wave builds its
-//            decay-scaled operands from the cumulative log-decay, forms its
-//            partial (K e^G) S and (Q e^G) S, and the four waves exchange
-//            them through LDS with one barrier; then every wave forms U,
-//            its rows of O and its rows of the next state.
+//            Wave w owns 32 state rows and one 16-token tile of the chunk;
+//            state rows and U tiles are exchanged through LDS, two
+//            barriers per chunk.
 //
 // Precision: v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  Operands that
 // are not exact bf16 values are split into hi + lo bf16 and multiplied in
 // three passes (hi*hi + hi*lo + lo*hi, ~16 bits); the K K^T Gram and the
-// (K e^G) S product use one bf16 rounding of the decay-scaled keys.  State,
+// (K e^G) operand of W and Q' use one bf16 rounding of the decay-scaled
+// keys.  State,
 // snapshots, outputs and every accumulation are fp32.
 //
 // Determinism: every reduction has a fixed order that depends neither on the

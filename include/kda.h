@@ -99,9 +99,10 @@ int64_t kda_snapshot_count(const int32_t *cu_seqlens_host, int32_t num_seqs,
                            int32_t interval);
 
 /*
- * Bytes of device workspace kda_prefill needs for this problem (may be 0;
- * then `workspace` may be NULL).  Returns 0 for unsupported configs too;
- * kda_prefill reports those.
+ * Bytes of device workspace kda_prefill needs for this problem: 512 B of
+ * offsets plus (floor(total_tokens / 64) + num_seqs) * num_heads * 164,352 B
+ * of per-chunk operands (about 2.6 KB per token and head).  Returns 0 for
+ * unsupported configs too; kda_prefill reports those.
  */
 size_t kda_prefill_workspace_size(const kda_config *cfg, int32_t num_seqs,
                                   int64_t total_tokens);
