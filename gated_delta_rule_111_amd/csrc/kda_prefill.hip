@@ -67,7 +67,7 @@ constexpr int C = 64;                // chunk rows
 constexpr int NT = 256;              // threads per workgroup (4 waves)
 constexpr int DKP = 128;             // state rows, zero-padded above dk
 constexpr int SL = 32;               // state rows per wave
-constexpr float SPAN_LIMIT = 80.0f;  // |exponent| bound for the diagonal Gram factors
+constexpr float SPAN_LIMIT = 115.0f; // |log2 exponent| bound for the diagonal Gram factors (~e^80)
 constexpr int PLANE = 512;           // uint4 per operand plane (4 row tiles x 2 K-steps x 64 lanes)
 
 __device__ __forceinline__ f32x4 mfma(const bf16x8_t& a, const bf16x8_t& b, const f32x4& c) {
@@ -85,7 +85,9 @@ __device__ __forceinline__ void lds_wave_sync() { asm volatile("s_waitcnt lgkmcn
 
 __device__ __forceinline__ uint16_t bfb(float x) { return f32_to_bf16_bits(x); }
 __device__ __forceinline__ float bff(uint32_t b) { return bf16_bits_to_f32(b); }
-__device__ __forceinline__ float ex(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+// 2^x; the prep kernel keeps its log-decays in log2 units
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+constexpr float LOG2E = 1.4426950408889634f;
 
 // x = hi + lo with hi = bf16(x), lo = bf16(x - hi) (x - hi is exact in fp32)
 __device__ __forceinline__ void split(float x, uint16_t& hi, uint16_t& lo) {
@@ -143,6 +145,9 @@ __device__ __forceinline__ bf16x8_t neg(const bf16x8_t& x) {
 // permutation differs between rows 8 apart (the transposing writes of one
 // instruction) and between neighbouring rows (the operand reads).
 __device__ __forceinline__ int vt_group(int j, int g) { return g ^ ((j ^ (j >> 3)) & 7); }
+// Storage slot of token group g in row c of (K e^G)^T: rows 8 channels apart
+// (the transposing writes of one instruction) land in different slots.
+__device__ __forceinline__ int kg_group(int c, int g) { return g ^ ((c >> 3) & 7); }
 
 // Row orders inside a chunk.  An accumulator tile holds rows 4*(lane/16)+e;
 // two tiles packed as one operand give a lane K positions 4*(lane/16)+e of
@@ -273,20 +278,21 @@ struct PrepSmem {
     static constexpr int KP = DKP + 16 / (int)sizeof(TIn);  // padded row of staged keys, queries
     static constexpr int NV = sizeof(TIn) == 2 ? 1 : 2;     // bf16 planes of a value (hi[, lo])
     union {
-        float G[C][DKP + 4];   // cumulative log-decay
+        float G[C][DKP + 4];   // cumulative log-decay, log2 units
         struct {
-            float T[C][C + 4];             // (I + A)^-1, once the decay-scaled operands are out
+            float TT[C][C + 4];            // (I + A)^-1 transposed, TT[s][t] = T[t][s]
             uint16_t VT[NV][DVP][C];       // V^T in bf16 planes, 16-byte groups swizzled by column
         } tv;
     } u;
     union {
-        float A[C][C + 1];     // strictly lower b_t sum_c k_t k_s e^{G_t - G_s}
-        float B[C][C + 1];     // lower sum_c q_t k_s e^{G_t - G_s}, once T is formed
-        float M[C][C + 1];     // B TB, once every wave holds its rows of B
+        float A[C][C + 4];     // strictly lower b_t sum_c k_t k_s e^{G_t - G_s}
+        float B[C][C + 4];     // lower sum_c q_t k_s e^{G_t - G_s}, once T is formed
+        float M[C][C + 4];     // B TB, once every wave holds its rows of B
     } ab;
     union {
         TIn kS[C][KP];             // the chunk's keys (zero past n and dk)
-        uint16_t KgT[DKP][C + 8];  // (K . e^G)^T in bf16, [channel][token], once kS is read
+        uint16_t KgT[DKP][C + 8];  // (K . e^G)^T in bf16, [channel][token], once kS is read;
+                                   // 16-byte token groups permuted by kg_group
     } k;
     float Bd[4][16][17];       // diagonal blocks of B from the pairwise path
     float Ms[3][16][17];       // block products of the forward substitution
@@ -429,14 +435,17 @@ void prep_kernel(PrepParams p) {
         const int n = x.n;
         uint4* __restrict__ dst = p.ops + (x.gc * p.H + x.h) * CHUNK_OPS;
 
-        // ---- stage this item's inputs (zero past n and dk) ----
+        // ---- stage this item's inputs (zero past n and dk); log-decays in
+        // log2 units, so every factor below is a bare exp2 ----
         {
             const int c = 4 * (tid & 31);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int t = 8 * i + (tid >> 5);
+                const float4 gv = raw.g[i];
                 *reinterpret_cast<float4*>(&sm.u.G[t][c]) =
-                    (t < n && c < dk) ? raw.g[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+                    (t < n && c < dk) ? make_float4(gv.x * LOG2E, gv.y * LOG2E, gv.z * LOG2E, gv.w * LOG2E)
+                                      : make_float4(0.f, 0.f, 0.f, 0.f);
             }
         }
         {
@@ -451,14 +460,20 @@ void prep_kernel(PrepParams p) {
         if (tid < C) sm.beta[tid] = tid < n ? raw.beta : 0.f;
         __syncthreads();
 
-        // ---- cumulative log-decay per channel ----
+        // ---- cumulative log-decay per channel; the span check of the
+        // diagonal Gram blocks (first and last row against the middle row of
+        // each 16-row tile) is independent of the running offset ----
+        int extreme = 0;
         {
             const int c = tid & 127, half = tid >> 7;
-            float run = 0.f;
-#pragma unroll 8
+            float run = 0.f, g0 = 0.f, g7 = 0.f;
+#pragma unroll
             for (int r = 0; r < 32; ++r) {
                 run += sm.u.G[half * 32 + r][c];
                 sm.u.G[half * 32 + r][c] = run;
+                if ((r & 15) == 0) g0 = run;
+                if ((r & 15) == 7) g7 = run;
+                if ((r & 15) == 15) extreme |= (g0 - g7 > SPAN_LIMIT) | (g7 - run > SPAN_LIMIT);
             }
             __syncthreads();
             if (half == 1) {
@@ -472,13 +487,12 @@ void prep_kernel(PrepParams p) {
         // ---- Gram matrices A and B, 16 x 16 blocks (row tile R, column tile ts <= R) ----
         // Off-diagonal blocks use the reference r = G at row 16R - 1, so both
         // factors e^{G_t - r} and e^{r - G_s} are <= 1.  The diagonal block
-        // uses r = G at row 16R + 7, keeping both factors within e^{+-span/2}
-        // of the block; spans beyond SPAN_LIMIT take the pairwise path.
+        // uses r = G at row 16R + 7, keeping both factors within 2^{+-span/2}
+        // of the block; half-spans beyond SPAN_LIMIT take the pairwise path.
         // Wave w forms row tiles gram_row(w, 0..1) over its channel half; the
         // partial sums of the row tile it does not own go to its partner
         // through LDS, so that wave w ends with row tile w summed over all
         // channels.
-        int extreme = 0;
         f32x4 accB[4];
         {
             f32x4 pA[2][4], pB[2][4];  // [row slot][column tile]
@@ -507,16 +521,14 @@ void prep_kernel(PrepParams p) {
                         Gt[e] = sm.u.G[t][c0 + e];
                         rw[e] = sm.u.G[R > 0 ? 16 * R - 1 : 0][c0 + e];
                         rm[e] = sm.u.G[16 * R + 7][c0 + e];
-                        extreme |= (sm.u.G[16 * R][c0 + e] - rm[e] > SPAN_LIMIT) |
-                                   (rm[e] - sm.u.G[16 * R + 15][c0 + e] > SPAN_LIMIT);
                     }
                     // diagonal block
                     {
                         float xk[8], xq[8], yv[8];
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
-                            const float xd = ex(Gt[e] - rm[e]);
-                            const float yd = ex(rm[e] - Gt[e]);
+                            const float xd = ex2(Gt[e] - rm[e]);
+                            const float yd = ex2(rm[e] - Gt[e]);
                             xk[e] = kt[e] * xd;
                             xq[e] = qt[e] * xd;
                             yv[e] = kt[e] * yd;
@@ -541,7 +553,7 @@ void prep_kernel(PrepParams p) {
                         float xk[8], xq[8];
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
-                            const float xo = ex(Gt[e] - rw[e]);
+                            const float xo = ex2(Gt[e] - rw[e]);
                             xk[e] = kt[e] * xo;
                             xq[e] = qt[e] * xo;
                         }
@@ -556,7 +568,7 @@ void prep_kernel(PrepParams p) {
                                 IO::f32x8(*reinterpret_cast<const typename IO::V8*>(&sm.k.kS[s][c0]), ksv);
                                 float yv[8];
 #pragma unroll
-                                for (int e = 0; e < 8; ++e) yv[e] = ksv[e] * ex(rw[e] - sm.u.G[s][c0 + e]);
+                                for (int e = 0; e < 8; ++e) yv[e] = ksv[e] * ex2(rw[e] - sm.u.G[s][c0 + e]);
                                 uint4 yh, yl;
                                 split8(yv, yh, yl);
                                 const bf16x8_t YH = as_op(yh), YL = as_op(yl);
@@ -601,7 +613,8 @@ void prep_kernel(PrepParams p) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int tr = 16 * w + 4 * g4 + e, sc = 16 * ts + i16;
-                    sm.ab.A[tr][sc] = (sc < tr) ? accA[ts][e] * sm.beta[tr] : 0.f;
+                    const float a = accA[ts][e] * sm.beta[tr];
+                    sm.ab.A[tr][sc] = (sc < tr) ? a : 0.f;
                 }
         }
         const int any_extreme = __syncthreads_or(extreme);
@@ -617,7 +630,7 @@ void prep_kernel(PrepParams p) {
                 for (int c = 0; c < dk; ++c) {
                     const float kt = IO::f32(sm.k.kS[t][c]), kv = IO::f32(sm.k.kS[s][c]);
                     const float qt = t < n ? IO::f32(IO::load1(p.q, ((x.row0 + t) * p.H + x.h) * (int64_t)dk + c)) : 0.f;
-                    const float e = ex(sm.u.G[t][c] - sm.u.G[s][c]);
+                    const float e = ex2(sm.u.G[t][c] - sm.u.G[s][c]);
                     sa = fmaf(kt * kv, e, sa);
                     sb = fmaf(qt * kv, e, sb);
                 }
@@ -625,6 +638,17 @@ void prep_kernel(PrepParams p) {
                 sm.Bd[blk][tl][sl] = sb;
             }
             __syncthreads();
+        }
+
+        // this item's v rows (16 rows x 8 columns per thread), requested here
+        // and staged as V^T after the diagonal blocks of T are solved
+        typename IO::V8 vr[4];
+        {
+            const int c = 8 * (tid & 15);
+            const int64_t vs = (int64_t)p.H * p.dv;
+            const int64_t vb = (x.row0 * p.H + x.h) * (int64_t)p.dv + (c < p.dv ? c : 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) vr[i] = IO::load8(p.v, vb + min(16 * i + (tid >> 4), n - 1) * vs);
         }
 
         // ---- decay-scaled operands: Kd planes, Qd planes, dec, then (K e^G)^T ----
@@ -638,7 +662,7 @@ void prep_kernel(PrepParams p) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int t = t0 + e;
-                kv[e] = IO::f32(sm.k.kS[t][c]) * ex(gcc - sm.u.G[t][c]);
+                kv[e] = IO::f32(sm.k.kS[t][c]) * ex2(gcc - sm.u.G[t][c]);
             }
             uint4 kh, kl;
             split8(kv, kh, kl);
@@ -658,31 +682,39 @@ void prep_kernel(PrepParams p) {
             IO::f32x8(*reinterpret_cast<const typename IO::V8*>(&sm.k.kS[t][c0]), kv);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float eg = ex(sm.u.G[t][c0 + e]);
+                const float eg = ex2(sm.u.G[t][c0 + e]);
                 qd[r][e] = qv[e] * eg;
                 kg[r][e] = bfb(kv[e] * eg);
             }
         }
-        if (tid < DKP) reinterpret_cast<float*>(dst + OP_DEC)[tid] = ex(sm.u.G[C - 1][tid]);
+        if (tid < DKP) reinterpret_cast<float*>(dst + OP_DEC)[tid] = ex2(sm.u.G[C - 1][tid]);
         __syncthreads();  // keys and G are read: their storage becomes (K e^G)^T, T and V^T
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = tok_of(w, i16), c0 = SL * r + 8 * g4;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sm.k.KgT[c0 + e][t] = kg[r][e];
+            for (int e = 0; e < 8; ++e) sm.k.KgT[c0 + e][kg_group(c0 + e, t >> 3) * 8 + (t & 7)] = kg[r][e];
         }
-        // this item's v rows (16 rows x 8 columns per thread), staged as V^T
-        // while the forward substitution runs; rows past n and columns past
-        // dv are zero.  V^T rows are 64 tokens; its 16-byte groups are
-        // permuted by vt_group so that neither the transposing writes nor the
-        // operand reads collide in LDS banks.
-        {
-            typename IO::V8 vr[4];
-            const int c = 8 * (tid & 15);
-            const int64_t vs = (int64_t)p.H * p.dv;
-            const int64_t vb = (x.row0 * p.H + x.h) * (int64_t)p.dv + (c < p.dv ? c : 0);
+        // ---- T = (I + A)^-1 by block forward substitution ----
+        if (lane < 16) {
+            // diagonal block w, column j = lane
+            const int bo = 16 * w, j = lane;
+            float xs[16];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) vr[i] = IO::load8(p.v, vb + min(16 * i + (tid >> 4), n - 1) * vs);
+            for (int r = 0; r < 16; ++r) {
+                float acc = 0.f;
+#pragma unroll
+                for (int m = 0; m < r; ++m) acc = fmaf(sm.ab.A[bo + r][bo + m], xs[m], acc);
+                xs[r] = (r == j) ? 1.f : -acc;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sm.u.tv.TT[bo + j][bo + r] = xs[r];
+        }
+        // V^T: rows past n and columns past dv are zero.  V^T rows are 64
+        // tokens; its 16-byte groups are permuted by vt_group so that neither
+        // the transposing writes nor the operand reads collide in LDS banks.
+        {
+            const int c = 8 * (tid & 15);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = 16 * i + (tid >> 4);
@@ -706,23 +738,6 @@ void prep_kernel(PrepParams p) {
             }
         }
         __syncthreads();
-
-        // ---- T = (I + A)^-1 by block forward substitution ----
-        if (lane < 16) {
-            // diagonal block w, column j = lane
-            const int bo = 16 * w, j = lane;
-            float xs[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float acc = 0.f;
-#pragma unroll
-                for (int m = 0; m < r; ++m) acc = fmaf(sm.ab.A[bo + r][bo + m], xs[m], acc);
-                xs[r] = (r == j) ? 1.f : -acc;
-            }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sm.u.tv.T[bo + r][bo + j] = xs[r];
-        }
-        __syncthreads();
         // Off-diagonal blocks band by band; wave I forms block (I, J = I - d):
         //   M = sum_{K=J}^{I-1} A_IK T_KJ,   T_IJ = -T_II M
         // on the fp32 MFMA (16x16x4, one fp32 value per lane and operand), so
@@ -737,7 +752,7 @@ void prep_kernel(PrepParams p) {
 #pragma unroll
                     for (int kk = 0; kk < 4; ++kk) {
                         const int k = 16 * K + 4 * kk + g4;
-                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.ab.A[ar][k], sm.u.tv.T[k][16 * J + i16],
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.ab.A[ar][k], sm.u.tv.TT[16 * J + i16][k],
                                                                  acc, 0, 0, 0);
                     }
                 float (*Mw)[17] = sm.Ms[w - 1];
@@ -748,10 +763,10 @@ void prep_kernel(PrepParams p) {
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
                     const int k = 4 * kk + g4;
-                    tm = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.u.tv.T[ar][16 * I + k], Mw[k][i16], tm, 0, 0, 0);
+                    tm = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.u.tv.TT[16 * I + k][ar], Mw[k][i16], tm, 0, 0, 0);
                 }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) sm.u.tv.T[16 * I + 4 * g4 + e][16 * J + i16] = -tm[e];
+                for (int e = 0; e < 4; ++e) sm.u.tv.TT[16 * J + i16][16 * I + 4 * g4 + e] = -tm[e];
             }
             __syncthreads();
         }
@@ -762,8 +777,10 @@ void prep_kernel(PrepParams p) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int tr = 16 * w + 4 * g4 + e, sc = 16 * ts + i16;
-                float v = accB[ts][e];
-                if (any_extreme && ts == w) v = sm.Bd[w][4 * g4 + e][i16];
+                // the pairwise value is read unconditionally and selected (a
+                // load under a condition becomes a branch and a wait)
+                const float bd = sm.Bd[w][4 * g4 + e][i16];
+                const float v = (any_extreme && ts == w) ? bd : accB[ts][e];
                 sm.ab.B[tr][sc] = (sc <= tr) ? v : 0.f;
             }
         __syncthreads();
@@ -782,7 +799,8 @@ void prep_kernel(PrepParams p) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int s = s0 + e;
-                    tv[e] = (s <= t) ? sm.u.tv.T[t][s] * sm.beta[s] : 0.f;
+                    const float x = sm.u.tv.TT[s][t] * sm.beta[s];
+                    tv[e] = (s <= t) ? x : 0.f;
                     bv[e] = sm.ab.B[t][s];
                 }
                 uint4 th, tl, bh, bl;
@@ -808,7 +826,8 @@ void prep_kernel(PrepParams p) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const int s = 32 * ks + 8 * g4 + e;
-                        cv[e] = (sc <= s) ? sm.u.tv.T[s][sc] * sm.beta[sc] : 0.f;
+                        const float x = sm.u.tv.TT[sc][s] * sm.beta[sc];
+                        cv[e] = (sc <= s) ? x : 0.f;
                     }
                     uint4 ch, cl;
                     split8(cv, ch, cl);
@@ -853,7 +872,7 @@ void prep_kernel(PrepParams p) {
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
                     const bf16x8_t kgo = as_op(*reinterpret_cast<const uint4*>(
-                        &sm.k.KgT[SL * r + chan_of(m, i16)][32 * ks + 8 * g4]));
+                        &sm.k.KgT[SL * r + chan_of(m, i16)][kg_group(SL * r + chan_of(m, i16), 4 * ks + g4) * 8]));
                     aw[m] = mfma(kgo, TBh[ks], aw[m]);
                     aw[m] = mfma(kgo, TBl[ks], aw[m]);
                     aq[m] = mfma(kgo, neg(Mh[ks]), aq[m]);
