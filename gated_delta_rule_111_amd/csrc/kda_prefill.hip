@@ -442,10 +442,11 @@ void prep_kernel(PrepParams p) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int t = 8 * i + (tid >> 5);
+                // rows past n and channels past dk were read from valid
+                // (finite) entries: a zero factor clears them without a branch
                 const float4 gv = raw.g[i];
-                *reinterpret_cast<float4*>(&sm.u.G[t][c]) =
-                    (t < n && c < dk) ? make_float4(gv.x * LOG2E, gv.y * LOG2E, gv.z * LOG2E, gv.w * LOG2E)
-                                      : make_float4(0.f, 0.f, 0.f, 0.f);
+                const float f = (t < n && c < dk) ? LOG2E : 0.f;
+                *reinterpret_cast<float4*>(&sm.u.G[t][c]) = make_float4(gv.x * f, gv.y * f, gv.z * f, gv.w * f);
             }
         }
         {
