@@ -149,6 +149,13 @@ __device__ __forceinline__ int vt_group(int j, int g) { return g ^ ((j ^ (j >> 3
 // (the transposing writes of one instruction) land in different slots.
 __device__ __forceinline__ int kg_group(int c, int g) { return g ^ ((c >> 3) & 7); }
 
+// eight consecutive fp32 of an LDS row (16-byte aligned) as two 128-bit reads
+__device__ __forceinline__ void lds8(const float* p, float (&x)[8]) {
+    const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
 // Row orders inside a chunk.  An accumulator tile holds rows 4*(lane/16)+e;
 // two tiles packed as one operand give a lane K positions 4*(lane/16)+e of
 // each.  Numbering the chunk's tokens and the wave's state rows so that
@@ -517,12 +524,9 @@ void prep_kernel(PrepParams p) {
                     const typename IO::V8 qx = kk ? raw.qg[2 * sl + 1] : raw.qg[2 * sl];
                     IO::f32x8((t < n && c0 < dk) ? qx : IO::zero8(), qt);
                     float Gt[8], rw[8], rm[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        Gt[e] = sm.u.G[t][c0 + e];
-                        rw[e] = sm.u.G[R > 0 ? 16 * R - 1 : 0][c0 + e];
-                        rm[e] = sm.u.G[16 * R + 7][c0 + e];
-                    }
+                    lds8(&sm.u.G[t][c0], Gt);
+                    lds8(&sm.u.G[R > 0 ? 16 * R - 1 : 0][c0], rw);
+                    lds8(&sm.u.G[16 * R + 7][c0], rm);
                     // diagonal block
                     {
                         float xk[8], xq[8], yv[8];
@@ -567,9 +571,10 @@ void prep_kernel(PrepParams p) {
                                 const int s = 16 * ts + i16;
                                 float ksv[8];
                                 IO::f32x8(*reinterpret_cast<const typename IO::V8*>(&sm.k.kS[s][c0]), ksv);
-                                float yv[8];
+                                float gs[8], yv[8];
+                                lds8(&sm.u.G[s][c0], gs);
 #pragma unroll
-                                for (int e = 0; e < 8; ++e) yv[e] = ksv[e] * ex2(rw[e] - sm.u.G[s][c0 + e]);
+                                for (int e = 0; e < 8; ++e) yv[e] = ksv[e] * ex2(rw[e] - gs[e]);
                                 uint4 yh, yl;
                                 split8(yv, yh, yl);
                                 const bf16x8_t YH = as_op(yh), YL = as_op(yl);
@@ -681,9 +686,11 @@ void prep_kernel(PrepParams p) {
             float qv[8], kv[8];
             IO::f32x8((t < n && c0 < dk) ? raw.qd[r] : IO::zero8(), qv);
             IO::f32x8(*reinterpret_cast<const typename IO::V8*>(&sm.k.kS[t][c0]), kv);
+            float gt[8];
+            lds8(&sm.u.G[t][c0], gt);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float eg = ex2(sm.u.G[t][c0 + e]);
+                const float eg = ex2(gt[e]);
                 qd[r][e] = qv[e] * eg;
                 kg[r][e] = bfb(kv[e] * eg);
             }
