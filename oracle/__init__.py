@@ -16,8 +16,11 @@ computed, and the passages it follows, are stated in the header of
   ``o_t = dk^-1/2 S_t^T q_t``.
 * "Day-0 vLLM support for Kimi K3", section "Kimi K3's architecture, and how
   vLLM serves it": state snapshots at block boundaries for prefix reuse.
+* "Kimi K3 technical FAQ", same question: queries and keys pass through a
+  short convolution, Swish and L2 normalisation first (``qk_frontend``).
 
-Parity pins for every function here are in ``tests/test_oracle_pins.py``.
+Parity pins for every function here are in ``tests/test_oracle_pins.py``
+and ``tests/test_frontend_pins.py``.
 """
 from __future__ import annotations
 
@@ -54,6 +57,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
                                       P, P, f64, P, i32]
     lib.kda_oracle_snapshot_count.restype = i64
     lib.kda_oracle_snapshot_count.argtypes = [i32, P, i64]
+    lib.kda_oracle_qk_frontend.restype = ctypes.c_int
+    lib.kda_oracle_qk_frontend.argtypes = [i32, P, i32, i32, i32, P, P, P, P, f64, P, P]
     return lib
 
 
@@ -150,6 +155,54 @@ class Oracle:
         return out, st
 
 
+    def qk_frontend(self, x, w, cu_seqlens, conv_width: int, eps: float,
+                    state=None, slots=None, num_slots: Optional[int] = None):
+        """Short convolution -> Swish -> L2 norm of one tensor (q or k).
+
+        x: [T, H, dk]; w: [H*dk, W] (or [H, dk, W]) convolution taps, tap W-1
+        on the current token; state: [S, W-1, H, dk] inputs that preceded each
+        slot's sequence (oldest first) or None for zero history; slots: [N]
+        state row of each sequence or None (identity).  Returns (y [T,H,dk]
+        fp64, new_state [S, W-1, H, dk] fp32): a copy of ``state`` (zeros when
+        it is None) whose rows of this call's sequences hold their last W-1
+        inputs.
+        """
+        x = self._f32(x)
+        T, H, dk = x.shape
+        W = int(conv_width)
+        w = self._f32(w).reshape(H * dk, W)
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+        N = len(cu) - 1
+        assert cu[0] == 0 and cu[-1] == T
+        sl = None
+        if slots is not None:
+            sl = np.ascontiguousarray(np.asarray(slots, dtype=np.int32))
+            assert sl.shape == (N,)
+        if state is not None:
+            new_state = np.array(state, dtype=np.float32, order="C", copy=True)
+            S = new_state.shape[0]
+            assert new_state.shape == (S, W - 1, H, dk)
+            st_in = new_state.copy()
+        else:
+            S = num_slots if num_slots is not None else (
+                N if sl is None else int(sl.max(initial=-1)) + 1)
+            new_state = np.zeros((S, W - 1, H, dk), dtype=np.float32)
+            st_in = None
+        if sl is not None and N:
+            assert sl.min() >= 0 and sl.max() < S and len(set(sl.tolist())) == N
+        else:
+            assert N <= S
+        y = np.zeros((T, H, dk), dtype=np.float64)
+        rc = self.lib.kda_oracle_qk_frontend(
+            N, cu.ctypes.data, H, dk, W, x.ctypes.data, w.ctypes.data,
+            None if st_in is None else st_in.ctypes.data,
+            None if sl is None else sl.ctypes.data, float(eps), y.ctypes.data,
+            new_state.ctypes.data)
+        if rc != 0:
+            raise ValueError("kda_oracle_qk_frontend rejected its arguments")
+        return y, new_state
+
+
 _DEFAULT: Optional[Oracle] = None
 
 
@@ -167,3 +220,7 @@ def prefill(*args, **kwargs):
 
 def decode(*args, **kwargs):
     return get().decode(*args, **kwargs)
+
+
+def qk_frontend(*args, **kwargs):
+    return get().qk_frontend(*args, **kwargs)

@@ -342,3 +342,113 @@ int kda_oracle_decode(int32_t steps, int32_t N, int32_t H, int32_t dk,
     pthread_mutex_destroy(&J.lock);
     return (rc != 0 || J.failed) ? -1 : 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Front end of q and k: short convolution -> Swish -> L2 normalisation.     */
+/*                                                                          */
+/* "Kimi K3 technical FAQ" (Runpod guide), question "What is KDA, and why    */
+/* does a serving engineer care?": queries and keys pass through a short     */
+/* convolution, Swish and L2 normalisation before the recurrence.  The page  */
+/* gives neither the width nor the exact forms; the reading used here is     */
+/*                                                                          */
+/*   z_t[c] = sum_{j=0}^{W-1} w[c][j] * x_{t-(W-1)+j}[c]    (c = h*dk + i)   */
+/*   a_t[c] = z_t[c] * sigmoid(z_t[c])                      (Swish, beta 1)  */
+/*   y_t[h] = a_t[h] / sqrt(|a_t[h]|^2 + eps)      (per token and head)      */
+/*                                                                          */
+/* a depthwise, causal convolution along each sequence's own tokens (no      */
+/* bias): tap W-1 weighs the current token, tap 0 the oldest.  Inputs before */
+/* the sequence's first token come from its convolution state (the W-1       */
+/* inputs that preceded it, oldest first) or are zero when there is none.    */
+/* After the call the state of sequence b holds its last W-1 inputs (taken   */
+/* from the state itself where the sequence is shorter than W-1).            */
+/*                                                                          */
+/* Layouts: x, y [T, H, dk]; w [H*dk, W]; states [num_slots, W-1, H, dk];    */
+/* slots (nullable = identity) maps sequence b to its state row.             */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    const int64_t *cu;
+    int32_t H, dk, W;
+    size_t C; /* channels per token, H * dk */
+    const float *x, *w, *state_in;
+} frontend_args;
+
+/* Input of channel ch at token u of sequence b (u may precede the start). */
+static double frontend_input(const frontend_args *A, int32_t b, int32_t slot,
+                             int64_t u, size_t ch)
+{
+    const int64_t start = A->cu[b];
+    if (u >= start)
+        return (double)A->x[(size_t)u * A->C + ch];
+    if (!A->state_in)
+        return 0.0;
+    /* state row r holds the input (W-1) - r tokens before the start */
+    return (double)A->state_in[((size_t)slot * (A->W - 1) +
+                                (size_t)((A->W - 1) + (u - start))) * A->C + ch];
+}
+
+int kda_oracle_qk_frontend(int32_t num_seqs, const int64_t *cu, int32_t H,
+                           int32_t dk, int32_t W, const float *x,
+                           const float *w, const float *state_in,
+                           const int32_t *slots, double eps, double *y,
+                           float *state_out)
+{
+    frontend_args A;
+    double *a = NULL;
+    float *tail = NULL;
+    int32_t b;
+    if (num_seqs < 0 || !cu || H <= 0 || dk <= 0 || W < 1 || !w || !(eps > 0.0))
+        return -1;
+    for (b = 0; b < num_seqs; ++b)
+        if (cu[b + 1] < cu[b])
+            return -1;
+    A.cu = cu;
+    A.H = H;
+    A.dk = dk;
+    A.W = W;
+    A.C = (size_t)H * dk;
+    A.x = x;
+    A.w = w;
+    A.state_in = state_in;
+    a = (double *)malloc(sizeof(double) * (size_t)dk);
+    tail = (float *)malloc(sizeof(float) * (A.C * (size_t)W + 1));
+    if (!a || !tail) {
+        free(a);
+        free(tail);
+        return -1;
+    }
+    for (b = 0; b < num_seqs; ++b) {
+        const int32_t slot = slots ? slots[b] : b;
+        int64_t t;
+        int32_t h, i, j, r;
+        for (t = cu[b]; t < cu[b + 1]; ++t) {
+            for (h = 0; h < H; ++h) {
+                double n2 = 0.0;
+                for (i = 0; i < dk; ++i) {
+                    const size_t ch = (size_t)h * dk + i;
+                    double z = 0.0;
+                    for (j = 0; j < W; ++j)
+                        z += (double)w[ch * W + j] *
+                             frontend_input(&A, b, slot, t - (W - 1) + j, ch);
+                    a[i] = z / (1.0 + exp(-z));
+                    n2 += a[i] * a[i];
+                }
+                for (i = 0; i < dk; ++i)
+                    y[((size_t)t * H + h) * dk + i] = a[i] / sqrt(n2 + eps);
+            }
+        }
+        /* new state: the last W-1 inputs, gathered before any is written so
+           that state_out may be state_in itself */
+        if (state_out && W > 1) {
+            size_t ch;
+            for (r = 0; r < W - 1; ++r)
+                for (ch = 0; ch < A.C; ++ch)
+                    tail[(size_t)r * A.C + ch] = (float)frontend_input(
+                        &A, b, slot, cu[b + 1] - (W - 1) + r, ch);
+            memcpy(state_out + (size_t)slot * (W - 1) * A.C, tail,
+                   sizeof(float) * A.C * (size_t)(W - 1));
+        }
+    }
+    free(a);
+    free(tail);
+    return 0;
+}

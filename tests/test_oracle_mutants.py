@@ -8,6 +8,7 @@ import shutil
 
 import pytest
 
+import frontend_pins
 import oracle
 import oracle_pins
 
@@ -33,12 +34,25 @@ MUTANTS = [
     ("decode_wrong_slot",
      "S = J->state + ((size_t)(J->slots ? J->slots[n] : n) * H + h) * ssz;",
      "S = J->state + ((size_t)n * H + h) * ssz;"),
+    # q/k front end (short convolution -> Swish -> L2 norm)
+    ("fe_taps_reversed", "z += (double)w[ch * W + j] *",
+     "z += (double)w[ch * W + (W - 1 - j)] *"),
+    ("fe_head_ignored", "z += (double)w[ch * W + j] *", "z += (double)w[(size_t)i * W + j] *"),
+    ("fe_no_swish", "a[i] = z / (1.0 + exp(-z));", "a[i] = z;"),
+    ("fe_sigmoid_only", "a[i] = z / (1.0 + exp(-z));", "a[i] = 1.0 / (1.0 + exp(-z));"),
+    ("fe_eps_outside_root", "a[i] / sqrt(n2 + eps);", "a[i] / (sqrt(n2) + eps);"),
+    ("fe_squared_norm", "a[i] / sqrt(n2 + eps);", "a[i] / (n2 + eps);"),
+    ("fe_crosses_sequences", "if (u >= start)", "if (u >= 0)"),
+    ("fe_history_reversed", "(size_t)((A->W - 1) + (u - start))) * A->C + ch];",
+     "(size_t)(-1 - (u - start))) * A->C + ch];"),
+    ("fe_state_rows_reversed", "tail[(size_t)r * A.C + ch] = (float)frontend_input(",
+     "tail[(size_t)(W - 2 - r) * A.C + ch] = (float)frontend_input("),
 ]
 
 
 def _run_pins(O):
     broken = []
-    for pin in oracle_pins.ALL_PINS:
+    for pin in oracle_pins.ALL_PINS + frontend_pins.ALL_FRONTEND_PINS:
         try:
             pin(O)
         except AssertionError:
