@@ -54,6 +54,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "decode": os.path.join(ROOT, "gated_delta_rule_111_amd", "csrc", "kda_decode.hip"),
     "prefill": os.path.join(ROOT, "gated_delta_rule_111_amd", "csrc", "kda_prefill.hip"),
+    "frontend": os.path.join(ROOT, "gated_delta_rule_111_amd", "csrc", "kda_frontend.hip"),
 }
 
 
@@ -74,9 +75,11 @@ def measured_traffic(kind: str, workload: str):
             rec = json.load(f).get(kind)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_sha256_16") != source_hash(kind) or rec.get("workload") != workload:
+    if not rec or rec.get("source_sha256_16") != source_hash(kind):
         return None
-    return rec.get("bytes_per_launch")
+    if "workloads" in rec:
+        return rec["workloads"].get(workload)
+    return rec.get("bytes_per_launch") if rec.get("workload") == workload else None
 
 
 def cpu_threads() -> int:
@@ -240,6 +243,96 @@ def cpu_prefill_baseline(inp, tokens: int):
 
 
 # ---------------------------------------------------------------------------
+def _time_graph(torch, fn, reps, inner=10):
+    """Per-call kernel time of `fn` (which launches on torch's current
+    stream) from HIP events around `reps` replays of a HIP graph holding
+    `inner` back-to-back calls, so the host's own per-call cost (argument
+    checks and marshalling) does not show up as idle GPU time.  Returns
+    (wall seconds per call, event seconds per call)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(inner):
+            fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(reps):
+        graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    n = reps * inner
+    return (time.perf_counter() - t0) / n, e0.elapsed_time(e1) / 1e3 / n
+
+
+def bench_frontend(torch, kda, inputs, reps):
+    """q/k front end (short convolution -> Swish -> L2 norm, W = 4) on the
+    prefill shape (T = 8192, H = 32, dk = 128, bf16 in and out) and on a
+    decode step of 256 sequences with their convolution states updated in
+    place, each call timed inside a HIP graph (see _time_graph).  Algorithmic bytes: x read and y written once per tensor
+    (2 * (2 + 2) B per channel), plus per decode sequence the W-1 history
+    rows read and written (2 * 2 * (W-1) * 2 B per channel)."""
+    dev = "cuda:0"
+    W, H, dk = inputs.FRONTEND_WIDTH, 32, 128
+    C = H * dk
+    res = {}
+    for name, lens, stateful in (("prefill-T8192-H32-dk128-W4", [8192], False),
+                                 ("decode-N256-H32-dk128-W4", [1] * 256, True)):
+        inp = inputs.frontend_inputs(lens, H, dk, W, seed=9, num_slots=len(lens) if stateful
+                                     else None, device=dev)
+        T = int(sum(lens))
+        cu_host = inp.cu_seqlens.cpu().tolist()
+        qo = torch.empty(T, H, dk, dtype=torch.bfloat16, device=dev)
+        ko = torch.empty_like(qo)
+        kw = dict(conv_state_q=inp.state_q, conv_state_k=inp.state_k,
+                  conv_state_out_q=inp.state_q, conv_state_out_k=inp.state_k) if stateful else {}
+
+        def call():
+            kda.qk_frontend(inp.xq, inp.xk, inp.wq, inp.wk, inp.cu_seqlens,
+                            cu_seqlens_host=cu_host, q_out=qo, k_out=ko, **kw)
+
+        wall, per_call = _time_graph(torch, call, reps)
+        nbytes = 2 * T * C * (2 + 2) + 2 * C * W * 4
+        if stateful:
+            nbytes += 2 * T * C * 2 * 2 * (W - 1)
+        gbs = nbytes / per_call / 1e9
+        log(f"[bench] frontend {name}: {per_call * 1e6:.1f} us/call, {gbs:.0f} GB/s")
+        res[name] = {
+            "tokens_per_s": round(T / wall, 1),
+            "kernel_us": round(per_call * 1e6, 2),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic("frontend", name),
+                         "kernel": "frontend_kernel<4,bf16,bf16>",
+                         "bytes_per_launch": nbytes},
+        }
+    return res
+
+
+def cpu_frontend_baseline(inputs, tokens: int):
+    import oracle
+    H, dk, W = 32, 128, inputs.FRONTEND_WIDTH
+    inp = inputs.frontend_inputs([tokens], H, dk, W, seed=9)
+    threads = 1
+    log(f"[bench] cpu oracle: frontend {tokens} tokens, q and k")
+    t0 = time.perf_counter()
+    for x, w in ((inp.xq, inp.wq), (inp.xk, inp.wk)):
+        oracle.qk_frontend(x.float().numpy(), w.numpy(), [0, tokens], W, 1e-6)
+    dt = time.perf_counter() - t0
+    return {"value": round(tokens / dt, 1), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"first {tokens} tokens of the prefill shape, q and k, fp64, one thread"}
+
+
+# ---------------------------------------------------------------------------
 def copy_calibration(torch, mib: int):
     """A plain device copy and an in-place scale of `mib` MiB, timed with HIP
     events: the practical read+write bandwidth ceiling for the decode step."""
@@ -270,6 +363,8 @@ def main():
     ap.add_argument("--prefill-reps", type=int, default=20)
     ap.add_argument("--long", action="store_true", help="also time the 1,048,576-token prefill")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-frontend", action="store_true")
+    ap.add_argument("--cpu-frontend-tokens", type=int, default=32768)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-decode-seqs", type=int, default=128)
     ap.add_argument("--cpu-decode-steps", type=int, default=1000)
@@ -305,12 +400,17 @@ def main():
                                   max(2, args.warmup // 10))
     if args.long:
         pre_long, _ = bench_prefill(torch, kda, inputs, inputs.LONG, 3, 1)
+    fe = None
+    if not args.no_frontend:
+        fe = bench_frontend(torch, kda, inputs, args.prefill_reps)
 
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_decode_baseline(dinp, args)
         if pre is not None:
             pre["cpu_baseline"] = cpu_prefill_baseline(pinp, args.cpu_prefill_tokens)
+        if fe is not None:
+            fe["cpu_baseline"] = cpu_frontend_baseline(inputs, args.cpu_frontend_tokens)
 
     line = {
         "metric": METRIC,
@@ -335,6 +435,8 @@ def main():
     }
     if pre_long is not None:
         line["prefill_long"] = pre_long
+    if fe is not None:
+        line["qk_frontend"] = fe
     print(json.dumps(line), flush=True)
 
 

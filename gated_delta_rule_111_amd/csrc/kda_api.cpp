@@ -73,6 +73,15 @@ kda_status check_ptrs(const PtrCheck* list, int n) {
     return KDA_OK;
 }
 
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const char* pa = static_cast<const char*>(a);
+    const char* pb = static_cast<const char*>(b);
+    return pa < pb + nb && pb < pa + na;
+}
+
+size_t dtype_bytes(kda_dtype d) { return d == KDA_BF16 ? 2 : 4; }
+
 }  // namespace
 
 extern "C" {
@@ -228,6 +237,113 @@ kda_status kda_decode(const kda_config* cfg, int32_t num_seqs, const void* q, co
     a.stream = static_cast<hipStream_t>(stream);
     hipError_t e = kda::launch_decode(a);
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+kda_status kda_qk_frontend(const kda_frontend_config* cfg, int32_t num_seqs,
+                           const int32_t* cu_host, const int32_t* cu_dev, const void* xq,
+                           const void* xk, const float* wq, const float* wk,
+                           const void* state_in_q, const void* state_in_k, void* state_out_q,
+                           void* state_out_k, const int32_t* slots, int32_t num_slots,
+                           void* q_out, void* k_out, void* stream) {
+    if (!cfg) return fail(KDA_ERR_INVALID_ARG, "cfg is NULL");
+    if (cfg->num_heads <= 0 || cfg->num_heads > 65535)
+        return fail(KDA_ERR_INVALID_ARG, "num_heads %d not in [1, 65535]", cfg->num_heads);
+    if (cfg->dk != 16 && cfg->dk != 32 && cfg->dk != 64 && cfg->dk != 128)
+        return fail(KDA_ERR_UNSUPPORTED, "head dim %d not in {16, 32, 64, 128}", cfg->dk);
+    if (cfg->conv_width < 1 || cfg->conv_width > 8)
+        return fail(KDA_ERR_UNSUPPORTED, "conv_width %d not in [1, 8]", cfg->conv_width);
+    if (cfg->in_dtype != KDA_BF16 && cfg->in_dtype != KDA_F32)
+        return fail(KDA_ERR_UNSUPPORTED, "in_dtype %d unknown", (int)cfg->in_dtype);
+    if (cfg->out_dtype != KDA_BF16 && cfg->out_dtype != KDA_F32)
+        return fail(KDA_ERR_UNSUPPORTED, "out_dtype %d unknown", (int)cfg->out_dtype);
+    if (!std::isfinite(cfg->eps) || !(cfg->eps > 0.f))
+        return fail(KDA_ERR_INVALID_ARG, "eps must be finite and > 0");
+    if (num_seqs < 0) return fail(KDA_ERR_INVALID_ARG, "num_seqs must be >= 0");
+    if (num_seqs == 0) return ok();
+    if (!cu_host) return fail(KDA_ERR_INVALID_ARG, "cu_seqlens_host is NULL");
+    if (cu_host[0] != 0) return fail(KDA_ERR_INVALID_ARG, "cu_seqlens[0] must be 0");
+    bool unit = true;  // every sequence has exactly one token (a decode step)
+    for (int32_t b = 0; b < num_seqs; ++b) {
+        if (cu_host[b + 1] < cu_host[b])
+            return fail(KDA_ERR_INVALID_ARG, "cu_seqlens decreases at index %d", b + 1);
+        unit = unit && cu_host[b + 1] == b + 1;
+    }
+    const int64_t T = cu_host[num_seqs];
+    const int W = cfg->conv_width;
+    const bool tok = T > 0;
+    const bool stateful = W > 1 && (state_in_q || state_in_k || state_out_q || state_out_k);
+    const PtrCheck ptrs[] = {
+        {"cu_seqlens_dev", cu_dev, true, 4},
+        {"xq", xq, tok, 16},
+        {"xk", xk, tok, 16},
+        {"wq", wq, true, 16},
+        {"wk", wk, true, 16},
+        {"conv_state_in_q", state_in_q, false, 16},
+        {"conv_state_in_k", state_in_k, false, 16},
+        {"conv_state_out_q", state_out_q, false, 16},
+        {"conv_state_out_k", state_out_k, false, 16},
+        {"state_slots_dev", slots, false, 4},
+        {"q_out", q_out, tok, 16},
+        {"k_out", k_out, tok, 16},
+    };
+    kda_status st = check_ptrs(ptrs, (int)(sizeof(ptrs) / sizeof(ptrs[0])));
+    if (st != KDA_OK) return st;
+    if (stateful) {
+        if (num_slots < 1) return fail(KDA_ERR_INVALID_ARG, "num_slots must be >= 1");
+        if (!slots && num_slots < num_seqs)
+            return fail(KDA_ERR_INVALID_ARG, "num_slots %d < num_seqs %d without state_slots_dev",
+                        num_slots, num_seqs);
+    }
+    const size_t C = (size_t)cfg->num_heads * cfg->dk;
+    const size_t xb = (size_t)T * C * dtype_bytes(cfg->in_dtype);
+    const size_t yb = (size_t)T * C * dtype_bytes(cfg->out_dtype);
+    const size_t sb = stateful ? (size_t)num_slots * (W - 1) * C * dtype_bytes(cfg->in_dtype) : 0;
+    const void* outs[2] = {q_out, k_out};
+    const void* ins[2] = {xq, xk};
+    const void* sins[2] = {state_in_q, state_in_k};
+    void* souts[2] = {state_out_q, state_out_k};
+    for (int i = 0; i < 2; ++i) {
+        for (int j = 0; j < 2; ++j)
+            if (overlap(outs[i], yb, ins[j], xb))
+                return fail(KDA_ERR_INVALID_ARG, "an output overlaps an input");
+        if (sins[i] != souts[i] && overlap(sins[i], sb, souts[i], sb))
+            return fail(KDA_ERR_INVALID_ARG, "a state output partially overlaps its input");
+        if (overlap(souts[i], sb, outs[0], yb) || overlap(souts[i], sb, outs[1], yb) ||
+            overlap(souts[i], sb, ins[0], xb) || overlap(souts[i], sb, ins[1], xb))
+            return fail(KDA_ERR_INVALID_ARG, "a state output overlaps a token tensor");
+    }
+    if (overlap(q_out, yb, k_out, yb)) return fail(KDA_ERR_INVALID_ARG, "q_out overlaps k_out");
+    if (overlap(state_out_q, sb, state_out_k, sb) ||
+        overlap(state_out_q, sb, state_in_k, sb) || overlap(state_out_k, sb, state_in_q, sb))
+        return fail(KDA_ERR_INVALID_ARG, "the q and k states overlap");
+
+    kda::FrontendArgs a{};
+    a.H = cfg->num_heads;
+    a.dk = cfg->dk;
+    a.W = W;
+    a.num_seqs = num_seqs;
+    a.in_bf16 = cfg->in_dtype == KDA_BF16;
+    a.out_bf16 = cfg->out_dtype == KDA_BF16;
+    a.unit_lengths = unit;
+    a.total_tokens = T;
+    a.cu_dev = cu_dev;
+    a.x[0] = xq;
+    a.x[1] = xk;
+    a.w[0] = wq;
+    a.w[1] = wk;
+    a.state_in[0] = W > 1 ? state_in_q : nullptr;
+    a.state_in[1] = W > 1 ? state_in_k : nullptr;
+    a.state_out[0] = W > 1 ? state_out_q : nullptr;
+    a.state_out[1] = W > 1 ? state_out_k : nullptr;
+    a.slots = slots;
+    a.y[0] = q_out;
+    a.y[1] = k_out;
+    a.eps = cfg->eps;
+    a.stream = static_cast<hipStream_t>(stream);
+    hipError_t e = kda::launch_frontend(a);
+    if (e != hipSuccess)
+        return fail(KDA_ERR_HIP, "front-end launch failed: %s", hipGetErrorString(e));
     return ok();
 }
 

@@ -40,7 +40,24 @@ struct PrefillArgs {
     hipStream_t stream;
 };
 
+struct FrontendArgs {
+    int H, dk, W, num_seqs;
+    bool in_bf16, out_bf16;
+    bool unit_lengths;            // cu[b] == b for every b (a decode step)
+    int64_t total_tokens;
+    const int32_t* cu_dev;        // [num_seqs + 1] device offsets
+    const void* x[2];             // q, k inputs [T, H, dk]
+    const float* w[2];            // taps [H * dk, W]
+    const void* state_in[2];      // nullable, [num_slots, W-1, H, dk]
+    void* state_out[2];           // nullable; may equal state_in
+    const int32_t* slots;         // nullable (identity)
+    void* y[2];                   // outputs [T, H, dk]
+    float eps;
+    hipStream_t stream;
+};
+
 hipError_t launch_decode(const DecodeArgs& a);
+hipError_t launch_frontend(const FrontendArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);
 size_t prefill_workspace_bytes(int dk, int dv, int H, int num_seqs, int64_t total_tokens);
 int prefill_chunk_rows();  // tokens per chunk; snapshot intervals are multiples of 64

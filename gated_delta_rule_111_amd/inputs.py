@@ -185,3 +185,47 @@ def make_decode(w: Workload, device="cpu", steps=None, N=None) -> DecodeInputs:
                          w.seed, w.in_dtype, w.decay_shift,
                          w.state_std if w.state_std is not None else 0.02,
                          device)
+
+
+# ---------------------------------------------------------------------------
+# q/k front end (short convolution -> Swish -> L2 norm).  The pages give no
+# width or initialisation; the taps are drawn like a freshly initialised
+# depthwise convolution, U(-1/sqrt(W), 1/sqrt(W)) (fan-in W), and the raw q/k
+# (the projections' outputs) and any convolution history as N(0, 1).
+# Drawing order: xq, xk, wq, wk, state_q, state_k.
+# ---------------------------------------------------------------------------
+FRONTEND_WIDTH = 4
+
+
+@dataclass
+class FrontendInputs:
+    xq: torch.Tensor                 # [T, H, dk] in_dtype
+    xk: torch.Tensor                 # [T, H, dk] in_dtype
+    wq: torch.Tensor                 # [H*dk, W]  fp32
+    wk: torch.Tensor                 # [H*dk, W]  fp32
+    cu_seqlens: torch.Tensor         # [N+1] int32
+    state_q: Optional[torch.Tensor]  # [S, W-1, H, dk] in_dtype or None
+    state_k: Optional[torch.Tensor]
+
+
+def frontend_inputs(seq_lens: Sequence[int], H: int, dk: int, W: int, seed: int,
+                    in_dtype=torch.bfloat16, num_slots: Optional[int] = None,
+                    device="cpu") -> FrontendInputs:
+    """Packed varlen front-end inputs; with num_slots, N(0,1) histories for
+    that many state rows."""
+    gen = _gen(seed, device)
+    T = int(sum(seq_lens))
+    xq = torch.randn(T, H, dk, generator=gen, device=device).to(in_dtype)
+    xk = torch.randn(T, H, dk, generator=gen, device=device).to(in_dtype)
+    bound = 1.0 / float(W) ** 0.5
+    wq = (torch.rand(H * dk, W, generator=gen, device=device) * 2 - 1) * bound
+    wk = (torch.rand(H * dk, W, generator=gen, device=device) * 2 - 1) * bound
+    sq = sk = None
+    if num_slots is not None:
+        sq = torch.randn(num_slots, W - 1, H, dk, generator=gen, device=device).to(in_dtype)
+        sk = torch.randn(num_slots, W - 1, H, dk, generator=gen, device=device).to(in_dtype)
+    cu = [0]
+    for L in seq_lens:
+        cu.append(cu[-1] + int(L))
+    cu_t = torch.tensor(cu, dtype=torch.int32, device=device)
+    return FrontendInputs(xq, xk, wq, wk, cu_t, sq, sk)

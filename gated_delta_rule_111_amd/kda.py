@@ -36,6 +36,12 @@ class Config(ctypes.Structure):
                 ("out_dtype", ctypes.c_int), ("scale", ctypes.c_float)]
 
 
+class FrontendConfig(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("dk", ctypes.c_int32),
+                ("conv_width", ctypes.c_int32), ("in_dtype", ctypes.c_int),
+                ("out_dtype", ctypes.c_int), ("eps", ctypes.c_float)]
+
+
 _lib: Optional[ctypes.CDLL] = None
 
 
@@ -63,6 +69,9 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_prefill.argtypes = [CP, i32, P, P, P, P, P, P, P, P, P, P, i32, P, P, sz, P]
     lib.kda_decode.restype = ctypes.c_int
     lib.kda_decode.argtypes = [CP, i32, P, P, P, P, P, P, P, P, P]
+    lib.kda_qk_frontend.restype = ctypes.c_int
+    lib.kda_qk_frontend.argtypes = [ctypes.POINTER(FrontendConfig), i32, P, P, P, P, P, P,
+                                    P, P, P, P, P, i32, P, P, P]
     _lib = lib
     return lib
 
@@ -207,3 +216,79 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
                           g.data_ptr(), beta.data_ptr(), state.data_ptr(), _ptr(slots),
                           out.data_ptr(), _stream(stream)))
     return out
+
+
+def frontend_config(H: int, dk: int, conv_width: int, in_dtype: torch.dtype,
+                    out_dtype: torch.dtype = torch.bfloat16, eps: float = 1e-6) -> FrontendConfig:
+    return FrontendConfig(H, dk, conv_width, _dtype_code(in_dtype), _dtype_code(out_dtype),
+                          float(eps))
+
+
+def qk_frontend(xq: torch.Tensor, xk: torch.Tensor, wq: torch.Tensor, wk: torch.Tensor,
+                cu_seqlens: torch.Tensor, eps: float = 1e-6,
+                conv_state_q: Optional[torch.Tensor] = None,
+                conv_state_k: Optional[torch.Tensor] = None,
+                conv_state_out_q: Optional[torch.Tensor] = None,
+                conv_state_out_k: Optional[torch.Tensor] = None,
+                slots: Optional[torch.Tensor] = None,
+                out_dtype: Optional[torch.dtype] = None,
+                cu_seqlens_host: Optional[Sequence[int]] = None,
+                q_out: Optional[torch.Tensor] = None, k_out: Optional[torch.Tensor] = None,
+                stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """kda_qk_frontend: short convolution -> Swish -> L2 norm of q and k.
+
+    xq, xk: [T, H, dk] (bf16 or fp32, same dtype); wq, wk: [H*dk, W] or
+    [H, dk, W] fp32 taps (tap W-1 on the current token); cu_seqlens: [N+1]
+    int32 on the device.  conv_state_q/k: [S, W-1, H, dk] in the dtype of x,
+    the history of each slot (None = zeros); conv_state_out_q/k: where the new
+    history goes (may be the same tensors: update in place; None = not
+    written).  slots: [N] int32 state rows (None = row b).  Returns (q, k)
+    normalised, [T, H, dk] in out_dtype (default bf16, the dtype kda_prefill
+    and kda_decode take).
+    """
+    lib = load()
+    dev = xq.device
+    T, H, dk = xq.shape
+    W = int(wq.shape[-1])
+    if cu_seqlens_host is None:
+        cu_seqlens_host = cu_seqlens.cpu().tolist()
+    cu_list = [int(x) for x in cu_seqlens_host]
+    N = len(cu_list) - 1
+    _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    _need(xq, "xq", (T, H, dk), xq.dtype, dev)
+    _need(xk, "xk", (T, H, dk), xq.dtype, dev)
+    for name, w in (("wq", wq), ("wk", wk)):
+        if w.numel() != H * dk * W:
+            raise ValueError(f"{name}: {tuple(w.shape)} does not hold [H*dk={H * dk}, W={W}]")
+        _need(w, name, tuple(w.shape), torch.float32, dev)
+    if cu_list[-1] != T:
+        raise ValueError(f"cu_seqlens ends at {cu_list[-1]} but xq has {T} tokens")
+    states = [conv_state_q, conv_state_k, conv_state_out_q, conv_state_out_k]
+    num_slots = 0
+    for name, st in zip(("conv_state_q", "conv_state_k", "conv_state_out_q",
+                         "conv_state_out_k"), states):
+        if st is None:
+            continue
+        if st.dim() != 4 or tuple(st.shape[1:]) != (W - 1, H, dk):
+            raise ValueError(f"{name}: shape {tuple(st.shape)} != [S, {W - 1}, {H}, {dk}]")
+        _need(st, name, tuple(st.shape), xq.dtype, dev)
+        if num_slots and st.shape[0] != num_slots:
+            raise ValueError("all convolution states must have the same number of rows")
+        num_slots = int(st.shape[0])
+    if slots is not None:
+        _need(slots, "slots", (N,), torch.int32, dev)
+    if out_dtype is None:
+        out_dtype = q_out.dtype if q_out is not None else torch.bfloat16
+    cfg = frontend_config(H, dk, W, xq.dtype, out_dtype, eps)
+    if q_out is None:
+        q_out = torch.empty(T, H, dk, dtype=out_dtype, device=dev)
+    if k_out is None:
+        k_out = torch.empty(T, H, dk, dtype=out_dtype, device=dev)
+    _need(q_out, "q_out", (T, H, dk), out_dtype, dev)
+    _need(k_out, "k_out", (T, H, dk), out_dtype, dev)
+    cu_arr = (ctypes.c_int32 * len(cu_list))(*cu_list)
+    _check(lib.kda_qk_frontend(
+        ctypes.byref(cfg), N, cu_arr, cu_seqlens.data_ptr(), xq.data_ptr(), xk.data_ptr(),
+        wq.data_ptr(), wk.data_ptr(), *(_ptr(st) for st in states), _ptr(slots), num_slots,
+        q_out.data_ptr(), k_out.data_ptr(), _stream(stream)))
+    return q_out, k_out

@@ -160,6 +160,72 @@ kda_status kda_decode(const kda_config *cfg, int32_t num_seqs, const void *q,
                       const float *beta, float *state,
                       const int32_t *state_slots_dev, void *out, void *stream);
 
+/*
+ * Front end of q and k: short convolution -> Swish -> L2 normalisation.
+ *
+ * "Kimi K3 technical FAQ" (Runpod guide), question "What is KDA, and why
+ * does a serving engineer care?": queries and keys pass through a short
+ * convolution, Swish and L2 normalisation before the recurrence.  The page
+ * states neither the width nor the exact forms; this library reads them as,
+ * for channel c = h*dk + i of token t,
+ *
+ *     z_t[c] = sum_{j=0}^{W-1} w[c][j] * x_{t-(W-1)+j}[c]
+ *     a_t[c] = z_t[c] * sigmoid(z_t[c])
+ *     y_t[h] = a_t[h] / sqrt(|a_t[h]|^2 + eps)      (|.| over the dk channels)
+ *
+ * a depthwise causal convolution along each sequence's own tokens (no bias;
+ * tap W-1 weighs the current token), Swish with unit slope, and a per
+ * (token, head) L2 normalisation.  q and k have their own taps and states.
+ */
+typedef struct {
+    int32_t num_heads;   /* H                                               */
+    int32_t dk;          /* channels per head: 16, 32, 64 or 128            */
+    int32_t conv_width;  /* W, taps per channel: 1 .. 8                     */
+    kda_dtype in_dtype;  /* dtype of xq, xk and of the convolution states   */
+    kda_dtype out_dtype; /* dtype of q_out, k_out (bf16 feeds kda_prefill
+                            and kda_decode directly)                        */
+    float eps;           /* > 0 and finite                                  */
+} kda_frontend_config;
+
+/*
+ * The front end over packed variable-length sequences (T = cu[num_seqs]
+ * tokens, sequence b owning tokens [cu[b], cu[b+1])), q and k in one call:
+ *   xq, xk   : [T, H, dk] in_dtype         raw (pre-convolution) q and k
+ *   wq, wk   : [H*dk, W] fp32              taps, channel-major
+ *   q_out, k_out : [T, H, dk] out_dtype    (written)
+ * Convolution states, one row of W-1 inputs per slot, oldest first:
+ *   conv_state_in_q/k  : [num_slots, W-1, H, dk] in_dtype, read: the inputs
+ *                        that preceded each sequence; NULL = zero history
+ *   conv_state_out_q/k : same layout (written): each sequence's last W-1
+ *                        inputs (state rows fill in where a sequence is
+ *                        shorter than W-1); NULL = not written.  May equal
+ *                        the matching input pointer (in-place update); no
+ *                        other overlap is allowed.
+ *   state_slots_dev    : [num_seqs] int32 device array, sequence b's state
+ *                        row, or NULL for row b; entries distinct and
+ *                        < num_slots (not checked on the device).
+ * num_slots is the number of rows of the state arrays (>= num_seqs when
+ * state_slots_dev is NULL; unused when both states are NULL or W == 1).
+ * A decode step is the call with cu = {0, 1, ..., num_seqs} and the states
+ * updated in place.  Slots of sequences not in the call are not touched.
+ * cu_seqlens_host and cu_seqlens_dev hold the same offsets: cu[0] == 0,
+ * non-decreasing; empty sequences are allowed (their output state is their
+ * input state, or zeros without one).
+ * Alignment: x, out, taps and states 16 bytes; cu and slots 4 bytes.
+ * Errors: KDA_ERR_INVALID_ARG (null required pointer, bad offsets, eps,
+ * overlapping buffers, num_slots too small), KDA_ERR_UNSUPPORTED (dk, W or
+ * dtype), KDA_ERR_ALIGNMENT, KDA_ERR_HIP.  num_seqs == 0 is a no-op.
+ */
+kda_status kda_qk_frontend(const kda_frontend_config *cfg, int32_t num_seqs,
+                           const int32_t *cu_seqlens_host,
+                           const int32_t *cu_seqlens_dev, const void *xq,
+                           const void *xk, const float *wq, const float *wk,
+                           const void *conv_state_in_q,
+                           const void *conv_state_in_k,
+                           void *conv_state_out_q, void *conv_state_out_k,
+                           const int32_t *state_slots_dev, int32_t num_slots,
+                           void *q_out, void *k_out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

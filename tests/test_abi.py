@@ -31,7 +31,7 @@ def test_header_declares_the_calls():
     names = declared_functions()
     for required in ("kda_prefill", "kda_decode", "kda_snapshot_count",
                      "kda_prefill_workspace_size", "kda_status_string",
-                     "kda_last_error_detail", "kda_version"):
+                     "kda_last_error_detail", "kda_version", "kda_qk_frontend"):
         assert required in names
 
 
@@ -149,3 +149,49 @@ def test_prefill_requires_workspace(lib):
     assert "workspace" in lib.kda_last_error_detail().decode()
     # the bound covers any split of the tokens into sequences
     assert libkda.workspace_size(cfg, 5, 200) >= need
+
+
+def _fe(lib, cu=(0, 64), H=2, dk=128, W=4, ind=0, outd=0, eps=1e-6, x=A, w=A, sin=(None, None),
+        sout=(None, None), slots=None, num_slots=1, out=(A + (1 << 24), A + (1 << 25)), cfg=True,
+        cu_dev=A):
+    from gated_delta_rule_111_amd import kda as libkda
+    c = libkda.FrontendConfig(H, dk, W, ind, outd, eps)
+    arr = (ctypes.c_int32 * len(cu))(*cu)
+    return lib.kda_qk_frontend(ctypes.byref(c) if cfg else None, len(cu) - 1, arr, cu_dev, x, x,
+                               w, w, sin[0], sin[1], sout[0], sout[1], slots, num_slots,
+                               out[0], out[1], None)
+
+
+def test_frontend_rejects_bad_arguments(lib):
+    E_ARG, E_UNS, E_ALN = 1, 2, 3
+    assert _fe(lib, cfg=False) == E_ARG
+    assert _fe(lib, dk=48) == E_UNS
+    assert _fe(lib, W=0) == E_UNS
+    assert _fe(lib, W=9) == E_UNS
+    assert _fe(lib, ind=5) == E_UNS
+    assert _fe(lib, eps=0.0) == E_ARG
+    assert _fe(lib, eps=float("nan")) == E_ARG
+    assert _fe(lib, H=0) == E_ARG
+    assert _fe(lib, cu=(1, 64)) == E_ARG
+    assert _fe(lib, cu=(0, 64, 10)) == E_ARG
+    assert _fe(lib, x=None) == E_ARG
+    assert _fe(lib, w=None) == E_ARG
+    assert _fe(lib, cu_dev=None) == E_ARG
+    assert _fe(lib, x=MIS) == E_ALN
+    assert _fe(lib, w=A + 4) == E_ALN
+    assert _fe(lib, slots=A + 2) == E_ALN
+    # outputs over the inputs
+    assert _fe(lib, out=(A, A + (1 << 25))) == E_ARG
+    assert "overlap" in lib.kda_last_error_detail().decode()
+    # state output partly over the state input; too few slots
+    S = A + (1 << 26)
+    assert _fe(lib, sin=(S, None), sout=(S + 256, None), num_slots=4) == E_ARG
+    assert _fe(lib, cu=(0, 3, 6), sin=(S, None), num_slots=1) == E_ARG
+    # in-place state update is allowed (validated, then it would launch: not called here)
+
+
+def test_frontend_zero_sequences_is_noop(lib):
+    from gated_delta_rule_111_amd import kda as libkda
+    c = libkda.FrontendConfig(2, 128, 4, 0, 0, 1e-6)
+    assert lib.kda_qk_frontend(ctypes.byref(c), 0, None, None, None, None, None, None, None,
+                               None, None, None, None, 0, None, None, None) == 0
