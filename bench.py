@@ -34,6 +34,7 @@ if ROOT not in sys.path:
 METRIC = "KDA prefill tokens/s + decode seq-steps/s; % of MFMA / HBM roofline, 1 GPU"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector (packed FMA), TFLOP/s
 
 # Algorithmic work per unit (the bytes a kernel must move and the flops the
 # chunked method must do, independent of how the kernels are written).
@@ -55,6 +56,7 @@ KERNEL_SOURCES = {
     "decode": os.path.join(ROOT, "gated_delta_rule_111_amd", "csrc", "kda_decode.hip"),
     "prefill": os.path.join(ROOT, "gated_delta_rule_111_amd", "csrc", "kda_prefill.hip"),
     "frontend": os.path.join(ROOT, "gated_delta_rule_111_amd", "csrc", "kda_frontend.hip"),
+    "multi": os.path.join(ROOT, "gated_delta_rule_111_amd", "csrc", "kda_decode_multi.hip"),
 }
 
 
@@ -317,6 +319,76 @@ def bench_frontend(torch, kda, inputs, reps):
     return res
 
 
+def bench_spec(torch, kda, inputs, reps, decode_us):
+    """Speculative decoding step on the decode shape (256 sequences x 32
+    heads, d = 128, fp32 states): verify 1 + 7 tokens, then commit the
+    accepted prefix (1 + Binomial(7, p), mean 4.73 or 2.61).  Algorithmic
+    bytes: verify reads each state once (64 KiB per sequence-head) plus the
+    8 tokens' inputs (q, k, v bf16, g fp32, beta) and writes their fp32
+    outputs; commit reads and writes each state once plus the accepted
+    tokens' k, v, g, beta.  Work: 7 dk dv flop per token and head for the
+    token-by-token update (decay, two reductions, rank-1 update)."""
+    dev = "cuda:0"
+    N, H, d, K = 256, 32, 128, inputs.SPEC_TOKENS
+    inp = inputs.multi_token_inputs(N, K, H, d, d, seed=11, device=dev)
+    state = inp.state.clone()
+    out = torch.empty(N, K, H, d, dtype=torch.float32, device=dev)
+    tok_in = 3 * d * 2 + d * 4 + 4            # q, k, v bf16 + g fp32 + beta per token-head
+    tok_commit = 2 * d * 2 + d * 4 + 4        # k, v, g, beta
+    res = {}
+    stream = torch.cuda.current_stream()
+    for name, mean in inputs.SPEC_MEAN_ACCEPTED.items():
+        acc = inputs.accepted_counts(N, K, mean, seed=12, device=dev)
+        n_acc = int(acc.sum().item())
+
+        def verify():
+            kda.decode_multi(inp.q, inp.k, inp.v, inp.g, inp.beta, state, mode="verify", out=out)
+
+        def commit():
+            kda.decode_multi(None, inp.k, inp.v, inp.g, inp.beta, state, mode="commit",
+                             accepted=acc)
+
+        times = {}
+        for label, fn in (("verify", verify), ("commit", commit)):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times[label] = e0.elapsed_time(e1) / 1e3 / reps
+        vb = N * H * (STATE_BYTES + K * (tok_in + d * 4))
+        cb = N * H * 2 * STATE_BYTES + n_acc * H * tok_commit
+        vflop = N * H * K * 7 * d * d
+        step = times["verify"] + times["commit"]
+        log(f"[bench] spec {name}: verify {times['verify'] * 1e6:.1f} us, commit "
+            f"{times['commit'] * 1e6:.1f} us, {n_acc / N:.2f} accepted/seq, "
+            f"{n_acc / step:.3e} accepted tokens/s")
+        res[name] = {
+            "mean_accepted": round(n_acc / N, 3),
+            "accepted_tokens_per_s": round(n_acc / step, 1),
+            "speedup_vs_single_token_decode": round((n_acc / step) / (N / (decode_us * 1e-6)), 3),
+            "verify_us": round(times["verify"] * 1e6, 2),
+            "commit_us": round(times["commit"] * 1e6, 2),
+            "verify_roofline": {"bound": "alu", "achieved": round(vflop / times["verify"] / 1e12, 2),
+                                "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                "frac": round(vflop / times["verify"] / 1e12 / FP32_VECTOR_PEAK_TFLOPS, 4),
+                                "hbm_GBps": round(vb / times["verify"] / 1e9, 1),
+                                "traffic": measured_traffic("multi", "verify-N256-H32-d128-K8"),
+                                "kernel": "decode_multi_kernel<verify>", "flop_per_launch": vflop,
+                                "bytes_per_launch": vb},
+            "commit_roofline": {"bound": "hbm", "achieved": round(cb / times["commit"] / 1e9, 1),
+                                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": round(cb / times["commit"] / 1e9 / HBM_PEAK_GBS, 4),
+                                "traffic": measured_traffic("multi", f"commit-{name}"),
+                                "kernel": "decode_multi_kernel<commit>", "bytes_per_launch": cb},
+        }
+    return res
+
+
 def cpu_frontend_baseline(inputs, tokens: int):
     import oracle
     H, dk, W = 32, 128, inputs.FRONTEND_WIDTH
@@ -364,6 +436,7 @@ def main():
     ap.add_argument("--long", action="store_true", help="also time the 1,048,576-token prefill")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-frontend", action="store_true")
+    ap.add_argument("--no-spec", action="store_true")
     ap.add_argument("--cpu-frontend-tokens", type=int, default=32768)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-decode-seqs", type=int, default=128)
@@ -400,6 +473,9 @@ def main():
                                   max(2, args.warmup // 10))
     if args.long:
         pre_long, _ = bench_prefill(torch, kda, inputs, inputs.LONG, 3, 1)
+    spec = None
+    if not args.no_spec:
+        spec = bench_spec(torch, kda, inputs, args.prefill_reps, dec["kernel_us"])
     fe = None
     if not args.no_frontend:
         fe = bench_frontend(torch, kda, inputs, args.prefill_reps)
@@ -437,6 +513,8 @@ def main():
         line["prefill_long"] = pre_long
     if fe is not None:
         line["qk_frontend"] = fe
+    if spec is not None:
+        line["spec_decode"] = spec
     print(json.dumps(line), flush=True)
 
 

@@ -240,6 +240,56 @@ kda_status kda_decode(const kda_config* cfg, int32_t num_seqs, const void* q, co
     return ok();
 }
 
+kda_status kda_decode_multi(const kda_config* cfg, int32_t num_seqs, int32_t num_tokens,
+                            kda_multi_mode mode, const void* q, const void* k, const void* v,
+                            const float* g, const float* beta, float* state, const int32_t* slots,
+                            const int32_t* accepted, void* out, void* stream) {
+    kda_status st = check_config(cfg);
+    if (st != KDA_OK) return st;
+    if (num_seqs < 0) return fail(KDA_ERR_INVALID_ARG, "num_seqs must be >= 0");
+    if (num_tokens < 1) return fail(KDA_ERR_INVALID_ARG, "num_tokens must be >= 1");
+    if (mode != KDA_MULTI_APPLY && mode != KDA_MULTI_VERIFY && mode != KDA_MULTI_COMMIT)
+        return fail(KDA_ERR_INVALID_ARG, "mode %d unknown", (int)mode);
+    if (num_seqs == 0) return ok();
+    if ((int64_t)num_seqs * cfg->num_heads > 0x7fffffffLL)
+        return fail(KDA_ERR_UNSUPPORTED, "num_seqs * num_heads exceeds the grid limit");
+    const bool outputs = mode != KDA_MULTI_COMMIT;
+    const PtrCheck ptrs[] = {
+        {"q", q, outputs, 16},  {"k", k, true, 16},         {"v", v, true, 16},
+        {"g", g, true, 16},     {"beta", beta, true, 4},    {"state", state, true, 16},
+        {"state_slots_dev", slots, false, 4},
+        {"accepted_dev", accepted, mode == KDA_MULTI_COMMIT, 4},
+        {"out", out, outputs, 16},
+    };
+    st = check_ptrs(ptrs, (int)(sizeof(ptrs) / sizeof(ptrs[0])));
+    if (st != KDA_OK) return st;
+
+    kda::DecodeMultiArgs a{};
+    a.dk = cfg->dk;
+    a.dv = cfg->dv;
+    a.H = cfg->num_heads;
+    a.num_seqs = num_seqs;
+    a.num_tokens = num_tokens;
+    a.mode = (int)mode;
+    a.in_bf16 = cfg->in_dtype == KDA_BF16;
+    a.out_bf16 = cfg->out_dtype == KDA_BF16;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.state = state;
+    a.slots = slots;
+    a.counts = mode == KDA_MULTI_COMMIT ? accepted : nullptr;
+    a.out = outputs ? out : nullptr;
+    a.scale = effective_scale(cfg);
+    a.stream = static_cast<hipStream_t>(stream);
+    hipError_t e = kda::launch_decode_multi(a);
+    if (e != hipSuccess)
+        return fail(KDA_ERR_HIP, "multi-token decode launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 kda_status kda_qk_frontend(const kda_frontend_config* cfg, int32_t num_seqs,
                            const int32_t* cu_host, const int32_t* cu_dev, const void* xq,
                            const void* xk, const float* wq, const float* wk,

@@ -56,7 +56,22 @@ struct FrontendArgs {
     hipStream_t stream;
 };
 
+struct DecodeMultiArgs {
+    int dk, dv, H, num_seqs, num_tokens;
+    int mode;                     // 0 apply, 1 verify, 2 commit
+    bool in_bf16, out_bf16;
+    const void *q, *k, *v;        // [num_seqs, num_tokens, H, d]
+    const float *g, *beta;
+    float* state;
+    const int32_t* slots;         // nullable (identity)
+    const int32_t* counts;        // commit: accepted tokens per sequence
+    void* out;                    // [num_seqs, num_tokens, H, dv]; unused in commit
+    float scale;
+    hipStream_t stream;
+};
+
 hipError_t launch_decode(const DecodeArgs& a);
+hipError_t launch_decode_multi(const DecodeMultiArgs& a);
 hipError_t launch_frontend(const FrontendArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);
 size_t prefill_workspace_bytes(int dk, int dv, int H, int num_seqs, int64_t total_tokens);

@@ -229,3 +229,34 @@ def frontend_inputs(seq_lens: Sequence[int], H: int, dk: int, W: int, seed: int,
         cu.append(cu[-1] + int(L))
     cu_t = torch.tensor(cu, dtype=torch.int32, device=device)
     return FrontendInputs(xq, xk, wq, wk, cu_t, sq, sk)
+
+
+# ---------------------------------------------------------------------------
+# Speculative decoding: K = 1 + 7 tokens per sequence per step ("Kimi K3
+# technical FAQ", question "What does it take to serve K3 today?": 7 draft
+# tokens).  Accepted tokens per step = 1 + Binomial(7, p) with p chosen for
+# the mean the pages report ("Moonshot releases Kimi K3 report...", section
+# "A third party tripled single-user decoding speed"): 4.73 for coding, 2.61
+# for creative writing.  The tensors of a step are drawn as for decode and
+# laid out [N, K, H, d] (sequence-major).
+# ---------------------------------------------------------------------------
+SPEC_TOKENS = 8
+SPEC_MEAN_ACCEPTED = {"coding": 4.73, "creative": 2.61}
+
+
+def accepted_counts(N: int, K: int, mean: float, seed: int, device="cpu") -> torch.Tensor:
+    """[N] int32 in [1, K]: 1 + Binomial(K - 1, (mean - 1) / (K - 1))."""
+    g = _gen(seed, "cpu")
+    p = (float(mean) - 1.0) / (K - 1)
+    draws = torch.rand(N, K - 1, generator=g) < p
+    return (1 + draws.sum(dim=1)).to(torch.int32).to(device)
+
+
+def multi_token_inputs(N: int, K: int, H: int, dk: int, dv: int, seed: int,
+                       in_dtype=torch.bfloat16, decay_shift: float = 2.0,
+                       state_std: float = 0.02, device="cpu") -> DecodeInputs:
+    """decode_inputs with the token axis second: q, k [N, K, H, dk] etc.;
+    the state stays [N, H, dk, dv]."""
+    d = decode_inputs(K, N, H, dk, dv, seed, in_dtype, decay_shift, state_std, device)
+    t = lambda x: x.transpose(0, 1).contiguous()
+    return DecodeInputs(t(d.q), t(d.k), t(d.v), t(d.g), t(d.beta), d.state)

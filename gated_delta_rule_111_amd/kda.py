@@ -69,6 +69,8 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_prefill.argtypes = [CP, i32, P, P, P, P, P, P, P, P, P, P, i32, P, P, sz, P]
     lib.kda_decode.restype = ctypes.c_int
     lib.kda_decode.argtypes = [CP, i32, P, P, P, P, P, P, P, P, P]
+    lib.kda_decode_multi.restype = ctypes.c_int
+    lib.kda_decode_multi.argtypes = [CP, i32, i32, ctypes.c_int, P, P, P, P, P, P, P, P, P, P]
     lib.kda_qk_frontend.restype = ctypes.c_int
     lib.kda_qk_frontend.argtypes = [ctypes.POINTER(FrontendConfig), i32, P, P, P, P, P, P,
                                     P, P, P, P, P, i32, P, P, P]
@@ -292,3 +294,62 @@ def qk_frontend(xq: torch.Tensor, xk: torch.Tensor, wq: torch.Tensor, wk: torch.
         wq.data_ptr(), wk.data_ptr(), *(_ptr(st) for st in states), _ptr(slots), num_slots,
         q_out.data_ptr(), k_out.data_ptr(), _stream(stream)))
     return q_out, k_out
+
+
+MULTI_MODES = {"apply": 0, "verify": 1, "commit": 2}
+
+
+def decode_multi(q: Optional[torch.Tensor], k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                 beta: torch.Tensor, state: torch.Tensor, mode: str = "apply",
+                 accepted: Optional[torch.Tensor] = None, slots: Optional[torch.Tensor] = None,
+                 out_dtype: Optional[torch.dtype] = None, scale: float = 0.0,
+                 out: Optional[torch.Tensor] = None, stream=None) -> Optional[torch.Tensor]:
+    """kda_decode_multi: K tokens per sequence against resident states.
+
+    k: [N, K, H, dk]; q: same (may be None in "commit"); v: [N, K, H, dv];
+    g: [N, K, H, dk] fp32; beta: [N, K, H] fp32; state: [S, H, dk, dv] fp32.
+    mode "apply" (outputs, state advanced by K), "verify" (outputs, state
+    only read) or "commit" (the first accepted[n] tokens applied, accepted an
+    [N] int32 device tensor; no output).  Returns out [N, K, H, dv] (None in
+    "commit").
+    """
+    lib = load()
+    if mode not in MULTI_MODES:
+        raise ValueError(f"mode {mode!r} not in {sorted(MULTI_MODES)}")
+    dev = k.device
+    N, K, H, dk = k.shape
+    dv = v.shape[3]
+    outputs = mode != "commit"
+    if outputs and q is None:
+        raise ValueError(f"q is required in mode {mode!r}")
+    checks = [("k", k, (N, K, H, dk), k.dtype), ("v", v, (N, K, H, dv), k.dtype),
+              ("g", g, (N, K, H, dk), torch.float32), ("beta", beta, (N, K, H), torch.float32)]
+    if q is not None:
+        checks.append(("q", q, (N, K, H, dk), k.dtype))
+    for name, t, shp, dt in checks:
+        _need(t, name, shp, dt, dev)
+    if state.dim() != 4 or tuple(state.shape[1:]) != (H, dk, dv):
+        raise ValueError(f"state: shape {tuple(state.shape)} != [S, {H}, {dk}, {dv}]")
+    _need(state, "state", tuple(state.shape), torch.float32, dev)
+    if slots is None and state.shape[0] < N:
+        raise ValueError("state has fewer rows than sequences")
+    if slots is not None:
+        _need(slots, "slots", (N,), torch.int32, dev)
+    if mode == "commit":
+        if accepted is None:
+            raise ValueError("accepted is required in mode 'commit'")
+        _need(accepted, "accepted", (N,), torch.int32, dev)
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else torch.float32
+    cfg = config(H, dk, dv, k.dtype, out_dtype, scale)
+    if outputs:
+        if out is None:
+            out = torch.empty(N, K, H, dv, dtype=out_dtype, device=dev)
+        _need(out, "out", (N, K, H, dv), out_dtype, dev)
+    else:
+        out = None
+    _check(lib.kda_decode_multi(ctypes.byref(cfg), N, K, MULTI_MODES[mode], _ptr(q), k.data_ptr(),
+                                v.data_ptr(), g.data_ptr(), beta.data_ptr(), state.data_ptr(),
+                                _ptr(slots), _ptr(accepted) if mode == "commit" else None,
+                                _ptr(out), _stream(stream)))
+    return out

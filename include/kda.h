@@ -161,6 +161,58 @@ kda_status kda_decode(const kda_config *cfg, int32_t num_seqs, const void *q,
                       const int32_t *state_slots_dev, void *out, void *stream);
 
 /*
+ * Several tokens per sequence against resident states, in one launch.
+ *
+ * "Kimi K3 technical FAQ" (Runpod guide), questions "What does it take to
+ * serve K3 today?" and "What is the speculative-decoding story?": K3 is
+ * served with a draft model proposing 7 tokens that the target verifies in
+ * one pass, so a decode step carries 1 + 7 tokens per sequence.  "Moonshot
+ * releases Kimi K3 report..." (runtimewire), section "A third party tripled
+ * single-user decoding speed": on average 4.73 (coding) or 2.61 (creative
+ * writing) draft tokens are accepted per step.  The modes:
+ *   KDA_MULTI_APPLY  all num_tokens tokens applied in order: out holds every
+ *                    position's output and the state advances by num_tokens
+ *                    (the same as that many chained kda_decode calls);
+ *   KDA_MULTI_VERIFY out holds every position's output as if the tokens were
+ *                    applied in order; the state is only read;
+ *   KDA_MULTI_COMMIT the first accepted_dev[n] tokens of sequence n (clamped
+ *                    to [0, num_tokens]) are applied to its state; no output
+ *                    (q and out may be NULL).
+ * VERIFY then COMMIT is a roll-back path: a state never moves past the
+ * accepted tokens, and no per-position state is kept.  Each launch reads
+ * each state once (and writes it once in APPLY and COMMIT), whatever
+ * num_tokens is.
+ */
+typedef enum {
+    KDA_MULTI_APPLY = 0,
+    KDA_MULTI_VERIFY = 1,
+    KDA_MULTI_COMMIT = 2
+} kda_multi_mode;
+
+/*
+ *   q, k : [num_seqs, num_tokens, H, dk] in_dtype (token j of sequence n at
+ *          row n*num_tokens + j)
+ *   v    : [num_seqs, num_tokens, H, dv] in_dtype
+ *   g    : [num_seqs, num_tokens, H, dk] fp32 (<= 0)
+ *   beta : [num_seqs, num_tokens, H] fp32
+ *   state : [num_slots, H, dk, dv] fp32, read (and written in place by APPLY
+ *           and COMMIT)
+ *   state_slots_dev : [num_seqs] int32 or NULL (identity), as in kda_decode
+ *   accepted_dev : [num_seqs] int32 device array (COMMIT only; else ignored)
+ *   out  : [num_seqs, num_tokens, H, dv] out_dtype (APPLY, VERIFY)
+ * Errors: KDA_ERR_INVALID_ARG (null required pointer, num_tokens < 1, bad
+ * mode), KDA_ERR_UNSUPPORTED, KDA_ERR_ALIGNMENT, KDA_ERR_HIP.
+ * num_seqs == 0 is a no-op.
+ */
+kda_status kda_decode_multi(const kda_config *cfg, int32_t num_seqs,
+                            int32_t num_tokens, kda_multi_mode mode,
+                            const void *q, const void *k, const void *v,
+                            const float *g, const float *beta, float *state,
+                            const int32_t *state_slots_dev,
+                            const int32_t *accepted_dev, void *out,
+                            void *stream);
+
+/*
  * Front end of q and k: short convolution -> Swish -> L2 normalisation.
  *
  * "Kimi K3 technical FAQ" (Runpod guide), question "What is KDA, and why

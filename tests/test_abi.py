@@ -31,7 +31,8 @@ def test_header_declares_the_calls():
     names = declared_functions()
     for required in ("kda_prefill", "kda_decode", "kda_snapshot_count",
                      "kda_prefill_workspace_size", "kda_status_string",
-                     "kda_last_error_detail", "kda_version", "kda_qk_frontend"):
+                     "kda_last_error_detail", "kda_version", "kda_qk_frontend",
+                     "kda_decode_multi"):
         assert required in names
 
 
@@ -195,3 +196,21 @@ def test_frontend_zero_sequences_is_noop(lib):
     c = libkda.FrontendConfig(2, 128, 4, 0, 0, 1e-6)
     assert lib.kda_qk_frontend(ctypes.byref(c), 0, None, None, None, None, None, None, None,
                                None, None, None, None, 0, None, None, None) == 0
+
+
+def test_decode_multi_rejects_bad_arguments(lib):
+    cfg = _cfg()
+    p = ctypes.byref(cfg)
+    f = lib.kda_decode_multi
+    assert f(None, 4, 8, 0, A, A, A, A, A, A, None, None, A, None) == 1
+    assert f(p, -1, 8, 0, A, A, A, A, A, A, None, None, A, None) == 1
+    assert f(p, 4, 0, 0, A, A, A, A, A, A, None, None, A, None) == 1      # num_tokens
+    assert f(p, 4, 8, 3, A, A, A, A, A, A, None, None, A, None) == 1      # mode
+    assert f(p, 4, 8, 0, None, A, A, A, A, A, None, None, A, None) == 1   # apply needs q
+    assert f(p, 4, 8, 1, A, A, A, A, A, A, None, None, None, None) == 1   # verify needs out
+    assert f(p, 4, 8, 2, None, A, A, A, A, A, None, None, None, None) == 1  # commit needs counts
+    assert f(p, 4, 8, 2, None, A, A, A, A, A, None, A + 2, None, None) == 3
+    assert f(p, 4, 8, 0, A, MIS, A, A, A, A, None, None, A, None) == 3
+    c2 = _cfg(d=48)
+    assert f(ctypes.byref(c2), 4, 8, 0, A, A, A, A, A, A, None, None, A, None) == 2
+    assert f(p, 0, 8, 0, None, None, None, None, None, None, None, None, None, None) == 0
