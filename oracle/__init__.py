@@ -50,13 +50,13 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     P = ctypes.c_void_p
     i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
     lib.kda_oracle_prefill.restype = ctypes.c_int
-    lib.kda_oracle_prefill.argtypes = [i32, P, i32, i32, i32, P, P, P, P, P,
+    lib.kda_oracle_prefill.argtypes = [i32, P, P, i32, i32, i32, P, P, P, P, P,
                                        P, f64, i64, P, P, P, i32]
     lib.kda_oracle_decode.restype = ctypes.c_int
     lib.kda_oracle_decode.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P,
                                       P, P, f64, P, i32]
     lib.kda_oracle_snapshot_count.restype = i64
-    lib.kda_oracle_snapshot_count.argtypes = [i32, P, i64]
+    lib.kda_oracle_snapshot_count.argtypes = [i32, P, P, i64]
     lib.kda_oracle_qk_frontend.restype = ctypes.c_int
     lib.kda_oracle_qk_frontend.argtypes = [i32, P, i32, i32, i32, P, P, P, P, f64, P, P]
     return lib
@@ -87,15 +87,28 @@ class Oracle:
     def _f32(x) -> np.ndarray:
         return np.ascontiguousarray(np.asarray(x, dtype=np.float32))
 
-    def snapshot_count(self, cu_seqlens, interval: int) -> int:
+    @staticmethod
+    def _starts(start_pos, n):
+        if start_pos is None:
+            return None
+        st = np.ascontiguousarray(np.asarray(start_pos, dtype=np.int64))
+        assert st.shape == (n,)
+        return st
+
+    def snapshot_count(self, cu_seqlens, interval: int, start_pos=None) -> int:
         cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+        st = self._starts(start_pos, len(cu) - 1)
         return int(self.lib.kda_oracle_snapshot_count(
-            len(cu) - 1, cu.ctypes.data, int(interval)))
+            len(cu) - 1, cu.ctypes.data, None if st is None else st.ctypes.data, int(interval)))
 
     def prefill(self, q, k, v, g, beta, cu_seqlens, initial_state=None,
                 scale: float = 0.0, snapshot_interval: int = 0,
-                nthreads: Optional[int] = None):
+                nthreads: Optional[int] = None, start_pos=None):
         """Run every (sequence, head) token by token in fp64.
+
+        start_pos: [N] absolute position of each sequence's first token
+        (default 0): snapshots are taken at the absolute multiples of the
+        interval.
 
         q, k, g: [T, H, dk]; v: [T, H, dv]; beta: [T, H] (any float dtype,
         converted exactly to fp32).  initial_state: [N, H, dk, dv] or None,
@@ -116,10 +129,12 @@ class Oracle:
             assert init.shape == (N, H, dk, dv)
         out = np.zeros((T, H, dv), dtype=np.float64)
         final = np.zeros((N, H, dk, dv), dtype=np.float64)
-        count = self.snapshot_count(cu, snapshot_interval)
+        st = self._starts(start_pos, N)
+        count = self.snapshot_count(cu, snapshot_interval, start_pos=st)
         snaps = np.zeros((count, H, dk, dv), dtype=np.float64)
         rc = self.lib.kda_oracle_prefill(
-            N, cu.ctypes.data, H, dk, dv, q.ctypes.data, k.ctypes.data,
+            N, cu.ctypes.data, None if st is None else st.ctypes.data, H, dk, dv,
+            q.ctypes.data, k.ctypes.data,
             v.ctypes.data, g.ctypes.data, beta.ctypes.data,
             None if init is None else init.ctypes.data, float(scale),
             int(snapshot_interval), out.ctypes.data, final.ctypes.data,

@@ -28,8 +28,12 @@
  *
  * "Day-0 vLLM support for Kimi K3" (vLLM blog), section "Kimi K3's
  * architecture, and how vLLM serves it": a prefix cache over recurrent state
- * reuses state snapshots taken at block boundaries.  Snapshot j (1-based) of
- * a sequence is the state after its first j*interval tokens.
+ * reuses state snapshots taken at block boundaries, with the prefix-match
+ * granularity separate from the physical state-block size.  A sequence's
+ * first token in a call sits at absolute position s (0 unless given), and a
+ * snapshot is the state after every absolute position P in (s, s + L] that is
+ * a multiple of the interval, in order of P: with s = 0, snapshot j (1-based)
+ * is the state after the sequence's first j*interval tokens.
  *
  * Precision: every quantity is fp64.  Inputs arrive as fp32 arrays holding
  * exactly the values the device path consumes (bf16 and fp32 values are both
@@ -93,6 +97,7 @@ static void kda_token(int dk, int dv, double *S, double *u, const float *qt,
 typedef struct {
     int32_t num_seqs, H, dk, dv;
     const int64_t *cu;
+    const int64_t *start; /* absolute position of each first token, or NULL */
     const float *q, *k, *v, *g, *beta;
     const double *init;
     double scale;
@@ -110,6 +115,7 @@ static void prefill_unit(prefill_job *J, int64_t unit, double *S, double *u)
     const int b = (int)(unit / H), h = (int)(unit % H);
     const size_t ssz = (size_t)dk * dv;
     const int64_t t0 = J->cu[b], t1 = J->cu[b + 1];
+    const int64_t s0 = J->start ? J->start[b] : 0;
     int64_t t;
 
     if (J->init)
@@ -122,8 +128,9 @@ static void prefill_unit(prefill_job *J, int64_t unit, double *S, double *u)
         kda_token(dk, dv, S, u, J->q + row * dk, J->k + row * dk,
                   J->v + row * dv, J->g + row * dk, (double)J->beta[row],
                   J->scale, J->out + row * dv);
-        if (J->interval > 0 && J->snapshots && ((t - t0 + 1) % J->interval) == 0) {
-            int64_t jsnap = (t - t0 + 1) / J->interval - 1;
+        /* absolute position reached after token t: s0 + (t - t0 + 1) */
+        if (J->interval > 0 && J->snapshots && ((s0 + t - t0 + 1) % J->interval) == 0) {
+            int64_t jsnap = (s0 + t - t0 + 1) / J->interval - s0 / J->interval - 1;
             double *dst = J->snapshots +
                           ((size_t)(J->snap_base[b] + jsnap) * H + h) * ssz;
             memcpy(dst, S, ssz * sizeof(double));
@@ -187,17 +194,20 @@ static int run_pool(void *(*fn)(void *), void *job, int nthreads)
 }
 
 /*
- * Number of snapshot rows the prefill writes: sum_b floor(L_b / interval).
+ * Number of snapshot rows the prefill writes: the multiples of the interval
+ * in (s_b, s_b + L_b] summed over the sequences (s_b = 0 when start is NULL).
  */
 int64_t kda_oracle_snapshot_count(int32_t num_seqs, const int64_t *cu,
-                                  int64_t interval)
+                                  const int64_t *start, int64_t interval)
 {
     int64_t n = 0;
     int32_t b;
     if (interval <= 0)
         return 0;
-    for (b = 0; b < num_seqs; ++b)
-        n += (cu[b + 1] - cu[b]) / interval;
+    for (b = 0; b < num_seqs; ++b) {
+        const int64_t s0 = start ? start[b] : 0;
+        n += (s0 + cu[b + 1] - cu[b]) / interval - s0 / interval;
+    }
     return n;
 }
 
@@ -206,8 +216,9 @@ int64_t kda_oracle_snapshot_count(int32_t num_seqs, const int64_t *cu,
  * initial_state may be NULL (zero state).  snapshots may be NULL only when
  * no snapshot falls due.  scale <= 0 selects dk^(-1/2).
  */
-int kda_oracle_prefill(int32_t num_seqs, const int64_t *cu_seqlens, int32_t H,
-                       int32_t dk, int32_t dv, const float *q, const float *k,
+int kda_oracle_prefill(int32_t num_seqs, const int64_t *cu_seqlens,
+                       const int64_t *start_pos, int32_t H, int32_t dk,
+                       int32_t dv, const float *q, const float *k,
                        const float *v, const float *g, const float *beta,
                        const double *initial_state, double scale,
                        int64_t interval, double *out, double *final_state,
@@ -222,9 +233,10 @@ int kda_oracle_prefill(int32_t num_seqs, const int64_t *cu_seqlens, int32_t H,
         !final_state || interval < 0)
         return -1;
     for (b = 0; b < num_seqs; ++b)
-        if (cu_seqlens[b + 1] < cu_seqlens[b])
+        if (cu_seqlens[b + 1] < cu_seqlens[b] || (start_pos && start_pos[b] < 0))
             return -1;
-    if (!snapshots && kda_oracle_snapshot_count(num_seqs, cu_seqlens, interval) > 0)
+    if (!snapshots &&
+        kda_oracle_snapshot_count(num_seqs, cu_seqlens, start_pos, interval) > 0)
         return -1;
 
     snap_base = (int64_t *)malloc(sizeof(int64_t) * ((size_t)num_seqs + 1));
@@ -233,7 +245,8 @@ int kda_oracle_prefill(int32_t num_seqs, const int64_t *cu_seqlens, int32_t H,
     snap_base[0] = 0;
     for (b = 0; b < num_seqs; ++b)
         snap_base[b + 1] = snap_base[b] +
-            (interval > 0 ? (cu_seqlens[b + 1] - cu_seqlens[b]) / interval : 0);
+            kda_oracle_snapshot_count(1, cu_seqlens + b, start_pos ? start_pos + b : NULL,
+                                      interval);
 
     memset(&J, 0, sizeof(J));
     J.num_seqs = num_seqs;
@@ -241,6 +254,7 @@ int kda_oracle_prefill(int32_t num_seqs, const int64_t *cu_seqlens, int32_t H,
     J.dk = dk;
     J.dv = dv;
     J.cu = cu_seqlens;
+    J.start = start_pos;
     J.q = q;
     J.k = k;
     J.v = v;

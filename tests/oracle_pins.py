@@ -374,7 +374,47 @@ def pin_decode_matches_prefill(O, dk=8, dv=6, T=20, N=3, H=2, seed=22):
         assert np.array_equal(st[slots[n]], f_p[0]), f"decode state seq {n}"
 
 
+# --------------------------------------------------------------------------
+# P11 absolute snapshot positions ("Day-0 vLLM support for Kimi K3", section
+#     "Kimi K3's architecture, and how vLLM serves it": snapshots at block
+#     boundaries, the prefix-match granularity independent of where a call
+#     starts).  A sequence whose first token sits at absolute position s gets
+#     a snapshot at every multiple P of the interval in (s, s + L]; it must be
+#     the final state of a separate run over the sequence's first P - s
+#     tokens, the count is sum floor((s + L) / I) - floor(s / I), rows come in
+#     sequence order, and start positions of 0 change nothing.
+def pin_absolute_snapshots(O, dk=5, dv=4, H=2, seed=23, interval=5):
+    rng = _rng(seed)
+    lens = [4, 0, 13, 9, 7]
+    starts = [3, 10, 12, 0, 6]      # 3 + 4 reaches 5; 10 + 0 takes nothing; ...
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T = int(cu[-1])
+    q, k, v, g, beta = _rand_problem(rng, T, H, dk, dv)
+    S0 = rng.standard_normal((len(lens), H, dk, dv))
+    _, final, snaps = O.prefill(q, k, v, g, beta, cu, initial_state=S0,
+                                snapshot_interval=interval, start_pos=starts)
+    want_count = sum((s + L) // interval - s // interval for s, L in zip(starts, lens))
+    assert snaps.shape[0] == want_count, f"{snaps.shape[0]} snapshots, expected {want_count}"
+    row = 0
+    for b, (s, L) in enumerate(zip(starts, lens)):
+        a, e = int(cu[b]), int(cu[b + 1])
+        for P in range((s // interval + 1) * interval, s + L + 1, interval):
+            m = P - s
+            _, sm, _ = O.prefill(q[a:a + m], k[a:a + m], v[a:a + m], g[a:a + m],
+                                 beta[a:a + m], [0, m], initial_state=S0[b:b + 1])
+            _close(snaps[row], sm[0], what=f"snapshot at absolute {P} of sequence {b}")
+            row += 1
+    assert row == want_count
+    # start positions of zero: the relative rule
+    _, f0, s_zero = O.prefill(q, k, v, g, beta, cu, initial_state=S0,
+                              snapshot_interval=interval, start_pos=[0] * len(lens))
+    _, f1, s_none = O.prefill(q, k, v, g, beta, cu, initial_state=S0,
+                              snapshot_interval=interval)
+    assert np.array_equal(s_zero, s_none) and np.array_equal(f0, f1)
+    assert s_none.shape[0] == sum(L // interval for L in lens)
+
+
 ALL_PINS = [pin_exact_write, pin_beta_zero, pin_split_resume, pin_product_form,
             pin_exact_rational, pin_orthonormal_recall, pin_scalar_iir,
             pin_linearity, pin_contraction, pin_permutation, pin_frozen_state,
-            pin_varlen_packing, pin_decode_matches_prefill]
+            pin_varlen_packing, pin_decode_matches_prefill, pin_absolute_snapshots]

@@ -34,6 +34,12 @@ MUTANTS = [
     ("decode_wrong_slot",
      "S = J->state + ((size_t)(J->slots ? J->slots[n] : n) * H + h) * ssz;",
      "S = J->state + ((size_t)n * H + h) * ssz;"),
+    # absolute snapshot positions
+    ("abs_ignores_start", "const int64_t s0 = J->start ? J->start[b] : 0;",
+     "const int64_t s0 = 0;"),
+    ("abs_base_relative",
+     "kda_oracle_snapshot_count(1, cu_seqlens + b, start_pos ? start_pos + b : NULL,",
+     "kda_oracle_snapshot_count(1, cu_seqlens + b, NULL,"),
     # q/k front end (short convolution -> Swish -> L2 norm)
     ("fe_taps_reversed", "z += (double)w[ch * W + j] *",
      "z += (double)w[ch * W + (W - 1 - j)] *"),
