@@ -118,59 +118,115 @@ size_t kda_prefill_workspace_size(const kda_config* cfg, int32_t num_seqs, int64
     return kda::prefill_workspace_bytes(cfg->dk, cfg->dv, cfg->num_heads, num_seqs, total_tokens);
 }
 
-kda_status kda_prefill(const kda_config* cfg, int32_t num_seqs, const int32_t* cu_host,
-                       const int32_t* cu_dev, const void* q, const void* k, const void* v,
-                       const float* g, const float* beta, const float* initial_state, void* out,
-                       float* final_state, int32_t snapshot_interval, float* snapshots,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+int64_t kda_snapshot_count_at(const int32_t* cu, const int32_t* start, int32_t num_seqs,
+                              int32_t interval) {
+    if (!cu || !start || num_seqs < 0) return -1;
+    if (interval <= 0) return 0;
+    int64_t n = 0;
+    for (int32_t b = 0; b < num_seqs; ++b) {
+        if (cu[b + 1] < cu[b] || start[b] < 0) return -1;
+        const int64_t s0 = start[b], L = cu[b + 1] - cu[b];
+        n += (s0 + L) / interval - s0 / interval;
+    }
+    return n;
+}
+
+size_t kda_prefill_pool_workspace_size(const kda_config* cfg, int32_t num_seqs,
+                                       int64_t total_tokens) {
+    if (check_config(cfg) != KDA_OK || num_seqs < 0 || total_tokens < 0) return 0;
+    return kda::prefill_workspace_bytes(cfg->dk, cfg->dv, cfg->num_heads, num_seqs, total_tokens,
+                                        true);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Both prefill entry points: without start positions (chunks from each
+// sequence's first token, snapshots every `interval` tokens of the call, the
+// initial and final states in rows b of two arrays), and over a state pool
+// (absolute start positions, slots).
+struct PrefillCall {
+    const int32_t *cu_host, *cu_dev;
+    const int32_t *start_host, *start_dev;  // null without start positions
+    const void *q, *k, *v;
+    const float *g, *beta;
+    const float* init;
+    bool init_if_started;
+    const int32_t* slots;
+    int32_t num_slots;                      // rows of init / final (pool), else num_seqs
+    void* out;
+    float* final_state;
+    int32_t interval;
+    float* snapshots;
+    void* workspace;
+    size_t workspace_bytes;
+    void* stream;
+};
+
+kda_status prefill_impl(const kda_config* cfg, int32_t num_seqs, const PrefillCall& c) {
     kda_status st = check_config(cfg);
     if (st != KDA_OK) return st;
     if (num_seqs < 0) return fail(KDA_ERR_INVALID_ARG, "num_seqs must be >= 0");
     if (num_seqs == 0) return ok();
+    const int32_t* cu_host = c.cu_host;
     if (!cu_host) return fail(KDA_ERR_INVALID_ARG, "cu_seqlens_host is NULL");
     if (cu_host[0] != 0) return fail(KDA_ERR_INVALID_ARG, "cu_seqlens[0] must be 0");
     if (cfg->num_heads > 65535)
         return fail(KDA_ERR_UNSUPPORTED, "num_heads %d exceeds 65535", cfg->num_heads);
+    const bool pool = c.start_host != nullptr;
     const int64_t crow = kda::prefill_chunk_rows();
     int64_t total_chunks = 0;
     for (int32_t b = 0; b < num_seqs; ++b) {
         if (cu_host[b + 1] < cu_host[b])
             return fail(KDA_ERR_INVALID_ARG, "cu_seqlens decreases at index %d", b + 1);
-        total_chunks += (cu_host[b + 1] - cu_host[b] + crow - 1) / crow;
+        const int64_t L = cu_host[b + 1] - cu_host[b];
+        const int64_t s0 = pool ? c.start_host[b] : 0;
+        if (s0 < 0 || s0 + L > 0x7fffffffLL)
+            return fail(KDA_ERR_INVALID_ARG, "start_pos[%d] = %lld out of range", b, (long long)s0);
+        total_chunks += L > 0 ? (s0 % crow + L + crow - 1) / crow : 0;
     }
     const int64_t T = cu_host[num_seqs];
-    if (snapshot_interval < 0 || snapshot_interval % 64 != 0)
+    if (c.interval < 0 || c.interval % 64 != 0)
         return fail(KDA_ERR_INVALID_ARG, "snapshot_interval %d is not a non-negative multiple of 64",
-                    snapshot_interval);
-    const int64_t nsnap = kda_snapshot_count(cu_host, num_seqs, snapshot_interval);
+                    c.interval);
+    const int64_t nsnap = pool ? kda_snapshot_count_at(cu_host, c.start_host, num_seqs, c.interval)
+                               : kda_snapshot_count(cu_host, num_seqs, c.interval);
     const bool tok = T > 0;
     const PtrCheck ptrs[] = {
-        {"cu_seqlens_dev", cu_dev, true, 4},
-        {"q", q, tok, 16},
-        {"k", k, tok, 16},
-        {"v", v, tok, 16},
-        {"g", g, tok, 16},
-        {"beta", beta, tok, 4},
-        {"initial_state", initial_state, false, 16},
-        {"out", out, tok, 16},
-        {"final_state", final_state, true, 16},
-        {"snapshots", snapshots, nsnap > 0, 16},
-        {"workspace", workspace, false, 16},
+        {"cu_seqlens_dev", c.cu_dev, true, 4},
+        {"start_pos_dev", c.start_dev, pool, 4},
+        {"q", c.q, tok, 16},
+        {"k", c.k, tok, 16},
+        {"v", c.v, tok, 16},
+        {"g", c.g, tok, 16},
+        {"beta", c.beta, tok, 4},
+        {pool ? "state_pool" : "initial_state", c.init, pool, 16},
+        {"state_slots_dev", c.slots, false, 4},
+        {"out", c.out, tok, 16},
+        {pool ? "state_pool" : "final_state", c.final_state, true, 16},
+        {"snapshots", c.snapshots, nsnap > 0, 16},
+        {"workspace", c.workspace, false, 16},
     };
     st = check_ptrs(ptrs, (int)(sizeof(ptrs) / sizeof(ptrs[0])));
     if (st != KDA_OK) return st;
-    if (initial_state && initial_state != final_state) {
+    if (pool) {
+        if (c.num_slots < 1 || (!c.slots && c.num_slots < num_seqs))
+            return fail(KDA_ERR_INVALID_ARG, "num_slots %d too small for %d sequences", c.num_slots,
+                        num_seqs);
+    } else if (c.init && c.init != c.final_state) {
         // final_state may alias initial_state exactly; partial overlap is not allowed
         const size_t bytes = (size_t)num_seqs * cfg->num_heads * cfg->dk * cfg->dv * sizeof(float);
-        const char* a = reinterpret_cast<const char*>(initial_state);
-        const char* b = reinterpret_cast<const char*>(final_state);
+        const char* a = reinterpret_cast<const char*>(c.init);
+        const char* b = reinterpret_cast<const char*>(c.final_state);
         if (a < b + bytes && b < a + bytes)
             return fail(KDA_ERR_INVALID_ARG, "final_state partially overlaps initial_state");
     }
-    const size_t need = kda::prefill_workspace_bytes(cfg->dk, cfg->dv, cfg->num_heads, num_seqs, T);
-    if (workspace_bytes < need || (need > 0 && !workspace))
+    const size_t need =
+        kda::prefill_workspace_bytes(cfg->dk, cfg->dv, cfg->num_heads, num_seqs, T, pool);
+    if (c.workspace_bytes < need || (need > 0 && !c.workspace))
         return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required",
-                    workspace_bytes, need);
+                    c.workspace_bytes, need);
 
     kda::PrefillArgs a{};
     a.dk = cfg->dk;
@@ -181,24 +237,89 @@ kda_status kda_prefill(const kda_config* cfg, int32_t num_seqs, const int32_t* c
     a.out_bf16 = cfg->out_dtype == KDA_BF16;
     a.total_tokens = T;
     a.total_chunks = total_chunks;
-    a.cu_dev = cu_dev;
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.g = g;
-    a.beta = beta;
-    a.init = initial_state;
-    a.out = out;
-    a.final_state = final_state;
-    a.interval = snapshot_interval;
-    a.snapshots = snapshots;
-    a.workspace = workspace;
-    a.workspace_bytes = workspace_bytes;
+    a.cu_dev = c.cu_dev;
+    a.start_dev = c.start_dev;
+    a.slots = c.slots;
+    a.q = c.q;
+    a.k = c.k;
+    a.v = c.v;
+    a.g = c.g;
+    a.beta = c.beta;
+    a.init = c.init;
+    a.init_if_started = c.init_if_started;
+    a.out = c.out;
+    a.final_state = c.final_state;
+    a.interval = c.interval;
+    a.snapshots = c.snapshots;
+    a.workspace = c.workspace;
+    a.workspace_bytes = c.workspace_bytes;
     a.scale = effective_scale(cfg);
-    a.stream = static_cast<hipStream_t>(stream);
+    a.stream = static_cast<hipStream_t>(c.stream);
     hipError_t e = kda::launch_prefill(a);
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_prefill(const kda_config* cfg, int32_t num_seqs, const int32_t* cu_host,
+                       const int32_t* cu_dev, const void* q, const void* k, const void* v,
+                       const float* g, const float* beta, const float* initial_state, void* out,
+                       float* final_state, int32_t snapshot_interval, float* snapshots,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    PrefillCall c{};
+    c.cu_host = cu_host;
+    c.cu_dev = cu_dev;
+    c.q = q;
+    c.k = k;
+    c.v = v;
+    c.g = g;
+    c.beta = beta;
+    c.init = initial_state;
+    c.num_slots = num_seqs;
+    c.out = out;
+    c.final_state = final_state;
+    c.interval = snapshot_interval;
+    c.snapshots = snapshots;
+    c.workspace = workspace;
+    c.workspace_bytes = workspace_bytes;
+    c.stream = stream;
+    return prefill_impl(cfg, num_seqs, c);
+}
+
+kda_status kda_prefill_pool(const kda_config* cfg, int32_t num_seqs, const int32_t* cu_host,
+                            const int32_t* cu_dev, const int32_t* start_host,
+                            const int32_t* start_dev, const void* q, const void* k, const void* v,
+                            const float* g, const float* beta, float* state_pool,
+                            const int32_t* slots, int32_t num_slots, void* out,
+                            int32_t snapshot_interval, float* snapshots, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+    if (num_seqs > 0 && !start_host)
+        return fail(KDA_ERR_INVALID_ARG, "start_pos_host is NULL");
+    PrefillCall c{};
+    c.cu_host = cu_host;
+    c.cu_dev = cu_dev;
+    c.start_host = start_host;
+    c.start_dev = start_dev;
+    c.q = q;
+    c.k = k;
+    c.v = v;
+    c.g = g;
+    c.beta = beta;
+    c.init = state_pool;
+    c.init_if_started = true;
+    c.slots = slots;
+    c.num_slots = num_slots;
+    c.out = out;
+    c.final_state = state_pool;
+    c.interval = snapshot_interval;
+    c.snapshots = snapshots;
+    c.workspace = workspace;
+    c.workspace_bytes = workspace_bytes;
+    c.stream = stream;
+    return prefill_impl(cfg, num_seqs, c);
 }
 
 kda_status kda_decode(const kda_config* cfg, int32_t num_seqs, const void* q, const void* k,

@@ -27,9 +27,12 @@ struct PrefillArgs {
     int64_t total_tokens;
     int64_t total_chunks;         // sum over sequences of ceil(L_b / chunk rows)
     const int32_t* cu_dev;        // [num_seqs + 1] device offsets
+    const int32_t* start_dev;     // nullable: absolute position of each first token
+    const int32_t* slots;         // nullable: state row of each sequence (init and final)
     const void *q, *k, *v;
     const float *g, *beta;
     const float* init;            // nullable
+    bool init_if_started;         // read init only for sequences with start > 0
     void* out;
     float* final_state;
     int32_t interval;             // 0 = no snapshots
@@ -74,7 +77,8 @@ hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_decode_multi(const DecodeMultiArgs& a);
 hipError_t launch_frontend(const FrontendArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);
-size_t prefill_workspace_bytes(int dk, int dv, int H, int num_seqs, int64_t total_tokens);
+size_t prefill_workspace_bytes(int dk, int dv, int H, int num_seqs, int64_t total_tokens,
+                               bool any_start = false);
 int prefill_chunk_rows();  // tokens per chunk; snapshot intervals are multiples of 64
 
 }  // namespace kda

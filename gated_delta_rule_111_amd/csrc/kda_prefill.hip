@@ -214,10 +214,15 @@ template <> struct In<float> {
 };
 
 // ---------------------------------------------------------------------------
-// plan: chunk_start[b] = sum_{b' < b} ceil(L_b' / C), snap_base[b] =
-// sum_{b' < b} floor(L_b' / interval), for b = 0 .. num_seqs.
+// plan: chunk_start[b] = sum_{b' < b} nch(b'), snap_base[b] = sum_{b' < b}
+// nsnap(b'), for b = 0 .. num_seqs.  A sequence whose first token sits at
+// absolute position s (0 without start positions) is cut into chunks at the
+// absolute multiples of C, so it has nch = ceil((s mod C + L) / C) chunks
+// (none when L = 0), and snapshots at the absolute multiples of the interval
+// in (s, s + L]: nsnap = floor((s + L) / interval) - floor(s / interval).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(NT) void plan_kernel(const int32_t* __restrict__ cu, int num_seqs,
+__global__ __launch_bounds__(NT) void plan_kernel(const int32_t* __restrict__ cu,
+                                                  const int32_t* __restrict__ start, int num_seqs,
                                                   int interval, int32_t* __restrict__ chunk_start,
                                                   int32_t* __restrict__ snap_base) {
     __shared__ int32_t wtot[2][4];
@@ -230,8 +235,9 @@ __global__ __launch_bounds__(NT) void plan_kernel(const int32_t* __restrict__ cu
         int vc = 0, vs = 0;
         if (b < num_seqs) {
             const int L = cu[b + 1] - cu[b];
-            vc = (L + C - 1) / C;
-            vs = interval > 0 ? L / interval : 0;
+            const int s0 = start ? start[b] : 0;
+            vc = L > 0 ? (s0 % C + L + C - 1) / C : 0;
+            vs = interval > 0 ? (s0 + L) / interval - s0 / interval : 0;
         }
         int ic = vc, is = vs;
 #pragma unroll
@@ -327,6 +333,7 @@ struct PrepParams {
     const float* g;
     const float* beta;
     const int32_t* cu;
+    const int32_t* start;  // absolute position of each sequence's first token, or null
     const int32_t* chunk_start;
     uint4* ops;  // [chunks][H][CHUNK_OPS]
     int H, dk, dv, num_seqs;
@@ -334,8 +341,8 @@ struct PrepParams {
 
 // Location of one (chunk, head) item.
 struct PrepItem {
-    int h, n;          // head; valid rows of the chunk (1 .. C)
-    int64_t gc, row0;  // global chunk index; first packed row
+    int h, lo, n;      // head; valid rows of the chunk are lo .. n-1
+    int64_t gc, row0;  // global chunk index; packed row of chunk row 0
 };
 
 __device__ __forceinline__ PrepItem prep_item(const PrepParams& p, int it) {
@@ -349,9 +356,14 @@ __device__ __forceinline__ PrepItem prep_item(const PrepParams& p, int it) {
         const int mid = (lo + hi) >> 1;
         if (p.chunk_start[mid] <= gc) lo = mid; else hi = mid;
     }
+    // chunks sit at absolute multiples of C: the first chunk of a sequence
+    // starting at absolute position s has s mod C leading rows that are not
+    // the sequence's (staged as zero tokens, which leave the state alone)
     const int ci = gc - p.chunk_start[lo];
-    r.row0 = (int64_t)p.cu[lo] + (int64_t)ci * C;
-    r.n = min(C, p.cu[lo + 1] - p.cu[lo] - ci * C);
+    const int pad = p.start ? p.start[lo] % C : 0;
+    r.row0 = (int64_t)p.cu[lo] - pad + (int64_t)ci * C;
+    r.n = min(C, pad + p.cu[lo + 1] - p.cu[lo] - ci * C);
+    r.lo = ci == 0 ? pad : 0;
     return r;
 }
 
@@ -365,8 +377,8 @@ __device__ __forceinline__ int gram_row(int w, int slot) {
 
 // This thread's share of one item's raw inputs: g rows 8r + tid/32, channels
 // 4*(tid%32)..+3; k, q rows 16r + tid/16, channels 8*(tid%16)..+7; beta of
-// row tid (tid < 64).  Rows past the chunk end are read from its last row
-// and channels past dk from channel 0; the values are masked when staged.
+// row tid (tid < 64).  Rows outside lo .. n-1 are read from the nearest valid
+// row and channels past dk from channel 0; the values are masked when staged.
 template <typename TIn>
 struct PrepRaw {
     float4 g[8];
@@ -389,7 +401,7 @@ __device__ __forceinline__ void prep_load(PrepRaw<TIn>& r, const PrepParams& p, 
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int t = 8 * i + (tid >> 5);
-            r.g[i] = *reinterpret_cast<const float4*>(p.g + base + min(t, x.n - 1) * rs + cl);
+            r.g[i] = *reinterpret_cast<const float4*>(p.g + base + min(max(t, x.lo), x.n - 1) * rs + cl);
         }
     }
     {
@@ -398,7 +410,7 @@ __device__ __forceinline__ void prep_load(PrepRaw<TIn>& r, const PrepParams& p, 
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int t = 16 * i + (tid >> 4);
-            r.k[i] = IO::load8(p.k, base + min(t, x.n - 1) * rs + cl);
+            r.k[i] = IO::load8(p.k, base + min(max(t, x.lo), x.n - 1) * rs + cl);
         }
     }
     {
@@ -408,17 +420,17 @@ __device__ __forceinline__ void prep_load(PrepRaw<TIn>& r, const PrepParams& p, 
         for (int u = 0; u < 4; ++u) {
             const int t = 16 * ((u >> 1) ? rb : ra) + (lane & 15);
             const int c = 32 * (2 * (w >> 1) + (u & 1)) + 8 * (lane >> 4);
-            r.qg[u] = IO::load8(p.q, base + min(t, x.n - 1) * rs + (c < dk ? c : 0));
+            r.qg[u] = IO::load8(p.q, base + min(max(t, x.lo), x.n - 1) * rs + (c < dk ? c : 0));
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int idx = tid + NT * u;
             const int ws = idx >> 8, mt = (idx >> 6) & 3, ln = idx & 63;
             const int tt = tok_of(mt, ln & 15), c = SL * ws + 8 * (ln >> 4);
-            r.qd[u] = IO::load8(p.q, base + min(tt, x.n - 1) * rs + (c < dk ? c : 0));
+            r.qd[u] = IO::load8(p.q, base + min(max(tt, x.lo), x.n - 1) * rs + (c < dk ? c : 0));
         }
     }
-    r.beta = p.beta[(x.row0 + min(tid & 63, x.n - 1)) * p.H + x.h];
+    r.beta = p.beta[(x.row0 + min(max(tid & 63, x.lo), x.n - 1)) * p.H + x.h];
 }
 
 // One workgroup per (chunk, head) item; two are resident per compute unit.
@@ -439,20 +451,21 @@ void prep_kernel(PrepParams p) {
     PrepRaw<TIn> raw;
     prep_load<TIn>(raw, p, x, tid);
     {
-        const int n = x.n;
+        const int n = x.n, lo = x.lo;
         uint4* __restrict__ dst = p.ops + (x.gc * p.H + x.h) * CHUNK_OPS;
 
-        // ---- stage this item's inputs (zero past n and dk); log-decays in
+        // ---- stage this item's inputs (zero outside rows lo .. n-1 and past
+        // dk); log-decays in
         // log2 units, so every factor below is a bare exp2 ----
         {
             const int c = 4 * (tid & 31);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int t = 8 * i + (tid >> 5);
-                // rows past n and channels past dk were read from valid
-                // (finite) entries: a zero factor clears them without a branch
+                // rows outside lo .. n-1 and channels past dk were read from
+                // valid (finite) entries: a zero factor clears them without a branch
                 const float4 gv = raw.g[i];
-                const float f = (t < n && c < dk) ? LOG2E : 0.f;
+                const float f = (t >= lo && t < n && c < dk) ? LOG2E : 0.f;
                 *reinterpret_cast<float4*>(&sm.u.G[t][c]) = make_float4(gv.x * f, gv.y * f, gv.z * f, gv.w * f);
             }
         }
@@ -461,11 +474,11 @@ void prep_kernel(PrepParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = 16 * i + (tid >> 4);
-                const typename IO::V8 kz = (t < n && c < dk) ? raw.k[i] : IO::zero8();
+                const typename IO::V8 kz = (t >= lo && t < n && c < dk) ? raw.k[i] : IO::zero8();
                 *reinterpret_cast<typename IO::V8*>(&sm.k.kS[t][c]) = kz;
             }
         }
-        if (tid < C) sm.beta[tid] = tid < n ? raw.beta : 0.f;
+        if (tid < C) sm.beta[tid] = (tid >= lo && tid < n) ? raw.beta : 0.f;
         __syncthreads();
 
         // ---- cumulative log-decay per channel; the span check of the
@@ -522,7 +535,7 @@ void prep_kernel(PrepParams p) {
                     float kt[8], qt[8];
                     IO::f32x8(*reinterpret_cast<const typename IO::V8*>(&sm.k.kS[t][c0]), kt);
                     const typename IO::V8 qx = kk ? raw.qg[2 * sl + 1] : raw.qg[2 * sl];
-                    IO::f32x8((t < n && c0 < dk) ? qx : IO::zero8(), qt);
+                    IO::f32x8((t >= lo && t < n && c0 < dk) ? qx : IO::zero8(), qt);
                     float Gt[8], rw[8], rm[8];
                     lds8(&sm.u.G[t][c0], Gt);
                     lds8(&sm.u.G[R > 0 ? 16 * R - 1 : 0][c0], rw);
@@ -635,7 +648,7 @@ void prep_kernel(PrepParams p) {
                 float sa = 0.f, sb = 0.f;
                 for (int c = 0; c < dk; ++c) {
                     const float kt = IO::f32(sm.k.kS[t][c]), kv = IO::f32(sm.k.kS[s][c]);
-                    const float qt = t < n ? IO::f32(IO::load1(p.q, ((x.row0 + t) * p.H + x.h) * (int64_t)dk + c)) : 0.f;
+                    const float qt = (t >= lo && t < n) ? IO::f32(IO::load1(p.q, ((x.row0 + t) * p.H + x.h) * (int64_t)dk + c)) : 0.f;
                     const float e = ex2(sm.u.G[t][c] - sm.u.G[s][c]);
                     sa = fmaf(kt * kv, e, sa);
                     sb = fmaf(qt * kv, e, sb);
@@ -654,7 +667,7 @@ void prep_kernel(PrepParams p) {
             const int64_t vs = (int64_t)p.H * p.dv;
             const int64_t vb = (x.row0 * p.H + x.h) * (int64_t)p.dv + (c < p.dv ? c : 0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) vr[i] = IO::load8(p.v, vb + min(16 * i + (tid >> 4), n - 1) * vs);
+            for (int i = 0; i < 4; ++i) vr[i] = IO::load8(p.v, vb + min(max(16 * i + (tid >> 4), lo), n - 1) * vs);
         }
 
         // ---- decay-scaled operands: Kd planes, Qd planes, dec, then (K e^G)^T ----
@@ -684,7 +697,7 @@ void prep_kernel(PrepParams p) {
         for (int r = 0; r < 4; ++r) {
             const int t = tok_of(w, i16), c0 = SL * r + 8 * g4;
             float qv[8], kv[8];
-            IO::f32x8((t < n && c0 < dk) ? raw.qd[r] : IO::zero8(), qv);
+            IO::f32x8((t >= lo && t < n && c0 < dk) ? raw.qd[r] : IO::zero8(), qv);
             IO::f32x8(*reinterpret_cast<const typename IO::V8*>(&sm.k.kS[t][c0]), kv);
             float gt[8];
             lds8(&sm.u.G[t][c0], gt);
@@ -718,7 +731,7 @@ void prep_kernel(PrepParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) sm.u.tv.TT[bo + j][bo + r] = xs[r];
         }
-        // V^T: rows past n and columns past dv are zero.  V^T rows are 64
+        // V^T: rows outside lo .. n-1 and columns past dv are zero.  V^T rows are 64
         // tokens; its 16-byte groups are permuted by vt_group so that neither
         // the transposing writes nor the operand reads collide in LDS banks.
         {
@@ -726,7 +739,7 @@ void prep_kernel(PrepParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = 16 * i + (tid >> 4);
-                const bool live = t < n && c < p.dv;
+                const bool live = t >= lo && t < n && c < p.dv;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int j = c + e;
@@ -944,10 +957,13 @@ struct ScanSmem {
 
 struct ScanParams {
     const int32_t* cu;
+    const int32_t* start;       // absolute start positions, or null (all 0)
+    const int32_t* slots;       // state row of each sequence, or null (row b)
     const int32_t* chunk_start;
     const int32_t* snap_base;
     const uint4* ops;
-    const float* init;
+    const float* init;          // null: zero initial states
+    int init_if_started;        // read init only for sequences with start > 0
     void* out;
     float* final_state;
     float* snapshots;
@@ -1051,20 +1067,25 @@ void scan_kernel(ScanParams p) {
     const int rot = tile & 3;
     const int64_t seq0 = p.cu[b];
     const int len = p.cu[b + 1] - p.cu[b];
-    const int nch = (len + C - 1) / C;
+    // chunks sit at absolute multiples of C (see plan_kernel): pad leading
+    // rows of the first chunk precede the sequence's first token
+    const int spos = p.start ? p.start[b] : 0;
+    const int pad = spos % C;
+    const int nch = len > 0 ? (pad + len + C - 1) / C : 0;
     const int64_t cbase = p.chunk_start[b];
     const int64_t sbase = p.snap_base[b];
 
     // state rows of this lane: 32w + chan_of(m, 4*g4 + e) = 32w + 8*g4 + 4m + e
     f32x4 S[2];
-    const int64_t srow = ((int64_t)b * p.H + h) * dk;
+    const int64_t srow = ((p.slots ? (int64_t)p.slots[b] : (int64_t)b) * p.H + h) * dk;
+    const bool has_init = p.init && (!p.init_if_started || spos > 0);
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int c = SL * w + 8 * g4 + 4 * m + e;
             S[m][e] = 0.f;
-            if (p.init) {
+            if (has_init) {
                 const float x = p.init[(srow + (c < dk ? c : 0)) * dv + j];
                 S[m][e] = c < dk ? x : 0.f;
             }
@@ -1092,8 +1113,10 @@ void scan_kernel(ScanParams p) {
         ooff[e] = (uint32_t)(((int64_t)tok_of(w, 4 * g4 + e) * orow + (int64_t)h * dv + j) * OB);
 
     auto chunk = [&](const int ci, ScanOps& o, ScanOps& nx) {
-        const int64_t row0 = seq0 + (int64_t)ci * C;
-        const int n = min(C, len - ci * C);
+        // chunk rows lo .. n-1 are tokens row0 + lo .. row0 + n - 1
+        const int64_t row0 = seq0 - pad + (int64_t)ci * C;
+        const int n = min(C, pad + len - ci * C);
+        const int lo = ci == 0 ? pad : 0;
         // the next chunk (the last chunk reloads itself, so the same loads are
         // issued on every path; that data is unused)
         const __amdgpu_buffer_rsrc_t nblk = scan_block(p, cbase + min(ci + 1, nch - 1), h);
@@ -1144,15 +1167,19 @@ void scan_kernel(ScanParams p) {
             }
             const f32x4 po = p0 + p1;
             const float ob[4] = {o.o.x, o.o.y, o.o.z, o.o.w};
+            // the resource spans rows lo .. n-1: a row below lo gets an
+            // offset that wraps past 2^32 - 1, so it falls outside too
             const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
-                static_cast<char*>(p.out) + row0 * orow * OB, 0, (int)((int64_t)n * orow * OB), 0x00020000);
+                static_cast<char*>(p.out) + (row0 + lo) * orow * OB, 0,
+                (int)((int64_t)(n - lo) * orow * OB), 0x00020000);
+            const uint32_t oshift = (uint32_t)((int64_t)lo * orow * OB);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float ov = p.scale * (po[e] + ob[e]);
                 if constexpr (OUT_BF16)
-                    __builtin_amdgcn_raw_buffer_store_b16(bfb(ov), orsrc, ooff[e], 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b16(bfb(ov), orsrc, ooff[e] - oshift, 0, 0);
                 else
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ov), orsrc, ooff[e], 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ov), orsrc, ooff[e] - oshift, 0, 0);
             }
         }
         lds_barrier();
@@ -1183,10 +1210,12 @@ void scan_kernel(ScanParams p) {
             }
         }
 
-        const int done = ci * C + n;
+        // absolute position reached: snapshots at the multiples of the interval
+        const int done = spos - pad + ci * C + n;
         if (p.interval > 0 && done % p.interval == 0) {
             float* __restrict__ dsts =
-                p.snapshots + ((sbase + done / p.interval - 1) * p.H + h) * (int64_t)dk * dv;
+                p.snapshots +
+                ((sbase + done / p.interval - spos / p.interval - 1) * p.H + h) * (int64_t)dk * dv;
 #pragma unroll
             for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -1242,8 +1271,8 @@ hipError_t launch_t(const PrefillArgs& a) {
     int32_t* snap_base = reinterpret_cast<int32_t*>(ws + l.snap_base);
     uint4* ops = reinterpret_cast<uint4*>(ws + l.ops);
 
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(NT), 0, a.stream, a.cu_dev, a.num_seqs, a.interval,
-                       chunk_start, snap_base);
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(NT), 0, a.stream, a.cu_dev, a.start_dev,
+                       a.num_seqs, a.interval, chunk_start, snap_base);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 
@@ -1255,6 +1284,7 @@ hipError_t launch_t(const PrefillArgs& a) {
         pp.g = a.g;
         pp.beta = a.beta;
         pp.cu = a.cu_dev;
+        pp.start = a.start_dev;
         pp.chunk_start = chunk_start;
         pp.ops = ops;
         pp.H = a.H;
@@ -1270,10 +1300,13 @@ hipError_t launch_t(const PrefillArgs& a) {
 
     ScanParams sp{};
     sp.cu = a.cu_dev;
+    sp.start = a.start_dev;
+    sp.slots = a.slots;
     sp.chunk_start = chunk_start;
     sp.snap_base = snap_base;
     sp.ops = ops;
     sp.init = a.init;
+    sp.init_if_started = a.init_if_started ? 1 : 0;
     sp.out = a.out;
     sp.final_state = a.final_state;
     sp.snapshots = a.snapshots;
@@ -1294,15 +1327,16 @@ hipError_t launch_t(const PrefillArgs& a) {
 
 }  // namespace
 
-int64_t prefill_max_chunks(int num_seqs, int64_t total_tokens) {
-    // sum_b ceil(L_b / C) <= floor(T / C) + num_seqs
-    return total_tokens / C + num_seqs;
+int64_t prefill_max_chunks(int num_seqs, int64_t total_tokens, bool any_start) {
+    // sum_b ceil(L_b / C) <= floor(T / C) + num_seqs; a leading partial chunk
+    // (a start position off the chunk grid) adds at most one more per sequence
+    return total_tokens / C + (int64_t)num_seqs * (any_start ? 2 : 1);
 }
 
 int prefill_chunk_rows() { return C; }
 
-size_t prefill_workspace_bytes(int, int, int H, int num_seqs, int64_t total_tokens) {
-    return ws_layout(H, num_seqs, prefill_max_chunks(num_seqs, total_tokens)).total;
+size_t prefill_workspace_bytes(int, int, int H, int num_seqs, int64_t total_tokens, bool any_start) {
+    return ws_layout(H, num_seqs, prefill_max_chunks(num_seqs, total_tokens, any_start)).total;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a) {

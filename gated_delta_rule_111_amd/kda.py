@@ -69,6 +69,13 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_prefill.argtypes = [CP, i32, P, P, P, P, P, P, P, P, P, P, i32, P, P, sz, P]
     lib.kda_decode.restype = ctypes.c_int
     lib.kda_decode.argtypes = [CP, i32, P, P, P, P, P, P, P, P, P]
+    lib.kda_prefill_pool.restype = ctypes.c_int
+    lib.kda_prefill_pool.argtypes = [CP, i32, P, P, P, P, P, P, P, P, P, P, P, i32, P, i32, P, P,
+                                     sz, P]
+    lib.kda_snapshot_count_at.restype = i64
+    lib.kda_snapshot_count_at.argtypes = [P, P, i32, i32]
+    lib.kda_prefill_pool_workspace_size.restype = sz
+    lib.kda_prefill_pool_workspace_size.argtypes = [CP, i32, i64]
     lib.kda_decode_multi.restype = ctypes.c_int
     lib.kda_decode_multi.argtypes = [CP, i32, i32, ctypes.c_int, P, P, P, P, P, P, P, P, P, P]
     lib.kda_qk_frontend.restype = ctypes.c_int
@@ -353,3 +360,85 @@ def decode_multi(q: Optional[torch.Tensor], k: torch.Tensor, v: torch.Tensor, g:
                                 _ptr(slots), _ptr(accepted) if mode == "commit" else None,
                                 _ptr(out), _stream(stream)))
     return out
+
+
+def snapshot_count_at(cu_seqlens_host: Sequence[int], start_pos_host: Sequence[int],
+                      interval: int) -> int:
+    n = len(cu_seqlens_host) - 1
+    cu = (ctypes.c_int32 * len(cu_seqlens_host))(*cu_seqlens_host)
+    st = (ctypes.c_int32 * n)(*start_pos_host)
+    r = load().kda_snapshot_count_at(cu, st, n, int(interval))
+    if r < 0:
+        raise ValueError("cu_seqlens must be non-decreasing and start positions >= 0")
+    return int(r)
+
+
+def pool_workspace_size(cfg: Config, num_seqs: int, total_tokens: int) -> int:
+    return int(load().kda_prefill_pool_workspace_size(ctypes.byref(cfg), num_seqs, total_tokens))
+
+
+def prefill_pool(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                 beta: torch.Tensor, cu_seqlens: torch.Tensor, start_pos: torch.Tensor,
+                 state_pool: torch.Tensor, slots: Optional[torch.Tensor] = None,
+                 snapshot_interval: int = 0, out_dtype: Optional[torch.dtype] = None,
+                 scale: float = 0.0, cu_seqlens_host: Optional[Sequence[int]] = None,
+                 start_pos_host: Optional[Sequence[int]] = None,
+                 out: Optional[torch.Tensor] = None, snapshots: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None,
+                 stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """kda_prefill_pool: prefill against a pool of resident states.
+
+    start_pos: [N] int32 device tensor, the absolute position of each
+    sequence's first token (0 = fresh sequence, zero state; > 0 = its pool
+    row holds the state after that many tokens).  state_pool: [S, H, dk, dv]
+    fp32, rows slots[b] (or b) read and overwritten with the final states.
+    Snapshots fall on absolute multiples of snapshot_interval.  Returns
+    (out, snapshots)."""
+    lib = load()
+    dev = q.device
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    if cu_seqlens_host is None:
+        cu_seqlens_host = cu_seqlens.cpu().tolist()
+    if start_pos_host is None:
+        start_pos_host = start_pos.cpu().tolist()
+    cu_list = [int(x) for x in cu_seqlens_host]
+    st_list = [int(x) for x in start_pos_host]
+    N = len(cu_list) - 1
+    _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    _need(start_pos, "start_pos", (N,), torch.int32, dev)
+    if len(st_list) != N:
+        raise ValueError("start_pos_host must hold one entry per sequence")
+    for name, t, shp, dt in (("q", q, (T, H, dk), q.dtype), ("k", k, (T, H, dk), q.dtype),
+                             ("v", v, (T, H, dv), q.dtype), ("g", g, (T, H, dk), torch.float32),
+                             ("beta", beta, (T, H), torch.float32)):
+        _need(t, name, shp, dt, dev)
+    if cu_list[-1] != T:
+        raise ValueError(f"cu_seqlens ends at {cu_list[-1]} but q has {T} tokens")
+    if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (H, dk, dv):
+        raise ValueError(f"state_pool: shape {tuple(state_pool.shape)} != [S, {H}, {dk}, {dv}]")
+    _need(state_pool, "state_pool", tuple(state_pool.shape), torch.float32, dev)
+    if slots is not None:
+        _need(slots, "slots", (N,), torch.int32, dev)
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else torch.float32
+    cfg = config(H, dk, dv, q.dtype, out_dtype, scale)
+    nsnap = snapshot_count_at(cu_list, st_list, snapshot_interval) if snapshot_interval > 0 else 0
+    if out is None:
+        out = torch.empty(T, H, dv, dtype=out_dtype, device=dev)
+    _need(out, "out", (T, H, dv), out_dtype, dev)
+    if snapshots is None:
+        snapshots = torch.empty(nsnap, H, dk, dv, dtype=torch.float32, device=dev)
+    _need(snapshots, "snapshots", (nsnap, H, dk, dv), torch.float32, dev)
+    ws_bytes = pool_workspace_size(cfg, N, T)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    cu_arr = (ctypes.c_int32 * len(cu_list))(*cu_list)
+    st_arr = (ctypes.c_int32 * max(1, N))(*st_list)
+    _check(lib.kda_prefill_pool(
+        ctypes.byref(cfg), N, cu_arr, cu_seqlens.data_ptr(), st_arr, start_pos.data_ptr(),
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta.data_ptr(),
+        state_pool.data_ptr(), _ptr(slots), int(state_pool.shape[0]), out.data_ptr(),
+        int(snapshot_interval), snapshots.data_ptr() if nsnap > 0 else None, _ptr(workspace),
+        workspace.numel() if workspace is not None else 0, _stream(stream)))
+    return out, snapshots

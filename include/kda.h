@@ -140,6 +140,67 @@ kda_status kda_prefill(const kda_config *cfg, int32_t num_seqs,
                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Prefill over a pool of resident states, with absolute token positions.
+ *
+ * "Day-0 vLLM support for Kimi K3" (vLLM blog), section "Kimi K3's
+ * architecture, and how vLLM serves it": a hybrid cache manager keeps
+ * compact recurrent-state blocks for the KDA layers, and prefix caching over
+ * recurrent state separates the prefix-match granularity from the physical
+ * state-block size, reusing state snapshots taken at block boundaries; the
+ * same page, section "Deployment notes, each from a real incident", says
+ * prefix caching covers the recurrent KDA state.  Here that means:
+ *   - sequence b's first token in this call sits at absolute position
+ *     start_pos[b] >= 0 (the tokens before it are the prefix whose state the
+ *     pool holds);
+ *   - its state lives in row state_slots_dev[b] (or b) of state_pool
+ *     [num_slots, H, dk, dv] fp32: read as the state after start_pos[b]
+ *     tokens when start_pos[b] > 0 (zero state when start_pos[b] == 0), and
+ *     overwritten with the state after the call's tokens;
+ *   - snapshots are taken at the absolute positions P in (start_pos[b],
+ *     start_pos[b] + L_b] with P % snapshot_interval == 0, in order of P,
+ *     sequence b's block starting at the sum of the earlier sequences'
+ *     counts (kda_snapshot_count_at), so a snapshot serves as the pool row for
+ *     a later call that starts at P, whatever block boundaries the first call
+ *     had;
+ *   - chunks are cut at absolute multiples of 64, so resuming from a
+ *     snapshot at P reproduces the uninterrupted run bit for bit.
+ * Other arguments as in kda_prefill (out is [T, H, dv]; the workspace comes
+ * from kda_prefill_pool_workspace_size).  Slots must be distinct and
+ * < num_slots (not checked on the device).
+ * Errors: KDA_ERR_INVALID_ARG (also a negative start_pos, or start_pos + L
+ * beyond 2^31 - 1, or num_slots too small), KDA_ERR_UNSUPPORTED,
+ * KDA_ERR_ALIGNMENT, KDA_ERR_WORKSPACE, KDA_ERR_HIP.
+ */
+kda_status kda_prefill_pool(const kda_config *cfg, int32_t num_seqs,
+                            const int32_t *cu_seqlens_host,
+                            const int32_t *cu_seqlens_dev,
+                            const int32_t *start_pos_host,
+                            const int32_t *start_pos_dev, const void *q,
+                            const void *k, const void *v, const float *g,
+                            const float *beta, float *state_pool,
+                            const int32_t *state_slots_dev, int32_t num_slots,
+                            void *out, int32_t snapshot_interval,
+                            float *snapshots, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/*
+ * Snapshot rows kda_prefill_pool writes: sum_b floor((s_b + L_b) / interval)
+ * - floor(s_b / interval), s_b = start_pos_host[b].  0 when interval <= 0;
+ * -1 for NULL arrays, decreasing offsets or a negative start.
+ */
+int64_t kda_snapshot_count_at(const int32_t *cu_seqlens_host,
+                              const int32_t *start_pos_host, int32_t num_seqs,
+                              int32_t interval);
+
+/*
+ * Workspace bytes for kda_prefill_pool: 512 B of offsets plus
+ * (floor(total_tokens / 64) + 2 * num_seqs) * num_heads * 164,352 B (a start
+ * position off the 64-token grid can add one chunk per sequence).
+ */
+size_t kda_prefill_pool_workspace_size(const kda_config *cfg, int32_t num_seqs,
+                                       int64_t total_tokens);
+
+/*
  * One decode step: one new token for each of num_seqs sequences against
  * states resident on the device, updated in place.
  *   q, k : [num_seqs, H, dk] in_dtype    v : [num_seqs, H, dv] in_dtype

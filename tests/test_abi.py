@@ -32,7 +32,8 @@ def test_header_declares_the_calls():
     for required in ("kda_prefill", "kda_decode", "kda_snapshot_count",
                      "kda_prefill_workspace_size", "kda_status_string",
                      "kda_last_error_detail", "kda_version", "kda_qk_frontend",
-                     "kda_decode_multi"):
+                     "kda_decode_multi", "kda_prefill_pool", "kda_snapshot_count_at",
+                     "kda_prefill_pool_workspace_size"):
         assert required in names
 
 
@@ -214,3 +215,35 @@ def test_decode_multi_rejects_bad_arguments(lib):
     c2 = _cfg(d=48)
     assert f(ctypes.byref(c2), 4, 8, 0, A, A, A, A, A, A, None, None, A, None) == 2
     assert f(p, 0, 8, 0, None, None, None, None, None, None, None, None, None, None) == 0
+
+
+def test_snapshot_count_at(lib):
+    from gated_delta_rule_111_amd import kda as libkda
+    # (3, 4): 5; (10, 0): none; (12, 13): 15, 20, 25
+    assert libkda.snapshot_count_at([0, 4, 4, 17], [3, 10, 12], 5) == 4
+    assert libkda.snapshot_count_at([0, 4, 4, 17], [0, 0, 0], 5) == 0 + 0 + 2
+    with pytest.raises(ValueError):
+        libkda.snapshot_count_at([0, 4], [-1], 5)
+
+
+def _pool(lib, cfg, cu, starts, ptr=A, pool=A, num_slots=4, ws_bytes=1 << 40, interval=0,
+          snaps=A, start_dev=A):
+    arr = (ctypes.c_int32 * len(cu))(*cu)
+    st = (ctypes.c_int32 * len(starts))(*starts) if starts is not None else None
+    return lib.kda_prefill_pool(ctypes.byref(cfg), len(cu) - 1, arr, A, st, start_dev, ptr, ptr,
+                                ptr, ptr, ptr, pool, None, num_slots, ptr, interval, snaps, A,
+                                ws_bytes, None)
+
+
+def test_prefill_pool_rejects_bad_arguments(lib):
+    cfg = _cfg()
+    assert _pool(lib, cfg, [0, 64], None) == 1                 # no start positions
+    assert _pool(lib, cfg, [0, 64], [-3]) == 1                 # negative start
+    assert _pool(lib, cfg, [0, 64], [0x7fffffff - 10]) == 1    # start + L overflows
+    assert _pool(lib, cfg, [0, 64], [0], pool=None) == 1
+    assert _pool(lib, cfg, [0, 64], [0], start_dev=None) == 1
+    assert _pool(lib, cfg, [0, 64, 128], [0, 0], num_slots=1) == 1
+    assert _pool(lib, cfg, [0, 64], [0], ws_bytes=16) == 4
+    assert _pool(lib, cfg, [0, 64], [0], pool=MIS) == 3
+    assert _pool(lib, cfg, [0, 64], [0], interval=100) == 1
+    assert _pool(lib, cfg, [0, 64], [100], interval=128, snaps=None) == 1  # 128 falls due
