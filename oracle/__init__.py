@@ -18,6 +18,10 @@ computed, and the passages it follows, are stated in the header of
   vLLM serves it": state snapshots at block boundaries for prefix reuse.
 * "Kimi K3 technical FAQ", same question: queries and keys pass through a
   short convolution, Swish and L2 normalisation first (``qk_frontend``).
+* "Kimi K3 technical FAQ", question "What does the architecture actually
+  look like?", and the vLLM page's architecture section: Attention Residuals,
+  a softmax over earlier block outputs with a learned pseudo-query, residual
+  add and RMSNorm (``attnres``).
 
 Parity pins for every function here are in ``tests/test_oracle_pins.py``
 and ``tests/test_frontend_pins.py``.
@@ -57,6 +61,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
                                       P, P, f64, P, i32]
     lib.kda_oracle_snapshot_count.restype = i64
     lib.kda_oracle_snapshot_count.argtypes = [i32, P, P, i64]
+    lib.kda_oracle_attnres.restype = ctypes.c_int
+    lib.kda_oracle_attnres.argtypes = [i32, i64, i32, P, P, P, P, f64, f64, P, P]
     lib.kda_oracle_qk_frontend.restype = ctypes.c_int
     lib.kda_oracle_qk_frontend.argtypes = [i32, P, i32, i32, i32, P, P, P, P, f64, P, P]
     return lib
@@ -218,6 +224,28 @@ class Oracle:
         return y, new_state
 
 
+    def attnres(self, sources, w, x=None, gamma=None, scale: float = 1.0, eps: float = 1e-6):
+        """Attention Residuals aggregation of one layer's input.
+
+        sources: [M, T, d] (or a list of M [T, d] arrays); w, gamma: [d];
+        x: [T, d] residual or None.  Returns (h, y) [T, d] fp64.
+        """
+        src = np.ascontiguousarray(np.stack([self._f32(s) for s in sources]))
+        M, T, d = src.shape
+        wv = self._f32(w).reshape(d)
+        xv = None if x is None else self._f32(x).reshape(T, d)
+        gv = None if gamma is None else self._f32(gamma).reshape(d)
+        h = np.zeros((T, d), dtype=np.float64)
+        y = np.zeros((T, d), dtype=np.float64)
+        rc = self.lib.kda_oracle_attnres(
+            M, T, d, src.ctypes.data, None if xv is None else xv.ctypes.data, wv.ctypes.data,
+            None if gv is None else gv.ctypes.data, float(scale), float(eps), h.ctypes.data,
+            y.ctypes.data)
+        if rc != 0:
+            raise ValueError("kda_oracle_attnres rejected its arguments")
+        return h, y
+
+
 _DEFAULT: Optional[Oracle] = None
 
 
@@ -239,3 +267,7 @@ def decode(*args, **kwargs):
 
 def qk_frontend(*args, **kwargs):
     return get().qk_frontend(*args, **kwargs)
+
+
+def attnres(*args, **kwargs):
+    return get().attnres(*args, **kwargs)

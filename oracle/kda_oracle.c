@@ -466,3 +466,74 @@ int kda_oracle_qk_frontend(int32_t num_seqs, const int64_t *cu, int32_t H,
     free(tail);
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Attention Residuals aggregation (block variant), one layer's input.       */
+/*                                                                          */
+/* "Kimi K3 technical FAQ" (Runpod guide), question "What does the          */
+/* architecture actually look like?": each layer can attend over the        */
+/* embedding plus the preceding block outputs through a learned             */
+/* pseudo-query (blocks of 12 layers, about 8 blocks).  "Day-0 vLLM support */
+/* for Kimi K3" (vLLM blog), section "Kimi K3's architecture, and how vLLM  */
+/* serves it": the fused kernel computes the logits, the softmax across the */
+/* previous layers and the aggregation, and folds in the residual add and   */
+/* the output RMSNorm.  The pages give no formula; the reading used here,   */
+/* per token t, with sources s_m (m < M), pseudo-query w and residual x:    */
+/*                                                                          */
+/*   l_m = scale * <w, s_m,t>            p = softmax_m(l)                   */
+/*   h_t = sum_m p_m s_m,t + x_t         (x absent: no residual add)        */
+/*   y_t = h_t / sqrt(mean_c h_t[c]^2 + eps) * gamma   (gamma absent: 1)    */
+/*                                                                          */
+/* Layouts: sources [M][T][d] (one array per source, contiguous here);      */
+/* x, h, y [T][d]; w, gamma [d].                                            */
+/* ------------------------------------------------------------------------ */
+int kda_oracle_attnres(int32_t M, int64_t T, int32_t d, const float *src,
+                       const float *x, const float *w, const float *gamma,
+                       double scale, double eps, double *h, double *y)
+{
+    double *l;
+    int64_t t;
+    int32_t m, c;
+    if (M < 1 || T < 0 || d < 1 || !src || !w || !h || !y || !(eps > 0.0))
+        return -1;
+    l = (double *)malloc(sizeof(double) * (size_t)M);
+    if (!l)
+        return -1;
+    for (t = 0; t < T; ++t) {
+        double mx, z = 0.0, ms = 0.0, r;
+        double *ht = h + (size_t)t * d, *yt = y + (size_t)t * d;
+        /* logits of the sources */
+        for (m = 0; m < M; ++m) {
+            const float *s = src + ((size_t)m * T + t) * d;
+            double acc = 0.0;
+            for (c = 0; c < d; ++c)
+                acc += (double)w[c] * (double)s[c];
+            l[m] = scale * acc;
+        }
+        /* softmax over the sources (shifted by the largest logit) */
+        mx = l[0];
+        for (m = 1; m < M; ++m)
+            if (l[m] > mx)
+                mx = l[m];
+        for (m = 0; m < M; ++m) {
+            l[m] = exp(l[m] - mx);
+            z += l[m];
+        }
+        for (m = 0; m < M; ++m)
+            l[m] /= z;
+        /* weighted sum of the sources, plus the residual */
+        for (c = 0; c < d; ++c) {
+            double acc = x ? (double)x[(size_t)t * d + c] : 0.0;
+            for (m = 0; m < M; ++m)
+                acc += l[m] * (double)src[((size_t)m * T + t) * d + c];
+            ht[c] = acc;
+            ms += acc * acc;
+        }
+        /* RMSNorm of the result */
+        r = 1.0 / sqrt(ms / d + eps);
+        for (c = 0; c < d; ++c)
+            yt[c] = ht[c] * r * (gamma ? (double)gamma[c] : 1.0);
+    }
+    free(l);
+    return 0;
+}

@@ -8,6 +8,7 @@ import shutil
 
 import pytest
 
+import attnres_pins
 import frontend_pins
 import oracle
 import oracle_pins
@@ -40,6 +41,16 @@ MUTANTS = [
     ("abs_base_relative",
      "kda_oracle_snapshot_count(1, cu_seqlens + b, start_pos ? start_pos + b : NULL,",
      "kda_oracle_snapshot_count(1, cu_seqlens + b, NULL,"),
+    # Attention Residuals aggregation
+    ("ar_no_scale", "l[m] = scale * acc;", "l[m] = acc;"),
+    ("ar_unnormalised", "        l[m] /= z;", "        l[m] /= 1.0;"),
+    ("ar_no_residual", "double acc = x ? (double)x[(size_t)t * d + c] : 0.0;",
+     "double acc = 0.0;"),
+    ("ar_rms_of_sum", "r = 1.0 / sqrt(ms / d + eps);", "r = 1.0 / sqrt(ms + eps);"),
+    ("ar_eps_outside", "r = 1.0 / sqrt(ms / d + eps);", "r = 1.0 / (sqrt(ms / d) + eps);"),
+    ("ar_no_gamma", "(gamma ? (double)gamma[c] : 1.0)", "1.0"),
+    ("ar_logits_of_first", "const float *s = src + ((size_t)m * T + t) * d;",
+     "const float *s = src + ((size_t)0 * T + t) * d;"),
     # q/k front end (short convolution -> Swish -> L2 norm)
     ("fe_taps_reversed", "z += (double)w[ch * W + j] *",
      "z += (double)w[ch * W + (W - 1 - j)] *"),
@@ -58,7 +69,8 @@ MUTANTS = [
 
 def _run_pins(O):
     broken = []
-    for pin in oracle_pins.ALL_PINS + frontend_pins.ALL_FRONTEND_PINS:
+    for pin in (oracle_pins.ALL_PINS + frontend_pins.ALL_FRONTEND_PINS +
+                attnres_pins.ALL_ATTNRES_PINS):
         try:
             pin(O)
         except AssertionError:
