@@ -57,6 +57,7 @@ KERNEL_SOURCES = {
     "prefill": os.path.join(ROOT, "gated_delta_rule_111_amd", "csrc", "kda_prefill.hip"),
     "frontend": os.path.join(ROOT, "gated_delta_rule_111_amd", "csrc", "kda_frontend.hip"),
     "multi": os.path.join(ROOT, "gated_delta_rule_111_amd", "csrc", "kda_decode_multi.hip"),
+    "attnres": os.path.join(ROOT, "gated_delta_rule_111_amd", "csrc", "kda_attnres.hip"),
 }
 
 
@@ -319,6 +320,111 @@ def bench_frontend(torch, kda, inputs, reps):
     return res
 
 
+def bench_attnres(torch, kda, inputs, reps):
+    """Attention Residuals aggregation at hidden 7168 with 8 sources, bf16 in
+    and out, h and y written: a prefill batch of 8192 tokens and a decode
+    batch of 256.  Algorithmic bytes per token: the 8 sources and the
+    residual read once, h and y written once ((8 + 1 + 2) * 7168 * 2 B), plus
+    the query and gamma once per launch."""
+    dev = "cuda:0"
+    d, M = inputs.ATTNRES_HIDDEN, inputs.ATTNRES_SOURCES
+    res = {}
+    for name, T in (("prefill-T8192-d7168-M8", 8192), ("decode-T256-d7168-M8", 256)):
+        inp = inputs.attnres_inputs(T, d, M, seed=17, device=dev)
+        h = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
+        y = torch.empty_like(h)
+
+        def call():
+            kda.attnres(inp.sources, inp.query, residual=inp.residual, gamma=inp.gamma,
+                        h_out=h, y_out=y)
+
+        wall, per_call = _time_graph(torch, call, reps)
+        nbytes = T * d * 2 * (M + 1 + 2) + 2 * d * 4
+        gbs = nbytes / per_call / 1e9
+        log(f"[bench] attnres {name}: {per_call * 1e6:.1f} us/call, {gbs:.0f} GB/s")
+        res[name] = {"tokens_per_s": round(T / wall, 1), "kernel_us": round(per_call * 1e6, 2),
+                     "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                                  "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                  "traffic": measured_traffic("attnres", name),
+                                  "kernel": "attnres_kernel<8,bf16,bf16>",
+                                  "bytes_per_launch": nbytes}}
+    return res
+
+
+def cpu_attnres_baseline(inputs, tokens: int):
+    import oracle
+    d, M = inputs.ATTNRES_HIDDEN, inputs.ATTNRES_SOURCES
+    inp = inputs.attnres_inputs(tokens, d, M, seed=17)
+    f = lambda t: t.float().numpy()
+    log(f"[bench] cpu oracle: attnres {tokens} tokens")
+    t0 = time.perf_counter()
+    oracle.attnres([f(s) for s in inp.sources], f(inp.query), x=f(inp.residual),
+                   gamma=f(inp.gamma))
+    dt = time.perf_counter() - t0
+    return {"value": round(tokens / dt, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"{tokens} tokens of the prefill shape (d = 7168, 8 sources), fp64, one thread"}
+
+
+def bench_prefill_pool(torch, kda, inputs, reps, warmup):
+    """Prefill against a state pool on a prefix-cache-hit shape: 8 sequences
+    of 1024 tokens (T = 8192, H = 32, d = 128, bf16) continuing from seeded
+    absolute positions in [1, 32768) (mostly off the 64-token grid, so each
+    first chunk carries leading padding), states read from and written back
+    to their pool rows, snapshots at absolute multiples of 1024.  Algorithmic
+    bytes: as for prefill (1796 B per token-head) plus the initial state read
+    per sequence-head, final states and snapshots."""
+    dev = "cuda:0"
+    lens = [1024] * 8
+    N, H, d = len(lens), 32, 128
+    inp = inputs.prefill_inputs(lens, H, d, d, seed=13, device=dev)
+    g = torch.Generator().manual_seed(14)
+    starts = torch.randint(1, 32768, (N,), generator=g, dtype=torch.int32).tolist()
+    st = torch.tensor(starts, dtype=torch.int32, device=dev)
+    pool0 = torch.randn(N, H, d, d, generator=torch.Generator(device=dev).manual_seed(15),
+                        device=dev) * 0.02
+    pool = pool0.clone()
+    cu_host = inp.cu_seqlens.cpu().tolist()
+    nsnap = kda.snapshot_count_at(cu_host, starts, 1024)
+    out = torch.empty(sum(lens), H, d, dtype=torch.float32, device=dev)
+    snaps = torch.empty(nsnap, H, d, d, dtype=torch.float32, device=dev)
+    cfg = kda.config(H, d, d, inp.q.dtype)
+    ws = torch.empty(kda.pool_workspace_size(cfg, N, sum(lens)), dtype=torch.uint8, device=dev)
+
+    def call():
+        kda.prefill_pool(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens, st, pool,
+                         snapshot_interval=1024, cu_seqlens_host=cu_host, start_pos_host=starts,
+                         out=out, snapshots=snaps, workspace=ws)
+
+    for _ in range(warmup):
+        pool.copy_(pool0)
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    total = 0.0
+    for _ in range(reps):  # each call from the same pool contents, the copy outside the timing
+        pool.copy_(pool0)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        total += e0.elapsed_time(e1) / 1e3
+    per_call = total / reps
+    T = sum(lens)
+    nbytes = T * H * PREFILL_BYTES_PER_TOKEN_HEAD + (2 * N + nsnap) * H * STATE_BYTES
+    gbs = nbytes / per_call / 1e9
+    log(f"[bench] prefill_pool 8x1024 from off-grid starts: {per_call * 1e3:.3f} ms/call, "
+        f"{T / per_call:.3e} tok/s, {gbs:.0f} GB/s, {nsnap} snapshots")
+    return {"workload": "pool-8x1024-H32-d128-offgrid-starts-snap1024",
+            "value": round(T / per_call, 1), "unit": "tokens/s",
+            "kernel_ms": round(per_call * 1e3, 4), "start_pos": starts, "snapshots": nsnap,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": None, "kernel": "plan + prep_kernel<bf16> + scan_kernel",
+                         "bytes_per_launch": nbytes}}
+
+
 def bench_spec(torch, kda, inputs, reps, decode_us):
     """Speculative decoding step on the decode shape (256 sequences x 32
     heads, d = 128, fp32 states): verify 1 + 7 tokens, then commit the
@@ -437,6 +543,9 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-frontend", action="store_true")
     ap.add_argument("--no-spec", action="store_true")
+    ap.add_argument("--no-pool", action="store_true")
+    ap.add_argument("--no-attnres", action="store_true")
+    ap.add_argument("--cpu-attnres-tokens", type=int, default=4096)
     ap.add_argument("--cpu-frontend-tokens", type=int, default=32768)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-decode-seqs", type=int, default=128)
@@ -473,6 +582,12 @@ def main():
                                   max(2, args.warmup // 10))
     if args.long:
         pre_long, _ = bench_prefill(torch, kda, inputs, inputs.LONG, 3, 1)
+    pool = None
+    if not args.no_prefill and not args.no_pool:
+        pool = bench_prefill_pool(torch, kda, inputs, args.prefill_reps, 2)
+    attn = None
+    if not args.no_attnres:
+        attn = bench_attnres(torch, kda, inputs, args.prefill_reps)
     spec = None
     if not args.no_spec:
         spec = bench_spec(torch, kda, inputs, args.prefill_reps, dec["kernel_us"])
@@ -487,6 +602,8 @@ def main():
             pre["cpu_baseline"] = cpu_prefill_baseline(pinp, args.cpu_prefill_tokens)
         if fe is not None:
             fe["cpu_baseline"] = cpu_frontend_baseline(inputs, args.cpu_frontend_tokens)
+        if attn is not None:
+            attn["cpu_baseline"] = cpu_attnres_baseline(inputs, args.cpu_attnres_tokens)
 
     line = {
         "metric": METRIC,
@@ -515,6 +632,10 @@ def main():
         line["qk_frontend"] = fe
     if spec is not None:
         line["spec_decode"] = spec
+    if pool is not None:
+        line["prefill_pool"] = pool
+    if attn is not None:
+        line["attnres"] = attn
     print(json.dumps(line), flush=True)
 
 

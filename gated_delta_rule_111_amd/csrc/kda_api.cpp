@@ -518,4 +518,66 @@ kda_status kda_qk_frontend(const kda_frontend_config* cfg, int32_t num_seqs,
     return ok();
 }
 
+kda_status kda_attnres(const kda_attnres_config* cfg, int64_t num_tokens,
+                       const void* const* sources, const void* residual, const float* query,
+                       const float* gamma, void* h_out, void* y_out, void* stream) {
+    if (!cfg) return fail(KDA_ERR_INVALID_ARG, "cfg is NULL");
+    const int M = cfg->num_sources, d = cfg->hidden;
+    if (M < 1 || M > 16) return fail(KDA_ERR_UNSUPPORTED, "num_sources %d not in [1, 16]", M);
+    if (d < 16 || d % 16 != 0 || d > kda::attnres_max_hidden(M))
+        return fail(KDA_ERR_UNSUPPORTED, "hidden %d not a multiple of 16 in [16, %d]", d,
+                    kda::attnres_max_hidden(M));
+    if (cfg->in_dtype != KDA_BF16 && cfg->in_dtype != KDA_F32)
+        return fail(KDA_ERR_UNSUPPORTED, "in_dtype %d unknown", (int)cfg->in_dtype);
+    if (cfg->out_dtype != KDA_BF16 && cfg->out_dtype != KDA_F32)
+        return fail(KDA_ERR_UNSUPPORTED, "out_dtype %d unknown", (int)cfg->out_dtype);
+    if (!std::isfinite(cfg->logit_scale))
+        return fail(KDA_ERR_INVALID_ARG, "logit_scale must be finite");
+    if (!std::isfinite(cfg->eps) || !(cfg->eps > 0.f))
+        return fail(KDA_ERR_INVALID_ARG, "eps must be finite and > 0");
+    if (num_tokens < 0 || num_tokens > 0x7fffffffLL)
+        return fail(KDA_ERR_INVALID_ARG, "num_tokens %lld out of range", (long long)num_tokens);
+    if (num_tokens == 0) return ok();
+    if (!sources) return fail(KDA_ERR_INVALID_ARG, "sources_host is NULL");
+    const PtrCheck ptrs[] = {
+        {"residual", residual, false, 16}, {"query", query, true, 16},
+        {"gamma", gamma, false, 16},       {"h_out", h_out, false, 16},
+        {"y_out", y_out, true, 16},
+    };
+    kda_status st = check_ptrs(ptrs, (int)(sizeof(ptrs) / sizeof(ptrs[0])));
+    if (st != KDA_OK) return st;
+    const size_t ib = (size_t)num_tokens * d * dtype_bytes(cfg->in_dtype);
+    const size_t ob = (size_t)num_tokens * d * dtype_bytes(cfg->out_dtype);
+    for (int m = 0; m < M; ++m) {
+        if (!sources[m]) return fail(KDA_ERR_INVALID_ARG, "sources[%d] is NULL", m);
+        if (!aligned(sources[m], 16))
+            return fail(KDA_ERR_ALIGNMENT, "sources[%d] is not 16-byte aligned", m);
+        if (overlap(y_out, ob, sources[m], ib) || overlap(h_out, ob, sources[m], ib))
+            return fail(KDA_ERR_INVALID_ARG, "an output overlaps sources[%d]", m);
+    }
+    if (overlap(y_out, ob, residual, ib) || overlap(h_out, ob, residual, ib) ||
+        overlap(y_out, ob, h_out, ob))
+        return fail(KDA_ERR_INVALID_ARG, "outputs overlap the residual or each other");
+
+    kda::AttnResArgs a{};
+    a.hidden = d;
+    a.num_sources = M;
+    a.num_tokens = num_tokens;
+    a.in_bf16 = cfg->in_dtype == KDA_BF16;
+    a.out_bf16 = cfg->out_dtype == KDA_BF16;
+    for (int m = 0; m < M; ++m) a.sources[m] = sources[m];
+    a.x = residual;
+    a.w = query;
+    a.gamma = gamma;
+    a.h = h_out;
+    a.y = y_out;
+    a.scale = cfg->logit_scale;
+    a.eps = cfg->eps;
+    a.stream = static_cast<hipStream_t>(stream);
+    hipError_t e = kda::launch_attnres(a);
+    if (e != hipSuccess)
+        return fail(KDA_ERR_HIP, "attnres launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 }  // extern "C"

@@ -1,0 +1,296 @@
+// kda_attnres.hip -- Attention Residuals aggregation: a layer's input as a
+// softmax-weighted sum of earlier block outputs, plus the residual, then
+// RMSNorm, in one launch.  gfx950.
+//
+// "Kimi K3 technical FAQ" (Runpod guide), question "What does the
+// architecture actually look like?": each layer can attend over the
+// embedding plus the preceding block outputs through a learned pseudo-query
+// (the block variant, blocks of 12 layers, about 8 blocks).  "Day-0 vLLM
+// support for Kimi K3" (vLLM blog), section "Kimi K3's architecture, and how
+// vLLM serves it": one fused kernel computes the logits, the softmax across
+// the previous layers and the aggregation, with the residual add and the
+// output RMSNorm folded in.  Per token t, sources s_m (m < M):
+//   l_m = scale <w, s_m,t>,  p = softmax(l),  h = sum_m p_m s_m,t + x_t,
+//   y = h / sqrt(mean(h^2) + eps) * gamma.
+//
+// The op is bound by HBM: every source row is read once.  Design: one
+// workgroup per token; thread i holds channels 8i .. 8i+7 of every source in
+// registers (one 16-byte load per bf16 source), so the
+// logits (M dot products over the hidden dimension, reduced across the
+// workgroup) and the weighted sum use the same registers without a second
+// read.  Two workgroup reductions: the M logits, then the sum of squares.
+#include "kda_common.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+constexpr int AR_MAX_SOURCES = 16;
+constexpr int AR_MAX_THREADS = 1024;
+// up to 11 sources fit 128 VGPRs (16 waves per workgroup); more sources take
+// smaller workgroups with room for 256
+constexpr int ar_max_threads(int M) { return M <= 11 ? 1024 : 512; }
+
+struct ArParams {
+    const void* src[AR_MAX_SOURCES];  // [T, d] each
+    const void* x;                    // [T, d] or null
+    const float* w;                   // [d]
+    const float* gamma;               // [d] or null
+    void* h;                          // [T, d] or null
+    void* y;                          // [T, d]
+    int d;
+    float scale, eps;
+};
+
+// EPT consecutive values as fp32
+template <int EPT>
+__device__ __forceinline__ void widen(const uint4 (&r)[EPT / 8], float (&v)[EPT]) {
+#pragma unroll
+    for (int q = 0; q < EPT / 8; ++q) {
+        const uint32_t u[4] = {r[q].x, r[q].y, r[q].z, r[q].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[8 * q + 2 * i] = bf16_bits_to_f32(u[i] & 0xffffu);
+            v[8 * q + 2 * i + 1] = bf16_bits_to_f32(u[i] >> 16);
+        }
+    }
+}
+
+// raw row slices: bf16 keeps EPT/8 uint4, fp32 keeps EPT/4 float4
+template <typename T, int EPT> struct Slice;
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+template <int EPT> struct Slice<bf16_t, EPT> {
+    uint4 r[EPT / 8];
+    __device__ __forceinline__ void load(const bf16_t* p) {
+#pragma unroll
+        for (int q = 0; q < EPT / 8; ++q) {  // streamed once: kept out of the caches
+            const u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p) + q);
+            r[q] = make_uint4(t[0], t[1], t[2], t[3]);
+        }
+    }
+    __device__ __forceinline__ void get(float (&v)[EPT]) const { widen<EPT>(r, v); }
+};
+template <int EPT> struct Slice<float, EPT> {
+    float4 r[EPT / 4];
+    __device__ __forceinline__ void load(const float* p) {
+#pragma unroll
+        for (int q = 0; q < EPT / 4; ++q) r[q] = reinterpret_cast<const float4*>(p)[q];
+    }
+    __device__ __forceinline__ void get(float (&v)[EPT]) const {
+#pragma unroll
+        for (int q = 0; q < EPT / 4; ++q) {
+            v[4 * q] = r[q].x; v[4 * q + 1] = r[q].y; v[4 * q + 2] = r[q].z; v[4 * q + 3] = r[q].w;
+        }
+    }
+};
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+template <int EPT>
+__device__ __forceinline__ void store_row(bf16_t* p, const float (&v)[EPT]) {
+#pragma unroll
+    for (int q = 0; q < EPT / 8; ++q) {
+        uint32_t u[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const f32x2_t pr = {v[8 * q + 2 * i], v[8 * q + 2 * i + 1]};
+            u[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2_t));
+        }
+        reinterpret_cast<uint4*>(p)[q] = make_uint4(u[0], u[1], u[2], u[3]);
+    }
+}
+template <int EPT>
+__device__ __forceinline__ void store_row(float* p, const float (&v)[EPT]) {
+#pragma unroll
+    for (int q = 0; q < EPT / 4; ++q)
+        reinterpret_cast<float4*>(p)[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+
+// sum over the 64 lanes of a wave, left in every lane: DPP inside each
+// 16-lane row, then the rows by lane permutes
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp<0x141>(v);  // row_half_mirror
+    v += dpp<0x128>(v);  // row_ror 8
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+template <int M, typename TIn, typename TOut>
+__global__ __launch_bounds__(ar_max_threads(M)) void attnres_kernel(ArParams p) {
+    constexpr int EPT = 8;  // channels per thread: one 16-byte load per bf16 source
+    __shared__ float red[AR_MAX_THREADS / 64][M + 1];
+    __shared__ float res[M + 1];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nw = blockDim.x >> 6;
+    const int d = p.d;
+    const int c0 = EPT * tid;
+    const bool live = c0 < d;          // threads past the row hold zeros
+    const int cc = live ? c0 : 0;
+    const int64_t row = (int64_t)blockIdx.x * d + cc;
+
+    // every source slice first (each row is read exactly once)
+    Slice<TIn, EPT> sl[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) sl[m].load(static_cast<const TIn*>(p.src[m]) + row);
+    Slice<TIn, EPT> xs;
+    if (p.x) xs.load(static_cast<const TIn*>(p.x) + row);
+    float w[EPT];
+#pragma unroll
+    for (int q = 0; q < EPT / 4; ++q) {
+        const float4 t = reinterpret_cast<const float4*>(p.w + cc)[q];
+        w[4 * q] = t.x; w[4 * q + 1] = t.y; w[4 * q + 2] = t.z; w[4 * q + 3] = t.w;
+    }
+
+    // logits: per-thread partial dot products, then across the workgroup
+    float part[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        float v[EPT];
+        sl[m].get(v);
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) acc = fmaf(w[i], v[i], acc);
+        part[m] = live ? acc : 0.f;
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) part[m] = wave_sum(part[m]);
+    if (lane == 0) {
+#pragma unroll
+        for (int m = 0; m < M; ++m) red[wave][m] = part[m];
+    }
+    __syncthreads();
+    if (tid < M) {
+        float s = 0.f;
+        for (int i = 0; i < nw; ++i) s += red[i][tid];
+        res[tid] = s * p.scale;
+    }
+    __syncthreads();
+
+    // softmax over the sources (every thread, from the shared logits)
+    float pr[M];
+    float mx = res[0];
+#pragma unroll
+    for (int m = 1; m < M; ++m) mx = fmaxf(mx, res[m]);
+    float z = 0.f;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        pr[m] = __expf(res[m] - mx);
+        z += pr[m];
+    }
+    const float iz = 1.f / z;
+
+    // h = sum_m p_m s_m + x
+    float h[EPT];
+    if (p.x) {
+        xs.get(h);
+    } else {
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) h[i] = 0.f;
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+        float v[EPT];
+        sl[m].get(v);
+        const float pm = pr[m] * iz;
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) h[i] = fmaf(pm, v[i], h[i]);
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) ss = fmaf(h[i], h[i], ss);
+    ss = wave_sum(live ? ss : 0.f);
+    if (lane == 0) red[wave][M] = ss;
+    __syncthreads();
+    if (tid == 0) {
+        float s = 0.f;
+        for (int i = 0; i < nw; ++i) s += red[i][M];
+        res[M] = rsqrtf(s / (float)d + p.eps);
+    }
+    __syncthreads();
+    if (!live) return;
+    const float r = res[M];
+    const int64_t orow = (int64_t)blockIdx.x * d + c0;
+    if (p.h) store_row<EPT>(static_cast<TOut*>(p.h) + orow, h);
+    float yv[EPT];
+    if (p.gamma) {
+#pragma unroll
+        for (int q = 0; q < EPT / 4; ++q) {
+            const float4 g = reinterpret_cast<const float4*>(p.gamma + c0)[q];
+            yv[4 * q] = h[4 * q] * r * g.x;
+            yv[4 * q + 1] = h[4 * q + 1] * r * g.y;
+            yv[4 * q + 2] = h[4 * q + 2] * r * g.z;
+            yv[4 * q + 3] = h[4 * q + 3] * r * g.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) yv[i] = h[i] * r;
+    }
+    store_row<EPT>(static_cast<TOut*>(p.y) + orow, yv);
+}
+
+template <int M, typename TIn, typename TOut>
+hipError_t launch_m(const ArParams& p, int64_t T, hipStream_t stream) {
+    constexpr int EPT = 8;
+    const int threads = (p.d / EPT + 63) / 64 * 64;
+    hipLaunchKernelGGL((attnres_kernel<M, TIn, TOut>), dim3((unsigned)T), dim3(threads), 0,
+                       stream, p);
+    return hipGetLastError();
+}
+
+template <typename TIn, typename TOut>
+hipError_t launch_t(const ArParams& p, int M, int64_t T, hipStream_t stream) {
+    switch (M) {
+        case 1: return launch_m<1, TIn, TOut>(p, T, stream);
+        case 2: return launch_m<2, TIn, TOut>(p, T, stream);
+        case 3: return launch_m<3, TIn, TOut>(p, T, stream);
+        case 4: return launch_m<4, TIn, TOut>(p, T, stream);
+        case 5: return launch_m<5, TIn, TOut>(p, T, stream);
+        case 6: return launch_m<6, TIn, TOut>(p, T, stream);
+        case 7: return launch_m<7, TIn, TOut>(p, T, stream);
+        case 8: return launch_m<8, TIn, TOut>(p, T, stream);
+        case 9: return launch_m<9, TIn, TOut>(p, T, stream);
+        case 10: return launch_m<10, TIn, TOut>(p, T, stream);
+        case 11: return launch_m<11, TIn, TOut>(p, T, stream);
+        case 12: return launch_m<12, TIn, TOut>(p, T, stream);
+        case 13: return launch_m<13, TIn, TOut>(p, T, stream);
+        case 14: return launch_m<14, TIn, TOut>(p, T, stream);
+        case 15: return launch_m<15, TIn, TOut>(p, T, stream);
+        case 16: return launch_m<16, TIn, TOut>(p, T, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int attnres_max_hidden(int num_sources) { return 8 * ar_max_threads(num_sources); }
+
+hipError_t launch_attnres(const AttnResArgs& a) {
+    ArParams p{};
+    for (int m = 0; m < a.num_sources; ++m) p.src[m] = a.sources[m];
+    p.x = a.x;
+    p.w = a.w;
+    p.gamma = a.gamma;
+    p.h = a.h;
+    p.y = a.y;
+    p.d = a.hidden;
+    p.scale = a.scale;
+    p.eps = a.eps;
+    if (a.num_tokens == 0) return hipSuccess;
+    if (a.in_bf16)
+        return a.out_bf16 ? launch_t<bf16_t, bf16_t>(p, a.num_sources, a.num_tokens, a.stream)
+                          : launch_t<bf16_t, float>(p, a.num_sources, a.num_tokens, a.stream);
+    return a.out_bf16 ? launch_t<float, bf16_t>(p, a.num_sources, a.num_tokens, a.stream)
+                      : launch_t<float, float>(p, a.num_sources, a.num_tokens, a.stream);
+}
+
+}  // namespace kda

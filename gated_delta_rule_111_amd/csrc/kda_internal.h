@@ -73,7 +73,21 @@ struct DecodeMultiArgs {
     hipStream_t stream;
 };
 
+struct AttnResArgs {
+    int hidden, num_sources;
+    int64_t num_tokens;
+    bool in_bf16, out_bf16;
+    const void* sources[16];      // [T, hidden] each
+    const void* x;                // [T, hidden] residual, nullable
+    const float *w, *gamma;       // [hidden]; gamma nullable
+    void *h, *y;                  // [T, hidden]; h nullable
+    float scale, eps;
+    hipStream_t stream;
+};
+
 hipError_t launch_decode(const DecodeArgs& a);
+hipError_t launch_attnres(const AttnResArgs& a);
+int attnres_max_hidden(int num_sources);
 hipError_t launch_decode_multi(const DecodeMultiArgs& a);
 hipError_t launch_frontend(const FrontendArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);

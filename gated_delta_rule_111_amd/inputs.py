@@ -260,3 +260,33 @@ def multi_token_inputs(N: int, K: int, H: int, dk: int, dv: int, seed: int,
     d = decode_inputs(K, N, H, dk, dv, seed, in_dtype, decay_shift, state_std, device)
     t = lambda x: x.transpose(0, 1).contiguous()
     return DecodeInputs(t(d.q), t(d.k), t(d.v), t(d.g), t(d.beta), d.state)
+
+
+# ---------------------------------------------------------------------------
+# Attention Residuals aggregation: M sources (the embedding and earlier block
+# outputs) and the residual ~ N(0, 1) rounded to the input dtype; the
+# pseudo-query ~ N(0, 1/d) (logits of order one); gamma = 1 + 0.1 N(0, 1).
+# Hidden size 7168 ("Kimi K3 technical FAQ", question "What does the
+# architecture actually look like?": the router's latent is half the 7,168
+# hidden size).  Drawing order: sources, residual, query, gamma.
+# ---------------------------------------------------------------------------
+ATTNRES_HIDDEN = 7168
+ATTNRES_SOURCES = 8
+
+
+@dataclass
+class AttnResInputs:
+    sources: List[torch.Tensor]  # M x [T, d]
+    residual: torch.Tensor       # [T, d]
+    query: torch.Tensor          # [d] fp32
+    gamma: torch.Tensor          # [d] fp32
+
+
+def attnres_inputs(T: int, d: int, M: int, seed: int, in_dtype=torch.bfloat16,
+                   device="cpu") -> AttnResInputs:
+    gen = _gen(seed, device)
+    src = [torch.randn(T, d, generator=gen, device=device).to(in_dtype) for _ in range(M)]
+    x = torch.randn(T, d, generator=gen, device=device).to(in_dtype)
+    w = torch.randn(d, generator=gen, device=device) / float(d) ** 0.5
+    gamma = 1 + 0.1 * torch.randn(d, generator=gen, device=device)
+    return AttnResInputs(src, x, w, gamma)

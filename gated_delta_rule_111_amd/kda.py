@@ -69,6 +69,8 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_prefill.argtypes = [CP, i32, P, P, P, P, P, P, P, P, P, P, i32, P, P, sz, P]
     lib.kda_decode.restype = ctypes.c_int
     lib.kda_decode.argtypes = [CP, i32, P, P, P, P, P, P, P, P, P]
+    lib.kda_attnres.restype = ctypes.c_int
+    lib.kda_attnres.argtypes = [ctypes.c_void_p, i64, P, P, P, P, P, P, P]
     lib.kda_prefill_pool.restype = ctypes.c_int
     lib.kda_prefill_pool.argtypes = [CP, i32, P, P, P, P, P, P, P, P, P, P, P, i32, P, i32, P, P,
                                      sz, P]
@@ -442,3 +444,50 @@ def prefill_pool(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Ten
         int(snapshot_interval), snapshots.data_ptr() if nsnap > 0 else None, _ptr(workspace),
         workspace.numel() if workspace is not None else 0, _stream(stream)))
     return out, snapshots
+
+
+class AttnResConfig(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("num_sources", ctypes.c_int32),
+                ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
+                ("logit_scale", ctypes.c_float), ("eps", ctypes.c_float)]
+
+
+def attnres(sources: Sequence[torch.Tensor], query: torch.Tensor,
+            residual: Optional[torch.Tensor] = None, gamma: Optional[torch.Tensor] = None,
+            logit_scale: float = 1.0, eps: float = 1e-6, out_dtype: Optional[torch.dtype] = None,
+            h_out: Optional[torch.Tensor] = None, y_out: Optional[torch.Tensor] = None,
+            want_h: bool = True, stream=None) -> Tuple[Optional[torch.Tensor], torch.Tensor]:
+    """kda_attnres: softmax over the sources (logits logit_scale * <query, s>),
+    weighted sum plus the residual (h), then RMSNorm with gamma (y).
+
+    sources: M tensors [T, d] (bf16 or fp32, one dtype); query, gamma: [d]
+    fp32; residual: [T, d] or None.  Returns (h or None, y)."""
+    lib = load()
+    M = len(sources)
+    if M < 1:
+        raise ValueError("at least one source")
+    T, d = sources[0].shape
+    dev = sources[0].device
+    dt = sources[0].dtype
+    for i, s in enumerate(sources):
+        _need(s, f"sources[{i}]", (T, d), dt, dev)
+    _need(query, "query", (d,), torch.float32, dev)
+    if residual is not None:
+        _need(residual, "residual", (T, d), dt, dev)
+    if gamma is not None:
+        _need(gamma, "gamma", (d,), torch.float32, dev)
+    if out_dtype is None:
+        out_dtype = y_out.dtype if y_out is not None else dt
+    if y_out is None:
+        y_out = torch.empty(T, d, dtype=out_dtype, device=dev)
+    _need(y_out, "y_out", (T, d), out_dtype, dev)
+    if want_h and h_out is None:
+        h_out = torch.empty(T, d, dtype=out_dtype, device=dev)
+    if h_out is not None:
+        _need(h_out, "h_out", (T, d), out_dtype, dev)
+    cfg = AttnResConfig(d, M, _dtype_code(dt), _dtype_code(out_dtype), float(logit_scale),
+                        float(eps))
+    ptrs = (ctypes.c_void_p * M)(*[s.data_ptr() for s in sources])
+    _check(lib.kda_attnres(ctypes.byref(cfg), T, ptrs, _ptr(residual), query.data_ptr(),
+                           _ptr(gamma), _ptr(h_out), y_out.data_ptr(), _stream(stream)))
+    return h_out, y_out

@@ -339,6 +339,51 @@ kda_status kda_qk_frontend(const kda_frontend_config *cfg, int32_t num_seqs,
                            const int32_t *state_slots_dev, int32_t num_slots,
                            void *q_out, void *k_out, void *stream);
 
+/*
+ * Attention Residuals aggregation (block variant): a layer's input as a
+ * softmax-weighted sum of earlier block outputs, plus the residual, then
+ * RMSNorm, in one launch.
+ *
+ * "Kimi K3 technical FAQ" (Runpod guide), question "What does the
+ * architecture actually look like?": each layer can attend over the
+ * embedding plus the preceding block outputs through a learned pseudo-query;
+ * K3 uses blocks of 12 layers (about 8 blocks).  "Day-0 vLLM support for
+ * Kimi K3" (vLLM blog), section "Kimi K3's architecture, and how vLLM serves
+ * it": the fused kernel computes the logits, the softmax across the previous
+ * layers and the aggregation, and folds in the residual add and the output
+ * RMSNorm.  The pages give no formula; read per token t, with sources s_m
+ * (m < num_sources), pseudo-query w, residual x and RMSNorm weight gamma, as
+ *
+ *     p = softmax_m(logit_scale * <w, s_m,t>),   h = sum_m p_m s_m,t + x_t,
+ *     y = h / sqrt(mean over the hidden channels of h^2 + eps) * gamma.
+ */
+typedef struct {
+    int32_t hidden;      /* d: a multiple of 16, at most 8192 (4096 with
+                            more than 11 sources)                           */
+    int32_t num_sources; /* 1 .. 16                                         */
+    kda_dtype in_dtype;  /* sources and residual                            */
+    kda_dtype out_dtype; /* h and y                                         */
+    float logit_scale;   /* finite                                          */
+    float eps;           /* > 0, finite                                     */
+} kda_attnres_config;
+
+/*
+ *   sources_host : host array of num_sources device pointers, each [T, d]
+ *                  in_dtype (separate buffers: the embedding and the block
+ *                  outputs)
+ *   residual     : [T, d] in_dtype, or NULL (no residual add)
+ *   query        : [d] fp32 pseudo-query          gamma : [d] fp32 or NULL (1)
+ *   h_out        : [T, d] out_dtype, or NULL (not written)
+ *   y_out        : [T, d] out_dtype
+ * The outputs may not overlap any input.  Device arrays 16-byte aligned.
+ * Errors: KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED (d, num_sources, dtype),
+ * KDA_ERR_ALIGNMENT, KDA_ERR_HIP.  num_tokens == 0 is a no-op.
+ */
+kda_status kda_attnres(const kda_attnres_config *cfg, int64_t num_tokens,
+                       const void *const *sources_host, const void *residual,
+                       const float *query, const float *gamma, void *h_out,
+                       void *y_out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -33,7 +33,7 @@ def test_header_declares_the_calls():
                      "kda_prefill_workspace_size", "kda_status_string",
                      "kda_last_error_detail", "kda_version", "kda_qk_frontend",
                      "kda_decode_multi", "kda_prefill_pool", "kda_snapshot_count_at",
-                     "kda_prefill_pool_workspace_size"):
+                     "kda_prefill_pool_workspace_size", "kda_attnres"):
         assert required in names
 
 
@@ -247,3 +247,28 @@ def test_prefill_pool_rejects_bad_arguments(lib):
     assert _pool(lib, cfg, [0, 64], [0], pool=MIS) == 3
     assert _pool(lib, cfg, [0, 64], [0], interval=100) == 1
     assert _pool(lib, cfg, [0, 64], [100], interval=128, snaps=None) == 1  # 128 falls due
+
+
+def test_attnres_rejects_bad_arguments(lib):
+    from gated_delta_rule_111_amd import kda as libkda
+
+    def call(d=7168, M=8, ind=0, outd=0, scale=1.0, eps=1e-6, T=4, srcs=None, query=A, y=A + (1 << 30),
+             h=None, res=None):
+        cfg = libkda.AttnResConfig(d, M, ind, outd, scale, eps)
+        arr = srcs if srcs is not None else (ctypes.c_void_p * 16)(*([A + (i << 26) for i in range(16)]))
+        return lib.kda_attnres(ctypes.byref(cfg), T, arr, res, query, None, h, y, None)
+
+    assert call(d=7160) == 2                  # not a multiple of 16
+    assert call(d=8208) == 2                  # above 8192
+    assert call(M=12, d=7168) == 2            # more than 11 sources: at most 4096
+    assert call(M=0) == 2 and call(M=17) == 2
+    assert call(eps=0.0) == 1
+    assert call(scale=float("inf")) == 1
+    assert call(T=-1) == 1
+    assert call(query=None) == 1
+    assert call(y=None) == 1
+    assert call(query=A + 8) == 3
+    bad = (ctypes.c_void_p * 16)(*([A] * 7 + [None] * 9))
+    assert call(srcs=bad) == 1
+    assert call(y=A) == 1                     # output over a source
+    assert call(T=0, srcs=None) == 0
