@@ -524,11 +524,11 @@ kda_status kda_attnres(const kda_attnres_config* cfg, int64_t num_tokens,
     if (!cfg) return fail(KDA_ERR_INVALID_ARG, "cfg is NULL");
     const int M = cfg->num_sources, d = cfg->hidden;
     if (M < 1 || M > 16) return fail(KDA_ERR_UNSUPPORTED, "num_sources %d not in [1, 16]", M);
-    if (d < 16 || d % 16 != 0 || d > kda::attnres_max_hidden(M))
-        return fail(KDA_ERR_UNSUPPORTED, "hidden %d not a multiple of 16 in [16, %d]", d,
-                    kda::attnres_max_hidden(M));
     if (cfg->in_dtype != KDA_BF16 && cfg->in_dtype != KDA_F32)
         return fail(KDA_ERR_UNSUPPORTED, "in_dtype %d unknown", (int)cfg->in_dtype);
+    const int dmax = kda::attnres_max_hidden(M, cfg->in_dtype == KDA_BF16);
+    if (d < 16 || d % 16 != 0 || d > dmax)
+        return fail(KDA_ERR_UNSUPPORTED, "hidden %d not a multiple of 16 in [16, %d]", d, dmax);
     if (cfg->out_dtype != KDA_BF16 && cfg->out_dtype != KDA_F32)
         return fail(KDA_ERR_UNSUPPORTED, "out_dtype %d unknown", (int)cfg->out_dtype);
     if (!std::isfinite(cfg->logit_scale))

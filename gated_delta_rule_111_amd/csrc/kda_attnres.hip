@@ -13,12 +13,17 @@
 //   l_m = scale <w, s_m,t>,  p = softmax(l),  h = sum_m p_m s_m,t + x_t,
 //   y = h / sqrt(mean(h^2) + eps) * gamma.
 //
-// The op is bound by HBM: every source row is read once.  Design: one
-// workgroup per token; thread i holds channels 8i .. 8i+7 of every source in
-// registers (one 16-byte load per bf16 source), so the
-// logits (M dot products over the hidden dimension, reduced across the
-// workgroup) and the weighted sum use the same registers without a second
-// read.  Two workgroup reductions: the M logits, then the sum of squares.
+// The op is bound by HBM: every source row is read once.  Design: a
+// workgroup per token at a time; thread i holds channels 8i .. 8i+7 of every
+// source in registers (one 16-byte load per bf16 source), so the logits (M
+// dot products over the hidden dimension, reduced across the workgroup) and
+// the weighted sum use the same registers without a second read.  Two
+// workgroup reductions per token: the M logits, then the sum of squares.
+// Only one such workgroup fits a compute unit at d = 7168, so the launch has
+// one workgroup per resident slot, each walking tokens with the next token's
+// rows requested before the current token's reductions.
+#include <algorithm>
+
 #include "kda_common.h"
 #include "kda_internal.h"
 
@@ -27,9 +32,11 @@ namespace {
 
 constexpr int AR_MAX_SOURCES = 16;
 constexpr int AR_MAX_THREADS = 1024;
-// up to 11 sources fit 128 VGPRs (16 waves per workgroup); more sources take
-// smaller workgroups with room for 256
-constexpr int ar_max_threads(int M) { return M <= 11 ? 1024 : 512; }
+// bf16 rows of two tokens (the current one and the next one in flight) fit
+// 128 VGPRs, so 16-wave workgroups, for up to 9 sources; fp32 rows (one token
+// at a time) for up to 10.  More sources take 8-wave workgroups with room
+// for 256 VGPRs.
+constexpr int ar_max_threads(int M, bool bf16) { return M <= (bf16 ? 9 : 10) ? 1024 : 512; }
 
 struct ArParams {
     const void* src[AR_MAX_SOURCES];  // [T, d] each
@@ -69,6 +76,14 @@ template <int EPT> struct Slice<bf16_t, EPT> {
         }
     }
     __device__ __forceinline__ void get(float (&v)[EPT]) const { widen<EPT>(r, v); }
+    // an empty asm that claims to rewrite the packed registers: the fp32
+    // values widened before it cannot be reused after it, so they are not
+    // kept alive (8 registers per slice) until their second use
+    __device__ __forceinline__ void fence() {
+#pragma unroll
+        for (int q = 0; q < EPT / 8; ++q)
+            asm volatile("" : "+v"(r[q].x), "+v"(r[q].y), "+v"(r[q].z), "+v"(r[q].w));
+    }
 };
 template <int EPT> struct Slice<float, EPT> {
     float4 r[EPT / 4];
@@ -82,6 +97,7 @@ template <int EPT> struct Slice<float, EPT> {
             v[4 * q] = r[q].x; v[4 * q + 1] = r[q].y; v[4 * q + 2] = r[q].z; v[4 * q + 3] = r[q].w;
         }
     }
+    __device__ __forceinline__ void fence() {}
 };
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -126,7 +142,8 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 template <int M, typename TIn, typename TOut>
-__global__ __launch_bounds__(ar_max_threads(M)) void attnres_kernel(ArParams p) {
+__global__ __launch_bounds__(ar_max_threads(M, sizeof(TIn) == 2))
+void attnres_kernel(ArParams p, int64_t T) {
     constexpr int EPT = 8;  // channels per thread: one 16-byte load per bf16 source
     __shared__ float red[AR_MAX_THREADS / 64][M + 1];
     __shared__ float res[M + 1];
@@ -136,114 +153,169 @@ __global__ __launch_bounds__(ar_max_threads(M)) void attnres_kernel(ArParams p) 
     const int c0 = EPT * tid;
     const bool live = c0 < d;          // threads past the row hold zeros
     const int cc = live ? c0 : 0;
-    const int64_t row = (int64_t)blockIdx.x * d + cc;
 
-    // every source slice first (each row is read exactly once)
-    Slice<TIn, EPT> sl[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m) sl[m].load(static_cast<const TIn*>(p.src[m]) + row);
-    Slice<TIn, EPT> xs;
-    if (p.x) xs.load(static_cast<const TIn*>(p.x) + row);
-    float w[EPT];
-#pragma unroll
-    for (int q = 0; q < EPT / 4; ++q) {
-        const float4 t = reinterpret_cast<const float4*>(p.w + cc)[q];
-        w[4 * q] = t.x; w[4 * q + 1] = t.y; w[4 * q + 2] = t.z; w[4 * q + 3] = t.w;
-    }
-
-    // logits: per-thread partial dot products, then across the workgroup
-    float part[M];
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-        float v[EPT];
-        sl[m].get(v);
-        float acc = 0.f;
-#pragma unroll
-        for (int i = 0; i < EPT; ++i) acc = fmaf(w[i], v[i], acc);
-        part[m] = live ? acc : 0.f;
-    }
-#pragma unroll
-    for (int m = 0; m < M; ++m) part[m] = wave_sum(part[m]);
-    if (lane == 0) {
-#pragma unroll
-        for (int m = 0; m < M; ++m) red[wave][m] = part[m];
-    }
-    __syncthreads();
-    if (tid < M) {
-        float s = 0.f;
-        for (int i = 0; i < nw; ++i) s += red[i][tid];
-        res[tid] = s * p.scale;
-    }
-    __syncthreads();
-
-    // softmax over the sources (every thread, from the shared logits)
-    float pr[M];
-    float mx = res[0];
-#pragma unroll
-    for (int m = 1; m < M; ++m) mx = fmaxf(mx, res[m]);
-    float z = 0.f;
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-        pr[m] = __expf(res[m] - mx);
-        z += pr[m];
-    }
-    const float iz = 1.f / z;
-
-    // h = sum_m p_m s_m + x
-    float h[EPT];
-    if (p.x) {
-        xs.get(h);
-    } else {
-#pragma unroll
-        for (int i = 0; i < EPT; ++i) h[i] = 0.f;
-    }
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-        float v[EPT];
-        sl[m].get(v);
-        const float pm = pr[m] * iz;
-#pragma unroll
-        for (int i = 0; i < EPT; ++i) h[i] = fmaf(pm, v[i], h[i]);
-    }
-    float ss = 0.f;
-#pragma unroll
-    for (int i = 0; i < EPT; ++i) ss = fmaf(h[i], h[i], ss);
-    ss = wave_sum(live ? ss : 0.f);
-    if (lane == 0) red[wave][M] = ss;
-    __syncthreads();
-    if (tid == 0) {
-        float s = 0.f;
-        for (int i = 0; i < nw; ++i) s += red[i][M];
-        res[M] = rsqrtf(s / (float)d + p.eps);
-    }
-    __syncthreads();
-    if (!live) return;
-    const float r = res[M];
-    const int64_t orow = (int64_t)blockIdx.x * d + c0;
-    if (p.h) store_row<EPT>(static_cast<TOut*>(p.h) + orow, h);
-    float yv[EPT];
-    if (p.gamma) {
+    // the query and gamma slices (cache-resident) are read at their use in
+    // every token, which keeps two tokens' rows within the register budget
+    auto slice4 = [&](const float* a, float (&v)[EPT]) {
 #pragma unroll
         for (int q = 0; q < EPT / 4; ++q) {
-            const float4 g = reinterpret_cast<const float4*>(p.gamma + c0)[q];
-            yv[4 * q] = h[4 * q] * r * g.x;
-            yv[4 * q + 1] = h[4 * q + 1] * r * g.y;
-            yv[4 * q + 2] = h[4 * q + 2] * r * g.z;
-            yv[4 * q + 3] = h[4 * q + 3] * r * g.w;
+            const float4 t = reinterpret_cast<const float4*>(a + cc)[q];
+            v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
+        }
+    };
+
+    // one token's rows: every source slice and the residual slice
+    struct Rows {
+        Slice<TIn, EPT> s[M];
+        Slice<TIn, EPT> x;
+    };
+    auto fetch = [&](Rows& r, int64_t t) {
+        const int64_t row = t * d + cc;
+#pragma unroll
+        for (int m = 0; m < M; ++m) r.s[m].load(static_cast<const TIn*>(p.src[m]) + row);
+        if (p.x) r.x.load(static_cast<const TIn*>(p.x) + row);
+    };
+
+    auto token = [&](Rows& r, int64_t t) {
+        // logits: per-thread partial dot products, then across the workgroup
+        float w[EPT];
+        slice4(p.w, w);
+        float part[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            float v[EPT];
+            r.s[m].get(v);
+            float acc = 0.f;
+#pragma unroll
+            for (int i = 0; i < EPT; ++i) acc = fmaf(w[i], v[i], acc);
+            part[m] = live ? acc : 0.f;
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m) r.s[m].fence();
+#pragma unroll
+        for (int m = 0; m < M; ++m) part[m] = wave_sum(part[m]);
+        if (lane == 0) {
+#pragma unroll
+            for (int m = 0; m < M; ++m) red[wave][m] = part[m];
+        }
+        __syncthreads();
+        if (tid < M) {
+            float s = 0.f;
+            for (int i = 0; i < nw; ++i) s += red[i][tid];
+            res[tid] = s * p.scale;
+        }
+        __syncthreads();
+
+        // softmax over the sources (every thread, from the shared logits)
+        float pr[M];
+        float mx = res[0];
+#pragma unroll
+        for (int m = 1; m < M; ++m) mx = fmaxf(mx, res[m]);
+        float z = 0.f;
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            pr[m] = __expf(res[m] - mx);
+            z += pr[m];
+        }
+        const float iz = 1.f / z;
+
+        // h = sum_m p_m s_m + x
+        float h[EPT];
+        if (p.x) {
+            r.x.get(h);
+        } else {
+#pragma unroll
+            for (int i = 0; i < EPT; ++i) h[i] = 0.f;
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+            float v[EPT];
+            r.s[m].get(v);
+            const float pm = pr[m] * iz;
+#pragma unroll
+            for (int i = 0; i < EPT; ++i) h[i] = fmaf(pm, v[i], h[i]);
+        }
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) ss = fmaf(h[i], h[i], ss);
+        ss = wave_sum(live ? ss : 0.f);
+        if (lane == 0) red[wave][M] = ss;
+        __syncthreads();
+        if (tid == 0) {
+            float s = 0.f;
+            for (int i = 0; i < nw; ++i) s += red[i][M];
+            res[M] = rsqrtf(s / (float)d + p.eps);
+        }
+        __syncthreads();
+        if (live) {
+            const float rr = res[M];
+            const int64_t orow = t * d + c0;
+            if (p.h) store_row<EPT>(static_cast<TOut*>(p.h) + orow, h);
+            float yv[EPT];
+            if (p.gamma) {
+                float gm[EPT];
+                slice4(p.gamma, gm);
+#pragma unroll
+                for (int i = 0; i < EPT; ++i) yv[i] = h[i] * rr * gm[i];
+            } else {
+#pragma unroll
+                for (int i = 0; i < EPT; ++i) yv[i] = h[i] * rr;
+            }
+            store_row<EPT>(static_cast<TOut*>(p.y) + orow, yv);
+        }
+    };
+
+    // tokens blockIdx.x, + gridDim.x, ...: with bf16 rows the next token's
+    // rows are requested before the current one is reduced (two register
+    // sets used in turn, so nothing loaded is copied); fp32 rows, twice the
+    // registers, go one token at a time
+    const int64_t step = gridDim.x;
+    int64_t t = blockIdx.x;
+    Rows ra;
+    if constexpr (sizeof(TIn) == 2) {
+        Rows rb;
+        if (t < T) fetch(ra, t);
+        for (; t < T; t += 2 * step) {
+            if (t + step < T) fetch(rb, t + step);
+            token(ra, t);
+            if (t + step >= T) break;
+            if (t + 2 * step < T) fetch(ra, t + 2 * step);
+            token(rb, t + step);
         }
     } else {
-#pragma unroll
-        for (int i = 0; i < EPT; ++i) yv[i] = h[i] * r;
+        for (; t < T; t += step) {
+            fetch(ra, t);
+            token(ra, t);
+        }
     }
-    store_row<EPT>(static_cast<TOut*>(p.y) + orow, yv);
+}
+
+int compute_units() {
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0, n = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            n > 0)
+            cus = n;
+        else
+            cus = 256;
+    }
+    return cus;
 }
 
 template <int M, typename TIn, typename TOut>
 hipError_t launch_m(const ArParams& p, int64_t T, hipStream_t stream) {
     constexpr int EPT = 8;
     const int threads = (p.d / EPT + 63) / 64 * 64;
-    hipLaunchKernelGGL((attnres_kernel<M, TIn, TOut>), dim3((unsigned)T), dim3(threads), 0,
-                       stream, p);
+    // as many workgroups as are resident at once; each walks its tokens
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attnres_kernel<M, TIn, TOut>,
+                                                     threads, 0) != hipSuccess || per_cu < 1)
+        per_cu = 1;
+    const int64_t grid = std::min<int64_t>(T, (int64_t)per_cu * compute_units());
+    hipLaunchKernelGGL((attnres_kernel<M, TIn, TOut>), dim3((unsigned)grid), dim3(threads), 0,
+                       stream, p, T);
     return hipGetLastError();
 }
 
@@ -272,7 +344,9 @@ hipError_t launch_t(const ArParams& p, int M, int64_t T, hipStream_t stream) {
 
 }  // namespace
 
-int attnres_max_hidden(int num_sources) { return 8 * ar_max_threads(num_sources); }
+int attnres_max_hidden(int num_sources, bool in_bf16) {
+    return 8 * ar_max_threads(num_sources, in_bf16);
+}
 
 hipError_t launch_attnres(const AttnResArgs& a) {
     ArParams p{};

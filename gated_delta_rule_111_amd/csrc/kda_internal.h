@@ -87,7 +87,7 @@ struct AttnResArgs {
 
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_attnres(const AttnResArgs& a);
-int attnres_max_hidden(int num_sources);
+int attnres_max_hidden(int num_sources, bool in_bf16);
 hipError_t launch_decode_multi(const DecodeMultiArgs& a);
 hipError_t launch_frontend(const FrontendArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);

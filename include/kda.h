@@ -359,7 +359,7 @@ kda_status kda_qk_frontend(const kda_frontend_config *cfg, int32_t num_seqs,
  */
 typedef struct {
     int32_t hidden;      /* d: a multiple of 16, at most 8192 (4096 with
-                            more than 11 sources)                           */
+                            more than 9 bf16 or 10 fp32 sources)            */
     int32_t num_sources; /* 1 .. 16                                         */
     kda_dtype in_dtype;  /* sources and residual                            */
     kda_dtype out_dtype; /* h and y                                         */

@@ -260,7 +260,9 @@ def test_attnres_rejects_bad_arguments(lib):
 
     assert call(d=7160) == 2                  # not a multiple of 16
     assert call(d=8208) == 2                  # above 8192
-    assert call(M=12, d=7168) == 2            # more than 11 sources: at most 4096
+    assert call(M=10, d=7168) == 2            # more than 9 bf16 sources: at most 4096
+    assert call(M=10, d=7168, ind=1) != 2     # fp32 sources: up to 10 at 8192
+    assert call(M=11, d=7168, ind=1) == 2
     assert call(M=0) == 2 and call(M=17) == 2
     assert call(eps=0.0) == 1
     assert call(scale=float("inf")) == 1
