@@ -427,8 +427,9 @@ def bench_prefill_pool(torch, kda, inputs, reps, warmup):
 
 def bench_spec(torch, kda, inputs, reps, decode_us):
     """Speculative decoding step on the decode shape (256 sequences x 32
-    heads, d = 128, fp32 states): verify 1 + 7 tokens, then commit the
-    accepted prefix (1 + Binomial(7, p), mean 4.73 or 2.61).  Algorithmic
+    heads, d = 128, fp32 states): the fused step (commit the previous step's
+    accepted prefix, 1 + Binomial(7, p) with mean 4.73 or 2.61, then verify
+    1 + 7 new tokens), and verify and commit as separate launches.  Algorithmic
     bytes: verify reads each state once (64 KiB per sequence-head) plus the
     8 tokens' inputs (q, k, v bf16, g fp32, beta) and writes their fp32
     outputs; commit reads and writes each state once plus the accepted
@@ -466,17 +467,36 @@ def bench_spec(torch, kda, inputs, reps, decode_us):
             e1.record(stream)
             torch.cuda.synchronize()
             times[label] = e0.elapsed_time(e1) / 1e3 / reps
+        prev = (inp.k, inp.v, inp.g, inp.beta)
+
+        def step():
+            kda.decode_spec_step(inp.q, inp.k, inp.v, inp.g, inp.beta, state, prev=prev,
+                                 accepted=acc, out=out)
+
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times["step"] = e0.elapsed_time(e1) / 1e3 / reps
         vb = N * H * (STATE_BYTES + K * (tok_in + d * 4))
         cb = N * H * 2 * STATE_BYTES + n_acc * H * tok_commit
         vflop = N * H * K * 7 * d * d
-        step = times["verify"] + times["commit"]
-        log(f"[bench] spec {name}: verify {times['verify'] * 1e6:.1f} us, commit "
-            f"{times['commit'] * 1e6:.1f} us, {n_acc / N:.2f} accepted/seq, "
-            f"{n_acc / step:.3e} accepted tokens/s")
+        step_s = times["step"]
+        log(f"[bench] spec {name}: fused step {step_s * 1e6:.1f} us (verify "
+            f"{times['verify'] * 1e6:.1f} us + commit {times['commit'] * 1e6:.1f} us apart), "
+            f"{n_acc / N:.2f} accepted/seq, {n_acc / step_s:.3e} accepted tokens/s")
         res[name] = {
             "mean_accepted": round(n_acc / N, 3),
-            "accepted_tokens_per_s": round(n_acc / step, 1),
-            "speedup_vs_single_token_decode": round((n_acc / step) / (N / (decode_us * 1e-6)), 3),
+            "accepted_tokens_per_s": round(n_acc / step_s, 1),
+            "speedup_vs_single_token_decode": round((n_acc / step_s) / (N / (decode_us * 1e-6)),
+                                                    3),
+            "step_us": round(step_s * 1e6, 2),
+            "step_hbm_GBps": round((cb + N * H * K * (tok_in + d * 4)) / step_s / 1e9, 1),
             "verify_us": round(times["verify"] * 1e6, 2),
             "commit_us": round(times["commit"] * 1e6, 2),
             "verify_roofline": {"bound": "alu", "achieved": round(vflop / times["verify"] / 1e12, 2),

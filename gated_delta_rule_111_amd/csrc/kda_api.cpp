@@ -411,6 +411,61 @@ kda_status kda_decode_multi(const kda_config* cfg, int32_t num_seqs, int32_t num
     return ok();
 }
 
+kda_status kda_decode_spec_step(const kda_config* cfg, int32_t num_seqs, int32_t num_tokens,
+                                const void* prev_k, const void* prev_v, const float* prev_g,
+                                const float* prev_beta, const int32_t* accepted, const void* q,
+                                const void* k, const void* v, const float* g, const float* beta,
+                                float* state, const int32_t* slots, void* out, void* stream) {
+    kda_status st = check_config(cfg);
+    if (st != KDA_OK) return st;
+    if (num_seqs < 0) return fail(KDA_ERR_INVALID_ARG, "num_seqs must be >= 0");
+    if (num_tokens < 1) return fail(KDA_ERR_INVALID_ARG, "num_tokens must be >= 1");
+    if (num_seqs == 0) return ok();
+    if ((int64_t)num_seqs * cfg->num_heads > 0x7fffffffLL)
+        return fail(KDA_ERR_UNSUPPORTED, "num_seqs * num_heads exceeds the grid limit");
+    const bool commit = accepted != nullptr;
+    const PtrCheck ptrs[] = {
+        {"prev_k", prev_k, commit, 16},       {"prev_v", prev_v, commit, 16},
+        {"prev_g", prev_g, commit, 16},       {"prev_beta", prev_beta, commit, 4},
+        {"accepted_dev", accepted, false, 4}, {"q", q, true, 16},
+        {"k", k, true, 16},                   {"v", v, true, 16},
+        {"g", g, true, 16},                   {"beta", beta, true, 4},
+        {"state", state, true, 16},           {"state_slots_dev", slots, false, 4},
+        {"out", out, true, 16},
+    };
+    st = check_ptrs(ptrs, (int)(sizeof(ptrs) / sizeof(ptrs[0])));
+    if (st != KDA_OK) return st;
+
+    kda::DecodeMultiArgs a{};
+    a.dk = cfg->dk;
+    a.dv = cfg->dv;
+    a.H = cfg->num_heads;
+    a.num_seqs = num_seqs;
+    a.num_tokens = num_tokens;
+    a.mode = commit ? 3 : 1;
+    a.in_bf16 = cfg->in_dtype == KDA_BF16;
+    a.out_bf16 = cfg->out_dtype == KDA_BF16;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.pk = prev_k;
+    a.pv = prev_v;
+    a.pg = prev_g;
+    a.pbeta = prev_beta;
+    a.state = state;
+    a.slots = slots;
+    a.counts = accepted;
+    a.out = out;
+    a.scale = effective_scale(cfg);
+    a.stream = static_cast<hipStream_t>(stream);
+    hipError_t e = kda::launch_decode_multi(a);
+    if (e != hipSuccess)
+        return fail(KDA_ERR_HIP, "speculative step launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 kda_status kda_qk_frontend(const kda_frontend_config* cfg, int32_t num_seqs,
                            const int32_t* cu_host, const int32_t* cu_dev, const void* xq,
                            const void* xk, const float* wq, const float* wk,

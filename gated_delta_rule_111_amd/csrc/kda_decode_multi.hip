@@ -8,7 +8,10 @@
 //           (the same as K chained single-token decode steps);
 //   verify  K draft tokens: K outputs, state only read;
 //   commit  the first accepted[n] of the K tokens applied to the state, no
-//           outputs.
+//           outputs;
+//   step    commit of the previous step's accepted tokens, the state written,
+//           then verify of the new K tokens from the registers: one state read
+//           and one write per speculative step.
 // "Kimi K3 technical FAQ" (Runpod guide), questions "What does it take to
 // serve K3 today?" and "What is the speculative-decoding story?": the model is
 // served with a draft proposing 7 tokens, which the target checks in one pass,
@@ -30,6 +33,8 @@
 // so the token loop reads only LDS.  The state is read once and, in apply and
 // commit, written once: HBM traffic per launch is that of one decode step,
 // whatever K is; the VALU work (4 dk dv per token) grows with K.
+#include <type_traits>
+
 #include "kda_common.h"
 #include "kda_internal.h"
 
@@ -52,6 +57,8 @@ struct MultiSmem {
 struct MultiParams {
     const void *q, *k, *v;
     const float *g, *beta;
+    const void *pk, *pv;       // spec step: the previous step's tokens to commit
+    const float *pg, *pbeta;
     float* state;
     const int32_t* slots;   // nullable (identity)
     const int32_t* counts;  // commit: accepted tokens per sequence
@@ -96,7 +103,11 @@ __device__ __forceinline__ float group_sum(float v) {
     return v;
 }
 
-template <int DK, int DV, int WAVES, typename TIn, typename TOut, bool OUT, bool WRITE>
+// MODE: 0 apply (outputs, state written), 1 verify (outputs only), 2 commit
+// (the accepted prefix, state written), 3 spec step (commit the previous
+// step's accepted tokens, write the state, then verify the new tokens from
+// the registers).
+template <int DK, int DV, int WAVES, typename TIn, typename TOut, int MODE>
 __global__ __launch_bounds__(64 * WAVES) void decode_multi_kernel(MultiParams p) {
     constexpr int NT = 64 * WAVES;
     constexpr int CW = DV / WAVES;   // columns per wave
@@ -120,8 +131,8 @@ __global__ __launch_bounds__(64 * WAVES) void decode_multi_kernel(MultiParams p)
     const int col = wave * CW + cg * 4;
     const int row0 = rg * RPL;
 
-    const int ntok = p.counts ? min(max(p.counts[n], 0), K) : K;
-    if (ntok == 0) return;  // nothing to apply or to output
+    const int ncount = p.counts ? min(max(p.counts[n], 0), K) : K;
+    if (MODE == 2 && ncount == 0) return;  // nothing to apply
 
     const int64_t slot = p.slots ? (int64_t)p.slots[n] : (int64_t)n;
     float* __restrict__ S = p.state + ((slot * H + h) * DK + row0) * (int64_t)DV + col;
@@ -129,121 +140,140 @@ __global__ __launch_bounds__(64 * WAVES) void decode_multi_kernel(MultiParams p)
 #pragma unroll
     for (int m = 0; m < RPL; ++m) s[m] = load_stream4(S + m * DV);
 
-    const TIn* __restrict__ qg = static_cast<const TIn*>(p.q);
-    const TIn* __restrict__ kg = static_cast<const TIn*>(p.k);
-    const TIn* __restrict__ vg = static_cast<const TIn*>(p.v);
     TOut* __restrict__ og = static_cast<TOut*>(p.out);
     const int64_t tok0 = (int64_t)n * K;  // first token row of this sequence
 
-    for (int j0 = 0; j0 < ntok; j0 += MT_STAGE) {
-        const int nst = min(MT_STAGE, ntok - j0);
-        if (j0 > 0) __syncthreads();  // the previous stage's LDS reads are done
-        // 8 consecutive values per thread and pass (16-byte global loads)
-        for (int idx = tid; idx < nst * (DK / 8); idx += NT) {
-            const int j = idx / (DK / 8), i8 = idx - j * (DK / 8);
-            const int64_t e = ((tok0 + j0 + j) * H + h) * DK + 8 * i8;
-            float4 lo, hi;
-            load8f(kg + e, lo, hi);
-            sm.k[j][2 * i8] = lo;
-            sm.k[j][2 * i8 + 1] = hi;
-            load8f(p.g + e, lo, hi);
-            sm.al[j][2 * i8] = exp4(lo);
-            sm.al[j][2 * i8 + 1] = exp4(hi);
-            if constexpr (OUT) {
-                load8f(qg + e, lo, hi);
-                sm.q[j][2 * i8] = lo;
-                sm.q[j][2 * i8 + 1] = hi;
+    // the first ntok tokens of one token set through the state in registers;
+    // OUT (a std::integral_constant) selects the output path
+    auto walk = [&](auto out_tag, const TIn* __restrict__ qg, const TIn* __restrict__ kg,
+                    const TIn* __restrict__ vg, const float* __restrict__ gg,
+                    const float* __restrict__ bg, int ntok) {
+        constexpr bool OUT = decltype(out_tag)::value;
+        for (int j0 = 0; j0 < ntok; j0 += MT_STAGE) {
+            const int nst = min(MT_STAGE, ntok - j0);
+            __syncthreads();  // earlier LDS reads of the stage buffers are done
+            // 8 consecutive values per thread and pass (16-byte global loads)
+            for (int idx = tid; idx < nst * (DK / 8); idx += NT) {
+                const int j = idx / (DK / 8), i8 = idx - j * (DK / 8);
+                const int64_t e = ((tok0 + j0 + j) * H + h) * DK + 8 * i8;
+                float4 lo, hi;
+                load8f(kg + e, lo, hi);
+                sm.k[j][2 * i8] = lo;
+                sm.k[j][2 * i8 + 1] = hi;
+                load8f(gg + e, lo, hi);
+                sm.al[j][2 * i8] = exp4(lo);
+                sm.al[j][2 * i8 + 1] = exp4(hi);
+                if constexpr (OUT) {
+                    load8f(qg + e, lo, hi);
+                    sm.q[j][2 * i8] = lo;
+                    sm.q[j][2 * i8 + 1] = hi;
+                }
             }
-        }
-        for (int idx = tid; idx < nst * (DV / 8); idx += NT) {
-            const int j = idx / (DV / 8), c8 = idx - j * (DV / 8);
-            float4 lo, hi;
-            load8f(vg + ((tok0 + j0 + j) * H + h) * DV + 8 * c8, lo, hi);
-            sm.v[j][2 * c8] = lo;
-            sm.v[j][2 * c8 + 1] = hi;
-        }
-        if (tid < nst) sm.beta[tid] = p.beta[(tok0 + j0 + tid) * H + h];
-        __syncthreads();
+            for (int idx = tid; idx < nst * (DV / 8); idx += NT) {
+                const int j = idx / (DV / 8), c8 = idx - j * (DV / 8);
+                float4 lo, hi;
+                load8f(vg + ((tok0 + j0 + j) * H + h) * DV + 8 * c8, lo, hi);
+                sm.v[j][2 * c8] = lo;
+                sm.v[j][2 * c8 + 1] = hi;
+            }
+            if (tid < nst) sm.beta[tid] = bg[(tok0 + j0 + tid) * H + h];
+            __syncthreads();
 
-        for (int j = 0; j < nst; ++j) {
-            float kr[RPL], ar[RPL], qr[RPL];
-            if constexpr (RPL % 4 == 0) {  // 128-bit LDS reads of the lane's rows
-#pragma unroll
-                for (int m = 0; m < RPL; m += 4) {
-                    const float4 tk = sm.k[j][(row0 + m) / 4];
-                    const float4 ta = sm.al[j][(row0 + m) / 4];
-                    kr[m] = tk.x; kr[m + 1] = tk.y; kr[m + 2] = tk.z; kr[m + 3] = tk.w;
-                    ar[m] = ta.x; ar[m + 1] = ta.y; ar[m + 2] = ta.z; ar[m + 3] = ta.w;
-                    if constexpr (OUT) {
-                        const float4 tq = sm.q[j][(row0 + m) / 4];
-                        qr[m] = tq.x; qr[m + 1] = tq.y; qr[m + 2] = tq.z; qr[m + 3] = tq.w;
+            for (int j = 0; j < nst; ++j) {
+                float kr[RPL], ar[RPL], qr[RPL];
+                if constexpr (RPL % 4 == 0) {  // 128-bit LDS reads of the lane's rows
+    #pragma unroll
+                    for (int m = 0; m < RPL; m += 4) {
+                        const float4 tk = sm.k[j][(row0 + m) / 4];
+                        const float4 ta = sm.al[j][(row0 + m) / 4];
+                        kr[m] = tk.x; kr[m + 1] = tk.y; kr[m + 2] = tk.z; kr[m + 3] = tk.w;
+                        ar[m] = ta.x; ar[m + 1] = ta.y; ar[m + 2] = ta.z; ar[m + 3] = ta.w;
+                        if constexpr (OUT) {
+                            const float4 tq = sm.q[j][(row0 + m) / 4];
+                            qr[m] = tq.x; qr[m + 1] = tq.y; qr[m + 2] = tq.z; qr[m + 3] = tq.w;
+                        }
+                    }
+                } else {  // one row per lane (dk = 16)
+                    const float* kf = reinterpret_cast<const float*>(sm.k[j]);
+                    const float* af = reinterpret_cast<const float*>(sm.al[j]);
+                    const float* qf = reinterpret_cast<const float*>(sm.q[j]);
+    #pragma unroll
+                    for (int m = 0; m < RPL; ++m) {
+                        kr[m] = kf[row0 + m];
+                        ar[m] = af[row0 + m];
+                        if constexpr (OUT) qr[m] = qf[row0 + m];
                     }
                 }
-            } else {  // one row per lane (dk = 16)
-                const float* kf = reinterpret_cast<const float*>(sm.k[j]);
-                const float* af = reinterpret_cast<const float*>(sm.al[j]);
-                const float* qf = reinterpret_cast<const float*>(sm.q[j]);
-#pragma unroll
-                for (int m = 0; m < RPL; ++m) {
-                    kr[m] = kf[row0 + m];
-                    ar[m] = af[row0 + m];
-                    if constexpr (OUT) qr[m] = qf[row0 + m];
-                }
-            }
-            const float4 vv = sm.v[j][col / 4];
-            const float bt = sm.beta[j];
+                const float4 vv = sm.v[j][col / 4];
+                const float bt = sm.beta[j];
 
-            // S' = Diag(alpha) S ; partial reductions over this lane's rows
-            float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-            float b0 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f;
-            float kq = 0.f;
-#pragma unroll
-            for (int m = 0; m < RPL; ++m) {
-                const float al = ar[m];
-                s[m].x *= al; s[m].y *= al; s[m].z *= al; s[m].w *= al;
-                a0 = fmaf(kr[m], s[m].x, a0); a1 = fmaf(kr[m], s[m].y, a1);
-                a2 = fmaf(kr[m], s[m].z, a2); a3 = fmaf(kr[m], s[m].w, a3);
-                if constexpr (OUT) {
-                    b0 = fmaf(qr[m], s[m].x, b0); b1 = fmaf(qr[m], s[m].y, b1);
-                    b2 = fmaf(qr[m], s[m].z, b2); b3 = fmaf(qr[m], s[m].w, b3);
-                    kq = fmaf(kr[m], qr[m], kq);
+                // S' = Diag(alpha) S ; partial reductions over this lane's rows
+                float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+                float b0 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f;
+                float kq = 0.f;
+    #pragma unroll
+                for (int m = 0; m < RPL; ++m) {
+                    const float al = ar[m];
+                    s[m].x *= al; s[m].y *= al; s[m].z *= al; s[m].w *= al;
+                    a0 = fmaf(kr[m], s[m].x, a0); a1 = fmaf(kr[m], s[m].y, a1);
+                    a2 = fmaf(kr[m], s[m].z, a2); a3 = fmaf(kr[m], s[m].w, a3);
+                    if constexpr (OUT) {
+                        b0 = fmaf(qr[m], s[m].x, b0); b1 = fmaf(qr[m], s[m].y, b1);
+                        b2 = fmaf(qr[m], s[m].z, b2); b3 = fmaf(qr[m], s[m].w, b3);
+                        kq = fmaf(kr[m], qr[m], kq);
+                    }
                 }
-            }
-            // sums over the RG row groups (RG consecutive lanes)
-            a0 = group_sum<RG>(a0); a1 = group_sum<RG>(a1);
-            a2 = group_sum<RG>(a2); a3 = group_sum<RG>(a3);
-            if constexpr (OUT) {
-                b0 = group_sum<RG>(b0); b1 = group_sum<RG>(b1);
-                b2 = group_sum<RG>(b2); b3 = group_sum<RG>(b3);
-                kq = group_sum<RG>(kq);
-            }
-            const float u0 = bt * (vv.x - a0), u1 = bt * (vv.y - a1);
-            const float u2 = bt * (vv.z - a2), u3 = bt * (vv.w - a3);
-            // S = S' + k u^T (kept in registers)
-#pragma unroll
-            for (int m = 0; m < RPL; ++m) {
-                s[m].x = fmaf(kr[m], u0, s[m].x); s[m].y = fmaf(kr[m], u1, s[m].y);
-                s[m].z = fmaf(kr[m], u2, s[m].z); s[m].w = fmaf(kr[m], u3, s[m].w);
-            }
-            if constexpr (OUT) {
-                if (rg == 0) {
-                    const float sc = p.scale;
-                    io<TOut>::store4(og + ((tok0 + j0 + j) * H + h) * DV + col,
-                                     sc * fmaf(kq, u0, b0), sc * fmaf(kq, u1, b1),
-                                     sc * fmaf(kq, u2, b2), sc * fmaf(kq, u3, b3));
+                // sums over the RG row groups (RG consecutive lanes)
+                a0 = group_sum<RG>(a0); a1 = group_sum<RG>(a1);
+                a2 = group_sum<RG>(a2); a3 = group_sum<RG>(a3);
+                if constexpr (OUT) {
+                    b0 = group_sum<RG>(b0); b1 = group_sum<RG>(b1);
+                    b2 = group_sum<RG>(b2); b3 = group_sum<RG>(b3);
+                    kq = group_sum<RG>(kq);
+                }
+                const float u0 = bt * (vv.x - a0), u1 = bt * (vv.y - a1);
+                const float u2 = bt * (vv.z - a2), u3 = bt * (vv.w - a3);
+                // S = S' + k u^T (kept in registers)
+    #pragma unroll
+                for (int m = 0; m < RPL; ++m) {
+                    s[m].x = fmaf(kr[m], u0, s[m].x); s[m].y = fmaf(kr[m], u1, s[m].y);
+                    s[m].z = fmaf(kr[m], u2, s[m].z); s[m].w = fmaf(kr[m], u3, s[m].w);
+                }
+                if constexpr (OUT) {
+                    if (rg == 0) {
+                        const float sc = p.scale;
+                        io<TOut>::store4(og + ((tok0 + j0 + j) * H + h) * DV + col,
+                                         sc * fmaf(kq, u0, b0), sc * fmaf(kq, u1, b1),
+                                         sc * fmaf(kq, u2, b2), sc * fmaf(kq, u3, b3));
+                    }
                 }
             }
         }
-    }
-    if constexpr (WRITE) {
+    };
+
+    const TIn* q = static_cast<const TIn*>(p.q);
+    const TIn* k = static_cast<const TIn*>(p.k);
+    const TIn* v = static_cast<const TIn*>(p.v);
+    if constexpr (MODE == 3) {
+        if (ncount > 0) {
+            walk(std::integral_constant<bool, false>{}, nullptr, static_cast<const TIn*>(p.pk),
+                 static_cast<const TIn*>(p.pv), p.pg, p.pbeta, ncount);
 #pragma unroll
-        for (int m = 0; m < RPL; ++m) store_stream4(S + m * DV, s[m]);
+            for (int m = 0; m < RPL; ++m) store_stream4(S + m * DV, s[m]);
+        }
+        walk(std::integral_constant<bool, true>{}, q, k, v, p.g, p.beta, K);
+    } else {
+        walk(std::integral_constant<bool, MODE != 2>{}, q, k, v, p.g, p.beta, ncount);
+        if constexpr (MODE == 0 || MODE == 2) {
+#pragma unroll
+            for (int m = 0; m < RPL; ++m) store_stream4(S + m * DV, s[m]);
+        }
     }
 }
 
-template <int DK, int WAVES, typename TIn, typename TOut, bool OUT, bool WRITE>
+template <int DK, int WAVES, typename TIn, typename TOut, int MODE>
 hipError_t launch_m(const MultiParams& p, int num_seqs, hipStream_t stream) {
-    hipLaunchKernelGGL((decode_multi_kernel<DK, DK, WAVES, TIn, TOut, OUT, WRITE>),
+    hipLaunchKernelGGL((decode_multi_kernel<DK, DK, WAVES, TIn, TOut, MODE>),
                        dim3((unsigned)((int64_t)num_seqs * p.H)), dim3(64 * WAVES), 0, stream, p);
     return hipGetLastError();
 }
@@ -251,9 +281,10 @@ hipError_t launch_m(const MultiParams& p, int num_seqs, hipStream_t stream) {
 template <int DK, int WAVES, typename TIn, typename TOut>
 hipError_t launch_mode(const MultiParams& p, int num_seqs, int mode, hipStream_t stream) {
     switch (mode) {
-        case 0: return launch_m<DK, WAVES, TIn, TOut, true, true>(p, num_seqs, stream);
-        case 1: return launch_m<DK, WAVES, TIn, TOut, true, false>(p, num_seqs, stream);
-        case 2: return launch_m<DK, WAVES, TIn, TOut, false, true>(p, num_seqs, stream);
+        case 0: return launch_m<DK, WAVES, TIn, TOut, 0>(p, num_seqs, stream);
+        case 1: return launch_m<DK, WAVES, TIn, TOut, 1>(p, num_seqs, stream);
+        case 2: return launch_m<DK, WAVES, TIn, TOut, 2>(p, num_seqs, stream);
+        case 3: return launch_m<DK, WAVES, TIn, TOut, 3>(p, num_seqs, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -276,6 +307,10 @@ hipError_t launch_decode_multi(const DecodeMultiArgs& a) {
     p.v = a.v;
     p.g = a.g;
     p.beta = a.beta;
+    p.pk = a.pk;
+    p.pv = a.pv;
+    p.pg = a.pg;
+    p.pbeta = a.pbeta;
     p.state = a.state;
     p.slots = a.slots;
     p.counts = a.counts;

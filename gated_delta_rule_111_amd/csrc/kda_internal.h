@@ -61,13 +61,15 @@ struct FrontendArgs {
 
 struct DecodeMultiArgs {
     int dk, dv, H, num_seqs, num_tokens;
-    int mode;                     // 0 apply, 1 verify, 2 commit
+    int mode;                     // 0 apply, 1 verify, 2 commit, 3 commit then verify
     bool in_bf16, out_bf16;
     const void *q, *k, *v;        // [num_seqs, num_tokens, H, d]
     const float *g, *beta;
+    const void *pk, *pv;          // mode 3: the previous step's tokens (same layout)
+    const float *pg, *pbeta;
     float* state;
     const int32_t* slots;         // nullable (identity)
-    const int32_t* counts;        // commit: accepted tokens per sequence
+    const int32_t* counts;        // commit, step: accepted tokens per sequence
     void* out;                    // [num_seqs, num_tokens, H, dv]; unused in commit
     float scale;
     hipStream_t stream;

@@ -78,6 +78,9 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_snapshot_count_at.argtypes = [P, P, i32, i32]
     lib.kda_prefill_pool_workspace_size.restype = sz
     lib.kda_prefill_pool_workspace_size.argtypes = [CP, i32, i64]
+    lib.kda_decode_spec_step.restype = ctypes.c_int
+    lib.kda_decode_spec_step.argtypes = [CP, i32, i32, P, P, P, P, P, P, P, P, P, P, P, P, P,
+                                         P]
     lib.kda_decode_multi.restype = ctypes.c_int
     lib.kda_decode_multi.argtypes = [CP, i32, i32, ctypes.c_int, P, P, P, P, P, P, P, P, P, P]
     lib.kda_qk_frontend.restype = ctypes.c_int
@@ -491,3 +494,54 @@ def attnres(sources: Sequence[torch.Tensor], query: torch.Tensor,
     _check(lib.kda_attnres(ctypes.byref(cfg), T, ptrs, _ptr(residual), query.data_ptr(),
                            _ptr(gamma), _ptr(h_out), y_out.data_ptr(), _stream(stream)))
     return h_out, y_out
+
+
+def decode_spec_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                     beta: torch.Tensor, state: torch.Tensor,
+                     prev: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor,
+                                          torch.Tensor]] = None,
+                     accepted: Optional[torch.Tensor] = None,
+                     slots: Optional[torch.Tensor] = None,
+                     out_dtype: Optional[torch.dtype] = None, scale: float = 0.0,
+                     out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """kda_decode_spec_step: commit accepted[n] tokens of the previous step
+    (prev = (k, v, g, beta) of that step, [N, K, H, d] etc.) to each state,
+    then verify the new draft q, k, v, g, beta [N, K, H, d]; returns its
+    outputs [N, K, H, dv].  accepted None: nothing to commit."""
+    lib = load()
+    dev = k.device
+    N, K, H, dk = k.shape
+    dv = v.shape[3]
+    checks = [("q", q, (N, K, H, dk), k.dtype), ("k", k, (N, K, H, dk), k.dtype),
+              ("v", v, (N, K, H, dv), k.dtype), ("g", g, (N, K, H, dk), torch.float32),
+              ("beta", beta, (N, K, H), torch.float32)]
+    if accepted is not None:
+        if prev is None:
+            raise ValueError("accepted needs the previous step's (k, v, g, beta)")
+        pk, pv, pg, pb = prev
+        checks += [("prev_k", pk, (N, K, H, dk), k.dtype), ("prev_v", pv, (N, K, H, dv), k.dtype),
+                   ("prev_g", pg, (N, K, H, dk), torch.float32),
+                   ("prev_beta", pb, (N, K, H), torch.float32)]
+        _need(accepted, "accepted", (N,), torch.int32, dev)
+    else:
+        pk = pv = pg = pb = None
+    for name, t, shp, dt in checks:
+        _need(t, name, shp, dt, dev)
+    if state.dim() != 4 or tuple(state.shape[1:]) != (H, dk, dv):
+        raise ValueError(f"state: shape {tuple(state.shape)} != [S, {H}, {dk}, {dv}]")
+    _need(state, "state", tuple(state.shape), torch.float32, dev)
+    if slots is None and state.shape[0] < N:
+        raise ValueError("state has fewer rows than sequences")
+    if slots is not None:
+        _need(slots, "slots", (N,), torch.int32, dev)
+    if out_dtype is None:
+        out_dtype = out.dtype if out is not None else torch.float32
+    cfg = config(H, dk, dv, k.dtype, out_dtype, scale)
+    if out is None:
+        out = torch.empty(N, K, H, dv, dtype=out_dtype, device=dev)
+    _need(out, "out", (N, K, H, dv), out_dtype, dev)
+    _check(lib.kda_decode_spec_step(ctypes.byref(cfg), N, K, _ptr(pk), _ptr(pv), _ptr(pg),
+                                    _ptr(pb), _ptr(accepted), q.data_ptr(), k.data_ptr(),
+                                    v.data_ptr(), g.data_ptr(), beta.data_ptr(), state.data_ptr(),
+                                    _ptr(slots), out.data_ptr(), _stream(stream)))
+    return out

@@ -274,6 +274,33 @@ kda_status kda_decode_multi(const kda_config *cfg, int32_t num_seqs,
                             void *stream);
 
 /*
+ * One speculative decoding step in one launch: the previous step's accepted
+ * tokens are committed to each state (written back), then the new draft of
+ * num_tokens tokens is verified from the committed state (outputs only).
+ * The same result as KDA_MULTI_COMMIT on the previous tokens followed by
+ * KDA_MULTI_VERIFY on the new ones, bit for bit, with one read and one write
+ * of each state instead of two reads and a write.
+ *   prev_k, prev_v : [num_seqs, num_tokens, H, d] in_dtype, prev_g fp32,
+ *   prev_beta [num_seqs, num_tokens, H] fp32: the previous step's tokens
+ *   accepted_dev   : [num_seqs] int32, tokens of the previous step to commit
+ *                    (clamped to [0, num_tokens]); NULL = nothing to commit
+ *                    (the first step), and the prev_* arrays are ignored
+ *   q, k, v, g, beta, out : the new draft and its outputs, as in
+ *                    kda_decode_multi
+ *   state, state_slots_dev: as in kda_decode_multi (written)
+ * Errors as for kda_decode_multi.  num_seqs == 0 is a no-op.
+ */
+kda_status kda_decode_spec_step(const kda_config *cfg, int32_t num_seqs,
+                                int32_t num_tokens, const void *prev_k,
+                                const void *prev_v, const float *prev_g,
+                                const float *prev_beta,
+                                const int32_t *accepted_dev, const void *q,
+                                const void *k, const void *v, const float *g,
+                                const float *beta, float *state,
+                                const int32_t *state_slots_dev, void *out,
+                                void *stream);
+
+/*
  * Front end of q and k: short convolution -> Swish -> L2 normalisation.
  *
  * "Kimi K3 technical FAQ" (Runpod guide), question "What is KDA, and why

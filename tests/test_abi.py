@@ -33,7 +33,8 @@ def test_header_declares_the_calls():
                      "kda_prefill_workspace_size", "kda_status_string",
                      "kda_last_error_detail", "kda_version", "kda_qk_frontend",
                      "kda_decode_multi", "kda_prefill_pool", "kda_snapshot_count_at",
-                     "kda_prefill_pool_workspace_size", "kda_attnres"):
+                     "kda_prefill_pool_workspace_size", "kda_attnres",
+                     "kda_decode_spec_step"):
         assert required in names
 
 
@@ -274,3 +275,19 @@ def test_attnres_rejects_bad_arguments(lib):
     assert call(srcs=bad) == 1
     assert call(y=A) == 1                     # output over a source
     assert call(T=0, srcs=None) == 0
+
+
+def test_spec_step_rejects_bad_arguments(lib):
+    cfg = _cfg()
+    p = ctypes.byref(cfg)
+    f = lib.kda_decode_spec_step
+    # prev k, v, g, beta, accepted, q, k, v, g, beta, state, slots, out, stream; every call
+    # here fails validation (nothing is launched)
+    args = [A, A, A, A, A, A, A, A, A, A, A, None, A, None]
+    assert f(p, 4, 0, *args) == 1                              # num_tokens
+    bad = list(args)
+    bad[0] = None                                              # prev_k needed with accepted
+    assert f(p, 4, 8, *bad) == 1
+    # first step (nothing to commit): the prev arrays may be NULL, q is checked
+    assert f(p, 4, 8, *[None] * 5, MIS, A, A, A, A, A, None, A, None) == 3
+    assert f(p, 0, 8, *[None] * 14) == 0

@@ -164,3 +164,70 @@ def test_multi_full_size():
     es = state_err(to_np(state[seqs]), ref_s)
     print(f"[multi full] verify err {eo:.2e} commit err {es:.2e}", flush=True)
     assert eo <= TOL and es <= TOL
+
+
+def test_spec_step_equals_commit_then_verify():
+    """The fused step (commit the previous step's accepted tokens, verify the
+    new draft) gives the commit-then-verify results bit for bit."""
+    from gated_delta_rule_111_amd import kda
+    from gated_delta_rule_111_amd.inputs import accepted_counts, multi_token_inputs
+    print("[spec step fused]", flush=True)
+    N, K, H, d = 12, 8, 4, 128
+    s_fused = torch.randn(N + 3, H, d, d, device=DEV) * 0.05
+    s_split = s_fused.clone()
+    slots = torch.tensor(np.random.default_rng(2).permutation(N + 3)[:N].astype(np.int32),
+                         device=DEV)
+    prev, acc = None, None
+    for step in range(4):
+        inp = multi_token_inputs(N, K, H, d, d, seed=700 + step, device=DEV)
+        of = kda.decode_spec_step(inp.q, inp.k, inp.v, inp.g, inp.beta, s_fused,
+                                  prev=prev, accepted=acc, slots=slots)
+        if acc is not None:
+            kda.decode_multi(None, prev[0], prev[1], prev[2], prev[3], s_split, mode="commit",
+                             accepted=acc, slots=slots)
+        osp = kda.decode_multi(inp.q, inp.k, inp.v, inp.g, inp.beta, s_split, mode="verify",
+                               slots=slots)
+        torch.cuda.synchronize()
+        assert torch.equal(of, osp), f"step {step}: outputs differ"
+        assert torch.equal(s_fused, s_split), f"step {step}: states differ"
+        prev = (inp.k, inp.v, inp.g, inp.beta)
+        acc = accepted_counts(N, K, 2.61 if step % 2 else 4.73, seed=800 + step, device=DEV)
+        if step == 2:
+            acc[0] = 0  # nothing accepted for one sequence
+            acc[1] = K
+
+
+def test_spec_step_chain_matches_oracle():
+    """Five fused steps and a last commit: the accepted outputs and final
+    states equal the oracle run over each sequence's accepted tokens."""
+    from gated_delta_rule_111_amd import kda
+    from gated_delta_rule_111_amd.inputs import accepted_counts, multi_token_inputs
+    import oracle
+    print("[spec step chain]", flush=True)
+    N, K, H, d, steps = 10, 8, 4, 128, 5
+    state = torch.randn(N, H, d, d, device=DEV) * 0.02
+    state0 = state.clone()
+    prev, acc, streams = None, None, []
+    for s in range(steps):
+        inp = multi_token_inputs(N, K, H, d, d, seed=900 + s, device=DEV)
+        out = kda.decode_spec_step(inp.q, inp.k, inp.v, inp.g, inp.beta, state, prev=prev,
+                                   accepted=acc)
+        acc = accepted_counts(N, K, 4.73, seed=950 + s, device=DEV)
+        prev = (inp.k, inp.v, inp.g, inp.beta)
+        streams.append((inp, to_np(acc), out))
+    kda.decode_multi(None, *prev, state, mode="commit", accepted=acc)
+    torch.cuda.synchronize()
+    for n in (0, 4, 9):
+        toks = {key: [] for key in ("q", "k", "v", "g", "beta")}
+        outs = []
+        for inp, a_np, out in streams:
+            a = int(a_np[n])
+            for key in toks:
+                toks[key].append(to_np(getattr(inp, key)[n, :a]))
+            outs.append(to_np(out[n, :a]))
+        cat = {key: np.concatenate(v) for key, v in toks.items()}
+        L = len(cat["k"])
+        o, fin, _ = oracle.prefill(cat["q"], cat["k"], cat["v"], cat["g"], cat["beta"], [0, L],
+                                   initial_state=to_np(state0[n:n + 1]).astype(np.float64))
+        assert slice_rel_err(np.concatenate(outs), o, slice_axes=(1,)) <= TOL, f"outputs of {n}"
+        assert state_err(to_np(state[n:n + 1]), fin) <= TOL, f"state of {n}"
