@@ -194,6 +194,16 @@ def bench_prefill(torch, kda, inputs, w, reps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per_call = e0.elapsed_time(e1) / 1e3 / reps
+    # each call on its own between events as well: median and minimum
+    singles = []
+    for _ in range(reps):
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        call()
+        a1.record(stream)
+        torch.cuda.synchronize()
+        singles.append(a0.elapsed_time(a1))
+    singles.sort()
     th = T * w.H
     nbytes = th * PREFILL_BYTES_PER_TOKEN_HEAD + (nsnap + N) * w.H * STATE_BYTES
     if inp.initial_state is not None:
@@ -209,6 +219,8 @@ def bench_prefill(torch, kda, inputs, w, reps, warmup):
         "unit": "tokens/s",
         "ms_per_call": round(wall * 1e3 / reps, 4),
         "kernel_ms": round(per_call * 1e3, 4),
+        "kernel_ms_median": round(singles[len(singles) // 2], 4),
+        "kernel_ms_min": round(singles[0], 4),
         "reps": reps,
         "dtype": "bf16 MFMA (hi/lo split operands) + f32 state",
         "roofline": {
@@ -531,9 +543,29 @@ def cpu_frontend_baseline(inputs, tokens: int):
 
 
 # ---------------------------------------------------------------------------
+def gemm_ceiling(torch, n: int = 8192):
+    """bf16 GEMM (torch.matmul, n x n x n) timed with HIP events: the
+    practical dense bf16 MFMA ceiling beside the 2.5 PFLOP/s vendor peak."""
+    a = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda:0", dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(10):
+        torch.matmul(a, b)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    sec = e0.elapsed_time(e1) / 1e3 / 10
+    return round(2 * n ** 3 / sec / 1e12, 1)
+
+
 def copy_calibration(torch, mib: int):
     """A plain device copy and an in-place scale of `mib` MiB, timed with HIP
-    events: the practical read+write bandwidth ceiling for the decode step."""
+    events: the practical read+write bandwidth ceiling for the decode step;
+    and a bf16 GEMM for the MFMA ceiling."""
     n = mib * (1 << 20) // 4
     src = torch.ones(n, dtype=torch.float32, device="cuda:0")
     dst = torch.empty_like(src)
@@ -550,6 +582,7 @@ def copy_calibration(torch, mib: int):
         torch.cuda.synchronize()
         sec = e0.elapsed_time(e1) / 1e3 / 10
         res[name + "_GBps"] = round(2 * n * 4 / sec / 1e9, 1)
+    res["bf16_gemm_8192_TFLOPs"] = gemm_ceiling(torch)
     print(json.dumps(res), flush=True)
 
 
@@ -560,6 +593,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--prefill-reps", type=int, default=20)
     ap.add_argument("--long", action="store_true", help="also time the 1,048,576-token prefill")
+    ap.add_argument("--varlen", action="store_true",
+                    help="also time the 16-sequence varlen prefill (lengths 1024..32768)")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-frontend", action="store_true")
     ap.add_argument("--no-spec", action="store_true")
@@ -602,6 +637,9 @@ def main():
                                   max(2, args.warmup // 10))
     if args.long:
         pre_long, _ = bench_prefill(torch, kda, inputs, inputs.LONG, 3, 1)
+    pre_var = None
+    if args.varlen:
+        pre_var, _ = bench_prefill(torch, kda, inputs, inputs.varlen_workload(), 5, 2)
     pool = None
     if not args.no_prefill and not args.no_pool:
         pool = bench_prefill_pool(torch, kda, inputs, args.prefill_reps, 2)
@@ -648,6 +686,8 @@ def main():
     }
     if pre_long is not None:
         line["prefill_long"] = pre_long
+    if pre_var is not None:
+        line["prefill_varlen"] = pre_var
     if fe is not None:
         line["qk_frontend"] = fe
     if spec is not None:

@@ -290,18 +290,15 @@ void attnres_kernel(ArParams p, int64_t T) {
     }
 }
 
+// compute units of the current device (asked on every launch: the library
+// keeps no state between calls)
 int compute_units() {
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0, n = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-            n > 0)
-            cus = n;
-        else
-            cus = 256;
-    }
-    return cus;
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        n > 0)
+        return n;
+    return 256;
 }
 
 template <int M, typename TIn, typename TOut>
