@@ -157,10 +157,12 @@ __device__ __forceinline__ void widen(const Raw8<float>& r, float (&v)[8]) {
     v[4] = r.b.x; v[5] = r.b.y; v[6] = r.b.z; v[7] = r.b.w;
 }
 
-template <int W, typename TIn, typename TOut>
+// G: tokens per group of loads (8; 1 for one-token sequences, where a run
+// holds a token or a few and the registers of larger groups would only
+// lower the occupancy)
+template <int W, int G, typename TIn, typename TOut>
 __global__ __launch_bounds__(64 * FE_WAVES) void frontend_kernel(FeParams p) {
     constexpr int NW = W > 1 ? W - 1 : 1;  // window rows (unused when W == 1)
-    constexpr int G = 8;                    // tokens per group of loads
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
@@ -390,8 +392,12 @@ __global__ __launch_bounds__(64 * FE_WAVES) void frontend_kernel(FeParams p) {
 
 template <int W, typename TIn, typename TOut>
 hipError_t launch_w(const FeParams& p, hipStream_t stream) {
-    hipLaunchKernelGGL((frontend_kernel<W, TIn, TOut>), dim3(p.nwg), dim3(64 * FE_WAVES), 0,
-                       stream, p);
+    if (p.unit)
+        hipLaunchKernelGGL((frontend_kernel<W, 1, TIn, TOut>), dim3(p.nwg), dim3(64 * FE_WAVES),
+                           0, stream, p);
+    else
+        hipLaunchKernelGGL((frontend_kernel<W, 8, TIn, TOut>), dim3(p.nwg), dim3(64 * FE_WAVES),
+                           0, stream, p);
     return hipGetLastError();
 }
 
