@@ -34,7 +34,6 @@ if ROOT not in sys.path:
 METRIC = "KDA prefill tokens/s + decode seq-steps/s; % of MFMA / HBM roofline, 1 GPU"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
-FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector (packed FMA), TFLOP/s
 
 # Algorithmic work per unit (the bytes a kernel must move and the flops the
 # chunked method must do, independent of how the kernels are written).
@@ -57,6 +56,7 @@ KERNEL_SOURCES = {
     "prefill": os.path.join(ROOT, "gated_delta_rule_111_amd", "csrc", "kda_prefill.hip"),
     "frontend": os.path.join(ROOT, "gated_delta_rule_111_amd", "csrc", "kda_frontend.hip"),
     "multi": os.path.join(ROOT, "gated_delta_rule_111_amd", "csrc", "kda_decode_multi.hip"),
+    "spec": os.path.join(ROOT, "gated_delta_rule_111_amd", "csrc", "kda_spec.hip"),
     "attnres": os.path.join(ROOT, "gated_delta_rule_111_amd", "csrc", "kda_attnres.hip"),
 }
 
@@ -441,12 +441,13 @@ def bench_spec(torch, kda, inputs, reps, decode_us):
     """Speculative decoding step on the decode shape (256 sequences x 32
     heads, d = 128, fp32 states): the fused step (commit the previous step's
     accepted prefix, 1 + Binomial(7, p) with mean 4.73 or 2.61, then verify
-    1 + 7 new tokens), and verify and commit as separate launches.  Algorithmic
-    bytes: verify reads each state once (64 KiB per sequence-head) plus the
-    8 tokens' inputs (q, k, v bf16, g fp32, beta) and writes their fp32
+    1 + 7 new tokens), and verify and commit as separate launches; drafts of
+    8 tokens take the chunked kernel (spec_kernel).  Algorithmic bytes:
+    verify reads each state once (64 KiB per sequence-head) plus the 8
+    tokens' inputs (q, k, v bf16, g fp32, beta) and writes their fp32
     outputs; commit reads and writes each state once plus the accepted
-    tokens' k, v, g, beta.  Work: 7 dk dv flop per token and head for the
-    token-by-token update (decay, two reductions, rank-1 update)."""
+    tokens' k, v, g, beta; the step is the commit's bytes plus the verify's
+    token inputs and outputs.  All three are bound by those bytes."""
     dev = "cuda:0"
     N, H, d, K = 256, 32, 128, inputs.SPEC_TOKENS
     inp = inputs.multi_token_inputs(N, K, H, d, d, seed=11, device=dev)
@@ -497,7 +498,7 @@ def bench_spec(torch, kda, inputs, reps, decode_us):
         times["step"] = e0.elapsed_time(e1) / 1e3 / reps
         vb = N * H * (STATE_BYTES + K * (tok_in + d * 4))
         cb = N * H * 2 * STATE_BYTES + n_acc * H * tok_commit
-        vflop = N * H * K * 7 * d * d
+        sb = cb + N * H * K * (tok_in + d * 4)
         step_s = times["step"]
         log(f"[bench] spec {name}: fused step {step_s * 1e6:.1f} us (verify "
             f"{times['verify'] * 1e6:.1f} us + commit {times['commit'] * 1e6:.1f} us apart), "
@@ -508,21 +509,23 @@ def bench_spec(torch, kda, inputs, reps, decode_us):
             "speedup_vs_single_token_decode": round((n_acc / step_s) / (N / (decode_us * 1e-6)),
                                                     3),
             "step_us": round(step_s * 1e6, 2),
-            "step_hbm_GBps": round((cb + N * H * K * (tok_in + d * 4)) / step_s / 1e9, 1),
             "verify_us": round(times["verify"] * 1e6, 2),
             "commit_us": round(times["commit"] * 1e6, 2),
-            "verify_roofline": {"bound": "alu", "achieved": round(vflop / times["verify"] / 1e12, 2),
-                                "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                "frac": round(vflop / times["verify"] / 1e12 / FP32_VECTOR_PEAK_TFLOPS, 4),
-                                "hbm_GBps": round(vb / times["verify"] / 1e9, 1),
-                                "traffic": measured_traffic("multi", "verify-N256-H32-d128-K8"),
-                                "kernel": "decode_multi_kernel<verify>", "flop_per_launch": vflop,
-                                "bytes_per_launch": vb},
+            "verify_roofline": {"bound": "hbm", "achieved": round(vb / times["verify"] / 1e9, 1),
+                                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": round(vb / times["verify"] / 1e9 / HBM_PEAK_GBS, 4),
+                                "traffic": measured_traffic("spec", "verify-N256-H32-d128-K8"),
+                                "kernel": "spec_kernel<verify>", "bytes_per_launch": vb},
             "commit_roofline": {"bound": "hbm", "achieved": round(cb / times["commit"] / 1e9, 1),
                                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                 "frac": round(cb / times["commit"] / 1e9 / HBM_PEAK_GBS, 4),
-                                "traffic": measured_traffic("multi", f"commit-{name}"),
-                                "kernel": "decode_multi_kernel<commit>", "bytes_per_launch": cb},
+                                "traffic": measured_traffic("spec", f"commit-{name}"),
+                                "kernel": "spec_kernel<commit>", "bytes_per_launch": cb},
+            "step_roofline": {"bound": "hbm", "achieved": round(sb / step_s / 1e9, 1),
+                              "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": round(sb / step_s / 1e9 / HBM_PEAK_GBS, 4),
+                              "traffic": measured_traffic("spec", f"step-{name}"),
+                              "kernel": "spec_kernel<step>", "bytes_per_launch": sb},
         }
     return res
 

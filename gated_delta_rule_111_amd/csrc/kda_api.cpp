@@ -405,7 +405,7 @@ kda_status kda_decode_multi(const kda_config* cfg, int32_t num_seqs, int32_t num
     a.out = outputs ? out : nullptr;
     a.scale = effective_scale(cfg);
     a.stream = static_cast<hipStream_t>(stream);
-    hipError_t e = kda::launch_decode_multi(a);
+    hipError_t e = kda::spec_chunked(a) ? kda::launch_spec(a) : kda::launch_decode_multi(a);
     if (e != hipSuccess)
         return fail(KDA_ERR_HIP, "multi-token decode launch failed: %s", hipGetErrorString(e));
     return ok();
@@ -460,7 +460,7 @@ kda_status kda_decode_spec_step(const kda_config* cfg, int32_t num_seqs, int32_t
     a.out = out;
     a.scale = effective_scale(cfg);
     a.stream = static_cast<hipStream_t>(stream);
-    hipError_t e = kda::launch_decode_multi(a);
+    hipError_t e = kda::spec_chunked(a) ? kda::launch_spec(a) : kda::launch_decode_multi(a);
     if (e != hipSuccess)
         return fail(KDA_ERR_HIP, "speculative step launch failed: %s", hipGetErrorString(e));
     return ok();

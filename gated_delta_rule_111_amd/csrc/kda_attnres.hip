@@ -123,24 +123,6 @@ __device__ __forceinline__ void store_row(float* p, const float (&v)[EPT]) {
         reinterpret_cast<float4*>(p)[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
 }
 
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-    return __builtin_bit_cast(
-        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
-}
-
-// sum over the 64 lanes of a wave, left in every lane: DPP inside each
-// 16-lane row, then the rows by lane permutes
-__device__ __forceinline__ float wave_sum(float v) {
-    v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
-    v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
-    v += dpp<0x141>(v);  // row_half_mirror
-    v += dpp<0x128>(v);  // row_ror 8
-    v += __shfl_xor(v, 16, 64);
-    v += __shfl_xor(v, 32, 64);
-    return v;
-}
-
 template <int M, typename TIn, typename TOut>
 __global__ __launch_bounds__(ar_max_threads(M, sizeof(TIn) == 2))
 void attnres_kernel(ArParams p, int64_t T) {

@@ -67,42 +67,6 @@ struct MultiParams {
     float scale;
 };
 
-// 8 consecutive input values as fp32 (one 16-byte load for bf16, two for fp32)
-__device__ __forceinline__ void load8f(const bf16_t* p, float4& lo, float4& hi) {
-    const uint4 t = *reinterpret_cast<const uint4*>(p);
-    lo = make_float4(bf16_bits_to_f32(t.x & 0xffffu), bf16_bits_to_f32(t.x >> 16),
-                     bf16_bits_to_f32(t.y & 0xffffu), bf16_bits_to_f32(t.y >> 16));
-    hi = make_float4(bf16_bits_to_f32(t.z & 0xffffu), bf16_bits_to_f32(t.z >> 16),
-                     bf16_bits_to_f32(t.w & 0xffffu), bf16_bits_to_f32(t.w >> 16));
-}
-__device__ __forceinline__ void load8f(const float* p, float4& lo, float4& hi) {
-    lo = reinterpret_cast<const float4*>(p)[0];
-    hi = reinterpret_cast<const float4*>(p)[1];
-}
-__device__ __forceinline__ float4 exp4(const float4& g) {
-    return make_float4(exp_gate(g.x), exp_gate(g.y), exp_gate(g.z), exp_gate(g.w));
-}
-
-// v from another lane of the same 16-lane row (DPP)
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-    return __builtin_bit_cast(
-        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
-}
-
-// sum over aligned groups of N consecutive lanes (N = 8 or 16), left in
-// every lane of the group: quad permutations for lane ^ 1 and lane ^ 2, the
-// half-row mirror for the other quad of 8, a row rotation by 8 for 16
-template <int N>
-__device__ __forceinline__ float group_sum(float v) {
-    static_assert(N == 8 || N == 16, "row groups per wave");
-    v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
-    v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
-    v += dpp<0x141>(v);  // row_half_mirror
-    if constexpr (N == 16) v += dpp<0x128>(v);  // row_ror 8
-    return v;
-}
-
 // MODE: 0 apply (outputs, state written), 1 verify (outputs only), 2 commit
 // (the accepted prefix, state written), 3 spec step (commit the previous
 // step's accepted tokens, write the state, then verify the new tokens from

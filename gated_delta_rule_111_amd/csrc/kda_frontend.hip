@@ -95,13 +95,6 @@ __device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
     reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
 
-// v from another lane of the same 16-lane row (DPP: no LDS round trip)
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-    return __builtin_bit_cast(
-        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
-}
-
 // sum over the `lanes` consecutive lanes of one head (2, 4, 8 or 16), left
 // in every one of them: pairs and quads by quad permutations, 8 lanes by
 // mirroring the half row, 16 lanes by rotating the row by 4 and then by 8

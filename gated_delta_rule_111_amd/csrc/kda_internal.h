@@ -91,6 +91,10 @@ hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_attnres(const AttnResArgs& a);
 int attnres_max_hidden(int num_sources, bool in_bf16);
 hipError_t launch_decode_multi(const DecodeMultiArgs& a);
+// verify, commit and step with at most 8 tokens per sequence take the
+// chunked form (launch_spec); apply and longer drafts walk the tokens
+bool spec_chunked(const DecodeMultiArgs& a);
+hipError_t launch_spec(const DecodeMultiArgs& a);
 hipError_t launch_frontend(const FrontendArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);
 size_t prefill_workspace_bytes(int dk, int dv, int H, int num_seqs, int64_t total_tokens,
