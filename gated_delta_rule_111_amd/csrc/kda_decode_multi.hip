@@ -22,6 +22,10 @@
 // path: the resident state never moves past the tokens that were accepted,
 // and no per-position state is stored.
 //
+// This kernel serves apply, and verify, commit and step with more than 8
+// tokens per sequence; drafts of at most 8 tokens take the chunked kernel of
+// kda_spec.hip (fewer vector instructions per state element and token).
+//
 // Design: the single-token decode kernel's decomposition (one workgroup per
 // (sequence, head); wave w owns dv/WAVES columns, a lane 4 columns and dk/RG
 // rows; reductions over rows are per-lane sums and then sums over the row

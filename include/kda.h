@@ -242,7 +242,10 @@ kda_status kda_decode(const kda_config *cfg, int32_t num_seqs, const void *q,
  * VERIFY then COMMIT is a roll-back path: a state never moves past the
  * accepted tokens, and no per-position state is kept.  Each launch reads
  * each state once (and writes it once in APPLY and COMMIT), whatever
- * num_tokens is.
+ * num_tokens is.  APPLY is bit-identical to chained kda_decode calls;
+ * VERIFY and COMMIT with num_tokens <= 8 use the chunked form of the
+ * recurrence (one short chunk), whose results differ from the token-by-token
+ * ones only by rounding order.
  */
 typedef enum {
     KDA_MULTI_APPLY = 0,
