@@ -121,17 +121,66 @@ __device__ __forceinline__ void split8(const float (&x)[8], uint4& hi, uint4& lo
 
 __device__ __forceinline__ bf16x8_t as_op(const uint4& u) { return __builtin_bit_cast(bf16x8_t, u); }
 
-// Two accumulator tiles (row blocks 0 and 1 of a 32-row K-step) as one MFMA
-// operand: elements 0..3 come from tile 0, 4..7 from tile 1, split hi / lo.
-__device__ __forceinline__ void pack_split(const f32x4& x0, const f32x4& x1, bf16x8_t& hi,
-                                           bf16x8_t& lo) {
-    uint4 h, l;
-    split2(x0[0], x0[1], h.x, l.x);
-    split2(x0[2], x0[3], h.y, l.y);
-    split2(x1[0], x1[1], h.z, l.z);
-    split2(x1[2], x1[3], h.w, l.w);
-    hi = as_op(h);
-    lo = as_op(l);
+// ---- fp16 operands of the scan.  Each tile is stored times a power of two
+// that puts its largest magnitude in [2^14, 2^15); products are scaled back
+// in fp32, so the fp16 range never limits the data. ----
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+constexpr int F16_TOP = 15;  // a tile with magnitudes < 2^e is stored times 2^(F16_TOP - e)
+
+__device__ __forceinline__ f32x4 mfma_h(const uint4& a, const uint4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+// fp16 of two values (round to nearest even), a in the low half
+__device__ __forceinline__ uint32_t h2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, f16x2_t));
+}
+// x = hi + lo in fp16 (x - hi is exact in fp32), packed like h2
+__device__ __forceinline__ void hsplit2(float a, float b, uint32_t& hi, uint32_t& lo) {
+    hi = h2(a, b);
+    const f16x2_t v = __builtin_bit_cast(f16x2_t, hi);
+    lo = h2(a - (float)v[0], b - (float)v[1]);
+}
+__device__ __forceinline__ float scl(float x, int s) { return __builtin_amdgcn_ldexpf(x, s); }
+__device__ __forceinline__ f32x4 scl4(const f32x4& x, int s) {
+    return f32x4{scl(x[0], s), scl(x[1], s), scl(x[2], s), scl(x[3], s)};
+}
+// Two accumulator tiles (row blocks 0 and 1 of a 32-row K-step) as one fp16
+// MFMA operand times 2^s: elements 0..3 come from tile 0, 4..7 from tile 1.
+__device__ __forceinline__ uint4 pack_h(const f32x4& x0, const f32x4& x1, int s) {
+    return make_uint4(h2(scl(x0[0], s), scl(x0[1], s)), h2(scl(x0[2], s), scl(x0[3], s)),
+                      h2(scl(x1[0], s), scl(x1[1], s)), h2(scl(x1[2], s), scl(x1[3], s)));
+}
+// |x| orders like its bit pattern with the sign cleared
+__device__ __forceinline__ uint32_t absbits(float x) { return __float_as_uint(x) & 0x7fffffffu; }
+template <int CTRL>
+__device__ __forceinline__ uint32_t dppu(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
+}
+// largest value over the 64 lanes (DPP inside each 16-lane row, then the
+// four rows), uniform
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, dppu<0xB1>(v));   // quad_perm [1,0,3,2]
+    v = max(v, dppu<0x4E>(v));   // quad_perm [2,3,0,1]
+    v = max(v, dppu<0x141>(v));  // row_half_mirror
+    v = max(v, dppu<0x140>(v));  // row_mirror
+    const uint32_t a = max((uint32_t)__builtin_amdgcn_readlane((int)v, 0),
+                           (uint32_t)__builtin_amdgcn_readlane((int)v, 16));
+    const uint32_t b = max((uint32_t)__builtin_amdgcn_readlane((int)v, 32),
+                           (uint32_t)__builtin_amdgcn_readlane((int)v, 48));
+    return max(a, b);
+}
+// e with m < 2^e for the magnitude whose bit pattern is b (frexp's exponent;
+// -126 for zero and subnormals), and the same as a byte e + 126
+__device__ __forceinline__ int bound_exp(uint32_t b) { return (int)(b >> 23) - 126; }
+__device__ __forceinline__ uint8_t exp_byte(uint32_t b) { return (uint8_t)(b >> 23); }
+// exponent byte i of a packed word
+__device__ __forceinline__ int byte_exp(uint32_t packed, int i) { return (int)((packed >> (8 * i)) & 0xffu) - 126; }
+// 2^e as a float, e clamped to the normal range
+__device__ __forceinline__ float pow2f(int e) {
+    e = min(max(e, -126), 127);
+    return __uint_as_float((uint32_t)(e + 127) << 23);
 }
 
 // -x for a bf16 operand (sign flips, exact)
@@ -265,25 +314,33 @@ __global__ __launch_bounds__(NT) void plan_kernel(const int32_t* __restrict__ cu
 // prep: per (chunk, head) every state-independent quantity of the chunk,
 // written to the workspace as MFMA operands in the order the scan reads them.
 // ---------------------------------------------------------------------------
-// Operand block of one (chunk, head), in 16-byte units (8 bf16 = one MFMA
+// Operand block of one (chunk, head), in 16-byte units (8 fp16 = one MFMA
 // operand of one lane, or 4 fp32 accumulator values of one lane).  Scan lane
 // (g = lane/16, i = lane%16) of wave w reads index [...][lane] of:
-//   W, Q'   [r][mt]      row tok_of(mt, i), channels 32r + 8g .. +7
-//   Kd      [w][m][ks]   channel 32w + chan_of(m, i), tokens 32ks + 8g .. +7
+//   W, Q'   [r][mt]      fp16 row tok_of(mt, i), channels 32r + 8g .. +7
+//   Kd      [w][m][ks]   fp16 channel 32w + chan_of(m, i), tokens 32ks + 8g .. +7
 //   U~, O~  [jt][mt]     fp32 rows tok_of(mt, 4g .. 4g+3), column 16jt + i
 //   dec     128 floats, e^{G_C} per channel
+//   exp     5 x 16 bytes of tile exponents (below)
 // with W = TB (K . e^G), M = B TB, Q' = Q . e^G - M (K . e^G),
-// Kd = (K . e^{G_C - G})^T as a hi plane followed by a lo plane, and
-// U~ = TB V, O~ = M V in fp32.  With these the chunk step is
+// Kd = (K . e^{G_C - G})^T, U~ = TB V and O~ = M V.  With these the chunk
+// step is
 //   U = U~ - W S,   O = scale (Q' S + O~),   S' = Diag(e^{G_C}) S + Kd U,
-// since B U = B TB V - B TB (K . e^G) S.
+// since B U = B TB V - B TB (K . e^G) S.  Each fp16 tile (one lane-operand
+// plane slice: 16 rows x 32 K positions) with magnitudes below 2^e is stored
+// times 2^(F16_TOP - e).  Exponents are kept as bytes e + 126 (0 .. 255
+// covers every fp32 magnitude), four to a 32-bit word: row w of exp holds
+// EW[w][r], EQ[w][r] (token tile w, K-step r) and EK[w][m][ks] (state rows of
+// wave w, byte 2m + ks); row 4 holds EU[mt] (every |U~| of token tile mt is
+// below 2^EU) and EWM[mt] = max_r EW[mt][r].
 constexpr int OP_W = 0;
-constexpr int OP_Q = 4 * PLANE;
-constexpr int OP_K = 8 * PLANE;
-constexpr int OP_U = 12 * PLANE;
-constexpr int OP_O = 16 * PLANE;
-constexpr int OP_DEC = 20 * PLANE;
-constexpr int CHUNK_OPS = 20 * PLANE + 32;
+constexpr int OP_Q = 2 * PLANE;
+constexpr int OP_K = 4 * PLANE;
+constexpr int OP_U = 6 * PLANE;
+constexpr int OP_O = 10 * PLANE;
+constexpr int OP_DEC = 14 * PLANE;
+constexpr int OP_EXP = 14 * PLANE + 32;
+constexpr int CHUNK_OPS = 14 * PLANE + 32 + 5;
 constexpr int DVP = 128;             // value columns the operand block holds
 
 template <typename TIn>
@@ -683,10 +740,16 @@ void prep_kernel(PrepParams p) {
                 const int t = t0 + e;
                 kv[e] = IO::f32(sm.k.kS[t][c]) * ex2(gcc - sm.u.G[t][c]);
             }
-            uint4 kh, kl;
-            split8(kv, kh, kl);
-            dst[OP_K + idx] = kh;
-            dst[OP_K + 2 * PLANE + idx] = kl;
+            // this wave's 64 lanes hold exactly tile (w' = r, m, ks) with
+            // m * 2 + ks = w: one exponent per tile
+            uint32_t mb = 0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) mb = max(mb, absbits(kv[e]));
+            const uint32_t kb = wave_max_u32(mb);
+            const int s = F16_TOP - bound_exp(kb);
+            dst[OP_K + idx] = make_uint4(h2(scl(kv[0], s), scl(kv[1], s)), h2(scl(kv[2], s), scl(kv[3], s)),
+                                         h2(scl(kv[4], s), scl(kv[5], s)), h2(scl(kv[6], s), scl(kv[7], s)));
+            if (lane == 0) reinterpret_cast<uint8_t*>(dst + OP_EXP + r)[8 + w] = exp_byte(kb);
         }
         // Q e^G of this thread's units (token tok_of(w, i16), channels
         // 32r + 8*g4 .. +7) stay in fp32 until Q' is formed; K e^G of the same
@@ -883,6 +946,7 @@ void prep_kernel(PrepParams p) {
         // formed transposed: accumulator rows are channels 32r + chan_of(m, .),
         // columns the tile's tokens, so the two row tiles of K-step r pack
         // directly into the scan's operand ----
+        uint32_t ewb[4], eqb[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             f32x4 aw[2], aq[2];
@@ -901,19 +965,34 @@ void prep_kernel(PrepParams p) {
                 }
             }
             const int idx = (r * 4 + w) * 64 + lane;
-            bf16x8_t hi, lo;
-            pack_split(aw[0], aw[1], hi, lo);
-            dst[OP_W + idx] = __builtin_bit_cast(uint4, hi);
-            dst[OP_W + 2 * PLANE + idx] = __builtin_bit_cast(uint4, lo);
-            pack_split(aq[0], aq[1], hi, lo);
-            dst[OP_Q + idx] = __builtin_bit_cast(uint4, hi);
-            dst[OP_Q + 2 * PLANE + idx] = __builtin_bit_cast(uint4, lo);
+            uint32_t mw = 0, mq = 0;
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    mw = max(mw, absbits(aw[m][e]));
+                    mq = max(mq, absbits(aq[m][e]));
+                }
+            ewb[r] = wave_max_u32(mw);
+            eqb[r] = wave_max_u32(mq);
+            dst[OP_W + idx] = pack_h(aw[0], aw[1], F16_TOP - bound_exp(ewb[r]));
+            dst[OP_Q + idx] = pack_h(aq[0], aq[1], F16_TOP - bound_exp(eqb[r]));
+        }
+        if (lane == 0) {
+            uint32_t* ex = reinterpret_cast<uint32_t*>(dst + OP_EXP + w);
+            ex[0] = exp_byte(ewb[0]) | (exp_byte(ewb[1]) << 8) | (exp_byte(ewb[2]) << 16) |
+                    ((uint32_t)exp_byte(ewb[3]) << 24);
+            ex[1] = exp_byte(eqb[0]) | (exp_byte(eqb[1]) << 8) | (exp_byte(eqb[2]) << 16) |
+                    ((uint32_t)exp_byte(eqb[3]) << 24);
+            reinterpret_cast<uint8_t*>(dst + OP_EXP + 4)[4 + w] =
+                exp_byte(max(max(ewb[0], ewb[1]), max(ewb[2], ewb[3])));
         }
 
         // ---- U~ = TB V and O~ = M V for token tile w, every value tile ----
         const int ntv = p.dv >> 4;
         float4* __restrict__ du = reinterpret_cast<float4*>(dst + OP_U);
         float4* __restrict__ dov = reinterpret_cast<float4*>(dst + OP_O);
+        uint32_t mu = 0;  // largest |U~| of the token tile over every value column
 #pragma unroll
         for (int jt = 0; jt < DVP / 16; ++jt) {
             if (jt >= ntv) break;
@@ -936,7 +1015,11 @@ void prep_kernel(PrepParams p) {
             }
             du[(jt * 4 + w) * 64 + lane] = make_float4(au[0], au[1], au[2], au[3]);
             dov[(jt * 4 + w) * 64 + lane] = make_float4(ao[0], ao[1], ao[2], ao[3]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mu = max(mu, absbits(au[e]));
         }
+        const uint32_t ub = wave_max_u32(mu);
+        if (lane == 0) reinterpret_cast<uint8_t*>(dst + OP_EXP + 4)[w] = exp_byte(ub);
     }
 }
 
@@ -953,6 +1036,7 @@ void prep_kernel(PrepParams p) {
 struct ScanSmem {
     uint4 sx[4][64][2];                               // state rows of wave r as K-step r operands [hi, lo]
     struct Ux { uint2 h[2]; uint2 l[2]; } ux[2][64];  // U operands per K-step, halves by token tile
+    uint32_t se;                                      // exponent bytes of the state-row blocks
 };
 
 struct ScanParams {
@@ -975,11 +1059,12 @@ struct ScanParams {
 
 // One chunk's operands for one lane, loaded a chunk ahead.
 struct ScanOps {
-    uint4 w[4][2];        // W  of this wave's token tile, K-step r = state rows 32r.. [r][hi, lo]
-    uint4 q[4][2];        // Q' of this wave's token tile [r][hi, lo]
-    uint4 kd[2][2][2];    // Kd of this wave's state rows [m][ks][hi, lo]
+    uint4 w[4];           // W  of this wave's token tile, K-step r = state rows 32((r + rot) & 3)..
+    uint4 q[4];           // Q' of this wave's token tile, likewise
+    uint4 kd[2][2];       // Kd of this wave's state rows [m][ks]
     float4 u, o;          // U~ and O~ of this wave's token tile, the workgroup's value tile
     float4 dec[2];        // e^{G_C} of the lane's state rows
+    uint4 ex, ex4;        // exponent rows w and 4 (the same in every lane)
 };
 
 // The next chunk's operands are loaded in three parts spread over the
@@ -1003,22 +1088,16 @@ __device__ __forceinline__ float4 ld16f(__amdgpu_buffer_rsrc_t r, uint32_t voff,
 __device__ __forceinline__ void scan_load1(ScanOps& o, __amdgpu_buffer_rsrc_t blk, int w, int tile,
                                            uint32_t vo, int rot) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int x = (((r + rot) & 3) * 4 + w) * 64;
-        o.w[r][0] = ld16(blk, vo, OP_W + x);
-        o.w[r][1] = ld16(blk, vo, OP_W + 2 * PLANE + x);
-    }
+    for (int r = 0; r < 4; ++r) o.w[r] = ld16(blk, vo, OP_W + (((r + rot) & 3) * 4 + w) * 64);
     o.u = ld16f(blk, vo, OP_U + (tile * 4 + w) * 64);
+    o.ex = ld16(blk, 0, OP_EXP + w);
+    o.ex4 = ld16(blk, 0, OP_EXP + 4);
 }
 
 __device__ __forceinline__ void scan_load2(ScanOps& o, __amdgpu_buffer_rsrc_t blk, int w, int tile,
                                            uint32_t vo, int rot) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int x = (((r + rot) & 3) * 4 + w) * 64;
-        o.q[r][0] = ld16(blk, vo, OP_Q + x);
-        o.q[r][1] = ld16(blk, vo, OP_Q + 2 * PLANE + x);
-    }
+    for (int r = 0; r < 4; ++r) o.q[r] = ld16(blk, vo, OP_Q + (((r + rot) & 3) * 4 + w) * 64);
     o.o = ld16f(blk, vo, OP_O + (tile * 4 + w) * 64);
 }
 
@@ -1028,21 +1107,18 @@ __device__ __forceinline__ void scan_load3(ScanOps& o, __amdgpu_buffer_rsrc_t bl
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int x = ((w * 2 + m) * 2 + ks) * 64;
-            o.kd[m][ks][0] = ld16(blk, vo, OP_K + x);
-            o.kd[m][ks][1] = ld16(blk, vo, OP_K + 2 * PLANE + x);
-        }
+        for (int ks = 0; ks < 2; ++ks) o.kd[m][ks] = ld16(blk, vo, OP_K + ((w * 2 + m) * 2 + ks) * 64);
     // e^{G_C} of channels 32w + 8*(lane/16) .. +7
     o.dec[0] = ld16f(blk, vd, OP_DEC + 8 * w);
     o.dec[1] = ld16f(blk, vd, OP_DEC + 8 * w + 1);
 }
 
-// hi and lo bf16 of four fp32 values, as two packed 64-bit halves
-__device__ __forceinline__ void split4(const f32x4& x, uint2& hi, uint2& lo) {
-    split2(x[0], x[1], hi.x, lo.x);
-    split2(x[2], x[3], hi.y, lo.y);
+// fp16 hi and lo of four fp32 values, as two packed 64-bit halves
+__device__ __forceinline__ void hsplit4(const f32x4& x, uint2& hi, uint2& lo) {
+    hsplit2(x[0], x[1], hi.x, lo.x);
+    hsplit2(x[2], x[3], hi.y, lo.y);
 }
+__device__ __forceinline__ uint32_t uni(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); }
 
 template <bool OUT_BF16>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -1121,51 +1197,110 @@ void scan_kernel(ScanParams p) {
         // issued on every path; that data is unused)
         const __amdgpu_buffer_rsrc_t nblk = scan_block(p, cbase + min(ci + 1, nch - 1), h);
 
-        // ---- publish this wave's state rows ----
+        // ---- publish this wave's state rows: fp16 hi + lo times 2^(F16_TOP - eS)
+        // with every |S| of the block below 2^eS ----
         {
-            bf16x8_t Sh, Sl;
-            pack_split(S[0], S[1], Sh, Sl);
-            sm.sx[w][lane][0] = __builtin_bit_cast(uint4, Sh);
-            sm.sx[w][lane][1] = __builtin_bit_cast(uint4, Sl);
+            uint32_t mb = 0;
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) mb = max(mb, absbits(S[m][e]));
+            const uint32_t sb = wave_max_u32(mb);
+            const float f = pow2f(F16_TOP - bound_exp(sb));
+            const f32x4 x0 = S[0] * f, x1 = S[1] * f;
+            uint4 h, l;
+            hsplit2(x0[0], x0[1], h.x, l.x);
+            hsplit2(x0[2], x0[3], h.y, l.y);
+            hsplit2(x1[0], x1[1], h.z, l.z);
+            hsplit2(x1[2], x1[3], h.w, l.w);
+            sm.sx[w][lane][0] = h;
+            sm.sx[w][lane][1] = l;
+            if (lane == 0) reinterpret_cast<uint8_t*>(&sm.se)[w] = exp_byte(sb);
         }
         scan_load1(nx, nblk, w, tile, vo, rot);
         lds_barrier();
 
-        // ---- this wave's token tile: U = U~ - W S and O = scale (Q' S + O~) ----
+        // exponents of this chunk (scalar): the state-row blocks in K-step
+        // order, and the bound of U over each pair of token tiles (a K-step of
+        // the state update): |U| <= |U~| + 128 max|W| max|S| < 2^bu[ks]
+        const uint32_t sp = uni(sm.se);
+        const uint32_t xw = uni(o.ex.x), xq = uni(o.ex.y), xk = uni(o.ex.z), xu = uni(o.ex4.x),
+                       xm = uni(o.ex4.y);
+        int es[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) es[r] = byte_exp(sp, (r + rot) & 3);
+        const int esmax = bound_exp(max(max(sp & 0xffu, (sp >> 8) & 0xffu),
+                                        max((sp >> 16) & 0xffu, sp >> 24)) << 23);
+        int bu[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+            bu[ks] = 1 + max(max(byte_exp(xu, 2 * ks), byte_exp(xu, 2 * ks + 1)),
+                             7 + max(byte_exp(xm, 2 * ks), byte_exp(xm, 2 * ks + 1)) + esmax);
+
+        // ---- this wave's token tile: U = U~ - W S, then Q' S on the matrix
+        // unit while U is formed and published ----
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        f32x4 pq[4];
         {
-            bf16x8_t Sh[4], Sl[4];
+            uint4 Sh[4], Sl[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                Sh[r] = as_op(sm.sx[(r + rot) & 3][lane][0]);
-                Sl[r] = as_op(sm.sx[(r + rot) & 3][lane][1]);
+                Sh[r] = sm.sx[(r + rot) & 3][lane][0];
+                Sl[r] = sm.sx[(r + rot) & 3][lane][1];
             }
-            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            f32x4 y0 = z, y1 = z, p0 = z, p1 = z;
+            f32x4 y[4];
 #pragma unroll
-            for (int r = 0; r < 4; r += 2) {
-                y0 = mfma(as_op(o.w[r][0]), Sh[r], y0);
-                y1 = mfma(as_op(o.w[r + 1][0]), Sh[r + 1], y1);
-                y0 = mfma(as_op(o.w[r][0]), Sl[r], y0);
-                y1 = mfma(as_op(o.w[r + 1][0]), Sl[r + 1], y1);
-                y0 = mfma(as_op(o.w[r][1]), Sh[r], y0);
-                y1 = mfma(as_op(o.w[r + 1][1]), Sh[r + 1], y1);
+            for (int r = 0; r < 4; ++r) y[r] = mfma_h(o.w[r], Sh[r], z);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) y[r] = mfma_h(o.w[r], Sl[r], y[r]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) pq[r] = mfma_h(o.q[r], Sh[r], z);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) pq[r] = mfma_h(o.q[r], Sl[r], pq[r]);
+            f32x4 ws = y[0] * pow2f(byte_exp(xw, rot & 3) + es[0] - 2 * F16_TOP);
+#pragma unroll
+            for (int r = 1; r < 4; ++r) {
+                const float f = pow2f(byte_exp(xw, (r + rot) & 3) + es[r] - 2 * F16_TOP);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ws[e] = __builtin_fmaf(y[r][e], f, ws[e]);
             }
-            const f32x4 u = f32x4{o.u.x, o.u.y, o.u.z, o.u.w} - (y0 + y1);
+            const f32x4 u = (f32x4{o.u.x, o.u.y, o.u.z, o.u.w} - ws) * pow2f(F16_TOP - bu[w >> 1]);
             uint2 uh, ul;
-            split4(u, uh, ul);
+            hsplit4(u, uh, ul);
             sm.ux[w >> 1][lane].h[w & 1] = uh;
             sm.ux[w >> 1][lane].l[w & 1] = ul;
-            scan_load2(nx, nblk, w, tile, vo, rot);
+        }
+        scan_load2(nx, nblk, w, tile, vo, rot);
+        lds_barrier();
+
+        // ---- the whole U: this wave's state rows, and this wave's output tile
+        // O = scale (Q' S + O~) while the products run ----
+        {
+            uint4 Uh[2], Ul[2];
 #pragma unroll
-            for (int r = 0; r < 4; r += 2) {
-                p0 = mfma(as_op(o.q[r][0]), Sh[r], p0);
-                p1 = mfma(as_op(o.q[r + 1][0]), Sh[r + 1], p1);
-                p0 = mfma(as_op(o.q[r][0]), Sl[r], p0);
-                p1 = mfma(as_op(o.q[r + 1][0]), Sl[r + 1], p1);
-                p0 = mfma(as_op(o.q[r][1]), Sh[r], p0);
-                p1 = mfma(as_op(o.q[r + 1][1]), Sh[r + 1], p1);
+            for (int ks = 0; ks < 2; ++ks) {
+                const ScanSmem::Ux x = sm.ux[ks][lane];
+                Uh[ks] = make_uint4(x.h[0].x, x.h[0].y, x.h[1].x, x.h[1].y);
+                Ul[ks] = make_uint4(x.l[0].x, x.l[0].y, x.l[1].x, x.l[1].y);
             }
-            const f32x4 po = p0 + p1;
+            f32x4 a[2][2];
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) a[m][ks] = mfma_h(o.kd[m][ks], Uh[ks], z);
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) a[m][ks] = mfma_h(o.kd[m][ks], Ul[ks], a[m][ks]);
+            scan_load3(nx, nblk, w, vo, vd);
+
+            f32x4 po = pq[0] * pow2f(byte_exp(xq, rot & 3) + es[0] - 2 * F16_TOP);
+#pragma unroll
+            for (int r = 1; r < 4; ++r) {
+                const float f = pow2f(byte_exp(xq, (r + rot) & 3) + es[r] - 2 * F16_TOP);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) po[e] = __builtin_fmaf(pq[r][e], f, po[e]);
+            }
             const float ob[4] = {o.o.x, o.o.y, o.o.z, o.o.w};
             // the resource spans rows lo .. n-1: a row below lo gets an
             // offset that wraps past 2^32 - 1, so it falls outside too
@@ -1181,19 +1316,7 @@ void scan_kernel(ScanParams p) {
                 else
                     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ov), orsrc, ooff[e] - oshift, 0, 0);
             }
-        }
-        lds_barrier();
 
-        // ---- the whole U: this wave's state rows ----
-        {
-            bf16x8_t Uh[2], Ul[2];
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const ScanSmem::Ux x = sm.ux[ks][lane];
-                Uh[ks] = __builtin_bit_cast(bf16x8_t, make_uint4(x.h[0].x, x.h[0].y, x.h[1].x, x.h[1].y));
-                Ul[ks] = __builtin_bit_cast(bf16x8_t, make_uint4(x.l[0].x, x.l[0].y, x.l[1].x, x.l[1].y));
-            }
-            scan_load3(nx, nblk, w, vo, vd);
             // S <- Diag(e^{G_C}) S + (K e^{G_C - G})^T U
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
@@ -1201,10 +1324,9 @@ void scan_kernel(ScanParams p) {
                 f32x4 sv = S[m] * f32x4{d.x, d.y, d.z, d.w};
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
-                    const bf16x8_t kh = as_op(o.kd[m][ks][0]), kl = as_op(o.kd[m][ks][1]);
-                    sv = mfma(kh, Uh[ks], sv);
-                    sv = mfma(kh, Ul[ks], sv);
-                    sv = mfma(kl, Uh[ks], sv);
+                    const float f = pow2f(byte_exp(xk, 2 * m + ks) + bu[ks] - 2 * F16_TOP);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sv[e] = __builtin_fmaf(a[m][ks][e], f, sv[e]);
                 }
                 S[m] = sv;
             }
