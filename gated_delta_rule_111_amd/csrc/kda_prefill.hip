@@ -136,6 +136,10 @@ __device__ __forceinline__ f32x4 mfma_h(const uint4& a, const uint4& b, const f3
 __device__ __forceinline__ uint32_t h2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, f16x2_t));
 }
+// eight values as one fp16 operand, rounded once
+__device__ __forceinline__ uint4 h8(const float (&x)[8]) {
+    return make_uint4(h2(x[0], x[1]), h2(x[2], x[3]), h2(x[4], x[5]), h2(x[6], x[7]));
+}
 // x = hi + lo in fp16 (x - hi is exact in fp32), packed like h2
 __device__ __forceinline__ void hsplit2(float a, float b, uint32_t& hi, uint32_t& lo) {
     hi = h2(a, b);
@@ -623,7 +627,8 @@ void prep_kernel(PrepParams p) {
                             }
                         }
                     }
-                    // off-diagonal blocks
+                    // off-diagonal blocks: both factors are at most 1
+                    // (g <= 0), so the operands are fp16, rounded once
                     if (R > 0) {
                         float xk[8], xq[8];
 #pragma unroll
@@ -632,9 +637,7 @@ void prep_kernel(PrepParams p) {
                             xk[e] = kt[e] * xo;
                             xq[e] = qt[e] * xo;
                         }
-                        uint4 xqh, xql;
-                        split8(xq, xqh, xql);
-                        const bf16x8_t XK = as_op(bf8(xk)), XQH = as_op(xqh), XQL = as_op(xql);
+                        const uint4 XK = h8(xk), XQ = h8(xq);
 #pragma unroll
                         for (int ts = 0; ts < 3; ++ts) {
                             if (ts < R) {
@@ -645,13 +648,9 @@ void prep_kernel(PrepParams p) {
                                 lds8(&sm.u.G[s][c0], gs);
 #pragma unroll
                                 for (int e = 0; e < 8; ++e) yv[e] = ksv[e] * ex2(rw[e] - gs[e]);
-                                uint4 yh, yl;
-                                split8(yv, yh, yl);
-                                const bf16x8_t YH = as_op(yh), YL = as_op(yl);
-                                pA[sl][ts] = mfma(XK, YH, pA[sl][ts]);
-                                pB[sl][ts] = mfma(XQH, YH, pB[sl][ts]);
-                                pB[sl][ts] = mfma(XQH, YL, pB[sl][ts]);
-                                pB[sl][ts] = mfma(XQL, YH, pB[sl][ts]);
+                                const uint4 Y = h8(yv);
+                                pA[sl][ts] = mfma_h(XK, Y, pA[sl][ts]);
+                                pB[sl][ts] = mfma_h(XQ, Y, pB[sl][ts]);
                             }
                         }
                     }
@@ -716,7 +715,8 @@ void prep_kernel(PrepParams p) {
             __syncthreads();
         }
 
-        // this item's v rows (16 rows x 8 columns per thread), requested here
+        // this item's v rows (4 rows x 8 columns per thread: the row pairs
+        // 2a, 2a + 1 and 2a + 32, 2a + 33 with a = tid / 16), requested here
         // and staged as V^T after the diagonal blocks of T are solved
         typename IO::V8 vr[4];
         {
@@ -724,7 +724,10 @@ void prep_kernel(PrepParams p) {
             const int64_t vs = (int64_t)p.H * p.dv;
             const int64_t vb = (x.row0 * p.H + x.h) * (int64_t)p.dv + (c < p.dv ? c : 0);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) vr[i] = IO::load8(p.v, vb + min(max(16 * i + (tid >> 4), lo), n - 1) * vs);
+            for (int i = 0; i < 4; ++i) {
+                const int t = 2 * (tid >> 4) + (i & 1) + 32 * (i >> 1);
+                vr[i] = IO::load8(p.v, vb + min(max(t, lo), n - 1) * vs);
+            }
         }
 
         // ---- decay-scaled operands: Kd planes, Qd planes, dec, then (K e^G)^T ----
@@ -799,20 +802,36 @@ void prep_kernel(PrepParams p) {
         // the transposing writes nor the operand reads collide in LDS banks.
         {
             const int c = 8 * (tid & 15);
+            if constexpr (sizeof(TIn) == 2) {
+                // two tokens of a column as one 32-bit word (row t in the low half)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 16 * i + (tid >> 4);
-                const bool live = t >= lo && t < n && c < p.dv;
+                for (int pr = 0; pr < 2; ++pr) {
+                    const int t = 2 * (tid >> 4) + 32 * pr;
+                    const uint32_t keep = ((t >= lo && t < n && c < p.dv) ? 0xffffu : 0u) |
+                                          ((t + 1 >= lo && t + 1 < n && c < p.dv) ? 0xffff0000u : 0u);
+                    const uint32_t* r0 = &vr[2 * pr].x;
+                    const uint32_t* r1 = &vr[2 * pr + 1].x;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int j = c + e;
-                    const int off = vt_group(j, t >> 3) * 8 + (t & 7);
-                    if constexpr (sizeof(TIn) == 2) {
-                        const uint32_t wd = (&vr[i].x)[e >> 1];
-                        sm.u.tv.VT[0][j][off] = live ? (uint16_t)((e & 1) ? (wd >> 16) : (wd & 0xffffu)) : 0;
-                    } else {
-                        float xv[8];
-                        IO::f32x8(vr[i], xv);
+                    for (int e = 0; e < 8; ++e) {
+                        const int j = c + e;
+                        const uint32_t wd = __builtin_amdgcn_perm(r1[e >> 1], r0[e >> 1],
+                                                                  (e & 1) ? 0x07060302u : 0x05040100u);
+                        *reinterpret_cast<uint32_t*>(&sm.u.tv.VT[0][j][vt_group(j, t >> 3) * 8 + (t & 7)]) =
+                            wd & keep;
+                    }
+                }
+            } else {
+                // fp32 values as hi and lo bf16 planes
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = 2 * (tid >> 4) + (i & 1) + 32 * (i >> 1);
+                    const bool live = t >= lo && t < n && c < p.dv;
+                    float xv[8];
+                    IO::f32x8(vr[i], xv);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int j = c + e;
+                        const int off = vt_group(j, t >> 3) * 8 + (t & 7);
                         uint16_t hi, lo;
                         split(live ? xv[e] : 0.f, hi, lo);
                         sm.u.tv.VT[0][j][off] = hi;
@@ -1188,14 +1207,30 @@ void scan_kernel(ScanParams p) {
     for (int e = 0; e < 4; ++e)
         ooff[e] = (uint32_t)(((int64_t)tok_of(w, 4 * g4 + e) * orow + (int64_t)h * dv + j) * OB);
 
+    // Snapshots fall at the absolute multiples of the interval in
+    // (spos, spos + len]; each is a chunk end, so the next one is tracked
+    // instead of dividing per chunk.  snap_off: element offset of the next
+    // snapshot's block for this head.
+    int64_t snap_next = p.interval > 0 ? ((int64_t)spos / p.interval + 1) * p.interval : -1;
+    int64_t snap_off = (sbase * p.H + h) * (int64_t)dk * dv;
+    const int64_t snap_step = (int64_t)p.H * dk * dv;
+    // operand block of the chunk after the current one (the last chunk
+    // reloads itself, so the same loads are issued on every path; that data
+    // is unused)
+    const int64_t blk_step = (int64_t)p.H * CHUNK_OPS;
+    const uint4* nptr = p.ops + ((cbase + min(1, nch - 1)) * p.H + h) * CHUNK_OPS;
+    // exponent bytes in K-step order: byte r of a rotated word is block (r + rot) & 3
+    const uint32_t rsh = 8 * rot;
+    auto rot_bytes = [rsh](uint32_t x) { return (x >> rsh) | (x << ((32 - rsh) & 31)); };
+
     auto chunk = [&](const int ci, ScanOps& o, ScanOps& nx) {
         // chunk rows lo .. n-1 are tokens row0 + lo .. row0 + n - 1
         const int64_t row0 = seq0 - pad + (int64_t)ci * C;
         const int n = min(C, pad + len - ci * C);
         const int lo = ci == 0 ? pad : 0;
-        // the next chunk (the last chunk reloads itself, so the same loads are
-        // issued on every path; that data is unused)
-        const __amdgpu_buffer_rsrc_t nblk = scan_block(p, cbase + min(ci + 1, nch - 1), h);
+        const __amdgpu_buffer_rsrc_t nblk =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(nptr), 0, CHUNK_OPS * 16, 0x00020000);
+        if (ci + 2 < nch) nptr += blk_step;
 
         // ---- publish this wave's state rows: fp16 hi + lo times 2^(F16_TOP - eS)
         // with every |S| of the block below 2^eS ----
@@ -1223,12 +1258,12 @@ void scan_kernel(ScanParams p) {
         // exponents of this chunk (scalar): the state-row blocks in K-step
         // order, and the bound of U over each pair of token tiles (a K-step of
         // the state update): |U| <= |U~| + 128 max|W| max|S| < 2^bu[ks]
-        const uint32_t sp = uni(sm.se);
-        const uint32_t xw = uni(o.ex.x), xq = uni(o.ex.y), xk = uni(o.ex.z), xu = uni(o.ex4.x),
-                       xm = uni(o.ex4.y);
+        const uint32_t sp = uni(sm.se), spr = rot_bytes(sp);
+        const uint32_t xw = rot_bytes(uni(o.ex.x)), xq = rot_bytes(uni(o.ex.y)), xk = uni(o.ex.z),
+                       xu = uni(o.ex4.x), xm = uni(o.ex4.y);
         int es[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) es[r] = byte_exp(sp, (r + rot) & 3);
+        for (int r = 0; r < 4; ++r) es[r] = byte_exp(spr, r);
         const int esmax = bound_exp(max(max(sp & 0xffu, (sp >> 8) & 0xffu),
                                         max((sp >> 16) & 0xffu, sp >> 24)) << 23);
         int bu[2];
@@ -1257,10 +1292,10 @@ void scan_kernel(ScanParams p) {
             for (int r = 0; r < 4; ++r) pq[r] = mfma_h(o.q[r], Sh[r], z);
 #pragma unroll
             for (int r = 0; r < 4; ++r) pq[r] = mfma_h(o.q[r], Sl[r], pq[r]);
-            f32x4 ws = y[0] * pow2f(byte_exp(xw, rot & 3) + es[0] - 2 * F16_TOP);
+            f32x4 ws = y[0] * pow2f(byte_exp(xw, 0) + es[0] - 2 * F16_TOP);
 #pragma unroll
             for (int r = 1; r < 4; ++r) {
-                const float f = pow2f(byte_exp(xw, (r + rot) & 3) + es[r] - 2 * F16_TOP);
+                const float f = pow2f(byte_exp(xw, r) + es[r] - 2 * F16_TOP);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) ws[e] = __builtin_fmaf(y[r][e], f, ws[e]);
             }
@@ -1294,10 +1329,10 @@ void scan_kernel(ScanParams p) {
                 for (int ks = 0; ks < 2; ++ks) a[m][ks] = mfma_h(o.kd[m][ks], Ul[ks], a[m][ks]);
             scan_load3(nx, nblk, w, vo, vd);
 
-            f32x4 po = pq[0] * pow2f(byte_exp(xq, rot & 3) + es[0] - 2 * F16_TOP);
+            f32x4 po = pq[0] * pow2f(byte_exp(xq, 0) + es[0] - 2 * F16_TOP);
 #pragma unroll
             for (int r = 1; r < 4; ++r) {
-                const float f = pow2f(byte_exp(xq, (r + rot) & 3) + es[r] - 2 * F16_TOP);
+                const float f = pow2f(byte_exp(xq, r) + es[r] - 2 * F16_TOP);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) po[e] = __builtin_fmaf(pq[r][e], f, po[e]);
             }
@@ -1332,12 +1367,9 @@ void scan_kernel(ScanParams p) {
             }
         }
 
-        // absolute position reached: snapshots at the multiples of the interval
-        const int done = spos - pad + ci * C + n;
-        if (p.interval > 0 && done % p.interval == 0) {
-            float* __restrict__ dsts =
-                p.snapshots +
-                ((sbase + done / p.interval - spos / p.interval - 1) * p.H + h) * (int64_t)dk * dv;
+        // absolute position reached
+        if ((int64_t)spos - pad + (int64_t)ci * C + n == snap_next) {
+            float* __restrict__ dsts = p.snapshots + snap_off;
 #pragma unroll
             for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -1345,6 +1377,8 @@ void scan_kernel(ScanParams p) {
                     const int c = SL * w + 8 * g4 + 4 * m + e;
                     if (c < dk) dsts[(int64_t)c * dv + j] = S[m][e];
                 }
+            snap_off += snap_step;
+            snap_next += p.interval;
         }
     };
 
