@@ -222,7 +222,7 @@ def bench_prefill(torch, kda, inputs, w, reps, warmup):
         "kernel_ms_median": round(singles[len(singles) // 2], 4),
         "kernel_ms_min": round(singles[0], 4),
         "reps": reps,
-        "dtype": "bf16 MFMA (hi/lo split operands) + f32 state",
+        "dtype": "bf16 in; bf16 and fp16 MFMA (split or per-tile-scaled operands) + f32 state",
         "roofline": {
             "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4),
@@ -433,7 +433,8 @@ def bench_prefill_pool(torch, kda, inputs, reps, warmup):
             "kernel_ms": round(per_call * 1e3, 4), "start_pos": starts, "snapshots": nsnap,
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                         "traffic": None, "kernel": "plan + prep_kernel<bf16> + scan_kernel",
+                         "traffic": measured_traffic("prefill", "pool-8x1024-H32-d128-offgrid-starts-snap1024"),
+                         "kernel": "plan + prep_kernel<bf16> + scan_kernel",
                          "bytes_per_launch": nbytes}}
 
 

@@ -100,8 +100,8 @@ int64_t kda_snapshot_count(const int32_t *cu_seqlens_host, int32_t num_seqs,
 
 /*
  * Bytes of device workspace kda_prefill needs for this problem: 512 B of
- * offsets plus (floor(total_tokens / 64) + num_seqs) * num_heads * 164,352 B
- * of per-chunk operands (about 2.6 KB per token and head).  Returns 0 for
+ * offsets plus (floor(total_tokens / 64) + num_seqs) * num_heads * 115,280 B
+ * of per-chunk operands (about 1.8 KB per token and head).  Returns 0 for
  * unsupported configs too; kda_prefill reports those.
  */
 size_t kda_prefill_workspace_size(const kda_config *cfg, int32_t num_seqs,
@@ -116,6 +116,11 @@ size_t kda_prefill_workspace_size(const kda_config *cfg, int32_t num_seqs,
  *   g    : [T, H, dk]  fp32, log of the forget gate, every entry <= 0
  *   beta : [T, H]      fp32, in [0, 1]
  *   initial_state : [num_seqs, H, dk, dv] fp32, or NULL for zero states
+ * Entries of q and k must be below 2^15 in magnitude (rows of unit L2 norm,
+ * as KDA feeds them, are far inside): the decay-scaled query and key factors
+ * of the off-diagonal Gram blocks are fp16 MFMA operands.  No other range
+ * limit applies: the scan's fp16 operands carry a power-of-two exponent per
+ * tile.
  *   out  : [T, H, dv]  out_dtype      (written)
  *   final_state : [num_seqs, H, dk, dv] fp32 (written; may alias
  *                 initial_state exactly, no other aliasing allowed)
@@ -194,7 +199,7 @@ int64_t kda_snapshot_count_at(const int32_t *cu_seqlens_host,
 
 /*
  * Workspace bytes for kda_prefill_pool: 512 B of offsets plus
- * (floor(total_tokens / 64) + 2 * num_seqs) * num_heads * 164,352 B (a start
+ * (floor(total_tokens / 64) + 2 * num_seqs) * num_heads * 115,280 B (a start
  * position off the 64-token grid can add one chunk per sequence).
  */
 size_t kda_prefill_pool_workspace_size(const kda_config *cfg, int32_t num_seqs,
