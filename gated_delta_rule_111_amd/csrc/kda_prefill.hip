@@ -156,8 +156,10 @@ __device__ __forceinline__ uint4 pack_h(const f32x4& x0, const f32x4& x1, int s)
     return make_uint4(h2(scl(x0[0], s), scl(x0[1], s)), h2(scl(x0[2], s), scl(x0[3], s)),
                       h2(scl(x1[0], s), scl(x1[1], s)), h2(scl(x1[2], s), scl(x1[3], s)));
 }
-// |x| orders like its bit pattern with the sign cleared
-__device__ __forceinline__ uint32_t absbits(float x) { return __float_as_uint(x) & 0x7fffffffu; }
+// the bit pattern of max(m, |x|): magnitudes order like their bit patterns
+// (fabsf folds into the max as a source modifier)
+__device__ __forceinline__ float amax(float m, float x) { return fmaxf(m, fabsf(x)); }
+__device__ __forceinline__ uint32_t bits(float x) { return __float_as_uint(x); }
 template <int CTRL>
 __device__ __forceinline__ uint32_t dppu(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xf, 0xf, false);
@@ -745,10 +747,10 @@ void prep_kernel(PrepParams p) {
             }
             // this wave's 64 lanes hold exactly tile (w' = r, m, ks) with
             // m * 2 + ks = w: one exponent per tile
-            uint32_t mb = 0;
+            float mb = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) mb = max(mb, absbits(kv[e]));
-            const uint32_t kb = wave_max_u32(mb);
+            for (int e = 0; e < 8; ++e) mb = amax(mb, kv[e]);
+            const uint32_t kb = wave_max_u32(bits(mb));
             const int s = F16_TOP - bound_exp(kb);
             dst[OP_K + idx] = make_uint4(h2(scl(kv[0], s), scl(kv[1], s)), h2(scl(kv[2], s), scl(kv[3], s)),
                                          h2(scl(kv[4], s), scl(kv[5], s)), h2(scl(kv[6], s), scl(kv[7], s)));
@@ -984,16 +986,16 @@ void prep_kernel(PrepParams p) {
                 }
             }
             const int idx = (r * 4 + w) * 64 + lane;
-            uint32_t mw = 0, mq = 0;
+            float mw = 0.f, mq = 0.f;
 #pragma unroll
             for (int m = 0; m < 2; ++m)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    mw = max(mw, absbits(aw[m][e]));
-                    mq = max(mq, absbits(aq[m][e]));
+                    mw = amax(mw, aw[m][e]);
+                    mq = amax(mq, aq[m][e]);
                 }
-            ewb[r] = wave_max_u32(mw);
-            eqb[r] = wave_max_u32(mq);
+            ewb[r] = wave_max_u32(bits(mw));
+            eqb[r] = wave_max_u32(bits(mq));
             dst[OP_W + idx] = pack_h(aw[0], aw[1], F16_TOP - bound_exp(ewb[r]));
             dst[OP_Q + idx] = pack_h(aq[0], aq[1], F16_TOP - bound_exp(eqb[r]));
         }
@@ -1011,7 +1013,7 @@ void prep_kernel(PrepParams p) {
         const int ntv = p.dv >> 4;
         float4* __restrict__ du = reinterpret_cast<float4*>(dst + OP_U);
         float4* __restrict__ dov = reinterpret_cast<float4*>(dst + OP_O);
-        uint32_t mu = 0;  // largest |U~| of the token tile over every value column
+        float mu = 0.f;  // largest |U~| of the token tile over every value column
 #pragma unroll
         for (int jt = 0; jt < DVP / 16; ++jt) {
             if (jt >= ntv) break;
@@ -1035,9 +1037,9 @@ void prep_kernel(PrepParams p) {
             du[(jt * 4 + w) * 64 + lane] = make_float4(au[0], au[1], au[2], au[3]);
             dov[(jt * 4 + w) * 64 + lane] = make_float4(ao[0], ao[1], ao[2], ao[3]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) mu = max(mu, absbits(au[e]));
+            for (int e = 0; e < 4; ++e) mu = amax(mu, au[e]);
         }
-        const uint32_t ub = wave_max_u32(mu);
+        const uint32_t ub = wave_max_u32(bits(mu));
         if (lane == 0) reinterpret_cast<uint8_t*>(dst + OP_EXP + 4)[w] = exp_byte(ub);
     }
 }
@@ -1235,12 +1237,12 @@ void scan_kernel(ScanParams p) {
         // ---- publish this wave's state rows: fp16 hi + lo times 2^(F16_TOP - eS)
         // with every |S| of the block below 2^eS ----
         {
-            uint32_t mb = 0;
+            float mb = 0.f;
 #pragma unroll
             for (int m = 0; m < 2; ++m)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) mb = max(mb, absbits(S[m][e]));
-            const uint32_t sb = wave_max_u32(mb);
+                for (int e = 0; e < 4; ++e) mb = amax(mb, S[m][e]);
+            const uint32_t sb = wave_max_u32(bits(mb));
             const float f = pow2f(F16_TOP - bound_exp(sb));
             const f32x4 x0 = S[0] * f, x1 = S[1] * f;
             uint4 h, l;

@@ -90,6 +90,29 @@ def test_extreme_decay_path():
     _check(inp, interval=64, label="extreme decay")
 
 
+@pytest.mark.parametrize("k", [20, -20])
+def test_value_scale_covariance(k):
+    """The recurrence is linear in (v, initial state) jointly, and the scan's
+    fp16 operands carry a power-of-two exponent per tile: scaling v and the
+    initial states by 2^k must scale every output, snapshot and final state
+    by exactly 2^k (bit for bit wherever the values are normal fp32 in both
+    runs).  A fixed fp16 scale, or an exponent combined wrongly, breaks this."""
+    from gated_delta_rule_111_amd.inputs import prefill_inputs
+    inp = prefill_inputs([300, 64, 129], H=3, dk=128, dv=128, seed=21, decay_shift=0.0,
+                         state_std=0.1, device=DEV)
+    out, fin, snaps = _gpu(inp, interval=64)
+    f = 2.0 ** k
+    inp.v = (inp.v.float() * f).to(inp.v.dtype)
+    inp.initial_state = inp.initial_state * f
+    out2, fin2, snaps2 = _gpu(inp, interval=64)
+    for name, a, b in (("out", out, out2), ("final", fin, fin2), ("snapshots", snaps, snaps2)):
+        want = a * f
+        normal = (a.abs() >= 2.0 ** -90) & (want.abs() >= 2.0 ** -90)
+        assert normal.float().mean().item() > 0.99, name
+        assert torch.equal(b[normal], want[normal]), name
+        assert (b[~normal].abs() <= 2.0 ** -60).all(), name
+
+
 def test_bf16_output():
     from gated_delta_rule_111_amd.inputs import prefill_inputs
     inp = prefill_inputs([300], H=2, dk=128, dv=128, seed=13, device=DEV)
