@@ -183,11 +183,10 @@ __device__ __forceinline__ int bound_exp(uint32_t b) { return (int)(b >> 23) - 1
 __device__ __forceinline__ uint8_t exp_byte(uint32_t b) { return (uint8_t)(b >> 23); }
 // exponent byte i of a packed word
 __device__ __forceinline__ int byte_exp(uint32_t packed, int i) { return (int)((packed >> (8 * i)) & 0xffu) - 126; }
-// 2^e as a float, e clamped to the normal range
-__device__ __forceinline__ float pow2f(int e) {
-    e = min(max(e, -126), 127);
-    return __uint_as_float((uint32_t)(e + 127) << 23);
-}
+// 2^e as a float: exact down to 2^-149 (subnormal), 0 below; e is capped at
+// 127 so that a zero accumulator never meets an infinite factor (a product
+// that needs a larger factor overflows fp32 anyway)
+__device__ __forceinline__ float pow2f(int e) { return __builtin_amdgcn_ldexpf(1.0f, min(e, 127)); }
 
 // -x for a bf16 operand (sign flips, exact)
 __device__ __forceinline__ bf16x8_t neg(const bf16x8_t& x) {
@@ -1243,8 +1242,8 @@ void scan_kernel(ScanParams p) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) mb = amax(mb, S[m][e]);
             const uint32_t sb = wave_max_u32(bits(mb));
-            const float f = pow2f(F16_TOP - bound_exp(sb));
-            const f32x4 x0 = S[0] * f, x1 = S[1] * f;
+            const int s = F16_TOP - bound_exp(sb);
+            const f32x4 x0 = scl4(S[0], s), x1 = scl4(S[1], s);
             uint4 h, l;
             hsplit2(x0[0], x0[1], h.x, l.x);
             hsplit2(x0[2], x0[3], h.y, l.y);
@@ -1301,7 +1300,7 @@ void scan_kernel(ScanParams p) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) ws[e] = __builtin_fmaf(y[r][e], f, ws[e]);
             }
-            const f32x4 u = (f32x4{o.u.x, o.u.y, o.u.z, o.u.w} - ws) * pow2f(F16_TOP - bu[w >> 1]);
+            const f32x4 u = scl4(f32x4{o.u.x, o.u.y, o.u.z, o.u.w} - ws, F16_TOP - bu[w >> 1]);
             uint2 uh, ul;
             hsplit4(u, uh, ul);
             sm.ux[w >> 1][lane].h[w & 1] = uh;

@@ -119,8 +119,9 @@ size_t kda_prefill_workspace_size(const kda_config *cfg, int32_t num_seqs,
  * Entries of q and k must be below 2^15 in magnitude (rows of unit L2 norm,
  * as KDA feeds them, are far inside): the decay-scaled query and key factors
  * of the off-diagonal Gram blocks are fp16 MFMA operands.  No other range
- * limit applies: the scan's fp16 operands carry a power-of-two exponent per
- * tile.
+ * limit applies beyond fp32's own: the scan's fp16 operands carry a
+ * power-of-two exponent per tile (v and initial states scaled by 2^100 and
+ * 2^-100 meet the same parity bar as at unit scale).
  *   out  : [T, H, dv]  out_dtype      (written)
  *   final_state : [num_seqs, H, dk, dv] fp32 (written; may alias
  *                 initial_state exactly, no other aliasing allowed)

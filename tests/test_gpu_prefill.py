@@ -113,6 +113,20 @@ def test_value_scale_covariance(k):
         assert (b[~normal].abs() <= 2.0 ** -60).all(), name
 
 
+@pytest.mark.parametrize("k", [100, -100])
+def test_value_scale_extremes(k):
+    """v and the initial states far from unit scale (2^100 and 2^-100): the
+    per-tile exponents of the scan's fp16 operands follow the data, so the
+    parity bar holds as it does at unit scale."""
+    from gated_delta_rule_111_amd.inputs import prefill_inputs
+    inp = prefill_inputs([300, 64, 129], H=2, dk=128, dv=128, seed=22, decay_shift=0.0,
+                         state_std=0.1, device=DEV)
+    f = 2.0 ** k
+    inp.v = (inp.v.float() * f).to(inp.v.dtype)
+    inp.initial_state = inp.initial_state * f
+    _check(inp, interval=64, label=f"scale 2^{k}")
+
+
 def test_bf16_output():
     from gated_delta_rule_111_amd.inputs import prefill_inputs
     inp = prefill_inputs([300], H=2, dk=128, dv=128, seed=13, device=DEV)
