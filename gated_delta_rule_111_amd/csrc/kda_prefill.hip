@@ -41,12 +41,16 @@
 //            state rows and U tiles are exchanged through LDS, two
 //            barriers per chunk.
 //
-// Precision: v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  Operands that
-// are not exact bf16 values are split into hi + lo bf16 and multiplied in
-// three passes (hi*hi + hi*lo + lo*hi, ~16 bits); the K K^T Gram and the
-// (K e^G) operand of W and Q' use one bf16 rounding of the decay-scaled
-// keys.  State,
-// snapshots, outputs and every accumulation are fp32.
+// Precision: MFMAs with fp32 accumulation; state, snapshots, outputs and
+// every accumulation are fp32.  In prep, operands that are not exact bf16
+// values are split into hi + lo bf16 and multiplied in three passes
+// (hi*hi + hi*lo + lo*hi, ~16 bits), except one bf16 rounding of the
+// decay-scaled keys in the diagonal K K^T Gram blocks and in the (K e^G)
+// operand of W and Q', and single fp16 operands in the off-diagonal Gram
+// blocks (both decay factors there are at most 1).  The scan's W, Q' and Kd
+// are single fp16 values with one power-of-two exponent per tile, its S and
+// U fp16 hi + lo pairs (~22 bits) with their own exponents, so each scan
+// product is two v_mfma_f32_16x16x32_f16 passes.
 //
 // Determinism: every reduction has a fixed order that depends neither on the
 // number of value tiles nor on where a sequence sits in the packed batch,
@@ -156,8 +160,9 @@ __device__ __forceinline__ uint4 pack_h(const f32x4& x0, const f32x4& x1, int s)
     return make_uint4(h2(scl(x0[0], s), scl(x0[1], s)), h2(scl(x0[2], s), scl(x0[3], s)),
                       h2(scl(x1[0], s), scl(x1[1], s)), h2(scl(x1[2], s), scl(x1[3], s)));
 }
-// the bit pattern of max(m, |x|): magnitudes order like their bit patterns
-// (fabsf folds into the max as a source modifier)
+// max(m, |x|) (fabsf folds into v_max3_f32 as a source modifier); the bit
+// patterns of non-negative floats order like their values, so the maxima
+// are reduced across lanes as integers
 __device__ __forceinline__ float amax(float m, float x) { return fmaxf(m, fabsf(x)); }
 __device__ __forceinline__ uint32_t bits(float x) { return __float_as_uint(x); }
 template <int CTRL>
