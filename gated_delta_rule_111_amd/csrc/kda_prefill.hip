@@ -1229,6 +1229,22 @@ void scan_kernel(ScanParams p) {
     const uint32_t rsh = 8 * rot;
     auto rot_bytes = [rsh](uint32_t x) { return (x >> rsh) | (x << ((32 - rsh) & 31)); };
 
+    // A chunk's output tile is stored during the next chunk, while that
+    // chunk waits for its state rows from LDS (the last one after the loop).
+    // orsrc spans rows lo .. n-1 of the chunk: a row below lo gets an offset
+    // that wraps past 2^32 - 1, so it falls outside too.
+    f32x4 opend = {0.f, 0.f, 0.f, 0.f};
+    __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(p.out, 0, 0, 0x00020000);
+    uint32_t oshift = 0;
+    auto store_out = [&]() {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if constexpr (OUT_BF16)
+                __builtin_amdgcn_raw_buffer_store_b16(bfb(opend[e]), orsrc, ooff[e] - oshift, 0, 0);
+            else
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(opend[e]), orsrc, ooff[e] - oshift, 0, 0);
+        }
+    };
     auto chunk = [&](const int ci, ScanOps& o, ScanOps& nx) {
         // chunk rows lo .. n-1 are tokens row0 + lo .. row0 + n - 1
         const int64_t row0 = seq0 - pad + (int64_t)ci * C;
@@ -1289,6 +1305,7 @@ void scan_kernel(ScanParams p) {
                 Sh[r] = sm.sx[(r + rot) & 3][lane][0];
                 Sl[r] = sm.sx[(r + rot) & 3][lane][1];
             }
+            if (ci > 0) store_out();
             f32x4 y[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) y[r] = mfma_h(o.w[r], Sh[r], z);
@@ -1343,20 +1360,11 @@ void scan_kernel(ScanParams p) {
                 for (int e = 0; e < 4; ++e) po[e] = __builtin_fmaf(pq[r][e], f, po[e]);
             }
             const float ob[4] = {o.o.x, o.o.y, o.o.z, o.o.w};
-            // the resource spans rows lo .. n-1: a row below lo gets an
-            // offset that wraps past 2^32 - 1, so it falls outside too
-            const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
-                static_cast<char*>(p.out) + (row0 + lo) * orow * OB, 0,
-                (int)((int64_t)(n - lo) * orow * OB), 0x00020000);
-            const uint32_t oshift = (uint32_t)((int64_t)lo * orow * OB);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float ov = p.scale * (po[e] + ob[e]);
-                if constexpr (OUT_BF16)
-                    __builtin_amdgcn_raw_buffer_store_b16(bfb(ov), orsrc, ooff[e] - oshift, 0, 0);
-                else
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ov), orsrc, ooff[e] - oshift, 0, 0);
-            }
+            for (int e = 0; e < 4; ++e) opend[e] = p.scale * (po[e] + ob[e]);
+            orsrc = __builtin_amdgcn_make_buffer_rsrc(static_cast<char*>(p.out) + (row0 + lo) * orow * OB, 0,
+                                                      (int)((int64_t)(n - lo) * orow * OB), 0x00020000);
+            oshift = (uint32_t)((int64_t)lo * orow * OB);
 
             // S <- Diag(e^{G_C}) S + (K e^{G_C - G})^T U
 #pragma unroll
@@ -1397,6 +1405,7 @@ void scan_kernel(ScanParams p) {
         chunk(ci + 1, opB, opA);
     }
     if (ci < nch) chunk(ci, opA, opB);
+    if (nch > 0) store_out();
 
 #pragma unroll
     for (int m = 0; m < 2; ++m)
