@@ -615,7 +615,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "
+        print(f"bench.py: the benchmark runs on one GPU only (asked for --gpus {args.gpus}, "
               f"WORLD_SIZE {world}); the KDA layer shards by sequence or head with no "
               "exchange, so a multi-GPU figure is N times the one-GPU one and is not "
               "measured here.", file=sys.stderr)

@@ -62,7 +62,7 @@ extern "C" {
 typedef enum {
     KDA_OK = 0,
     KDA_ERR_INVALID_ARG = 1, /* null pointer, bad size, bad cu_seqlens ...  */
-    KDA_ERR_UNSUPPORTED = 2, /* shape or dtype this build does not provide  */
+    KDA_ERR_UNSUPPORTED = 2, /* shape or dtype the library does not provide */
     KDA_ERR_ALIGNMENT = 3,   /* a device pointer is under-aligned           */
     KDA_ERR_WORKSPACE = 4,   /* workspace smaller than the size required    */
     KDA_ERR_HIP = 5          /* the HIP runtime reported a launch error     */
