@@ -181,6 +181,33 @@ def test_beta_zero_closed_form():
     assert (fin[0].double() - S_t[-1]).abs().max().item() <= 1e-5 * S_t[-1].abs().max().item()
 
 
+def test_zero_values_give_exact_zeros():
+    """v = 0 with zero initial states: every output, snapshot and final state is
+    exactly 0 (the tile exponents sit at their floor for all-zero tiles, and
+    no scale factor may turn a zero into a NaN); then the same with one
+    sequence carrying a nonzero state, which must leave the others at 0."""
+    from gated_delta_rule_111_amd import kda
+    from gated_delta_rule_111_amd.inputs import prefill_inputs
+    inp = prefill_inputs([200, 64, 7], H=2, dk=128, dv=128, seed=23, device=DEV)
+    v0 = torch.zeros_like(inp.v)
+    out, fin, snaps = kda.prefill(inp.q, inp.k, v0, inp.g, inp.beta, inp.cu_seqlens,
+                                  snapshot_interval=64)
+    torch.cuda.synchronize()
+    assert out.abs().max().item() == 0.0 and fin.abs().max().item() == 0.0
+    assert snaps.abs().max().item() == 0.0
+    init = torch.zeros(3, 2, 128, 128, device=DEV)
+    init[1] = torch.randn(2, 128, 128, device=DEV)
+    out, fin, _ = kda.prefill(inp.q, inp.k, v0, inp.g, inp.beta, inp.cu_seqlens,
+                              initial_state=init)
+    torch.cuda.synchronize()
+    cu = inp.cu_seqlens.tolist()
+    assert torch.isfinite(out).all() and torch.isfinite(fin).all()
+    assert out[cu[1]:cu[2]].abs().max().item() > 0.0
+    for b in (0, 2):
+        assert out[cu[b]:cu[b + 1]].abs().max().item() == 0.0
+        assert fin[b].abs().max().item() == 0.0
+
+
 def test_resume_bit_exact_and_tiling_independent():
     """Resuming from a snapshot reproduces the uninterrupted run bit for bit,
     also when the resumed call has a different batch (and so a different
