@@ -44,13 +44,15 @@
 // Precision: MFMAs with fp32 accumulation; state, snapshots, outputs and
 // every accumulation are fp32.  In prep, operands that are not exact bf16
 // values are split into hi + lo bf16 and multiplied in three passes
-// (hi*hi + hi*lo + lo*hi, ~16 bits), except one bf16 rounding of the
-// decay-scaled keys in the diagonal K K^T Gram blocks and in the (K e^G)
-// operand of W and Q', and single fp16 operands in the off-diagonal Gram
-// blocks (both decay factors there are at most 1).  The scan's W, Q' and Kd
-// are single fp16 values with one power-of-two exponent per tile, its S and
-// U fp16 hi + lo pairs (~22 bits) with their own exponents, so each scan
-// product is two v_mfma_f32_16x16x32_f16 passes.
+// (hi*hi + hi*lo + lo*hi, ~16 bits), except single fp16 operands in the
+// off-diagonal Gram blocks (both decay factors there are at most 1, and A
+// and B share the key factor).  The diagonal blocks of A and B round alike
+// and K e^G enters W and Q' as a hi + lo pair: with q = k and beta = 1 the
+// output is formed by cancellation (B = I + A, so M = B TB = I), and a
+// single bf16 rounding of either leaves ~4e-3 at dk = 16.  The scan's W, Q'
+// and Kd are single fp16 values with one power-of-two exponent per tile,
+// its S and U fp16 hi + lo pairs (~22 bits) with their own exponents, so
+// each scan product is two v_mfma_f32_16x16x32_f16 passes.
 //
 // Determinism: every reduction has a fixed order that depends neither on the
 // number of value tiles nor on where a sequence sits in the packed batch,
@@ -360,7 +362,11 @@ struct PrepSmem {
     union {
         float G[C][DKP + 4];   // cumulative log-decay, log2 units
         struct {
-            float TT[C][C + 4];            // (I + A)^-1 transposed, TT[s][t] = T[t][s]
+            union {
+                float TT[C][C + 4];        // (I + A)^-1 transposed, TT[s][t] = T[t][s]
+                uint16_t KgL[DKP][C];      // low bf16 half of (K . e^G)^T, once T is read;
+                                           // 16-byte token groups permuted by vt_group
+            } t;
             uint16_t VT[NV][DVP][C];       // V^T in bf16 planes, 16-byte groups swizzled by column
         } tv;
     } u;
@@ -607,7 +613,9 @@ void prep_kernel(PrepParams p) {
                     lds8(&sm.u.G[t][c0], Gt);
                     lds8(&sm.u.G[R > 0 ? 16 * R - 1 : 0][c0], rw);
                     lds8(&sm.u.G[16 * R + 7][c0], rm);
-                    // diagonal block
+                    // diagonal block: both Grams in three passes (hi*hi + hi*lo
+                    // + lo*hi), so that A and B round alike -- with q = k and
+                    // beta = 1, B = I + A and M = B TB must come out as I
                     {
                         float xk[8], xq[8], yv[8];
 #pragma unroll
@@ -618,15 +626,18 @@ void prep_kernel(PrepParams p) {
                             xq[e] = qt[e] * xd;
                             yv[e] = kt[e] * yd;
                         }
-                        uint4 xqh, xql, yh, yl;
+                        uint4 xkh, xkl, xqh, xql, yh, yl;
+                        split8(xk, xkh, xkl);
                         split8(xq, xqh, xql);
                         split8(yv, yh, yl);
-                        const bf16x8_t XK = as_op(bf8(xk)), XQH = as_op(xqh), XQL = as_op(xql),
-                                       YH = as_op(yh), YL = as_op(yl);
+                        const bf16x8_t XKH = as_op(xkh), XKL = as_op(xkl), XQH = as_op(xqh),
+                                       XQL = as_op(xql), YH = as_op(yh), YL = as_op(yl);
 #pragma unroll
                         for (int ts = 0; ts < 4; ++ts) {
                             if (ts == R) {
-                                pA[sl][ts] = mfma(XK, YH, pA[sl][ts]);
+                                pA[sl][ts] = mfma(XKH, YH, pA[sl][ts]);
+                                pA[sl][ts] = mfma(XKH, YL, pA[sl][ts]);
+                                pA[sl][ts] = mfma(XKL, YH, pA[sl][ts]);
                                 pB[sl][ts] = mfma(XQH, YH, pB[sl][ts]);
                                 pB[sl][ts] = mfma(XQH, YL, pB[sl][ts]);
                                 pB[sl][ts] = mfma(XQL, YH, pB[sl][ts]);
@@ -762,9 +773,11 @@ void prep_kernel(PrepParams p) {
         }
         // Q e^G of this thread's units (token tok_of(w, i16), channels
         // 32r + 8*g4 .. +7) stay in fp32 until Q' is formed; K e^G of the same
-        // units goes to the transposed bf16 copy
+        // units goes to the transposed copy as bf16 hi (now) and lo (held in
+        // registers until T is read, then written over it)
         float qd[4][8];
         uint16_t kg[4][8];
+        uint32_t kgl[4][4];  // lo halves, channels c0 + 2i (low) and c0 + 2i + 1 (high)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = tok_of(w, i16), c0 = SL * r + 8 * g4;
@@ -773,11 +786,19 @@ void prep_kernel(PrepParams p) {
             IO::f32x8(*reinterpret_cast<const typename IO::V8*>(&sm.k.kS[t][c0]), kv);
             float gt[8];
             lds8(&sm.u.G[t][c0], gt);
+            float kx[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float eg = ex2(gt[e]);
                 qd[r][e] = qv[e] * eg;
-                kg[r][e] = bfb(kv[e] * eg);
+                kx[e] = kv[e] * eg;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint32_t hi;
+                split2(kx[2 * i], kx[2 * i + 1], hi, kgl[r][i]);
+                kg[r][2 * i] = (uint16_t)(hi & 0xffffu);
+                kg[r][2 * i + 1] = (uint16_t)(hi >> 16);
             }
         }
         if (tid < DKP) reinterpret_cast<float*>(dst + OP_DEC)[tid] = ex2(sm.u.G[C - 1][tid]);
@@ -801,7 +822,7 @@ void prep_kernel(PrepParams p) {
                 xs[r] = (r == j) ? 1.f : -acc;
             }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sm.u.tv.TT[bo + j][bo + r] = xs[r];
+            for (int r = 0; r < 16; ++r) sm.u.tv.t.TT[bo + j][bo + r] = xs[r];
         }
         // V^T: rows outside lo .. n-1 and columns past dv are zero.  V^T rows are 64
         // tokens; its 16-byte groups are permuted by vt_group so that neither
@@ -861,7 +882,7 @@ void prep_kernel(PrepParams p) {
 #pragma unroll
                     for (int kk = 0; kk < 4; ++kk) {
                         const int k = 16 * K + 4 * kk + g4;
-                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.ab.A[ar][k], sm.u.tv.TT[16 * J + i16][k],
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.ab.A[ar][k], sm.u.tv.t.TT[16 * J + i16][k],
                                                                  acc, 0, 0, 0);
                     }
                 float (*Mw)[17] = sm.Ms[w - 1];
@@ -872,10 +893,10 @@ void prep_kernel(PrepParams p) {
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
                     const int k = 4 * kk + g4;
-                    tm = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.u.tv.TT[16 * I + k][ar], Mw[k][i16], tm, 0, 0, 0);
+                    tm = __builtin_amdgcn_mfma_f32_16x16x4f32(sm.u.tv.t.TT[16 * I + k][ar], Mw[k][i16], tm, 0, 0, 0);
                 }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) sm.u.tv.TT[16 * J + i16][16 * I + 4 * g4 + e] = -tm[e];
+                for (int e = 0; e < 4; ++e) sm.u.tv.t.TT[16 * J + i16][16 * I + 4 * g4 + e] = -tm[e];
             }
             __syncthreads();
         }
@@ -908,7 +929,7 @@ void prep_kernel(PrepParams p) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const int s = s0 + e;
-                    const float x = sm.u.tv.TT[s][t] * sm.beta[s];
+                    const float x = sm.u.tv.t.TT[s][t] * sm.beta[s];
                     tv[e] = (s <= t) ? x : 0.f;
                     bv[e] = sm.ab.B[t][s];
                 }
@@ -935,7 +956,7 @@ void prep_kernel(PrepParams p) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const int s = 32 * ks + 8 * g4 + e;
-                        const float x = sm.u.tv.TT[sc][s] * sm.beta[sc];
+                        const float x = sm.u.tv.t.TT[sc][s] * sm.beta[sc];
                         cv[e] = (sc <= s) ? x : 0.f;
                     }
                     uint4 ch, cl;
@@ -946,11 +967,22 @@ void prep_kernel(PrepParams p) {
                     acc[nt] = mfma(Bl[ks], CH, acc[nt]);
                 }
             }
-            __syncthreads();  // every row of B is read: its storage becomes M
+            __syncthreads();  // every row of B and of T is read: their storage becomes M
+                              // and the low half of (K e^G)^T
 #pragma unroll
             for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) sm.ab.M[tok_of(w, 4 * g4 + e)][16 * nt + i16] = acc[nt][e];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int c0 = SL * r + 8 * g4;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t x = kgl[r][e >> 1];
+                    sm.u.tv.t.KgL[c0 + e][vt_group(c0 + e, t >> 3) * 8 + (t & 7)] =
+                        (uint16_t)((e & 1) ? (x >> 16) : (x & 0xffffu));
+                }
+            }
         }
         __syncthreads();
         {
@@ -981,12 +1013,17 @@ void prep_kernel(PrepParams p) {
                 aq[m] = f32x4{qd[r][4 * m], qd[r][4 * m + 1], qd[r][4 * m + 2], qd[r][4 * m + 3]};
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
+                    const int cr = SL * r + chan_of(m, i16);
                     const bf16x8_t kgo = as_op(*reinterpret_cast<const uint4*>(
-                        &sm.k.KgT[SL * r + chan_of(m, i16)][kg_group(SL * r + chan_of(m, i16), 4 * ks + g4) * 8]));
+                        &sm.k.KgT[cr][kg_group(cr, 4 * ks + g4) * 8]));
+                    const bf16x8_t kgl = as_op(*reinterpret_cast<const uint4*>(
+                        &sm.u.tv.t.KgL[cr][vt_group(cr, 4 * ks + g4) * 8]));
                     aw[m] = mfma(kgo, TBh[ks], aw[m]);
                     aw[m] = mfma(kgo, TBl[ks], aw[m]);
+                    aw[m] = mfma(kgl, TBh[ks], aw[m]);
                     aq[m] = mfma(kgo, neg(Mh[ks]), aq[m]);
                     aq[m] = mfma(kgo, neg(Ml[ks]), aq[m]);
+                    aq[m] = mfma(kgl, neg(Mh[ks]), aq[m]);
                 }
             }
             const int idx = (r * 4 + w) * 64 + lane;

@@ -12,7 +12,8 @@ initial states last):
 * q, k ~ N(0, 1) in fp32, L2-normalised per (token, head) in fp32, then
   rounded to the input dtype (bf16 with round-to-nearest-even, or kept fp32);
 * v ~ N(0, 1), rounded to the input dtype;
-* beta = sigmoid(N(0, 1)) in fp32;
+* beta = sigmoid(N(0, 1) + beta_shift) in fp32 (beta_shift 0 for every
+  workload; +4 gives beta ~ 0.98, the full-write regime of the stress runs);
 * g = log(alpha) = -softplus(N(0, 1) + decay_shift) in fp32, so
   alpha = exp(-softplus(N(0, 1) + decay_shift)) per key channel;
 * initial states ~ N(0, state_std^2) in fp32 (std, not variance), or absent.
@@ -70,11 +71,11 @@ def varlen_lengths(num: int, lo: int, hi: int, seed: int) -> List[int]:
     return torch.randint(lo, hi + 1, (num,), generator=g).tolist()
 
 
-def _draw_token_block(gen, n, H, dk, dv, in_dtype, decay_shift, device):
+def _draw_token_block(gen, n, H, dk, dv, in_dtype, decay_shift, device, beta_shift=0.0):
     q = _unit_rows(torch.randn(n, H, dk, generator=gen, device=device)).to(in_dtype)
     k = _unit_rows(torch.randn(n, H, dk, generator=gen, device=device)).to(in_dtype)
     v = torch.randn(n, H, dv, generator=gen, device=device).to(in_dtype)
-    beta = torch.sigmoid(torch.randn(n, H, generator=gen, device=device))
+    beta = torch.sigmoid(torch.randn(n, H, generator=gen, device=device) + beta_shift)
     g = -torch.nn.functional.softplus(
         torch.randn(n, H, dk, generator=gen, device=device) + decay_shift)
     return q, k, v, g, beta
@@ -83,7 +84,7 @@ def _draw_token_block(gen, n, H, dk, dv, in_dtype, decay_shift, device):
 def prefill_inputs(seq_lens: Sequence[int], H: int, dk: int, dv: int,
                    seed: int, in_dtype=torch.bfloat16, decay_shift: float = 2.0,
                    state_std: Optional[float] = None, device="cpu",
-                   block_tokens: int = 65536) -> PrefillInputs:
+                   block_tokens: int = 65536, beta_shift: float = 0.0) -> PrefillInputs:
     """Packed varlen prefill inputs; sequence b occupies rows
     [cu[b], cu[b+1]) of every [T, H, *] tensor."""
     gen = _gen(seed, device)
@@ -96,7 +97,7 @@ def prefill_inputs(seq_lens: Sequence[int], H: int, dk: int, dv: int,
     for t0 in range(0, T, block_tokens):
         n = min(block_tokens, T - t0)
         bq, bk, bv, bg, bb = _draw_token_block(gen, n, H, dk, dv, in_dtype,
-                                               decay_shift, device)
+                                               decay_shift, device, beta_shift)
         q[t0:t0 + n] = bq
         k[t0:t0 + n] = bk
         v[t0:t0 + n] = bv
