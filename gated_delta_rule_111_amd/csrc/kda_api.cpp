@@ -187,6 +187,14 @@ kda_status prefill_impl(const kda_config* cfg, int32_t num_seqs, const PrefillCa
         total_chunks += L > 0 ? (s0 % crow + L + crow - 1) / crow : 0;
     }
     const int64_t T = cu_host[num_seqs];
+    // one prep workgroup per (chunk, head) and one scan workgroup per
+    // (sequence, head, 16 value columns): both grids must fit a launch
+    if (total_chunks * cfg->num_heads > 0x7fffffffLL)
+        return fail(KDA_ERR_UNSUPPORTED, "%lld chunks x %d heads exceed one launch grid",
+                    (long long)total_chunks, cfg->num_heads);
+    if ((int64_t)num_seqs * cfg->num_heads * (cfg->dv / 16) > 0x7fffffffLL)
+        return fail(KDA_ERR_UNSUPPORTED, "%d sequences x %d heads exceed one launch grid",
+                    num_seqs, cfg->num_heads);
     if (c.interval < 0 || c.interval % 64 != 0)
         return fail(KDA_ERR_INVALID_ARG, "snapshot_interval %d is not a non-negative multiple of 64",
                     c.interval);

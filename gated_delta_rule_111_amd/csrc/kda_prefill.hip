@@ -1500,7 +1500,6 @@ hipError_t launch_t(const PrefillArgs& a) {
         pp.dv = a.dv;
         pp.num_seqs = a.num_seqs;
         const int64_t items = a.total_chunks * a.H;
-        if (items > 0x7fffffffLL) return hipErrorInvalidValue;
         hipLaunchKernelGGL((prep_kernel<TIn>), dim3((unsigned)items), dim3(NT), 0, a.stream, pp);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -1549,7 +1548,9 @@ size_t prefill_workspace_bytes(int, int, int H, int num_seqs, int64_t total_toke
 
 hipError_t launch_prefill(const PrefillArgs& a) {
     if (a.dk > DKP || a.dv > DVP || a.dv % 16 != 0) return hipErrorInvalidValue;
+    // the host API rejects these before calling; nothing has been launched yet
     if ((int64_t)a.num_seqs * a.H * (a.dv / 16) > 0x7fffffffLL) return hipErrorInvalidValue;
+    if (a.total_chunks * a.H > 0x7fffffffLL) return hipErrorInvalidValue;
     return a.in_bf16 ? launch_t<bf16_t>(a) : launch_t<float>(a);
 }
 

@@ -124,6 +124,18 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
+def _empty(stream, *shape, dtype, device) -> torch.Tensor:
+    """torch.empty from the pool of the stream the kernels run on.  The
+    caching allocator orders a block's reuse only on the stream it was
+    allocated on: a workspace taken from the current stream's pool and
+    freed on return could be handed to the next allocation there while the
+    kernels enqueued on ``stream`` still read it."""
+    if stream is None:
+        return torch.empty(*shape, dtype=dtype, device=device)
+    with torch.cuda.stream(stream):
+        return torch.empty(*shape, dtype=dtype, device=device)
+
+
 def config(H: int, dk: int, dv: int, in_dtype: torch.dtype,
            out_dtype: torch.dtype = torch.float32, scale: float = 0.0) -> Config:
     return Config(H, dk, dv, _dtype_code(in_dtype), _dtype_code(out_dtype), float(scale))
@@ -177,17 +189,17 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
     cfg = config(H, dk, dv, q.dtype, out_dtype, scale)
     nsnap = snapshot_count(cu_list, snapshot_interval) if snapshot_interval > 0 else 0
     if out is None:
-        out = torch.empty(T, H, dv, dtype=out_dtype, device=dev)
+        out = _empty(stream, T, H, dv, dtype=out_dtype, device=dev)
     _need(out, "out", (T, H, dv), out_dtype, dev)
     if final_state is None:
-        final_state = torch.empty(N, H, dk, dv, dtype=torch.float32, device=dev)
+        final_state = _empty(stream, N, H, dk, dv, dtype=torch.float32, device=dev)
     _need(final_state, "final_state", (N, H, dk, dv), torch.float32, dev)
     if snapshots is None:
-        snapshots = torch.empty(nsnap, H, dk, dv, dtype=torch.float32, device=dev)
+        snapshots = _empty(stream, nsnap, H, dk, dv, dtype=torch.float32, device=dev)
     _need(snapshots, "snapshots", (nsnap, H, dk, dv), torch.float32, dev)
     ws_bytes = workspace_size(cfg, N, T)
     if workspace is None and ws_bytes > 0:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        workspace = _empty(stream, ws_bytes, dtype=torch.uint8, device=dev)
     cu_arr = (ctypes.c_int32 * len(cu_list))(*cu_list)
     _check(lib.kda_prefill(
         ctypes.byref(cfg), N, cu_arr, cu_seqlens.data_ptr(), q.data_ptr(), k.data_ptr(),
@@ -224,7 +236,7 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
         out_dtype = out.dtype if out is not None else torch.float32
     cfg = config(H, dk, dv, q.dtype, out_dtype, scale)
     if out is None:
-        out = torch.empty(N, H, dv, dtype=out_dtype, device=dev)
+        out = _empty(stream, N, H, dv, dtype=out_dtype, device=dev)
     _need(out, "out", (N, H, dv), out_dtype, dev)
     _check(lib.kda_decode(ctypes.byref(cfg), N, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                           g.data_ptr(), beta.data_ptr(), state.data_ptr(), _ptr(slots),
@@ -295,9 +307,9 @@ def qk_frontend(xq: torch.Tensor, xk: torch.Tensor, wq: torch.Tensor, wk: torch.
         out_dtype = q_out.dtype if q_out is not None else torch.bfloat16
     cfg = frontend_config(H, dk, W, xq.dtype, out_dtype, eps)
     if q_out is None:
-        q_out = torch.empty(T, H, dk, dtype=out_dtype, device=dev)
+        q_out = _empty(stream, T, H, dk, dtype=out_dtype, device=dev)
     if k_out is None:
-        k_out = torch.empty(T, H, dk, dtype=out_dtype, device=dev)
+        k_out = _empty(stream, T, H, dk, dtype=out_dtype, device=dev)
     _need(q_out, "q_out", (T, H, dk), out_dtype, dev)
     _need(k_out, "k_out", (T, H, dk), out_dtype, dev)
     cu_arr = (ctypes.c_int32 * len(cu_list))(*cu_list)
@@ -356,7 +368,7 @@ def decode_multi(q: Optional[torch.Tensor], k: torch.Tensor, v: torch.Tensor, g:
     cfg = config(H, dk, dv, k.dtype, out_dtype, scale)
     if outputs:
         if out is None:
-            out = torch.empty(N, K, H, dv, dtype=out_dtype, device=dev)
+            out = _empty(stream, N, K, H, dv, dtype=out_dtype, device=dev)
         _need(out, "out", (N, K, H, dv), out_dtype, dev)
     else:
         out = None
@@ -430,14 +442,14 @@ def prefill_pool(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Ten
     cfg = config(H, dk, dv, q.dtype, out_dtype, scale)
     nsnap = snapshot_count_at(cu_list, st_list, snapshot_interval) if snapshot_interval > 0 else 0
     if out is None:
-        out = torch.empty(T, H, dv, dtype=out_dtype, device=dev)
+        out = _empty(stream, T, H, dv, dtype=out_dtype, device=dev)
     _need(out, "out", (T, H, dv), out_dtype, dev)
     if snapshots is None:
-        snapshots = torch.empty(nsnap, H, dk, dv, dtype=torch.float32, device=dev)
+        snapshots = _empty(stream, nsnap, H, dk, dv, dtype=torch.float32, device=dev)
     _need(snapshots, "snapshots", (nsnap, H, dk, dv), torch.float32, dev)
     ws_bytes = pool_workspace_size(cfg, N, T)
     if workspace is None and ws_bytes > 0:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        workspace = _empty(stream, ws_bytes, dtype=torch.uint8, device=dev)
     cu_arr = (ctypes.c_int32 * len(cu_list))(*cu_list)
     st_arr = (ctypes.c_int32 * max(1, N))(*st_list)
     _check(lib.kda_prefill_pool(
@@ -482,10 +494,10 @@ def attnres(sources: Sequence[torch.Tensor], query: torch.Tensor,
     if out_dtype is None:
         out_dtype = y_out.dtype if y_out is not None else dt
     if y_out is None:
-        y_out = torch.empty(T, d, dtype=out_dtype, device=dev)
+        y_out = _empty(stream, T, d, dtype=out_dtype, device=dev)
     _need(y_out, "y_out", (T, d), out_dtype, dev)
     if want_h and h_out is None:
-        h_out = torch.empty(T, d, dtype=out_dtype, device=dev)
+        h_out = _empty(stream, T, d, dtype=out_dtype, device=dev)
     if h_out is not None:
         _need(h_out, "h_out", (T, d), out_dtype, dev)
     cfg = AttnResConfig(d, M, _dtype_code(dt), _dtype_code(out_dtype), float(logit_scale),
@@ -538,7 +550,7 @@ def decode_spec_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch
         out_dtype = out.dtype if out is not None else torch.float32
     cfg = config(H, dk, dv, k.dtype, out_dtype, scale)
     if out is None:
-        out = torch.empty(N, K, H, dv, dtype=out_dtype, device=dev)
+        out = _empty(stream, N, K, H, dv, dtype=out_dtype, device=dev)
     _need(out, "out", (N, K, H, dv), out_dtype, dev)
     _check(lib.kda_decode_spec_step(ctypes.byref(cfg), N, K, _ptr(pk), _ptr(pv), _ptr(pg),
                                     _ptr(pb), _ptr(accepted), q.data_ptr(), k.data_ptr(),

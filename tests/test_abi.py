@@ -110,6 +110,19 @@ def test_prefill_rejects_bad_arguments(lib):
     assert "overlap" in detail
 
 
+def test_prefill_rejects_grids_beyond_one_launch(lib):
+    """(chunks x heads) prep workgroups must fit one launch grid: rejected
+    with KDA_ERR_UNSUPPORTED by the host checks, before anything is enqueued
+    (the fake device addresses here are never touched)."""
+    E_UNS = 2
+    cfg = _cfg(H=40000, d=16)
+    # 2^22 tokens = 65,536 chunks; x 40,000 heads > 2^31 - 1
+    assert _prefill(lib, cfg, [0, 1 << 22], ws=A, ws_bytes=1 << 62) == E_UNS
+    assert "grid" in lib.kda_last_error_detail().decode()
+    # just below the limit passes the grid check (and then fails on the workspace)
+    assert _prefill(lib, _cfg(H=32767, d=16), [0, 1 << 22], ws=A, ws_bytes=16) == 4
+
+
 def test_prefill_zero_sequences_is_noop(lib):
     from gated_delta_rule_111_amd import kda as libkda
     cfg = _cfg()
