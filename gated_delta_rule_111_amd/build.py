@@ -21,7 +21,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["kda_api.cpp", "kda_attnres.hip", "kda_decode.hip", "kda_decode_multi.hip",
-           "kda_frontend.hip", "kda_prefill.hip", "kda_spec.hip"]
+           "kda_frontend.hip", "kda_noalloc.hip", "kda_prefill.hip", "kda_spec.hip"]
 
 # Packed fp32 VALU ops are switched off for every device pass; the host pass
 # warns that it does not know the feature, which is harmless.  MFMA

@@ -84,6 +84,10 @@ size_t dtype_bytes(kda_dtype d) { return d == KDA_BF16 ? 2 : 4; }
 
 }  // namespace
 
+namespace kda {
+void set_error_detail(const char* msg) { snprintf(g_detail, sizeof(g_detail), "%s", msg); }
+}  // namespace kda
+
 extern "C" {
 
 int32_t kda_version(void) { return KDA_VERSION; }

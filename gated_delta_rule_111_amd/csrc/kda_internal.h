@@ -101,4 +101,7 @@ size_t prefill_workspace_bytes(int dk, int dv, int H, int num_seqs, int64_t tota
                                bool any_start = false);
 int prefill_chunk_rows();  // tokens per chunk; snapshot intervals are multiples of 64
 
+// Sets the text kda_last_error_detail() returns on this thread (kda_api.cpp).
+void set_error_detail(const char* msg);
+
 }  // namespace kda

@@ -67,6 +67,8 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.kda_prefill_workspace_size.argtypes = [CP, i32, i64]
     lib.kda_prefill.restype = ctypes.c_int
     lib.kda_prefill.argtypes = [CP, i32, P, P, P, P, P, P, P, P, P, P, i32, P, P, sz, P]
+    lib.kda_prefill_noalloc.restype = ctypes.c_int
+    lib.kda_prefill_noalloc.argtypes = [CP, i32, P, P, P, P, P, P, P, P, P, P, i32, P, P]
     lib.kda_decode.restype = ctypes.c_int
     lib.kda_decode.argtypes = [CP, i32, P, P, P, P, P, P, P, P, P]
     lib.kda_attnres.restype = ctypes.c_int
@@ -207,6 +209,59 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
         final_state.data_ptr(), int(snapshot_interval),
         snapshots.data_ptr() if nsnap > 0 else None, _ptr(workspace),
         workspace.numel() if workspace is not None else 0, _stream(stream)))
+    return out, final_state, snapshots
+
+
+NOALLOC_SCRATCH_BYTES = 128 * 1024 * 1024  # KDA_NOALLOC_SCRATCH_BYTES
+
+
+def prefill_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                    beta: torch.Tensor, cu_seqlens: torch.Tensor,
+                    initial_state: Optional[torch.Tensor] = None, snapshot_interval: int = 0,
+                    cu_seqlens_host: Optional[Sequence[int]] = None,
+                    out: Optional[torch.Tensor] = None,
+                    final_state: Optional[torch.Tensor] = None,
+                    snapshots: Optional[torch.Tensor] = None, scale: float = 0.0,
+                    stream=None) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """kda_prefill_noalloc: kda_prefill with the chunk operands in the
+    library's fixed per-GPU array (no workspace).  Pass out, final_state and
+    snapshots (and cu_seqlens_host) to make the call allocate nothing on the
+    Python side either; whatever is not passed is allocated here."""
+    lib = load()
+    dev = q.device
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    if cu_seqlens_host is None:
+        cu_seqlens_host = cu_seqlens.cpu().tolist()
+    cu_list = [int(x) for x in cu_seqlens_host]
+    N = len(cu_list) - 1
+    _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    for name, t, shp, dt in (("q", q, (T, H, dk), q.dtype), ("k", k, (T, H, dk), q.dtype),
+                             ("v", v, (T, H, dv), q.dtype), ("g", g, (T, H, dk), torch.float32),
+                             ("beta", beta, (T, H), torch.float32)):
+        _need(t, name, shp, dt, dev)
+    if cu_list[-1] != T:
+        raise ValueError(f"cu_seqlens ends at {cu_list[-1]} but q has {T} tokens")
+    if initial_state is not None:
+        _need(initial_state, "initial_state", (N, H, dk, dv), torch.float32, dev)
+    out_dtype = out.dtype if out is not None else torch.float32
+    cfg = config(H, dk, dv, q.dtype, out_dtype, scale)
+    nsnap = snapshot_count(cu_list, snapshot_interval) if snapshot_interval > 0 else 0
+    if out is None:
+        out = _empty(stream, T, H, dv, dtype=out_dtype, device=dev)
+    _need(out, "out", (T, H, dv), out_dtype, dev)
+    if final_state is None:
+        final_state = _empty(stream, N, H, dk, dv, dtype=torch.float32, device=dev)
+    _need(final_state, "final_state", (N, H, dk, dv), torch.float32, dev)
+    if snapshots is None:
+        snapshots = _empty(stream, nsnap, H, dk, dv, dtype=torch.float32, device=dev)
+    _need(snapshots, "snapshots", (nsnap, H, dk, dv), torch.float32, dev)
+    cu_arr = (ctypes.c_int32 * len(cu_list))(*cu_list)
+    _check(lib.kda_prefill_noalloc(
+        ctypes.byref(cfg), N, cu_arr, cu_seqlens.data_ptr(), q.data_ptr(), k.data_ptr(),
+        v.data_ptr(), g.data_ptr(), beta.data_ptr(), _ptr(initial_state), out.data_ptr(),
+        final_state.data_ptr(), int(snapshot_interval),
+        snapshots.data_ptr() if nsnap > 0 else None, _stream(stream)))
     return out, final_state, snapshots
 
 

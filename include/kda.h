@@ -146,6 +146,35 @@ kda_status kda_prefill(const kda_config *cfg, int32_t num_seqs,
                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Bytes of device memory kda_prefill_noalloc holds on each GPU it runs on
+ * (from its first call there until the process ends): room for
+ * kda_prefill_workspace_size() <= 128 MiB, e.g. one sequence of up to 2,303
+ * tokens at 32 heads.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (128u * 1024u * 1024u)
+
+/*
+ * kda_prefill without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The chunk operands go to a fixed device
+ * array of KDA_NOALLOC_SCRATCH_BYTES per GPU that the library owns; the call
+ * allocates nothing.  Arguments, results and errors are those of kda_prefill
+ * (same kernels, bit-identical results), plus KDA_ERR_WORKSPACE when
+ * kda_prefill_workspace_size() for the call exceeds the array (nothing is
+ * launched then) and KDA_ERR_HIP if the array's device address cannot be
+ * obtained.  Every call on one GPU uses that GPU's array: calls that overlap
+ * on one GPU (two streams, two host threads) race and must not be issued.
+ */
+kda_status kda_prefill_noalloc(const kda_config *cfg, int32_t num_seqs,
+                               const int32_t *cu_seqlens_host,
+                               const int32_t *cu_seqlens_dev, const void *q,
+                               const void *k, const void *v, const float *g,
+                               const float *beta, const float *initial_state,
+                               void *out, float *final_state,
+                               int32_t snapshot_interval, float *snapshots,
+                               void *stream);
+
+/*
  * Prefill over a pool of resident states, with absolute token positions.
  *
  * "Day-0 vLLM support for Kimi K3" (vLLM blog), section "Kimi K3's

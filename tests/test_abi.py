@@ -123,6 +123,19 @@ def test_prefill_rejects_grids_beyond_one_launch(lib):
     assert _prefill(lib, _cfg(H=32767, d=16), [0, 1 << 22], ws=A, ws_bytes=16) == 4
 
 
+def test_prefill_noalloc_rejects_problems_beyond_its_array(lib):
+    """kda_prefill_noalloc refuses, before any HIP call, a problem whose chunk
+    operands exceed KDA_NOALLOC_SCRATCH_BYTES; argument errors are those of
+    kda_prefill."""
+    cfg = _cfg(H=32, d=128)
+    cu = (ctypes.c_int32 * 2)(0, 1 << 20)
+    assert lib.kda_prefill_noalloc(ctypes.byref(cfg), 1, cu, A, A, A, A, A, A, None, A, A, 0,
+                                   None, None) == 4
+    assert "KDA_NOALLOC_SCRATCH_BYTES" in lib.kda_last_error_detail().decode()
+    assert lib.kda_prefill_noalloc(None, 1, cu, A, A, A, A, A, A, None, A, A, 0, None,
+                                   None) == 1
+
+
 def test_prefill_zero_sequences_is_noop(lib):
     from gated_delta_rule_111_amd import kda as libkda
     cfg = _cfg()
