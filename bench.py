@@ -1,16 +1,19 @@
-"""libkda benchmark: KDA decode seq-steps/s and chunked-prefill tokens/s on
-one MI355X, each with its roofline fraction, and the fp64 oracle timed on the
-host beside them.
+"""libkda benchmark: the five KDA workloads on one MI355X, each with its
+roofline fraction, and the fp64 oracle timed on the host beside them.
 
-    python bench.py [--steps K] [--warmup W] [--prefill-reps R] [--long]
+    python bench.py [--steps K] [--warmup W] [--prefill-reps R] [--no-long] ...
 
 One JSON line is printed.  Its ``value`` is the decode rate on the workload
 256 sequences x 32 heads, dk = dv = 128, bf16 q/k/v, fp32 states resident in
 HBM, chained steps (a "step" advances every sequence by one token through
-one KDA layer, all 32 heads).  ``prefill`` holds the chunked-prefill rate on
-B=1, H=32, T=8192 with snapshots every 1024 tokens (``prefill_long``, with
---long, the same at T=1,048,576 with snapshots every 65,536).  All inputs are
-seeded synthetic tensors generated on the device before timing starts.
+one KDA layer, all 32 heads).  ``configs`` holds every workload by number:
+1 the tiny fp32 prefill (us per call), 2 that decode step, 3 the prefill of
+B=1, H=32, T=8192 with snapshots every 1024 tokens, 4 the packed varlen
+prefill of 16 sequences of 1024..32768 tokens, 5 the prefill of
+T=1,048,576 with snapshots every 65,536 and the 512 decode steps that
+follow it; each with ``roofline`` and ``cpu_baseline`` (the oracle on a
+stated sample of the same workload).  All inputs are seeded synthetic
+tensors generated on the device before timing starts.
 
 Kernel durations come from HIP events recorded on the stream the kernels are
 launched on (torch's current stream, which the binding passes to the C ABI).
@@ -238,7 +241,7 @@ def bench_prefill(torch, kda, inputs, w, reps, warmup):
                 tflops / min(BF16_MFMA_PEAK_TFLOPS, flops / nbytes * HBM_PEAK_GBS / 1e3), 4),
         },
     }
-    return res, inp
+    return res, inp, fin
 
 
 def cpu_prefill_baseline(inp, tokens: int):
@@ -255,6 +258,158 @@ def cpu_prefill_baseline(inp, tokens: int):
             "seconds": round(dt, 2),
             "sample": f"first {T} tokens of the sequence, all heads, fp64 token-by-token "
                       "(parallel over the heads only)"}
+
+
+def cpu_varlen_baseline(inp, tokens_per_seq: int):
+    """The oracle on the first `tokens_per_seq` tokens of each sequence of the
+    varlen workload, all heads, from the workload's initial states."""
+    import numpy as np
+    import oracle
+    cu = inp.cu_seqlens.cpu().tolist()
+    parts = [(cu[b], min(cu[b + 1], cu[b] + tokens_per_seq)) for b in range(len(cu) - 1)]
+    cat = lambda t: np.concatenate([t[a:e].float().cpu().numpy() for a, e in parts])
+    cu2 = [0]
+    for a, e in parts:
+        cu2.append(cu2[-1] + e - a)
+    threads = cpu_threads()
+    log(f"[bench] cpu oracle: varlen first {tokens_per_seq} tokens of {len(parts)} sequences "
+        f"on {threads} threads")
+    q, k, v, g, b = cat(inp.q), cat(inp.k), cat(inp.v), cat(inp.g), cat(inp.beta)
+    init = inp.initial_state.cpu().numpy()
+    t0 = time.perf_counter()
+    oracle.prefill(q, k, v, g, b, cu2, initial_state=init, nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": round(cu2[-1] / dt, 1), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"first {tokens_per_seq} tokens of each of the {len(parts)} sequences "
+                      f"({cu2[-1]} tokens), all 32 heads, from the initial states, fp64 "
+                      "token-by-token"}
+
+
+def bench_tiny(torch, kda, inputs, reps):
+    """The tiny prefill (B=1, H=1, T=64, dk=dv=16, fp32 throughout): a
+    latency case.  Kernel time per call from a HIP graph of back-to-back
+    calls; wall time per eager call (host checks and marshalling included).
+    Algorithmic bytes: q, k, v, g fp32 in and o fp32 out (5 x 64 x 16 x 4 B),
+    beta (256 B), the final state (1 KiB)."""
+    dev = "cuda:0"
+    w = inputs.TINY
+    inp = inputs.make_prefill(w, device=dev)
+    cu_host = inp.cu_seqlens.cpu().tolist()
+    out = torch.empty(64, 1, 16, dtype=torch.float32, device=dev)
+    fin = torch.empty(1, 1, 16, 16, dtype=torch.float32, device=dev)
+    cfg = kda.config(1, 16, 16, inp.q.dtype)
+    ws = torch.empty(kda.workspace_size(cfg, 1, 64), dtype=torch.uint8, device=dev)
+
+    def call():
+        kda.prefill(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.cu_seqlens,
+                    cu_seqlens_host=cu_host, out=out, final_state=fin, workspace=ws)
+
+    for _ in range(5):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        call()
+    torch.cuda.synchronize()
+    eager = (time.perf_counter() - t0) / reps
+    _, per_call = _time_graph(torch, call, max(2, reps // 10))
+    nbytes = 5 * 64 * 16 * 4 + 64 * 4 + 16 * 16 * 4
+    gbs = nbytes / per_call / 1e9
+    log(f"[bench] tiny prefill: {per_call * 1e6:.2f} us/call (graph), {eager * 1e6:.1f} us "
+        f"eager call")
+    return {"workload": w.name, "value": round(per_call * 1e6, 3), "unit": "us/call",
+            "higher_is_better": False, "kernel_us": round(per_call * 1e6, 3),
+            "eager_call_us": round(eager * 1e6, 2),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 3), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 6),
+                         "traffic": measured_traffic("prefill", w.name),
+                         "kernel": "plan + prep_kernel<float> + scan_kernel (whole call)",
+                         "bytes_per_launch": nbytes,
+                         "note": "latency-bound: three launches for 22 KB of data"}}
+
+
+def cpu_tiny_baseline(inputs, reps: int):
+    import oracle
+    inp = inputs.make_prefill(inputs.TINY)
+    a = [t.numpy() for t in (inp.q, inp.k, inp.v, inp.g, inp.beta)]
+    cu = inp.cu_seqlens.tolist()
+    oracle.prefill(*a, cu, nthreads=1)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        oracle.prefill(*a, cu, nthreads=1)
+    dt = (time.perf_counter() - t0) / reps
+    return {"value": round(dt * 1e6, 2), "unit": "us/call", "cores": 1, "kind": "oracle",
+            "seconds": round(dt * reps, 2),
+            "sample": f"the whole tiny workload, {reps} calls, fp64, one thread"}
+
+
+def bench_decode_tail(torch, kda, inputs, fin, steps):
+    """512 single-token decode steps of one sequence (N = 1, H = 32, d = 128)
+    from the 1,048,576-token prefill's final state, tokens drawn with seed
+    4 + 1000.  Kernel time per step from a HIP graph of the chained steps
+    (replayed, so the state keeps advancing); wall time per eager step.
+    Algorithmic bytes per step: 32 x (2 x 64 KiB of state + 1,796 B of
+    token I/O)."""
+    dev = "cuda:0"
+    w = inputs.LONG
+    d = inputs.decode_inputs(steps=steps, N=1, H=w.H, dk=w.dk, dv=w.dv, seed=w.seed + 1000,
+                             device=dev)
+    state = fin.clone()
+    out = torch.empty(steps, 1, w.H, w.dv, dtype=torch.float32, device=dev)
+
+    def chain():
+        for s in range(steps):
+            kda.decode(d.q[s], d.k[s], d.v[s], d.g[s], d.beta[s], state, out=out[s])
+
+    chain()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    chain()
+    torch.cuda.synchronize()
+    eager = (time.perf_counter() - t0) / steps
+    _, per_chain = _time_graph(torch, chain, 3, inner=1)
+    per_step = per_chain / steps
+    nbytes = w.H * (DECODE_STATE_BYTES + DECODE_IO_BYTES)
+    gbs = nbytes / per_step / 1e9
+    log(f"[bench] decode tail N=1: {per_step * 1e6:.2f} us/step (graph), {eager * 1e6:.1f} us "
+        f"eager step")
+    return {"workload": "decode-N1-H32-d128-512steps-after-1M-prefill",
+            "value": round(1.0 / per_step, 1), "unit": "seq-steps/s",
+            "us_per_step": round(per_step * 1e6, 3), "eager_step_us": round(eager * 1e6, 2),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic("decode", "decode-N1-H32-d128"),
+                         "kernel": "decode_kernel<128,128,4,bf16,f32>",
+                         "bytes_per_launch": nbytes,
+                         "note": "latency-bound: 32 workgroups move 4.25 MB per step"}}, d, state
+
+
+def cpu_long_baseline(inp, tokens: int, dinp, fin_host):
+    """The oracle on the first `tokens` tokens of the 1M-token sequence (all
+    heads), and on the 512-step decode tail from the GPU's final state."""
+    import numpy as np
+    import oracle
+    f = lambda t: t[:tokens].float().cpu().numpy()
+    threads = cpu_threads()
+    log(f"[bench] cpu oracle: long prefill first {tokens} tokens on {threads} threads")
+    q, k, v, g, b = f(inp.q), f(inp.k), f(inp.v), f(inp.g), f(inp.beta)
+    t0 = time.perf_counter()
+    oracle.prefill(q, k, v, g, b, [0, tokens], nthreads=threads)
+    dt = time.perf_counter() - t0
+    h = lambda t: t.float().cpu().numpy()
+    t1 = time.perf_counter()
+    oracle.decode(h(dinp.q), h(dinp.k), h(dinp.v), h(dinp.g), h(dinp.beta),
+                  fin_host.astype(np.float64), nthreads=threads)
+    dt_dec = time.perf_counter() - t1
+    steps = int(dinp.q.shape[0])
+    return {"value": round(tokens / dt, 1), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"first {tokens} tokens of the 1,048,576, all 32 heads, fp64 token-by-token "
+                      "(parallel over the heads only)",
+            "decode_tail": {"value": round(steps / dt_dec, 1), "unit": "seq-steps/s",
+                            "seconds": round(dt_dec, 3),
+                            "sample": f"the {steps} decode steps (N = 1, 32 heads)"}}
 
 
 # ---------------------------------------------------------------------------
@@ -596,9 +751,11 @@ def main():
     ap.add_argument("--steps", type=int, default=1000, help="timed chained decode steps")
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--prefill-reps", type=int, default=20)
-    ap.add_argument("--long", action="store_true", help="also time the 1,048,576-token prefill")
-    ap.add_argument("--varlen", action="store_true",
-                    help="also time the 16-sequence varlen prefill (lengths 1024..32768)")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the 1,048,576-token prefill and its 512-step decode tail")
+    ap.add_argument("--no-varlen", action="store_true",
+                    help="skip the 16-sequence varlen prefill (lengths 1024..32768)")
+    ap.add_argument("--no-tiny", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-frontend", action="store_true")
     ap.add_argument("--no-spec", action="store_true")
@@ -610,6 +767,10 @@ def main():
     ap.add_argument("--cpu-decode-seqs", type=int, default=128)
     ap.add_argument("--cpu-decode-steps", type=int, default=1000)
     ap.add_argument("--cpu-prefill-tokens", type=int, default=8192)
+    ap.add_argument("--cpu-varlen-tokens", type=int, default=4096,
+                    help="oracle sample: the first N tokens of every varlen sequence")
+    ap.add_argument("--cpu-long-tokens", type=int, default=65536,
+                    help="oracle sample: the first N tokens of the 1M-token sequence")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MiB")
     args = ap.parse_args()
 
@@ -632,40 +793,71 @@ def main():
 
     from gated_delta_rule_111_amd import inputs, kda
     kda.load()
+    cpu_on = not args.no_cpu_baseline
+    configs = {}
 
+    # config 2 (the headline): decode, 256 sequences x 32 heads
     dec, dinp = bench_decode(args, torch, kda, inputs)
-    pre = pre_long = None
-    pinp = None
+    configs["2"] = {"workload": dec["workload"], "value": round(dec["seq_steps_per_s"], 1),
+                    "unit": "seq-steps/s", "us_per_step": round(dec["kernel_us"], 2),
+                    "roofline": dec["roofline"]}
+    cpu = cpu_decode_baseline(dinp, args) if cpu_on else None
+    configs["2"]["cpu_baseline"] = cpu
+    del dinp
+
+    # config 1: tiny prefill (latency)
+    if not args.no_tiny:
+        configs["1"] = bench_tiny(torch, kda, inputs, 200)
+        if cpu_on:
+            configs["1"]["cpu_baseline"] = cpu_tiny_baseline(inputs, 500)
+
+    # config 3: 8k prefill
     if not args.no_prefill:
-        pre, pinp = bench_prefill(torch, kda, inputs, inputs.PREFILL_8K, args.prefill_reps,
-                                  max(2, args.warmup // 10))
-    if args.long:
-        pre_long, _ = bench_prefill(torch, kda, inputs, inputs.LONG, 3, 1)
-    pre_var = None
-    if args.varlen:
-        pre_var, _ = bench_prefill(torch, kda, inputs, inputs.varlen_workload(), 5, 2)
+        pre, pinp, _ = bench_prefill(torch, kda, inputs, inputs.PREFILL_8K, args.prefill_reps,
+                                     max(2, args.warmup // 10))
+        if cpu_on:
+            pre["cpu_baseline"] = cpu_prefill_baseline(pinp, args.cpu_prefill_tokens)
+        configs["3"] = pre
+        del pinp
+
+    # config 4: varlen prefill
+    if not args.no_varlen:
+        var, vinp, _ = bench_prefill(torch, kda, inputs, inputs.varlen_workload(), 5, 2)
+        if cpu_on:
+            var["cpu_baseline"] = cpu_varlen_baseline(vinp, args.cpu_varlen_tokens)
+        var["seq_lens"] = list(inputs.varlen_workload().seq_lens)
+        configs["4"] = var
+        del vinp
+        torch.cuda.empty_cache()
+
+    # config 5: 1,048,576-token prefill, then 512 decode steps of that sequence
+    if not args.no_long:
+        lng, linp, lfin = bench_prefill(torch, kda, inputs, inputs.LONG, 3, 1)
+        tail, tinp, _ = bench_decode_tail(torch, kda, inputs, lfin, inputs.LONG.decode_steps)
+        lng["decode_tail"] = tail
+        if cpu_on:
+            lng["cpu_baseline"] = cpu_long_baseline(linp, args.cpu_long_tokens, tinp,
+                                                    lfin.cpu().numpy())
+        configs["5"] = lng
+        del linp, lfin, tinp
+        torch.cuda.empty_cache()
+
     pool = None
     if not args.no_prefill and not args.no_pool:
         pool = bench_prefill_pool(torch, kda, inputs, args.prefill_reps, 2)
     attn = None
     if not args.no_attnres:
         attn = bench_attnres(torch, kda, inputs, args.prefill_reps)
+        if cpu_on:
+            attn["cpu_baseline"] = cpu_attnres_baseline(inputs, args.cpu_attnres_tokens)
     spec = None
     if not args.no_spec:
         spec = bench_spec(torch, kda, inputs, args.prefill_reps, dec["kernel_us"])
     fe = None
     if not args.no_frontend:
         fe = bench_frontend(torch, kda, inputs, args.prefill_reps)
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_decode_baseline(dinp, args)
-        if pre is not None:
-            pre["cpu_baseline"] = cpu_prefill_baseline(pinp, args.cpu_prefill_tokens)
-        if fe is not None:
+        if cpu_on:
             fe["cpu_baseline"] = cpu_frontend_baseline(inputs, args.cpu_frontend_tokens)
-        if attn is not None:
-            attn["cpu_baseline"] = cpu_attnres_baseline(inputs, args.cpu_attnres_tokens)
 
     line = {
         "metric": METRIC,
@@ -686,12 +878,8 @@ def main():
         "roofline": dec["roofline"],
         "cpu_baseline": cpu,
         "decode_kernel_us": round(dec["kernel_us"], 2),
-        "prefill": pre,
+        "configs": configs,
     }
-    if pre_long is not None:
-        line["prefill_long"] = pre_long
-    if pre_var is not None:
-        line["prefill_varlen"] = pre_var
     if fe is not None:
         line["qk_frontend"] = fe
     if spec is not None:
