@@ -196,7 +196,7 @@ kda_status prefill_impl(const kda_config* cfg, int32_t num_seqs, const PrefillCa
     if (total_chunks * cfg->num_heads > 0x7fffffffLL)
         return fail(KDA_ERR_UNSUPPORTED, "%lld chunks x %d heads exceed one launch grid",
                     (long long)total_chunks, cfg->num_heads);
-    if ((int64_t)num_seqs * cfg->num_heads * (cfg->dv / 16) > 0x7fffffffLL)
+    if (((int64_t)num_seqs * cfg->num_heads + 7) / 8 * 8 * (cfg->dv / 16) > 0x7fffffffLL)
         return fail(KDA_ERR_UNSUPPORTED, "%d sequences x %d heads exceed one launch grid",
                     num_seqs, cfg->num_heads);
     if (c.interval < 0 || c.interval % 64 != 0)

@@ -276,18 +276,31 @@ template <> struct In<float> {
 
 // ---------------------------------------------------------------------------
 // plan: chunk_start[b] = sum_{b' < b} nch(b'), snap_base[b] = sum_{b' < b}
-// nsnap(b'), for b = 0 .. num_seqs.  A sequence whose first token sits at
+// nsnap(b'), for b = 0 .. num_seqs, and order[]: the sequences by decreasing
+// chunk count (ties by index) when there are at most LPT_MAX of them, else
+// in index order.  The scan deals its chains out in that order, so the
+// longest recurrences start first instead of trailing the batch.  A sequence whose first token sits at
 // absolute position s (0 without start positions) is cut into chunks at the
 // absolute multiples of C, so it has nch = ceil((s mod C + L) / C) chunks
 // (none when L = 0), and snapshots at the absolute multiples of the interval
 // in (s, s + L]: nsnap = floor((s + L) / interval) - floor(s / interval).
 // ---------------------------------------------------------------------------
+constexpr int LPT_MAX = 512;
+
+__device__ __forceinline__ int seq_chunks(const int32_t* cu, const int32_t* start, int b) {
+    const int L = cu[b + 1] - cu[b];
+    const int s0 = start ? start[b] : 0;
+    return L > 0 ? (s0 % C + L + C - 1) / C : 0;
+}
+
 __global__ __launch_bounds__(NT) void plan_kernel(const int32_t* __restrict__ cu,
                                                   const int32_t* __restrict__ start, int num_seqs,
                                                   int interval, int32_t* __restrict__ chunk_start,
-                                                  int32_t* __restrict__ snap_base) {
+                                                  int32_t* __restrict__ snap_base,
+                                                  int32_t* __restrict__ order) {
     __shared__ int32_t wtot[2][4];
     __shared__ int32_t carry[2];
+    __shared__ int32_t keys[LPT_MAX];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (tid == 0) carry[0] = carry[1] = 0;
     __syncthreads();
@@ -297,7 +310,7 @@ __global__ __launch_bounds__(NT) void plan_kernel(const int32_t* __restrict__ cu
         if (b < num_seqs) {
             const int L = cu[b + 1] - cu[b];
             const int s0 = start ? start[b] : 0;
-            vc = L > 0 ? (s0 % C + L + C - 1) / C : 0;
+            vc = seq_chunks(cu, start, b);
             vs = interval > 0 ? (s0 + L) / interval - s0 / interval : 0;
         }
         int ic = vc, is = vs;
@@ -319,6 +332,21 @@ __global__ __launch_bounds__(NT) void plan_kernel(const int32_t* __restrict__ cu
             for (int w = 0; w < 4; ++w) { carry[0] += wtot[0][w]; carry[1] += wtot[1][w]; }
         }
         __syncthreads();
+    }
+    if (num_seqs > LPT_MAX) {
+        for (int b = tid; b < num_seqs; b += NT) order[b] = b;
+        return;
+    }
+    for (int b = tid; b < num_seqs; b += NT) keys[b] = seq_chunks(cu, start, b);
+    __syncthreads();
+    for (int b = tid; b < num_seqs; b += NT) {
+        const int key = keys[b];
+        int rank = 0;
+        for (int b2 = 0; b2 < num_seqs; ++b2) {
+            const int k2 = keys[b2];
+            rank += (k2 > key) | ((k2 == key) & (b2 < b));
+        }
+        order[rank] = b;
     }
 }
 
@@ -1086,19 +1114,26 @@ void prep_kernel(PrepParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// scan: per (sequence, head, 16 value columns) the recurrence over chunks.
-// Wave w owns state rows 32w .. 32w+31 and token tile w of the chunk.  Per
-// chunk the waves publish their state rows (as hi/lo MFMA operands) through
-// LDS; each wave then forms its token tile of W S, U = TB V - W S and
-// (Q e^G) S over all 128 state rows and publishes its tile of U; after the
-// second barrier each wave updates its state rows from the whole U and
-// writes its token tile of O.  Nothing is reduced across waves, so the LDS
-// traffic per chunk is the state once and U once.
+// scan: per (sequence, head, TPW x 16 value columns) the recurrence over
+// chunks.  Wave w owns state rows 32w .. 32w+31 and token tile w of the
+// chunk.  Per chunk the waves publish their state rows (as hi/lo MFMA
+// operands) through LDS; each wave then forms its token tile of W S,
+// U = TB V - W S and (Q e^G) S over all 128 state rows and publishes its
+// tile of U; after the second barrier each wave updates its state rows from
+// the whole U and writes its token tile of O.  Nothing is reduced across
+// waves, so the LDS traffic per chunk is the state once and U once.
+//
+// A wave carries TPW value tiles of 16 columns: the chunk's W, Q' and Kd
+// operands (48 KB of the 57 KB a tile reads per chunk) are loaded once for
+// all of them.  Each 16-column tile keeps its own exponents and runs the
+// same instructions in the same order whatever TPW is, so results do not
+// depend on the width a call chose.
 // ---------------------------------------------------------------------------
+template <int TPW>
 struct ScanSmem {
-    uint4 sx[4][64][2];                               // state rows of wave r as K-step r operands [hi, lo]
-    struct Ux { uint2 h[2]; uint2 l[2]; } ux[2][64];  // U operands per K-step, halves by token tile
-    uint32_t se;                                      // exponent bytes of the state-row blocks
+    uint4 sx[TPW][4][64][2];                               // state rows of wave r as K-step r operands [hi, lo]
+    struct Ux { uint2 h[2]; uint2 l[2]; } ux[TPW][2][64];  // U operands per K-step, halves by token tile
+    uint32_t se[TPW];                                      // exponent bytes of the state-row blocks
 };
 
 struct ScanParams {
@@ -1107,6 +1142,7 @@ struct ScanParams {
     const int32_t* slots;       // state row of each sequence, or null (row b)
     const int32_t* chunk_start;
     const int32_t* snap_base;
+    const int32_t* order;       // sequences, longest first (see plan_kernel)
     const uint4* ops;
     const float* init;          // null: zero initial states
     int init_if_started;        // read init only for sequences with start > 0
@@ -1115,26 +1151,25 @@ struct ScanParams {
     float* snapshots;
     int interval;
     int H, dk, dv;
-    int ntiles, nwg;
+    int ngroups, nchains;       // value-tile groups of TPW tiles per chain; chains
     float scale;
 };
 
-// One chunk's operands for one lane, loaded a chunk ahead.
+// One chunk's operands for one lane, loaded ahead.
+template <int TPW>
 struct ScanOps {
-    uint4 w[4];           // W  of this wave's token tile, K-step r = state rows 32((r + rot) & 3)..
+    uint4 w[4];           // W  of this wave's token tile, K-step r = state rows 32r ..
     uint4 q[4];           // Q' of this wave's token tile, likewise
     uint4 kd[2][2];       // Kd of this wave's state rows [m][ks]
-    float4 u, o;          // U~ and O~ of this wave's token tile, the workgroup's value tile
+    float4 u[TPW], o[TPW];  // U~ and O~ of this wave's token tile, per value tile
     float4 dec[2];        // e^{G_C} of the lane's state rows
     uint4 ex, ex4;        // exponent rows w and 4 (the same in every lane)
 };
 
 // The next chunk's operands are loaded in three parts spread over the
-// current chunk, so the wave never stalls on a full memory queue.  rot
-// rotates the order of the state-row blocks, so the value tiles of one head
-// do not all request the same lines at once.  Loads go through a buffer
-// resource of the chunk's block: the lane's offset is one register for every
-// load, the rest of each address is a scalar.
+// current chunk, so the wave never stalls on a full memory queue.  Loads go
+// through a buffer resource of the chunk's block: the lane's offset is one
+// register for every load, the rest of each address is a scalar.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t scan_block(const ScanParams& p, int64_t gc, int h) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(p.ops + (gc * p.H + h) * CHUNK_OPS), 0,
                                              CHUNK_OPS * 16, 0x00020000);
@@ -1146,25 +1181,30 @@ __device__ __forceinline__ float4 ld16f(__amdgpu_buffer_rsrc_t r, uint32_t voff,
     return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, unit * 16, 0));
 }
 
-// vo = 16 * lane
-__device__ __forceinline__ void scan_load1(ScanOps& o, __amdgpu_buffer_rsrc_t blk, int w, int tile,
-                                           uint32_t vo, int rot) {
+// vo = 16 * lane; tile0 = first value tile of the workgroup
+template <int TPW>
+__device__ __forceinline__ void scan_load1(ScanOps<TPW>& o, __amdgpu_buffer_rsrc_t blk, int w, int tile0,
+                                           uint32_t vo) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) o.w[r] = ld16(blk, vo, OP_W + (((r + rot) & 3) * 4 + w) * 64);
-    o.u = ld16f(blk, vo, OP_U + (tile * 4 + w) * 64);
+    for (int r = 0; r < 4; ++r) o.w[r] = ld16(blk, vo, OP_W + (r * 4 + w) * 64);
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) o.u[t] = ld16f(blk, vo, OP_U + ((tile0 + t) * 4 + w) * 64);
     o.ex = ld16(blk, 0, OP_EXP + w);
     o.ex4 = ld16(blk, 0, OP_EXP + 4);
 }
 
-__device__ __forceinline__ void scan_load2(ScanOps& o, __amdgpu_buffer_rsrc_t blk, int w, int tile,
-                                           uint32_t vo, int rot) {
+template <int TPW>
+__device__ __forceinline__ void scan_load2(ScanOps<TPW>& o, __amdgpu_buffer_rsrc_t blk, int w, int tile0,
+                                           uint32_t vo) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) o.q[r] = ld16(blk, vo, OP_Q + (((r + rot) & 3) * 4 + w) * 64);
-    o.o = ld16f(blk, vo, OP_O + (tile * 4 + w) * 64);
+    for (int r = 0; r < 4; ++r) o.q[r] = ld16(blk, vo, OP_Q + (r * 4 + w) * 64);
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) o.o[t] = ld16f(blk, vo, OP_O + ((tile0 + t) * 4 + w) * 64);
 }
 
 // vd = 32 * (lane / 16)
-__device__ __forceinline__ void scan_load3(ScanOps& o, __amdgpu_buffer_rsrc_t blk, int w, uint32_t vo,
+template <int TPW>
+__device__ __forceinline__ void scan_load3(ScanOps<TPW>& o, __amdgpu_buffer_rsrc_t blk, int w, uint32_t vo,
                                            uint32_t vd) {
 #pragma unroll
     for (int m = 0; m < 2; ++m)
@@ -1182,27 +1222,34 @@ __device__ __forceinline__ void hsplit4(const f32x4& x, uint2& hi, uint2& lo) {
 }
 __device__ __forceinline__ uint32_t uni(uint32_t x) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)x); }
 
-template <bool OUT_BF16>
+// DB: the next chunk's operands go to a second register set while the
+// current chunk runs (the deepest prefetch, one workgroup per compute unit:
+// for few, long recurrences).  !DB: one register set, each part reloaded
+// as soon as the current chunk has consumed it.  The arithmetic is the same
+// instruction for instruction, so both give the same bits.
+template <bool OUT_BF16, bool DB, int TPW>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void scan_kernel(ScanParams p) {
-    __shared__ ScanSmem sm;
+    __shared__ ScanSmem<TPW> sm;
     // the wave index is uniform: kept in a scalar register, so addresses that
     // depend on it are formed on the scalar unit
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g4 = lane >> 4, i16 = lane & 15;
     (void)tid;
 
-    // workgroup -> (sequence, head, value tile).  Workgroups are dealt
-    // round-robin over the 8 XCDs; the remap gives each XCD a contiguous
-    // range of logical ids, so the tiles of one head share its L2.
-    int L = blockIdx.x;
-    if ((p.nwg & 7) == 0) L = (blockIdx.x & 7) * (p.nwg >> 3) + (blockIdx.x >> 3);
-    const int tile = L % p.ntiles;
-    const int chain = L / p.ntiles;
-    const int b = chain / p.H, h = chain - b * p.H;
+    // workgroup -> (chain, group of TPW value tiles); a chain is a
+    // (sequence, head) pair with its sequences taken longest first.
+    // Workgroups are dealt round-robin over the 8 XCDs: chain rho goes to XCD
+    // rho mod 8, where its groups follow each other in dispatch order, so the
+    // tiles of one head share an L2 and the chains start in order of length.
+    const int pos = blockIdx.x >> 3;
+    const int chain = (pos / p.ngroups) * 8 + (blockIdx.x & 7);
+    if (chain >= p.nchains) return;
+    const int tile0 = (pos % p.ngroups) * TPW;
+    const int rk = chain / p.H, h = chain - rk * p.H;
+    const int b = p.order[rk];
     const int dk = p.dk, dv = p.dv;
-    const int j = 16 * tile + i16;
-    const int rot = tile & 3;
+    const int j0 = 16 * tile0 + i16;  // value column of this lane in tile t: j0 + 16 t
     const int64_t seq0 = p.cu[b];
     const int len = p.cu[b + 1] - p.cu[b];
     // chunks sit at absolute multiples of C (see plan_kernel): pad leading
@@ -1214,41 +1261,44 @@ void scan_kernel(ScanParams p) {
     const int64_t sbase = p.snap_base[b];
 
     // state rows of this lane: 32w + chan_of(m, 4*g4 + e) = 32w + 8*g4 + 4m + e
-    f32x4 S[2];
+    f32x4 S[TPW][2];
     const int64_t srow = ((p.slots ? (int64_t)p.slots[b] : (int64_t)b) * p.H + h) * dk;
     const bool has_init = p.init && (!p.init_if_started || spos > 0);
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int t = 0; t < TPW; ++t)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int c = SL * w + 8 * g4 + 4 * m + e;
-            S[m][e] = 0.f;
-            if (has_init) {
-                const float x = p.init[(srow + (c < dk ? c : 0)) * dv + j];
-                S[m][e] = c < dk ? x : 0.f;
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c = SL * w + 8 * g4 + 4 * m + e;
+                S[t][m][e] = 0.f;
+                if (has_init) {
+                    const float x = p.init[(srow + (c < dk ? c : 0)) * dv + j0 + 16 * t];
+                    S[t][m][e] = c < dk ? x : 0.f;
+                }
             }
-        }
 
-    // Operands are prefetched one chunk ahead into two register sets used in
-    // turn (the loop body is instantiated twice with the roles swapped), so
-    // no loaded value is copied and nothing waits early for the next chunk.
+    // Operands are prefetched into two register sets used in turn (DB: the
+    // loop body is instantiated twice with the roles swapped, so no loaded
+    // value is copied) or into one set reloaded part by part (!DB).
     const uint32_t vo = 16 * lane, vd = 32 * g4;
-    ScanOps opA, opB;
+    ScanOps<TPW> opA, opB;
     if (nch > 0) {
         const __amdgpu_buffer_rsrc_t blk = scan_block(p, cbase, h);
-        scan_load1(opA, blk, w, tile, vo, rot);
-        scan_load2(opA, blk, w, tile, vo, rot);
+        scan_load1(opA, blk, w, tile0, vo);
+        scan_load2(opA, blk, w, tile0, vo);
         scan_load3(opA, blk, w, vo, vd);
     }
 
     // Output rows of a chunk through a buffer resource that ends at the
     // sequence's last row: stores past it fall outside and are dropped.
+    // Tile t's columns sit 16 t elements after tile 0's (a scalar offset).
     constexpr int OB = OUT_BF16 ? 2 : 4;
     const int64_t orow = (int64_t)p.H * dv;  // elements per token row
     uint32_t ooff[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-        ooff[e] = (uint32_t)(((int64_t)tok_of(w, 4 * g4 + e) * orow + (int64_t)h * dv + j) * OB);
+        ooff[e] = (uint32_t)(((int64_t)tok_of(w, 4 * g4 + e) * orow + (int64_t)h * dv + j0) * OB);
 
     // Snapshots fall at the absolute multiples of the interval in
     // (spos, spos + len]; each is a chunk end, so the next one is tracked
@@ -1262,27 +1312,30 @@ void scan_kernel(ScanParams p) {
     // is unused)
     const int64_t blk_step = (int64_t)p.H * CHUNK_OPS;
     const uint4* nptr = p.ops + ((cbase + min(1, nch - 1)) * p.H + h) * CHUNK_OPS;
-    // exponent bytes in K-step order: byte r of a rotated word is block (r + rot) & 3
-    const uint32_t rsh = 8 * rot;
-    auto rot_bytes = [rsh](uint32_t x) { return (x >> rsh) | (x << ((32 - rsh) & 31)); };
 
-    // A chunk's output tile is stored during the next chunk, while that
-    // chunk waits for its state rows from LDS (the last one after the loop).
+    // A chunk's output tiles are stored during the next chunk, while that
+    // chunk waits for its state rows from LDS (the last ones after the loop).
     // orsrc spans rows lo .. n-1 of the chunk: a row below lo gets an offset
     // that wraps past 2^32 - 1, so it falls outside too.
-    f32x4 opend = {0.f, 0.f, 0.f, 0.f};
+    f32x4 opend[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) opend[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(p.out, 0, 0, 0x00020000);
     uint32_t oshift = 0;
     auto store_out = [&]() {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            if constexpr (OUT_BF16)
-                __builtin_amdgcn_raw_buffer_store_b16(bfb(opend[e]), orsrc, ooff[e] - oshift, 0, 0);
-            else
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(opend[e]), orsrc, ooff[e] - oshift, 0, 0);
-        }
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if constexpr (OUT_BF16)
+                    __builtin_amdgcn_raw_buffer_store_b16(bfb(opend[t][e]), orsrc, ooff[e] - oshift,
+                                                          16 * t * OB, 0);
+                else
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(opend[t][e]), orsrc,
+                                                          ooff[e] - oshift, 16 * t * OB, 0);
+            }
     };
-    auto chunk = [&](const int ci, ScanOps& o, ScanOps& nx) {
+    auto chunk = [&](const int ci, ScanOps<TPW>& o, ScanOps<TPW>& nx) {
         // chunk rows lo .. n-1 are tokens row0 + lo .. row0 + n - 1
         const int64_t row0 = seq0 - pad + (int64_t)ci * C;
         const int n = min(C, pad + len - ci * C);
@@ -1291,166 +1344,192 @@ void scan_kernel(ScanParams p) {
             __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4*>(nptr), 0, CHUNK_OPS * 16, 0x00020000);
         if (ci + 2 < nch) nptr += blk_step;
 
-        // ---- publish this wave's state rows: fp16 hi + lo times 2^(F16_TOP - eS)
-        // with every |S| of the block below 2^eS ----
-        {
+        // ---- publish this wave's state rows, per value tile: fp16 hi + lo
+        // times 2^(F16_TOP - eS) with every |S| of the block below 2^eS ----
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
             float mb = 0.f;
 #pragma unroll
             for (int m = 0; m < 2; ++m)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) mb = amax(mb, S[m][e]);
+                for (int e = 0; e < 4; ++e) mb = amax(mb, S[t][m][e]);
             const uint32_t sb = wave_max_u32(bits(mb));
             const int s = F16_TOP - bound_exp(sb);
-            const f32x4 x0 = scl4(S[0], s), x1 = scl4(S[1], s);
-            uint4 h, l;
-            hsplit2(x0[0], x0[1], h.x, l.x);
-            hsplit2(x0[2], x0[3], h.y, l.y);
-            hsplit2(x1[0], x1[1], h.z, l.z);
-            hsplit2(x1[2], x1[3], h.w, l.w);
-            sm.sx[w][lane][0] = h;
-            sm.sx[w][lane][1] = l;
-            if (lane == 0) reinterpret_cast<uint8_t*>(&sm.se)[w] = exp_byte(sb);
+            const f32x4 x0 = scl4(S[t][0], s), x1 = scl4(S[t][1], s);
+            uint4 hh, ll;
+            hsplit2(x0[0], x0[1], hh.x, ll.x);
+            hsplit2(x0[2], x0[3], hh.y, ll.y);
+            hsplit2(x1[0], x1[1], hh.z, ll.z);
+            hsplit2(x1[2], x1[3], hh.w, ll.w);
+            sm.sx[t][w][lane][0] = hh;
+            sm.sx[t][w][lane][1] = ll;
+            if (lane == 0) reinterpret_cast<uint8_t*>(&sm.se[t])[w] = exp_byte(sb);
         }
-        scan_load1(nx, nblk, w, tile, vo, rot);
+        if constexpr (DB) scan_load1(nx, nblk, w, tile0, vo);
         lds_barrier();
 
-        // exponents of this chunk (scalar): the state-row blocks in K-step
-        // order, and the bound of U over each pair of token tiles (a K-step of
-        // the state update): |U| <= |U~| + 128 max|W| max|S| < 2^bu[ks]
-        const uint32_t sp = uni(sm.se), spr = rot_bytes(sp);
-        const uint32_t xw = rot_bytes(uni(o.ex.x)), xq = rot_bytes(uni(o.ex.y)), xk = uni(o.ex.z),
+        // exponents of this chunk (scalar): the state-row blocks of each tile,
+        // and the bound of U over each pair of token tiles (a K-step of the
+        // state update): |U| <= |U~| + 128 max|W| max|S| < 2^bu[t][ks]
+        const uint32_t xw = uni(o.ex.x), xq = uni(o.ex.y), xk = uni(o.ex.z),
                        xu = uni(o.ex4.x), xm = uni(o.ex4.y);
-        int es[4];
+        int es[TPW][4], bu[TPW][2];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) es[r] = byte_exp(spr, r);
-        const int esmax = bound_exp(max(max(sp & 0xffu, (sp >> 8) & 0xffu),
-                                        max((sp >> 16) & 0xffu, sp >> 24)) << 23);
-        int bu[2];
+        for (int t = 0; t < TPW; ++t) {
+            const uint32_t sp = uni(sm.se[t]);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-            bu[ks] = 1 + max(max(byte_exp(xu, 2 * ks), byte_exp(xu, 2 * ks + 1)),
-                             7 + max(byte_exp(xm, 2 * ks), byte_exp(xm, 2 * ks + 1)) + esmax);
+            for (int r = 0; r < 4; ++r) es[t][r] = byte_exp(sp, r);
+            const int esmax = bound_exp(max(max(sp & 0xffu, (sp >> 8) & 0xffu),
+                                            max((sp >> 16) & 0xffu, sp >> 24)) << 23);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                bu[t][ks] = 1 + max(max(byte_exp(xu, 2 * ks), byte_exp(xu, 2 * ks + 1)),
+                                    7 + max(byte_exp(xm, 2 * ks), byte_exp(xm, 2 * ks + 1)) + esmax);
+        }
 
         // ---- this wave's token tile: U = U~ - W S, then Q' S on the matrix
         // unit while U is formed and published ----
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        f32x4 pq[4];
-        {
+        f32x4 pq[TPW][4];
+        if (ci > 0) store_out();
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
             uint4 Sh[4], Sl[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                Sh[r] = sm.sx[(r + rot) & 3][lane][0];
-                Sl[r] = sm.sx[(r + rot) & 3][lane][1];
+                Sh[r] = sm.sx[t][r][lane][0];
+                Sl[r] = sm.sx[t][r][lane][1];
             }
-            if (ci > 0) store_out();
             f32x4 y[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) y[r] = mfma_h(o.w[r], Sh[r], z);
 #pragma unroll
             for (int r = 0; r < 4; ++r) y[r] = mfma_h(o.w[r], Sl[r], y[r]);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) pq[r] = mfma_h(o.q[r], Sh[r], z);
+            for (int r = 0; r < 4; ++r) pq[t][r] = mfma_h(o.q[r], Sh[r], z);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) pq[r] = mfma_h(o.q[r], Sl[r], pq[r]);
-            f32x4 ws = y[0] * pow2f(byte_exp(xw, 0) + es[0] - 2 * F16_TOP);
+            for (int r = 0; r < 4; ++r) pq[t][r] = mfma_h(o.q[r], Sl[r], pq[t][r]);
+            f32x4 ws = y[0] * pow2f(byte_exp(xw, 0) + es[t][0] - 2 * F16_TOP);
 #pragma unroll
             for (int r = 1; r < 4; ++r) {
-                const float f = pow2f(byte_exp(xw, r) + es[r] - 2 * F16_TOP);
+                const float f = pow2f(byte_exp(xw, r) + es[t][r] - 2 * F16_TOP);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) ws[e] = __builtin_fmaf(y[r][e], f, ws[e]);
             }
-            const f32x4 u = scl4(f32x4{o.u.x, o.u.y, o.u.z, o.u.w} - ws, F16_TOP - bu[w >> 1]);
+            const float4 ut = o.u[t];
+            const f32x4 u = scl4(f32x4{ut.x, ut.y, ut.z, ut.w} - ws, F16_TOP - bu[t][w >> 1]);
             uint2 uh, ul;
             hsplit4(u, uh, ul);
-            sm.ux[w >> 1][lane].h[w & 1] = uh;
-            sm.ux[w >> 1][lane].l[w & 1] = ul;
+            sm.ux[t][w >> 1][lane].h[w & 1] = uh;
+            sm.ux[t][w >> 1][lane].l[w & 1] = ul;
         }
-        scan_load2(nx, nblk, w, tile, vo, rot);
+        if constexpr (DB) scan_load2(nx, nblk, w, tile0, vo);
+        else scan_load1(nx, nblk, w, tile0, vo);  // W, U~ and the exponents are consumed
         lds_barrier();
 
-        // ---- the whole U: this wave's state rows, and this wave's output tile
-        // O = scale (Q' S + O~) while the products run ----
-        {
+        // ---- the whole U: this wave's state rows, and this wave's output
+        // tiles O = scale (Q' S + O~) while the products run ----
+        f32x4 a[TPW][2][2];
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
             uint4 Uh[2], Ul[2];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const ScanSmem::Ux x = sm.ux[ks][lane];
+                const typename ScanSmem<TPW>::Ux x = sm.ux[t][ks][lane];
                 Uh[ks] = make_uint4(x.h[0].x, x.h[0].y, x.h[1].x, x.h[1].y);
                 Ul[ks] = make_uint4(x.l[0].x, x.l[0].y, x.l[1].x, x.l[1].y);
             }
-            f32x4 a[2][2];
 #pragma unroll
             for (int m = 0; m < 2; ++m)
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) a[m][ks] = mfma_h(o.kd[m][ks], Uh[ks], z);
+                for (int ks = 0; ks < 2; ++ks) a[t][m][ks] = mfma_h(o.kd[m][ks], Uh[ks], z);
 #pragma unroll
             for (int m = 0; m < 2; ++m)
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) a[m][ks] = mfma_h(o.kd[m][ks], Ul[ks], a[m][ks]);
-            scan_load3(nx, nblk, w, vo, vd);
+                for (int ks = 0; ks < 2; ++ks) a[t][m][ks] = mfma_h(o.kd[m][ks], Ul[ks], a[t][m][ks]);
+        }
+        if constexpr (DB) scan_load3(nx, nblk, w, vo, vd);
 
-            f32x4 po = pq[0] * pow2f(byte_exp(xq, 0) + es[0] - 2 * F16_TOP);
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            f32x4 po = pq[t][0] * pow2f(byte_exp(xq, 0) + es[t][0] - 2 * F16_TOP);
 #pragma unroll
             for (int r = 1; r < 4; ++r) {
-                const float f = pow2f(byte_exp(xq, r) + es[r] - 2 * F16_TOP);
+                const float f = pow2f(byte_exp(xq, r) + es[t][r] - 2 * F16_TOP);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) po[e] = __builtin_fmaf(pq[r][e], f, po[e]);
+                for (int e = 0; e < 4; ++e) po[e] = __builtin_fmaf(pq[t][r][e], f, po[e]);
             }
-            const float ob[4] = {o.o.x, o.o.y, o.o.z, o.o.w};
+            const float4 ot = o.o[t];
+            const float ob[4] = {ot.x, ot.y, ot.z, ot.w};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) opend[e] = p.scale * (po[e] + ob[e]);
-            orsrc = __builtin_amdgcn_make_buffer_rsrc(static_cast<char*>(p.out) + (row0 + lo) * orow * OB, 0,
-                                                      (int)((int64_t)(n - lo) * orow * OB), 0x00020000);
-            oshift = (uint32_t)((int64_t)lo * orow * OB);
+            for (int e = 0; e < 4; ++e) opend[t][e] = p.scale * (po[e] + ob[e]);
+        }
+        orsrc = __builtin_amdgcn_make_buffer_rsrc(static_cast<char*>(p.out) + (row0 + lo) * orow * OB, 0,
+                                                  (int)((int64_t)(n - lo) * orow * OB), 0x00020000);
+        oshift = (uint32_t)((int64_t)lo * orow * OB);
 
-            // S <- Diag(e^{G_C}) S + (K e^{G_C - G})^T U
+        // S <- Diag(e^{G_C}) S + (K e^{G_C - G})^T U
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
                 const float4 d = o.dec[m];
-                f32x4 sv = S[m] * f32x4{d.x, d.y, d.z, d.w};
+                f32x4 sv = S[t][m] * f32x4{d.x, d.y, d.z, d.w};
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
-                    const float f = pow2f(byte_exp(xk, 2 * m + ks) + bu[ks] - 2 * F16_TOP);
+                    const float f = pow2f(byte_exp(xk, 2 * m + ks) + bu[t][ks] - 2 * F16_TOP);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) sv[e] = __builtin_fmaf(a[m][ks][e], f, sv[e]);
+                    for (int e = 0; e < 4; ++e) sv[e] = __builtin_fmaf(a[t][m][ks][e], f, sv[e]);
                 }
-                S[m] = sv;
+                S[t][m] = sv;
             }
+        if constexpr (!DB) {  // Q', O~, Kd and e^{G_C} are consumed
+            scan_load2(nx, nblk, w, tile0, vo);
+            scan_load3(nx, nblk, w, vo, vd);
         }
 
         // absolute position reached
         if ((int64_t)spos - pad + (int64_t)ci * C + n == snap_next) {
             float* __restrict__ dsts = p.snapshots + snap_off;
 #pragma unroll
-            for (int m = 0; m < 2; ++m)
+            for (int t = 0; t < TPW; ++t)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int c = SL * w + 8 * g4 + 4 * m + e;
-                    if (c < dk) dsts[(int64_t)c * dv + j] = S[m][e];
-                }
+                for (int m = 0; m < 2; ++m)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int c = SL * w + 8 * g4 + 4 * m + e;
+                        if (c < dk) dsts[(int64_t)c * dv + j0 + 16 * t] = S[t][m][e];
+                    }
             snap_off += snap_step;
             snap_next += p.interval;
         }
     };
 
-    // The loop body always runs both halves, so the back edge is reached
+    // DB: the loop body always runs both halves, so the back edge is reached
     // only after the second half has consumed what the first half loaded;
     // an odd last chunk runs after the loop.
     int ci = 0;
-    for (; ci + 1 < nch; ci += 2) {
-        chunk(ci, opA, opB);
-        chunk(ci + 1, opB, opA);
+    if constexpr (DB) {
+        for (; ci + 1 < nch; ci += 2) {
+            chunk(ci, opA, opB);
+            chunk(ci + 1, opB, opA);
+        }
+        if (ci < nch) chunk(ci, opA, opB);
+    } else {
+        (void)opB;
+        for (; ci < nch; ++ci) chunk(ci, opA, opA);
     }
-    if (ci < nch) chunk(ci, opA, opB);
     if (nch > 0) store_out();
 
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int t = 0; t < TPW; ++t)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int c = SL * w + 8 * g4 + 4 * m + e;
-            if (c < dk) p.final_state[(srow + c) * dv + j] = S[m][e];
-        }
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int c = SL * w + 8 * g4 + 4 * m + e;
+                if (c < dk) p.final_state[(srow + c) * dv + j0 + 16 * t] = S[t][m][e];
+            }
 }
 
 // ---------------------------------------------------------------------------
@@ -1459,14 +1538,16 @@ void scan_kernel(ScanParams p) {
 constexpr size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WsLayout {
-    size_t chunk_start, snap_base, ops, total;
+    size_t chunk_start, snap_base, order, ops, total;
 };
 
 WsLayout ws_layout(int H, int num_seqs, int64_t max_chunks) {
     WsLayout l;
+    const size_t idx = align_up((size_t)(num_seqs + 1) * 4, 256);
     l.chunk_start = 0;
-    l.snap_base = align_up((size_t)(num_seqs + 1) * 4, 256);
-    l.ops = l.snap_base + align_up((size_t)(num_seqs + 1) * 4, 256);
+    l.snap_base = idx;
+    l.order = 2 * idx;
+    l.ops = 3 * idx;
     l.total = l.ops + (size_t)max_chunks * H * CHUNK_OPS * sizeof(uint4);
     return l;
 }
@@ -1477,10 +1558,11 @@ hipError_t launch_t(const PrefillArgs& a) {
     char* ws = static_cast<char*>(a.workspace);
     int32_t* chunk_start = reinterpret_cast<int32_t*>(ws + l.chunk_start);
     int32_t* snap_base = reinterpret_cast<int32_t*>(ws + l.snap_base);
+    int32_t* order = reinterpret_cast<int32_t*>(ws + l.order);
     uint4* ops = reinterpret_cast<uint4*>(ws + l.ops);
 
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(NT), 0, a.stream, a.cu_dev, a.start_dev,
-                       a.num_seqs, a.interval, chunk_start, snap_base);
+                       a.num_seqs, a.interval, chunk_start, snap_base, order);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 
@@ -1511,6 +1593,7 @@ hipError_t launch_t(const PrefillArgs& a) {
     sp.slots = a.slots;
     sp.chunk_start = chunk_start;
     sp.snap_base = snap_base;
+    sp.order = order;
     sp.ops = ops;
     sp.init = a.init;
     sp.init_if_started = a.init_if_started ? 1 : 0;
@@ -1521,14 +1604,30 @@ hipError_t launch_t(const PrefillArgs& a) {
     sp.H = a.H;
     sp.dk = a.dk;
     sp.dv = a.dv;
-    sp.ntiles = a.dv / 16;
     sp.scale = a.scale;
-    const int64_t nwg = (int64_t)a.num_seqs * a.H * sp.ntiles;
-    sp.nwg = (int)nwg;
-    if (a.out_bf16)
-        hipLaunchKernelGGL((scan_kernel<true>), dim3((unsigned)nwg), dim3(NT), 0, a.stream, sp);
-    else
-        hipLaunchKernelGGL((scan_kernel<false>), dim3((unsigned)nwg), dim3(NT), 0, a.stream, sp);
+    sp.nchains = a.num_seqs * a.H;
+    // the value-tile width: one 16-column tile per workgroup while that
+    // leaves at most two chains' worth of workgroups per compute unit (few,
+    // long recurrences: every unit runs one latency-bound chain and the
+    // double-buffered prefetch hides the loads); with more chains, two tiles
+    // per workgroup (W, Q', Kd loaded once for 32 columns), the loads being
+    // what bounds the scan then
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess)
+        (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    const int tiles = a.dv / 16;
+    const bool wide = tiles % 2 == 0 && ((int64_t)sp.nchains + 7) / 8 * 8 * tiles >= 2 * (int64_t)cus;
+    const int tpw = wide ? 2 : 1;
+    sp.ngroups = tiles / tpw;
+    const int64_t nwg = ((int64_t)sp.nchains + 7) / 8 * 8 * sp.ngroups;
+    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(NT), 0, a.stream, sp); };
+    if (a.out_bf16) {
+        if (wide) go(scan_kernel<true, true, 2>);
+        else go(scan_kernel<true, true, 1>);
+    } else {
+        if (wide) go(scan_kernel<false, true, 2>);
+        else go(scan_kernel<false, true, 1>);
+    }
     return hipGetLastError();
 }
 
@@ -1549,7 +1648,7 @@ size_t prefill_workspace_bytes(int, int, int H, int num_seqs, int64_t total_toke
 hipError_t launch_prefill(const PrefillArgs& a) {
     if (a.dk > DKP || a.dv > DVP || a.dv % 16 != 0) return hipErrorInvalidValue;
     // the host API rejects these before calling; nothing has been launched yet
-    if ((int64_t)a.num_seqs * a.H * (a.dv / 16) > 0x7fffffffLL) return hipErrorInvalidValue;
+    if (((int64_t)a.num_seqs * a.H + 7) / 8 * 8 * (a.dv / 16) > 0x7fffffffLL) return hipErrorInvalidValue;
     if (a.total_chunks * a.H > 0x7fffffffLL) return hipErrorInvalidValue;
     return a.in_bf16 ? launch_t<bf16_t>(a) : launch_t<float>(a);
 }

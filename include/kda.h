@@ -99,10 +99,12 @@ int64_t kda_snapshot_count(const int32_t *cu_seqlens_host, int32_t num_seqs,
                            int32_t interval);
 
 /*
- * Bytes of device workspace kda_prefill needs for this problem: 512 B of
- * offsets plus (floor(total_tokens / 64) + num_seqs) * num_heads * 115,280 B
- * of per-chunk operands (about 1.8 KB per token and head).  Returns 0 for
- * unsupported configs too; kda_prefill reports those.
+ * Bytes of device workspace kda_prefill needs for this problem: three
+ * per-sequence index arrays of 4 * (num_seqs + 1) bytes each, each rounded up
+ * to 256 (768 B for up to 63 sequences), plus (floor(total_tokens / 64) +
+ * num_seqs) * num_heads * 115,280 B of per-chunk operands (about 1.8 KB per
+ * token and head).  Returns 0 for unsupported configs too; kda_prefill
+ * reports those.
  */
 size_t kda_prefill_workspace_size(const kda_config *cfg, int32_t num_seqs,
                                   int64_t total_tokens);
@@ -228,9 +230,10 @@ int64_t kda_snapshot_count_at(const int32_t *cu_seqlens_host,
                               int32_t interval);
 
 /*
- * Workspace bytes for kda_prefill_pool: 512 B of offsets plus
- * (floor(total_tokens / 64) + 2 * num_seqs) * num_heads * 115,280 B (a start
- * position off the 64-token grid can add one chunk per sequence).
+ * Workspace bytes for kda_prefill_pool: the same index arrays as
+ * kda_prefill_workspace_size plus (floor(total_tokens / 64) + 2 * num_seqs) *
+ * num_heads * 115,280 B (a start position off the 64-token grid can add one
+ * chunk per sequence).
  */
 size_t kda_prefill_pool_workspace_size(const kda_config *cfg, int32_t num_seqs,
                                        int64_t total_tokens);

@@ -180,15 +180,18 @@ def test_prefill_requires_workspace(lib):
     assert libkda.workspace_size(cfg, 5, 200) >= need
 
 
-@pytest.mark.parametrize("N,T,H", [(1, 200, 2), (3, 64, 32), (16, 240704, 32), (1, 1 << 20, 32)])
+@pytest.mark.parametrize("N,T,H", [(1, 200, 2), (3, 64, 32), (16, 240736, 32), (1, 1 << 20, 32),
+                                   (700, 70000, 4)])
 def test_workspace_size_formula(lib, N, T, H):
-    """The sizes kda.h documents: 512 B of offsets plus (floor(T/64) + N)
-    operand blocks of 115,280 B per head (plain prefill), and
-    (floor(T/64) + 2N) blocks for the pool prefill."""
+    """The sizes kda.h documents: three index arrays of 4 (N + 1) bytes, each
+    rounded up to 256, plus (floor(T/64) + N) operand blocks of 115,280 B per
+    head (plain prefill), and (floor(T/64) + 2N) blocks for the pool
+    prefill."""
     from gated_delta_rule_111_amd import kda as libkda
     cfg = _cfg(H=H, d=128)
-    assert libkda.workspace_size(cfg, N, T) == 512 + (T // 64 + N) * H * 115280
-    assert libkda.pool_workspace_size(cfg, N, T) == 512 + (T // 64 + 2 * N) * H * 115280
+    idx = 3 * ((4 * (N + 1) + 255) // 256 * 256)
+    assert libkda.workspace_size(cfg, N, T) == idx + (T // 64 + N) * H * 115280
+    assert libkda.pool_workspace_size(cfg, N, T) == idx + (T // 64 + 2 * N) * H * 115280
 
 
 def _fe(lib, cu=(0, 64), H=2, dk=128, W=4, ind=0, outd=0, eps=1e-6, x=A, w=A, sin=(None, None),

@@ -235,8 +235,10 @@ def test_zero_values_give_exact_zeros():
 
 def test_resume_bit_exact_and_tiling_independent():
     """Resuming from a snapshot reproduces the uninterrupted run bit for bit,
-    also when the resumed call has a different batch (and so a different
-    dv-tile width)."""
+    also when the resumed call has a different batch and so a different
+    value-tile width: the uninterrupted call has 4 x 32 chains (two 16-column
+    tiles per workgroup), sequence 0 resumed alone has 32 (one tile per
+    workgroup), and its outputs and final state must still match exactly."""
     from gated_delta_rule_111_amd import kda
     from gated_delta_rule_111_amd.inputs import prefill_inputs
     lens = [1024, 700, 512, 333]
@@ -322,3 +324,15 @@ def test_prefill_on_side_stream():
         torch.cuda.synchronize()
         for a, b in zip(res, ref):
             assert torch.equal(a, b)
+
+
+def test_many_sequences_index_order():
+    """More sequences than the longest-first ordering handles (512): the scan
+    then deals its chains out in index order.  600 short sequences of
+    0..100 tokens, with initial states and snapshots, against the oracle."""
+    from gated_delta_rule_111_amd.inputs import prefill_inputs
+    g = torch.Generator().manual_seed(71)
+    lens = torch.randint(0, 101, (600,), generator=g).tolist()
+    inp = prefill_inputs(lens, H=2, dk=64, dv=64, seed=72, state_std=0.05, decay_shift=0.0,
+                         device=DEV)
+    _check(inp, interval=64, label="600 sequences")
