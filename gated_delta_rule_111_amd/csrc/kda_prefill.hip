@@ -1158,7 +1158,7 @@ struct ScanParams {
 // One chunk's operands for one lane, loaded ahead.
 template <int TPW>
 struct ScanOps {
-    uint4 w[4];           // W  of this wave's token tile, K-step r = state rows 32r ..
+    uint4 w[4];           // W  of this wave's token tile, K-step r = state rows 32((r + rot) & 3) ..
     uint4 q[4];           // Q' of this wave's token tile, likewise
     uint4 kd[2][2];       // Kd of this wave's state rows [m][ks]
     float4 u[TPW], o[TPW];  // U~ and O~ of this wave's token tile, per value tile
@@ -1181,12 +1181,15 @@ __device__ __forceinline__ float4 ld16f(__amdgpu_buffer_rsrc_t r, uint32_t voff,
     return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, unit * 16, 0));
 }
 
-// vo = 16 * lane; tile0 = first value tile of the workgroup
+// vo = 16 * lane; tile0 = first value tile of the workgroup.  K-step r of
+// W and Q' holds the state rows of block (r + rot) & 3: the workgroups of
+// one head take the blocks in different orders, so they do not all request
+// the same lines at once.
 template <int TPW>
 __device__ __forceinline__ void scan_load1(ScanOps<TPW>& o, __amdgpu_buffer_rsrc_t blk, int w, int tile0,
-                                           uint32_t vo) {
+                                           uint32_t vo, int rot) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) o.w[r] = ld16(blk, vo, OP_W + (r * 4 + w) * 64);
+    for (int r = 0; r < 4; ++r) o.w[r] = ld16(blk, vo, OP_W + (((r + rot) & 3) * 4 + w) * 64);
 #pragma unroll
     for (int t = 0; t < TPW; ++t) o.u[t] = ld16f(blk, vo, OP_U + ((tile0 + t) * 4 + w) * 64);
     o.ex = ld16(blk, 0, OP_EXP + w);
@@ -1195,9 +1198,9 @@ __device__ __forceinline__ void scan_load1(ScanOps<TPW>& o, __amdgpu_buffer_rsrc
 
 template <int TPW>
 __device__ __forceinline__ void scan_load2(ScanOps<TPW>& o, __amdgpu_buffer_rsrc_t blk, int w, int tile0,
-                                           uint32_t vo) {
+                                           uint32_t vo, int rot) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) o.q[r] = ld16(blk, vo, OP_Q + (r * 4 + w) * 64);
+    for (int r = 0; r < 4; ++r) o.q[r] = ld16(blk, vo, OP_Q + (((r + rot) & 3) * 4 + w) * 64);
 #pragma unroll
     for (int t = 0; t < TPW; ++t) o.o[t] = ld16f(blk, vo, OP_O + ((tile0 + t) * 4 + w) * 64);
 }
@@ -1250,6 +1253,11 @@ void scan_kernel(ScanParams p) {
     const int b = p.order[rk];
     const int dk = p.dk, dv = p.dv;
     const int j0 = 16 * tile0 + i16;  // value column of this lane in tile t: j0 + 16 t
+    // the order of the state-row blocks (see scan_load1): a function of the
+    // pair of tiles, so the same for a tile at either width
+    const int rot = (tile0 >> 1) & 3;
+    const uint32_t rsh = 8 * rot;
+    auto rot_bytes = [rsh](uint32_t x) { return (x >> rsh) | (x << ((32 - rsh) & 31)); };
     const int64_t seq0 = p.cu[b];
     const int len = p.cu[b + 1] - p.cu[b];
     // chunks sit at absolute multiples of C (see plan_kernel): pad leading
@@ -1285,8 +1293,8 @@ void scan_kernel(ScanParams p) {
     ScanOps<TPW> opA, opB;
     if (nch > 0) {
         const __amdgpu_buffer_rsrc_t blk = scan_block(p, cbase, h);
-        scan_load1(opA, blk, w, tile0, vo);
-        scan_load2(opA, blk, w, tile0, vo);
+        scan_load1(opA, blk, w, tile0, vo, rot);
+        scan_load2(opA, blk, w, tile0, vo, rot);
         scan_load3(opA, blk, w, vo, vd);
     }
 
@@ -1365,20 +1373,20 @@ void scan_kernel(ScanParams p) {
             sm.sx[t][w][lane][1] = ll;
             if (lane == 0) reinterpret_cast<uint8_t*>(&sm.se[t])[w] = exp_byte(sb);
         }
-        if constexpr (DB) scan_load1(nx, nblk, w, tile0, vo);
+        if constexpr (DB) scan_load1(nx, nblk, w, tile0, vo, rot);
         lds_barrier();
 
         // exponents of this chunk (scalar): the state-row blocks of each tile,
         // and the bound of U over each pair of token tiles (a K-step of the
         // state update): |U| <= |U~| + 128 max|W| max|S| < 2^bu[t][ks]
-        const uint32_t xw = uni(o.ex.x), xq = uni(o.ex.y), xk = uni(o.ex.z),
+        const uint32_t xw = rot_bytes(uni(o.ex.x)), xq = rot_bytes(uni(o.ex.y)), xk = uni(o.ex.z),
                        xu = uni(o.ex4.x), xm = uni(o.ex4.y);
         int es[TPW][4], bu[TPW][2];
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
-            const uint32_t sp = uni(sm.se[t]);
+            const uint32_t sp = uni(sm.se[t]), spr = rot_bytes(sp);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) es[t][r] = byte_exp(sp, r);
+            for (int r = 0; r < 4; ++r) es[t][r] = byte_exp(spr, r);
             const int esmax = bound_exp(max(max(sp & 0xffu, (sp >> 8) & 0xffu),
                                             max((sp >> 16) & 0xffu, sp >> 24)) << 23);
 #pragma unroll
@@ -1397,8 +1405,8 @@ void scan_kernel(ScanParams p) {
             uint4 Sh[4], Sl[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                Sh[r] = sm.sx[t][r][lane][0];
-                Sl[r] = sm.sx[t][r][lane][1];
+                Sh[r] = sm.sx[t][(r + rot) & 3][lane][0];
+                Sl[r] = sm.sx[t][(r + rot) & 3][lane][1];
             }
             f32x4 y[4];
 #pragma unroll
@@ -1423,8 +1431,8 @@ void scan_kernel(ScanParams p) {
             sm.ux[t][w >> 1][lane].h[w & 1] = uh;
             sm.ux[t][w >> 1][lane].l[w & 1] = ul;
         }
-        if constexpr (DB) scan_load2(nx, nblk, w, tile0, vo);
-        else scan_load1(nx, nblk, w, tile0, vo);  // W, U~ and the exponents are consumed
+        if constexpr (DB) scan_load2(nx, nblk, w, tile0, vo, rot);
+        else scan_load1(nx, nblk, w, tile0, vo, rot);  // W, U~ and the exponents are consumed
         lds_barrier();
 
         // ---- the whole U: this wave's state rows, and this wave's output
@@ -1484,7 +1492,7 @@ void scan_kernel(ScanParams p) {
                 S[t][m] = sv;
             }
         if constexpr (!DB) {  // Q', O~, Kd and e^{G_C} are consumed
-            scan_load2(nx, nblk, w, tile0, vo);
+            scan_load2(nx, nblk, w, tile0, vo, rot);
             scan_load3(nx, nblk, w, vo, vd);
         }
 
