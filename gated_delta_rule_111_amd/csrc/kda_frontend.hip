@@ -25,8 +25,9 @@
 // - each head's sum of squares is reduced over its dk/8 lanes with DPP row
 //   operations (cross-lane moves inside the VALU, no LDS);
 // - runs ignore sequence boundaries: a wave finds the sequence of its first
-//   token with a 64-way search of the offsets (none when every sequence has
-//   one token, the decode step) and then follows them;
+//   token with a 64-way search of the offsets and then follows them;
+// - when every sequence has one token (a decode step) a kernel of its own
+//   gives each wave a few sequences and loads all their rows at once;
 // - the first W-1 tokens of every sequence, and its convolution state, belong
 //   to the run holding the sequence's first token (which may go up to W-2
 //   tokens past its own end).  Exactly one wave reads and writes each slice
@@ -95,6 +96,22 @@ __device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
     reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
 
+// the same with a nontemporal hint: the decode step's outputs and new states
+// are not read again by this launch, and streaming them past the caches
+// shortens its end (measured: 7.2 -> 6.8 us for 256 sequences x 4096 channels)
+typedef uint32_t u32x4_v __attribute__((ext_vector_type(4)));
+typedef float f32x4_v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store8_stream(bf16_t* p, const float (&v)[8]) {
+    const u32x4_v t = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                       pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+    __builtin_nontemporal_store(t, reinterpret_cast<u32x4_v*>(p));
+}
+__device__ __forceinline__ void store8_stream(float* p, const float (&v)[8]) {
+    const f32x4_v a = {v[0], v[1], v[2], v[3]}, b = {v[4], v[5], v[6], v[7]};
+    __builtin_nontemporal_store(a, reinterpret_cast<f32x4_v*>(p));
+    __builtin_nontemporal_store(b, reinterpret_cast<f32x4_v*>(p) + 1);
+}
+
 // sum over the `lanes` consecutive lanes of one head (2, 4, 8 or 16), left
 // in every one of them: pairs and quads by quad permutations, 8 lanes by
 // mirroring the half row, 16 lanes by rotating the row by 4 and then by 8
@@ -150,9 +167,7 @@ __device__ __forceinline__ void widen(const Raw8<float>& r, float (&v)[8]) {
     v[4] = r.b.x; v[5] = r.b.y; v[6] = r.b.z; v[7] = r.b.w;
 }
 
-// G: tokens per group of loads (8; 1 for one-token sequences, where a run
-// holds a token or a few and the registers of larger groups would only
-// lower the occupancy)
+// G: tokens per group of loads (the launch uses 8)
 template <int W, int G, typename TIn, typename TOut>
 __global__ __launch_bounds__(64 * FE_WAVES) void frontend_kernel(FeParams p) {
     constexpr int NW = W > 1 ? W - 1 : 1;  // window rows (unused when W == 1)
@@ -256,8 +271,8 @@ __global__ __launch_bounds__(64 * FE_WAVES) void frontend_kernel(FeParams p) {
     // Sequence bookkeeping (uniform across the wave).  b is the sequence of
     // the current token, [s, e) its tokens; `owned` when it starts in this
     // run, in which case this wave reads and writes its state.
-    auto cu_at = [&](int i) { return p.unit ? i : p.cu[i]; };
-    int b = p.unit ? t_begin : first_seq_reaching(p.cu, p.N, t_begin, lane);
+    auto cu_at = [&](int i) { return p.cu[i]; };
+    int b = first_seq_reaching(p.cu, p.N, t_begin, lane);
     int s = cu_at(b), e = cu_at(b + 1);
     bool owned = s >= t_begin;
     int64_t slot = 0;
@@ -383,10 +398,115 @@ __global__ __launch_bounds__(64 * FE_WAVES) void frontend_kernel(FeParams p) {
     }
 }
 
+// One-token sequences (a decode step): each sequence is one token whose
+// window is its state, so a wave takes FE_UNIT tokens of one slab and issues,
+// before any arithmetic, the slot lookups, then every token's input and state
+// rows, then the taps (read once for all its tokens).  The new state of a
+// sequence is its old state shifted by one row with the token appended; each
+// state slice is read and written by the one wave that owns the token, reads
+// first, so the state may be updated in place.  (256 sequences x 4096
+// channels: 9.5 us with the general kernel, one token per wave; 7.2 us with
+// 2 or 4 tokens per wave; 8 tokens per wave leave too few waves.)
+constexpr int FE_UNIT = 4;
+
+template <int W, typename TIn, typename TOut>
+__global__ __launch_bounds__(64 * FE_WAVES) void frontend_unit_kernel(FeParams p) {
+    constexpr int NW = W > 1 ? W - 1 : 1;
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int L = blockIdx.x;
+    if ((p.nwg & 7) == 0) L = (blockIdx.x & 7) * (p.nwg >> 3) + (blockIdx.x >> 3);
+    const int grp = L % p.ngroups;
+    const int rest = L / p.ngroups;
+    const int slab = rest % p.nslab;
+    const int tsel = rest / p.nslab;
+    const int t0 = (grp * FE_WAVES + wv) * FE_UNIT;
+    if (t0 >= p.T) return;
+    const int T = p.T;
+    const int ch0 = slab * FE_SLAB + lane * FE_LANE_CH;
+    const bool live = ch0 < p.C;
+    const int ch = live ? ch0 : 0;
+    const int64_t C = p.C;
+    const TIn* __restrict__ x = static_cast<const TIn*>(p.x[tsel]) + ch;
+    TOut* __restrict__ y = static_cast<TOut*>(p.y[tsel]) + ch;
+    const TIn* sin = static_cast<const TIn*>(p.sin[tsel]);   // may alias sout
+    TIn* sout = static_cast<TIn*>(p.sout[tsel]);
+
+    int64_t slot[FE_UNIT];
+#pragma unroll
+    for (int u = 0; u < FE_UNIT; ++u) {
+        const int t = min(t0 + u, T - 1);
+        slot[u] = p.slots ? p.slots[t] : t;
+    }
+    Raw8<TIn> xr[FE_UNIT];
+#pragma unroll
+    for (int u = 0; u < FE_UNIT; ++u) xr[u] = load_raw(x + (int64_t)min(t0 + u, T - 1) * C);
+    Raw8<TIn> hr[FE_UNIT][NW];
+    if (W > 1 && sin) {
+#pragma unroll
+        for (int u = 0; u < FE_UNIT; ++u)
+#pragma unroll
+            for (int j = 0; j < W - 1; ++j) hr[u][j] = load_raw(sin + (slot[u] * (W - 1) + j) * C + ch);
+    }
+    float wt[W][8];  // -log2(e) w[ch + i][j], as in frontend_kernel
+    {
+        const float4* wp = reinterpret_cast<const float4*>(p.w[tsel] + (int64_t)ch * W);
+        float buf[8 * W];
+#pragma unroll
+        for (int i = 0; i < 2 * W; ++i) {
+            const float4 t = wp[i];
+            buf[4 * i] = t.x; buf[4 * i + 1] = t.y; buf[4 * i + 2] = t.z; buf[4 * i + 3] = t.w;
+        }
+#pragma unroll
+        for (int j = 0; j < W; ++j)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) wt[j][i] = buf[i * W + j] * -1.4426950408889634f;
+    }
+    const int head_lanes = p.dk / FE_LANE_CH;
+#pragma unroll
+    for (int u = 0; u < FE_UNIT; ++u) {
+        if (t0 + u >= T) break;
+        float xv[8], win[NW][8];
+        widen(xr[u], xv);
+#pragma unroll
+        for (int j = 0; j < W - 1; ++j) {
+            if (sin) {
+                widen(hr[u][j], win[j]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) win[j][i] = 0.f;
+            }
+        }
+        float a[8];
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float zz = wt[W - 1][i] * xv[i];
+#pragma unroll
+            for (int j = 0; j < W - 1; ++j) zz = fmaf(wt[j][i], win[j][i], zz);
+            a[i] = zz * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(zz));
+            ss = fmaf(a[i], a[i], ss);
+        }
+        ss = head_sum(ss, head_lanes);
+        const float inv = -__builtin_amdgcn_rsqf(ss + p.eps2);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a[i] *= inv;
+        if (live) {
+            store8_stream(y + (int64_t)(t0 + u) * C, a);
+            if (W > 1 && sout) {
+                // the new history: the old rows 1 .. W-2, then this token
+#pragma unroll
+                for (int j = 0; j + 1 < W - 1; ++j) store8_stream(sout + (slot[u] * (W - 1) + j) * C + ch, win[j + 1]);
+                store8_stream(sout + (slot[u] * (W - 1) + (W - 2)) * C + ch, xv);
+            }
+        }
+    }
+}
+
 template <int W, typename TIn, typename TOut>
 hipError_t launch_w(const FeParams& p, hipStream_t stream) {
     if (p.unit)
-        hipLaunchKernelGGL((frontend_kernel<W, 1, TIn, TOut>), dim3(p.nwg), dim3(64 * FE_WAVES),
+        hipLaunchKernelGGL((frontend_unit_kernel<W, TIn, TOut>), dim3(p.nwg), dim3(64 * FE_WAVES),
                            0, stream, p);
     else
         hipLaunchKernelGGL((frontend_kernel<W, 8, TIn, TOut>), dim3(p.nwg), dim3(64 * FE_WAVES),
@@ -432,8 +552,8 @@ hipError_t launch_frontend(const FrontendArgs& a) {
     p.unit = a.unit_lengths ? 1 : 0;
     // runs of one-token sequences each read and write a state per token, so
     // they stay short
-    p.R = std::min(p.unit ? 4 : FE_MAX_RUN,
-                   std::max(1, (int)(((int64_t)p.T + runs_wanted - 1) / runs_wanted)));
+    p.R = p.unit ? FE_UNIT
+                 : std::min(FE_MAX_RUN, std::max(1, (int)(((int64_t)p.T + runs_wanted - 1) / runs_wanted)));
     p.nrun = p.T > 0 ? (p.T + p.R - 1) / p.R : 1;
     p.ngroups = (p.nrun + FE_WAVES - 1) / FE_WAVES;
     p.nwg = 2 * p.nslab * p.ngroups;

@@ -151,6 +151,48 @@ def test_frontend_decode_in_place():
             assert np.array_equal(to_np(st[int(slots[b])]), new_st[0]), f"state of {b}"
 
 
+@pytest.mark.parametrize("W", [1, 2, 4, 8])
+@pytest.mark.parametrize("in_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("N", [1, 37])
+def test_frontend_one_token_sequences(W, in_dtype, N):
+    """Every sequence one token long (the decode-step launch): an odd count
+    (the last wave holds fewer tokens), H*dk = 320 (a part-empty slab), history
+    from one pool through permuted slots, new history to another; then the
+    same call with no history (zeros) and no state written."""
+    from gated_delta_rule_111_amd import kda
+    from gated_delta_rule_111_amd.inputs import frontend_inputs
+    print(f"[frontend one-token] W={W} in={in_dtype} N={N}", flush=True)
+    S = N + 5
+    inp = frontend_inputs([1] * N, 5, 64, W, seed=300 + W + N, in_dtype=in_dtype,
+                          num_slots=S if W > 1 else None, device=DEV)
+    cu_host = list(range(N + 1))
+    cu = to_np(inp.cu_seqlens)
+    if W > 1:  # W = 1 has no history
+        slots = torch.tensor(np.random.default_rng(W + N).permutation(S)[:N].astype(np.int32),
+                             device=DEV)
+        out_q = torch.full_like(inp.state_q, 3.0)
+        out_k = torch.full_like(inp.state_k, -3.0)
+        q, k = kda.qk_frontend(inp.xq, inp.xk, inp.wq, inp.wk, inp.cu_seqlens, eps=1e-6,
+                               conv_state_q=inp.state_q, conv_state_k=inp.state_k,
+                               conv_state_out_q=out_q, conv_state_out_k=out_k, slots=slots,
+                               cu_seqlens_host=cu_host, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        yq, yk, sq, sk = _oracle(inp, W, 1e-6, inp.state_q, inp.state_k, slots)
+        assert seq_head_err(to_np(q), yq, cu) <= TOL and seq_head_err(to_np(k), yk, cu) <= TOL
+        used = to_np(slots).tolist()
+        for s in range(S):
+            if s in used:
+                assert np.array_equal(to_np(out_q[s]), sq[s]), f"q state of slot {s}"
+                assert np.array_equal(to_np(out_k[s]), sk[s]), f"k state of slot {s}"
+            else:
+                assert torch.all(out_q[s] == 3.0) and torch.all(out_k[s] == -3.0), f"slot {s}"
+    q0, k0 = kda.qk_frontend(inp.xq, inp.xk, inp.wq, inp.wk, inp.cu_seqlens, eps=1e-6,
+                             cu_seqlens_host=cu_host, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    zq, zk, _, _ = _oracle(inp, W, 1e-6)
+    assert seq_head_err(to_np(q0), zq, cu) <= TOL and seq_head_err(to_np(k0), zk, cu) <= TOL
+
+
 def test_frontend_full_size():
     """T = 8192 tokens, H = 32, dk = 128, W = 4, bf16 in: the launch shape of
     the benchmark (runs of 16 tokens).  fp32 outputs against the oracle on
