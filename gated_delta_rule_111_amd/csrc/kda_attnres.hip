@@ -136,12 +136,30 @@ void attnres_kernel(ArParams p, int64_t T) {
     const bool live = c0 < d;          // threads past the row hold zeros
     const int cc = live ? c0 : 0;
 
-    // the query and gamma slices (cache-resident) are read at their use in
-    // every token, which keeps two tokens' rows within the register budget
-    auto slice4 = [&](const float* a, float (&v)[EPT]) {
+    // The query and gamma slices are copied to LDS once (dynamic LDS of
+    // 2 x blockDim.x x EPT floats) and read there at their use in every
+    // token: that keeps two tokens' rows within the register budget, and an
+    // LDS read does not wait on the vector-memory counter, which the loads of
+    // the next token's rows hold (vector-memory operations complete in issue
+    // order, so waiting for a load issued after them waits for them too).
+    // Each thread reads back only the slices it wrote: no barrier.
+    extern __shared__ __align__(16) float qg[];
+    auto stage = [&]() {
+        const float4* wq = reinterpret_cast<const float4*>(p.w + cc);
+        const float4* gq = reinterpret_cast<const float4*>((p.gamma ? p.gamma : p.w) + cc);
+        float4* dq = reinterpret_cast<float4*>(&qg[EPT * tid]);
+        float4* dg = reinterpret_cast<float4*>(&qg[EPT * (blockDim.x + tid)]);
 #pragma unroll
         for (int q = 0; q < EPT / 4; ++q) {
-            const float4 t = reinterpret_cast<const float4*>(a + cc)[q];
+            dq[q] = wq[q];
+            dg[q] = gq[q];
+        }
+    };
+    auto slice4 = [&](int which, float (&v)[EPT]) {
+        const float* src = &qg[EPT * (which * blockDim.x + tid)];
+#pragma unroll
+        for (int q = 0; q < EPT / 4; ++q) {
+            const float4 t = reinterpret_cast<const float4*>(src)[q];
             v[4 * q] = t.x; v[4 * q + 1] = t.y; v[4 * q + 2] = t.z; v[4 * q + 3] = t.w;
         }
     };
@@ -151,17 +169,23 @@ void attnres_kernel(ArParams p, int64_t T) {
         Slice<TIn, EPT> s[M];
         Slice<TIn, EPT> x;
     };
-    auto fetch = [&](Rows& r, int64_t t) {
-        const int64_t row = t * d + cc;
+    // The row loads are unconditional: a token past the end loads the rows
+    // of t_else (a token this workgroup has just loaded, so cache hits) and
+    // a missing residual reads source 0, unused.  A load under a branch
+    // would leave the compiler copying its registers where the paths join,
+    // which waits for the load to land and undoes the prefetch.
+    const TIn* xs = static_cast<const TIn*>(p.x ? p.x : p.src[0]);
+    auto fetch = [&](Rows& r, int64_t t, int64_t t_else) {
+        const int64_t row = (t < T ? t : t_else) * d + cc;
 #pragma unroll
         for (int m = 0; m < M; ++m) r.s[m].load(static_cast<const TIn*>(p.src[m]) + row);
-        if (p.x) r.x.load(static_cast<const TIn*>(p.x) + row);
+        r.x.load(xs + row);
     };
 
     auto token = [&](Rows& r, int64_t t) {
         // logits: per-thread partial dot products, then across the workgroup
         float w[EPT];
-        slice4(p.w, w);
+        slice4(0, w);
         float part[M];
 #pragma unroll
         for (int m = 0; m < M; ++m) {
@@ -180,13 +204,13 @@ void attnres_kernel(ArParams p, int64_t T) {
 #pragma unroll
             for (int m = 0; m < M; ++m) red[wave][m] = part[m];
         }
-        __syncthreads();
+        __barrier(__CLK_LOCAL_MEM_FENCE);
         if (tid < M) {
             float s = 0.f;
             for (int i = 0; i < nw; ++i) s += red[i][tid];
             res[tid] = s * p.scale;
         }
-        __syncthreads();
+        __barrier(__CLK_LOCAL_MEM_FENCE);
 
         // softmax over the sources (every thread, from the shared logits)
         float pr[M];
@@ -222,13 +246,13 @@ void attnres_kernel(ArParams p, int64_t T) {
         for (int i = 0; i < EPT; ++i) ss = fmaf(h[i], h[i], ss);
         ss = wave_sum(live ? ss : 0.f);
         if (lane == 0) red[wave][M] = ss;
-        __syncthreads();
+        __barrier(__CLK_LOCAL_MEM_FENCE);
         if (tid == 0) {
             float s = 0.f;
             for (int i = 0; i < nw; ++i) s += red[i][M];
             res[M] = rsqrtf(s / (float)d + p.eps);
         }
-        __syncthreads();
+        __barrier(__CLK_LOCAL_MEM_FENCE);
         if (live) {
             const float rr = res[M];
             const int64_t orow = t * d + c0;
@@ -236,7 +260,7 @@ void attnres_kernel(ArParams p, int64_t T) {
             float yv[EPT];
             if (p.gamma) {
                 float gm[EPT];
-                slice4(p.gamma, gm);
+                slice4(1, gm);
 #pragma unroll
                 for (int i = 0; i < EPT; ++i) yv[i] = h[i] * rr * gm[i];
             } else {
@@ -250,23 +274,30 @@ void attnres_kernel(ArParams p, int64_t T) {
     // tokens blockIdx.x, + gridDim.x, ...: with bf16 rows the next token's
     // rows are requested before the current one is reduced (two register
     // sets used in turn, so nothing loaded is copied); fp32 rows, twice the
-    // registers, go one token at a time
+    // registers, go one token at a time.  The workgroup barriers inside a
+    // token leave loads in flight (they order LDS only).
     const int64_t step = gridDim.x;
     int64_t t = blockIdx.x;
     Rows ra;
     if constexpr (sizeof(TIn) == 2) {
         Rows rb;
-        if (t < T) fetch(ra, t);
+        fetch(ra, t, t);
+        stage();
+        if (t + step >= T) {  // one token for this workgroup
+            token(ra, t);
+            return;
+        }
         for (; t < T; t += 2 * step) {
-            if (t + step < T) fetch(rb, t + step);
+            fetch(rb, t + step, t);  // past the end: the current rows again (cache hits)
             token(ra, t);
             if (t + step >= T) break;
-            if (t + 2 * step < T) fetch(ra, t + 2 * step);
+            fetch(ra, t + 2 * step, t + step);
             token(rb, t + step);
         }
     } else {
+        stage();
         for (; t < T; t += step) {
-            fetch(ra, t);
+            fetch(ra, t, t);
             token(ra, t);
         }
     }
@@ -288,12 +319,13 @@ hipError_t launch_m(const ArParams& p, int64_t T, hipStream_t stream) {
     constexpr int EPT = 8;
     const int threads = (p.d / EPT + 63) / 64 * 64;
     // as many workgroups as are resident at once; each walks its tokens
+    const size_t lds = 2 * sizeof(float) * EPT * threads;  // query and gamma slices
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attnres_kernel<M, TIn, TOut>,
-                                                     threads, 0) != hipSuccess || per_cu < 1)
+                                                     threads, lds) != hipSuccess || per_cu < 1)
         per_cu = 1;
     const int64_t grid = std::min<int64_t>(T, (int64_t)per_cu * compute_units());
-    hipLaunchKernelGGL((attnres_kernel<M, TIn, TOut>), dim3((unsigned)grid), dim3(threads), 0,
+    hipLaunchKernelGGL((attnres_kernel<M, TIn, TOut>), dim3((unsigned)grid), dim3(threads), lds,
                        stream, p, T);
     return hipGetLastError();
 }
