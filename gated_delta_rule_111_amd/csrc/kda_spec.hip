@@ -54,7 +54,8 @@ struct SpecLayout {
 // one draft's tokens in fp32; G holds g, then its cumulative sum.  Once the
 // Grams are formed, q holds Q' (verify) or W (commit) and, in a commit, k
 // holds k_t e^(G_{a-1} - G_t), each written by the thread that owns the
-// channel.
+// channel; v holds O~ (verify) or U~ (commit), each written by the thread
+// that owns the column.
 template <int DK, int DV>
 struct SpecTokens {
     float k[SP_MAX][DK];
@@ -68,8 +69,9 @@ struct SpecTokens {
 template <int DK, int DV, int NB, int RH>
 struct __align__(16) SpecSmem {
     SpecTokens<DK, DV> tok[NB];
-    float Y[NB][SP_MAX][DV];   // per draft: O~ (verify) or U~ (commit)
-    float P[RH][SP_MAX][DV];   // each row half's sums of X S
+    // each row half's sums of X S; with two drafts (DK = DV) these live in
+    // the drafts' G arrays instead, dead by the time the state is multiplied
+    float P[NB == 1 ? RH : 1][SP_MAX][DV];
     float dec[DK];             // e^(G_{a-1}) (commit)
     float A[SP_MAX][SP_MAX];
     float B[SP_MAX][SP_MAX];
@@ -139,7 +141,8 @@ __device__ __forceinline__ void lds_rows(const float* p, float (&x)[RPL]) {
 
 // MODE 1 verify, 2 commit, 3 step (commit the previous draft, then verify)
 template <int DK, int DV, typename TIn, typename TOut, int MODE>
-__global__ __launch_bounds__((64 * SpecLayout<DK, DV>::WAVES)) __attribute__((amdgpu_waves_per_eu(6)))
+__global__ __launch_bounds__((64 * SpecLayout<DK, DV>::WAVES))
+__attribute__((amdgpu_waves_per_eu(MODE == 3 ? 8 : 6)))
 void spec_kernel(SpecParams p) {
     using L = SpecLayout<DK, DV>;
     constexpr int WAVES = L::WAVES;
@@ -243,25 +246,29 @@ void spec_kernel(SpecParams p) {
     // the n x n Grams (B only when verifying), then T, TB (and M)
     auto grams = [&](const SpecTokens<DK, DV>& b, int nt, bool with_b) {
         __syncthreads();  // the buffers are complete; earlier reads of the work arrays done
+        // one pair (t, s), s <= t, per 16-lane group (4 per wave), DK / 16
+        // channels per lane, summed over the group by DPP moves; the groups
+        // of a wave start at different channels (fewer LDS bank conflicts)
         const int pairs = nt * (nt + 1) / 2;
-        for (int pr = wave; pr < pairs; pr += WAVES) {
-            // pair index -> (t, s), s <= t, row by row over the lower triangle
+        const int grp = lane >> 4, gl = lane & 15;
+        for (int pr0 = 4 * wave; pr0 < pairs; pr0 += 4 * WAVES) {
+            const int pr = pr0 + grp;
+            // pair index -> (t, s), row by row over the lower triangle
+            const int pc = pr < pairs ? pr : 0;
             int t = 0;
-            while ((t + 1) * (t + 2) / 2 <= pr) ++t;
-            const int s2 = pr - t * (t + 1) / 2;
+            while ((t + 1) * (t + 2) / 2 <= pc) ++t;
+            const int s2 = pc - t * (t + 1) / 2;
             float ka = 0.f, qb = 0.f;
-#pragma unroll
-            for (int c0 = 0; c0 < DK; c0 += 64) {
-                const int c = c0 + lane;
-                if (c < DK) {
-                    const float ks = b.k[s2][c] * exp_gate(b.G[t][c] - b.G[s2][c]);
-                    ka = fmaf(b.k[t][c], ks, ka);
-                    if (with_b) qb = fmaf(b.q[t][c], ks, qb);
-                }
+#pragma unroll 2
+            for (int i = 0; i < DK / 16; ++i) {
+                const int c = (gl + 16 * (i + grp)) % DK;
+                const float ks = b.k[s2][c] * exp_gate(b.G[t][c] - b.G[s2][c]);
+                ka = fmaf(b.k[t][c], ks, ka);
+                if (with_b) qb = fmaf(b.q[t][c], ks, qb);
             }
-            ka = wave_sum(ka);
-            if (with_b) qb = wave_sum(qb);
-            if (lane == 0) {
+            ka = group_sum<16>(ka);
+            if (with_b) qb = group_sum<16>(qb);
+            if (gl == 0 && pr < pairs) {
                 sm.A[t][s2] = s2 < t ? b.beta[t] * ka : 0.f;
                 if (with_b) sm.B[t][s2] = qb;
             }
@@ -298,6 +305,15 @@ void spec_kernel(SpecParams p) {
         }
     };
 
+    // the partial sums of row half r
+    auto pbuf = [&](int r) -> float (*)[DV] {
+        if constexpr (NB == 1) {
+            return sm.P[r];
+        } else {
+            static_assert(DK == DV && RH <= NB, "partial sums in the G arrays");
+            return sm.tok[r].G;
+        }
+    };
     // P[rh][t] = this row half's sums of X_t S over its rows, for t < nt
     auto xs = [&](const float (*X)[DK], int nt) {
         for (int t = 0; t < nt; ++t) {
@@ -312,15 +328,15 @@ void spec_kernel(SpecParams p) {
             y0 = group_sum<RG>(y0); y1 = group_sum<RG>(y1);
             y2 = group_sum<RG>(y2); y3 = group_sum<RG>(y3);
             if (rg == 0)
-                *reinterpret_cast<float4*>(&sm.P[rh][t][col]) = make_float4(y0, y1, y2, y3);
+                *reinterpret_cast<float4*>(&pbuf(rh)[t][col]) = make_float4(y0, y1, y2, y3);
         }
         __syncthreads();
     };
     // sum of the row halves' partials at (t, columns c .. c+3)
     auto psum = [&](int t, int c) {
-        float4 r = *reinterpret_cast<const float4*>(&sm.P[0][t][c]);
+        float4 r = *reinterpret_cast<const float4*>(&pbuf(0)[t][c]);
         if constexpr (RH == 2) {
-            const float4 r1 = *reinterpret_cast<const float4*>(&sm.P[1][t][c]);
+            const float4 r1 = *reinterpret_cast<const float4*>(&pbuf(1)[t][c]);
             r.x += r1.x; r.y += r1.y; r.z += r1.z; r.w += r1.w;
         }
         return r;
@@ -328,7 +344,7 @@ void spec_kernel(SpecParams p) {
 
     // verify: O = scale (Q' S + O~) for the nt tokens of buffer b; the
     // token-side part first (no state needed), then the outputs
-    auto prep_verify = [&](SpecTokens<DK, DV>& b, int nt, float (*Y)[DV]) {
+    auto prep_verify = [&](SpecTokens<DK, DV>& b, int nt) {
         grams(b, nt, true);
         if (tid < DK) {  // Q' = Q e^G - M (K e^G) in place of q, one channel per thread
             const int c = tid;
@@ -345,20 +361,23 @@ void spec_kernel(SpecParams p) {
                     b.q[t][c] = x;
                 }
             }
-        } else if (tid < DK + DV) {  // O~ = M V, one column per thread
+        } else if (tid < DK + DV) {  // O~ = M V in place of v, one column per thread
             const int j = tid - DK;
+            float vv[SP_MAX];
+#pragma unroll
+            for (int s2 = 0; s2 < SP_MAX; ++s2) vv[s2] = s2 < nt ? b.v[s2][j] : 0.f;
 #pragma unroll
             for (int t = 0; t < SP_MAX; ++t) {
                 if (t < nt) {
                     float x = 0.f;
 #pragma unroll
-                    for (int s2 = 0; s2 <= t; ++s2) x = fmaf(sm.M[t][s2], b.v[s2][j], x);
-                    Y[t][j] = x;
+                    for (int s2 = 0; s2 <= t; ++s2) x = fmaf(sm.M[t][s2], vv[s2], x);
+                    b.v[t][j] = x;
                 }
             }
         }
     };
-    auto emit_verify = [&](SpecTokens<DK, DV>& b, int nt, const float (*Y)[DV]) {
+    auto emit_verify = [&](SpecTokens<DK, DV>& b, int nt) {
         __syncthreads();
         xs(b.q, nt);
         // outputs, 4 consecutive columns of one token per thread
@@ -367,7 +386,7 @@ void spec_kernel(SpecParams p) {
         for (int i = tid; i < nt * (DV / 4); i += NT) {
             const int t = i / (DV / 4), c = 4 * (i - t * (DV / 4));
             const float4 o = psum(t, c);
-            const float4 y = *reinterpret_cast<const float4*>(&Y[t][c]);
+            const float4 y = *reinterpret_cast<const float4*>(&b.v[t][c]);
             io<TOut>::store4(og + ((tok0 + t) * H + h) * DV + c, sc * (o.x + y.x),
                              sc * (o.y + y.y), sc * (o.z + y.z), sc * (o.w + y.w));
         }
@@ -375,7 +394,7 @@ void spec_kernel(SpecParams p) {
 
     // commit: the state after the first nt tokens of buffer b, stored; the
     // token-side part first, then the state update
-    auto prep_commit = [&](SpecTokens<DK, DV>& b, int nt, float (*Y)[DV]) {
+    auto prep_commit = [&](SpecTokens<DK, DV>& b, int nt) {
         grams(b, nt, false);
         if (tid < DK) {  // W = TB (K e^G) in q, Kd in k, dec; one channel per thread
             const int c = tid;
@@ -395,20 +414,23 @@ void spec_kernel(SpecParams p) {
                 }
             }
             sm.dec[c] = exp_gate(gl);
-        } else if (tid < DK + DV) {  // U~ = TB V, one column per thread
+        } else if (tid < DK + DV) {  // U~ = TB V in place of v, one column per thread
             const int j = tid - DK;
+            float vv[SP_MAX];
+#pragma unroll
+            for (int s2 = 0; s2 < SP_MAX; ++s2) vv[s2] = s2 < nt ? b.v[s2][j] : 0.f;
 #pragma unroll
             for (int t = 0; t < SP_MAX; ++t) {
                 if (t < nt) {
                     float x = 0.f;
 #pragma unroll
-                    for (int s2 = 0; s2 <= t; ++s2) x = fmaf(sm.TB[t][s2], b.v[s2][j], x);
-                    Y[t][j] = x;
+                    for (int s2 = 0; s2 <= t; ++s2) x = fmaf(sm.TB[t][s2], vv[s2], x);
+                    b.v[t][j] = x;
                 }
             }
         }
     };
-    auto apply_commit = [&](SpecTokens<DK, DV>& b, int nt, const float (*Y)[DV]) {
+    auto apply_commit = [&](SpecTokens<DK, DV>& b, int nt) {
         __syncthreads();
         xs(b.q, nt);  // W S
         // S' = Diag(e^(G_{nt-1})) S + sum_t Kd_t u_t^T with u_t = U~_t - (W S)_t
@@ -424,7 +446,7 @@ void spec_kernel(SpecParams p) {
             float kr[RPL];
             lds_rows<RPL>(&b.k[t][row0], kr);
             const float4 ws = psum(t, col);
-            const float4 ut = *reinterpret_cast<const float4*>(&Y[t][col]);
+            const float4 ut = *reinterpret_cast<const float4*>(&b.v[t][col]);
             const float4 u = make_float4(ut.x - ws.x, ut.y - ws.y, ut.z - ws.z, ut.w - ws.w);
 #pragma unroll
             for (int m = 0; m < RPL; ++m) {
@@ -437,17 +459,17 @@ void spec_kernel(SpecParams p) {
     };
 
     if constexpr (MODE == 1) {
-        prep_verify(sm.tok[0], K, sm.Y[0]);
-        emit_verify(sm.tok[0], K, sm.Y[0]);
+        prep_verify(sm.tok[0], K);
+        emit_verify(sm.tok[0], K);
     } else if constexpr (MODE == 2) {
-        prep_commit(sm.tok[0], acc, sm.Y[0]);
-        apply_commit(sm.tok[0], acc, sm.Y[0]);
+        prep_commit(sm.tok[0], acc);
+        apply_commit(sm.tok[0], acc);
     } else {
         // both drafts' token-side work before the state is needed
-        if (acc > 0) prep_commit(sm.tok[0], acc, sm.Y[0]);
-        prep_verify(sm.tok[NB - 1], K, sm.Y[NB - 1]);
-        if (acc > 0) apply_commit(sm.tok[0], acc, sm.Y[0]);
-        emit_verify(sm.tok[NB - 1], K, sm.Y[NB - 1]);
+        if (acc > 0) prep_commit(sm.tok[0], acc);
+        prep_verify(sm.tok[NB - 1], K);
+        if (acc > 0) apply_commit(sm.tok[0], acc);
+        emit_verify(sm.tok[NB - 1], K);
     }
 }
 
