@@ -481,7 +481,8 @@ def bench_frontend(torch, kda, inputs, reps):
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                          "traffic": measured_traffic("frontend", name),
-                         "kernel": "frontend_kernel<4,bf16,bf16>",
+                         "kernel": ("frontend_unit_kernel<4,bf16,bf16>" if stateful
+                                    else "frontend_kernel<4,8,bf16,bf16>"),
                          "bytes_per_launch": nbytes},
         }
     return res

@@ -32,9 +32,11 @@
  * --------------------------
  * - All tensors are caller-owned device memory, row-major and contiguous.
  *   The library allocates no device memory and keeps no pointer after a call
- *   returns.
- * - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
- *   stream).  KDA_OK means "validated and enqueued"; results are visible
+ *   returns (kda_prefill_noalloc uses one fixed device array per GPU that the
+ *   library holds, below).
+ * - Calls are asynchronous on `stream`, a hipStream_t passed as void * so
+ *   that this header compiles as plain C without the HIP headers (NULL = the
+ *   default stream).  KDA_OK means "validated and enqueued"; results are visible
  *   after the stream is synchronised.
  * - Every argument check happens before anything is enqueued: a call that
  *   returns an error has launched nothing and written nothing.
@@ -89,7 +91,10 @@ const char *kda_status_string(kda_status status);
 const char *kda_last_error_detail(void);
 
 /*
- * Number of snapshot rows kda_prefill writes for these sequences:
+ * Number of snapshot rows kda_prefill writes for these sequences ("Day-0 vLLM
+ * support for Kimi K3", section "Kimi K3's architecture, and how vLLM serves
+ * it": prefix caching reuses recurrent-state snapshots taken at block
+ * boundaries; one snapshot per interval tokens of each sequence):
  * sum_b floor(L_b / interval), L_b = cu_seqlens_host[b+1] - cu_seqlens_host[b].
  * Sequence b's snapshots occupy rows starting at sum_{b'<b} floor(L_b'/interval),
  * in order j = 1 .. floor(L_b/interval).  Returns 0 when interval <= 0 and
@@ -99,12 +104,18 @@ int64_t kda_snapshot_count(const int32_t *cu_seqlens_host, int32_t num_seqs,
                            int32_t interval);
 
 /*
- * Bytes of device workspace kda_prefill needs for this problem: three
- * per-sequence index arrays of 4 * (num_seqs + 1) bytes each, each rounded up
- * to 256 (768 B for up to 63 sequences), plus (floor(total_tokens / 64) +
- * num_seqs) * num_heads * 115,280 B of per-chunk operands (about 1.8 KB per
- * token and head).  Returns 0 for unsupported configs too; kda_prefill
- * reports those.
+ * Bytes of device workspace kda_prefill needs for this problem.  The chunked
+ * form ("Kimi K3 technical FAQ", question "What is KDA, and why does a
+ * serving engineer care?": parallel within a chunk, recurrent across chunks)
+ * computes every chunk's state-independent operands in parallel first and
+ * keeps them here for the recurrent pass: three per-sequence index arrays of
+ * 4 * (num_seqs + 1) bytes each, each rounded up to 256 (768 B for up to 63
+ * sequences), plus (floor(total_tokens / 64) + num_seqs) * num_heads *
+ * 115,280 B of per-chunk operands (about 1.8 KB per token and head).  The
+ * operand block is laid out for 128 state rows and 128 value columns whatever
+ * dk and dv are (rows and columns past them hold zeros), so at dk = dv = 16 it
+ * is 8 times larger than the data it holds.  Returns 0 for unsupported
+ * configs too; kda_prefill reports those.
  */
 size_t kda_prefill_workspace_size(const kda_config *cfg, int32_t num_seqs,
                                   int64_t total_tokens);
