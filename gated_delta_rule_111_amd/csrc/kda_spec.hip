@@ -73,9 +73,9 @@ struct __align__(16) SpecSmem {
     // the drafts' G arrays instead, dead by the time the state is multiplied
     float P[NB == 1 ? RH : 1][SP_MAX][DV];
     float dec[DK];             // e^(G_{a-1}) (commit)
-    float A[SP_MAX][SP_MAX];
-    float B[SP_MAX][SP_MAX];
-    float TB[SP_MAX][SP_MAX];
+    float A[NB][SP_MAX][SP_MAX];    // per draft (commit: 0, verify: NB - 1)
+    float B[SP_MAX][SP_MAX];        // verified draft only
+    float TB[NB][SP_MAX][SP_MAX];
     float M[SP_MAX][SP_MAX];
 };
 
@@ -243,62 +243,74 @@ void spec_kernel(SpecParams p) {
         }
     }
 
-    // the n x n Grams (B only when verifying), then T, TB (and M)
-    auto grams = [&](const SpecTokens<DK, DV>& b, int nt, bool with_b) {
+    // The token side of both drafts at once: the committed draft (nc tokens,
+    // buffer 0; nc = 0 when there is none) and the verified one (nv tokens,
+    // buffer NB - 1; nv = 0 when there is none).  Every quantity is computed
+    // by the same arithmetic whichever drafts the launch holds, so the fused
+    // step is bit-identical to commit followed by verify.
+    // The n x n Grams (B for the verified draft only), then T, TB, and M.
+    auto grams = [&](int nc, int nv) {
         __syncthreads();  // the buffers are complete; earlier reads of the work arrays done
         // one pair (t, s), s <= t, per 16-lane group (4 per wave), DK / 16
-        // channels per lane, summed over the group by DPP moves; the groups
-        // of a wave start at different channels (fewer LDS bank conflicts)
-        const int pairs = nt * (nt + 1) / 2;
+        // channels per lane, summed over the group by DPP moves; the pairs of
+        // the committed draft come first.  A pair's channels start at a
+        // rotation fixed by the pair (fewer LDS bank conflicts between the
+        // groups of a wave, and the same order in every launch).
+        const int pc = nc * (nc + 1) / 2, pairs = pc + nv * (nv + 1) / 2;
         const int grp = lane >> 4, gl = lane & 15;
         for (int pr0 = 4 * wave; pr0 < pairs; pr0 += 4 * WAVES) {
             const int pr = pr0 + grp;
+            const bool ver = pr >= pc;
+            const SpecTokens<DK, DV>& b = sm.tok[ver ? NB - 1 : 0];
             // pair index -> (t, s), row by row over the lower triangle
-            const int pc = pr < pairs ? pr : 0;
+            const int pl = pr < pairs ? (ver ? pr - pc : pr) : 0;
             int t = 0;
-            while ((t + 1) * (t + 2) / 2 <= pc) ++t;
-            const int s2 = pc - t * (t + 1) / 2;
+            while ((t + 1) * (t + 2) / 2 <= pl) ++t;
+            const int s2 = pl - t * (t + 1) / 2;
             float ka = 0.f, qb = 0.f;
 #pragma unroll 2
             for (int i = 0; i < DK / 16; ++i) {
-                const int c = (gl + 16 * (i + grp)) % DK;
+                const int c = (gl + 16 * (i + pl)) % DK;
                 const float ks = b.k[s2][c] * exp_gate(b.G[t][c] - b.G[s2][c]);
                 ka = fmaf(b.k[t][c], ks, ka);
-                if (with_b) qb = fmaf(b.q[t][c], ks, qb);
+                if (ver) qb = fmaf(b.q[t][c], ks, qb);
             }
             ka = group_sum<16>(ka);
-            if (with_b) qb = group_sum<16>(qb);
+            qb = group_sum<16>(qb);
             if (gl == 0 && pr < pairs) {
-                sm.A[t][s2] = s2 < t ? b.beta[t] * ka : 0.f;
-                if (with_b) sm.B[t][s2] = qb;
+                sm.A[ver ? NB - 1 : 0][t][s2] = s2 < t ? b.beta[t] * ka : 0.f;
+                if (ver) sm.B[t][s2] = qb;
             }
         }
         __syncthreads();
-        // T = (I + A)^-1 by forward substitution, one column per thread:
-        // T_t,sc = [t == sc] - sum_{m<t} A_tm T_m,sc (zero above the diagonal)
-        if (tid < nt) {
-            const int sc = tid;
+        // T = (I + A)^-1 by forward substitution, one column per thread
+        // (threads 0 .. nc - 1 the committed draft, SP_MAX .. SP_MAX + nv - 1
+        // the verified one): T_t,sc = [t == sc] - sum_{m<t} A_tm T_m,sc (zero
+        // above the diagonal)
+        if (tid < nc || (tid >= SP_MAX && tid < SP_MAX + nv)) {
+            const bool ver = tid >= SP_MAX;
+            const int bi = ver ? NB - 1 : 0, nt = ver ? nv : nc, sc = ver ? tid - SP_MAX : tid;
             float col_t[SP_MAX];
 #pragma unroll
             for (int t = 0; t < SP_MAX; ++t) {
                 float x = t == sc ? 1.f : 0.f;
                 if (t < nt) {
 #pragma unroll
-                    for (int m = 0; m < t; ++m) x = fmaf(-sm.A[t][m], col_t[m], x);
+                    for (int m = 0; m < t; ++m) x = fmaf(-sm.A[bi][t][m], col_t[m], x);
                 }
                 col_t[t] = x;
             }
-            const float bs = b.beta[sc];
+            const float bs = sm.tok[bi].beta[sc];
 #pragma unroll
             for (int t = 0; t < SP_MAX; ++t)
-                if (t < nt) sm.TB[t][sc] = col_t[t] * bs;
+                if (t < nt) sm.TB[bi][t][sc] = col_t[t] * bs;
         }
         __syncthreads();
-        if (with_b) {
-            if (tid < nt * nt) {
-                const int t = tid / nt, s2 = tid - t * nt;
+        if (nv > 0) {
+            if (tid < nv * nv) {
+                const int t = tid / nv, s2 = tid - t * nv;
                 float x = 0.f;
-                for (int m = s2; m <= t; ++m) x = fmaf(sm.B[t][m], sm.TB[m][s2], x);
+                for (int m = s2; m <= t; ++m) x = fmaf(sm.B[t][m], sm.TB[NB - 1][m][s2], x);
                 sm.M[t][s2] = s2 <= t ? x : 0.f;
             }
             __syncthreads();
@@ -344,10 +356,11 @@ void spec_kernel(SpecParams p) {
 
     // verify: O = scale (Q' S + O~) for the nt tokens of buffer b; the
     // token-side part first (no state needed), then the outputs
-    auto prep_verify = [&](SpecTokens<DK, DV>& b, int nt) {
-        grams(b, nt, true);
-        if (tid < DK) {  // Q' = Q e^G - M (K e^G) in place of q, one channel per thread
-            const int c = tid;
+    // threads u = tid - base .. of the verified draft's token side
+    auto prep_verify = [&](SpecTokens<DK, DV>& b, int nt, int base) {
+        const int u = tid - base;
+        if (u >= 0 && u < DK) {  // Q' = Q e^G - M (K e^G) in place of q, one channel per thread
+            const int c = u;
             float ek[SP_MAX];
 #pragma unroll
             for (int s2 = 0; s2 < SP_MAX; ++s2)
@@ -361,8 +374,8 @@ void spec_kernel(SpecParams p) {
                     b.q[t][c] = x;
                 }
             }
-        } else if (tid < DK + DV) {  // O~ = M V in place of v, one column per thread
-            const int j = tid - DK;
+        } else if (u >= DK && u < DK + DV) {  // O~ = M V in place of v, one column per thread
+            const int j = u - DK;
             float vv[SP_MAX];
 #pragma unroll
             for (int s2 = 0; s2 < SP_MAX; ++s2) vv[s2] = s2 < nt ? b.v[s2][j] : 0.f;
@@ -395,7 +408,6 @@ void spec_kernel(SpecParams p) {
     // commit: the state after the first nt tokens of buffer b, stored; the
     // token-side part first, then the state update
     auto prep_commit = [&](SpecTokens<DK, DV>& b, int nt) {
-        grams(b, nt, false);
         if (tid < DK) {  // W = TB (K e^G) in q, Kd in k, dec; one channel per thread
             const int c = tid;
             float ek[SP_MAX];
@@ -408,13 +420,13 @@ void spec_kernel(SpecParams p) {
                 if (t < nt) {
                     float x = 0.f;
 #pragma unroll
-                    for (int s2 = 0; s2 <= t; ++s2) x = fmaf(sm.TB[t][s2], ek[s2], x);
+                    for (int s2 = 0; s2 <= t; ++s2) x = fmaf(sm.TB[0][t][s2], ek[s2], x);
                     b.q[t][c] = x;
                     b.k[t][c] *= exp_gate(gl - b.G[t][c]);
                 }
             }
             sm.dec[c] = exp_gate(gl);
-        } else if (tid < DK + DV) {  // U~ = TB V in place of v, one column per thread
+        } else if (tid < DK + DV) {  // U~ = TB V in place of v, one column per thread (threads DK ..)
             const int j = tid - DK;
             float vv[SP_MAX];
 #pragma unroll
@@ -424,7 +436,7 @@ void spec_kernel(SpecParams p) {
                 if (t < nt) {
                     float x = 0.f;
 #pragma unroll
-                    for (int s2 = 0; s2 <= t; ++s2) x = fmaf(sm.TB[t][s2], vv[s2], x);
+                    for (int s2 = 0; s2 <= t; ++s2) x = fmaf(sm.TB[0][t][s2], vv[s2], x);
                     b.v[t][j] = x;
                 }
             }
@@ -459,15 +471,19 @@ void spec_kernel(SpecParams p) {
     };
 
     if constexpr (MODE == 1) {
-        prep_verify(sm.tok[0], K);
+        grams(0, K);
+        prep_verify(sm.tok[0], K, 0);
         emit_verify(sm.tok[0], K);
     } else if constexpr (MODE == 2) {
+        grams(acc, 0);
         prep_commit(sm.tok[0], acc);
         apply_commit(sm.tok[0], acc);
     } else {
-        // both drafts' token-side work before the state is needed
+        // both drafts' token side, side by side, before the state is needed
+        static_assert(2 * (DK + DV) <= NT, "one thread per channel and column of each draft");
+        grams(acc, K);
         if (acc > 0) prep_commit(sm.tok[0], acc);
-        prep_verify(sm.tok[NB - 1], K);
+        prep_verify(sm.tok[NB - 1], K, DK + DV);
         if (acc > 0) apply_commit(sm.tok[0], acc);
         emit_verify(sm.tok[NB - 1], K);
     }
