@@ -186,7 +186,7 @@ def bench_prefill(torch, kda, inputs, w, reps, warmup):
 
     for _ in range(warmup):
         call()
-    torch.cuda.synchronize()
+    _spin_up(torch, call)
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -413,12 +413,27 @@ def cpu_long_baseline(inp, tokens: int, dinp, fin_host):
 
 
 # ---------------------------------------------------------------------------
+def _spin_up(torch, fn, seconds=0.2):
+    """Call `fn` back to back for `seconds` before a timed section: the GPU
+    idles during the host-side set-up between sections (input generation,
+    oracle baselines) and its clocks take a few tens of milliseconds of load
+    to come back up; without this the first section after a pause runs up
+    to 15% slow."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+
+
 def _time_graph(torch, fn, reps, inner=10):
     """Per-call kernel time of `fn` (which launches on torch's current
     stream) from HIP events around `reps` replays of a HIP graph holding
     `inner` back-to-back calls, so the host's own per-call cost (argument
     checks and marshalling) does not show up as idle GPU time.  Returns
     (wall seconds per call, event seconds per call)."""
+    _spin_up(torch, fn)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -564,10 +579,13 @@ def bench_prefill_pool(torch, kda, inputs, reps, warmup):
                          snapshot_interval=1024, cu_seqlens_host=cu_host, start_pos_host=starts,
                          out=out, snapshots=snaps, workspace=ws)
 
-    for _ in range(warmup):
+    def fresh_call():
         pool.copy_(pool0)
         call()
-    torch.cuda.synchronize()
+
+    for _ in range(warmup):
+        fresh_call()
+    _spin_up(torch, fresh_call)
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     total = 0.0
@@ -627,8 +645,7 @@ def bench_spec(torch, kda, inputs, reps, decode_us):
 
         times = {}
         for label, fn in (("verify", verify), ("commit", commit)):
-            for _ in range(3):
-                fn()
+            _spin_up(torch, fn)
             torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
@@ -643,9 +660,7 @@ def bench_spec(torch, kda, inputs, reps, decode_us):
             kda.decode_spec_step(inp.q, inp.k, inp.v, inp.g, inp.beta, state, prev=prev,
                                  accepted=acc, out=out)
 
-        for _ in range(3):
-            step()
-        torch.cuda.synchronize()
+        _spin_up(torch, step)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(reps):
