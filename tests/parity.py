@@ -11,6 +11,14 @@ import torch
 
 TOL = 2e-3
 
+# Regression gate of the prefill tests: half the bar.  Every prefill result
+# measured on the MI355X (ragged and varlen batches, every head size and
+# decay regime, the exact-write and no-forgetting runs, the full-size
+# workloads) has stayed at or below 5.7e-4, and the kernels are deterministic
+# (fixed reduction orders, no atomics), so a change that roughly doubles an
+# error fails here while still inside the bar.
+REG = 1e-3
+
 
 def to_np(t):
     if isinstance(t, torch.Tensor):
