@@ -253,6 +253,10 @@ template <> struct In<bf16_t> {
     }
     __device__ __forceinline__ static float f32(V1 x) { return bff(x); }
     __device__ __forceinline__ static float f32(bf16_t x) { return bff(x.bits); }
+    // 8 values at byte offset voff of a buffer resource (zero outside it)
+    __device__ __forceinline__ static V8 bload8(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+        return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+    }
 };
 template <> struct In<float> {
     struct V8 { float4 a, b; };
@@ -272,7 +276,21 @@ template <> struct In<float> {
         return static_cast<const float*>(base)[idx];
     }
     __device__ __forceinline__ static float f32(V1 x) { return x; }
+    __device__ __forceinline__ static V8 bload8(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+        return V8{__builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0)),
+                  __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 16, 0))};
+    }
 };
+
+// Rows lo .. n-1 of one head of a [T, H, d] tensor (elements of es bytes) as
+// a buffer resource based at row lo: byte offset (t - lo) * H * d * es + c * es
+// addresses row t, and every row outside lo .. n-1 falls outside the
+// resource (a row below lo wraps past 2^32 - 1), where loads return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t item_rows(const void* base, int64_t row_lo, int H, int h,
+                                                            int d, int es, int rows) {
+    const char* p = static_cast<const char*>(base) + ((row_lo * H + h) * (int64_t)d) * es;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), 0, rows * H * d * es, 0x00020000);
+}
 
 // ---------------------------------------------------------------------------
 // plan: chunk_start[b] = sum_{b' < b} nch(b'), snap_base[b] = sum_{b' < b}
@@ -476,10 +494,11 @@ __device__ __forceinline__ int gram_row(int w, int slot) {
     return slot ? 3 - ra : ra;
 }
 
-// This thread's share of one item's raw inputs: g rows 8r + tid/32, channels
-// 4*(tid%32)..+3; k, q rows 16r + tid/16, channels 8*(tid%16)..+7; beta of
-// row tid (tid < 64).  Rows outside lo .. n-1 are read from the nearest valid
-// row and channels past dk from channel 0; the values are masked when staged.
+// This thread's share of one item's raw inputs: g rows 8*(tid/32) + r,
+// channels 4*(tid%32)..+3; k, q rows 16r + tid/16, channels 8*(tid%16)..+7; beta of
+// row tid (tid < 64).  Rows outside lo .. n-1 read as zero (they fall outside
+// the item's buffer resources) and channels past dk are read from channel 0;
+// the values are masked when staged.
 template <typename TIn>
 struct PrepRaw {
     float4 g[8];
@@ -493,25 +512,31 @@ template <typename TIn>
 __device__ __forceinline__ void prep_load(PrepRaw<TIn>& r, const PrepParams& p, const PrepItem& x,
                                           int tid) {
     using IO = In<TIn>;
+    constexpr int ES = (int)sizeof(TIn);
     const int dk = p.dk;
-    const int64_t rs = (int64_t)p.H * dk;                    // row stride
-    const int64_t base = (x.row0 * p.H + x.h) * (int64_t)dk;  // row 0, channel 0
+    const int rows = x.n - x.lo;
+    const int64_t rlo = x.row0 + x.lo;
+    const uint32_t rsb = (uint32_t)(p.H * dk);  // row stride in elements
     {
+        const __amdgpu_buffer_rsrc_t gb = item_rows(p.g, rlo, p.H, x.h, dk, 4, rows);
         const int c = 4 * (tid & 31);
-        const int cl = c < dk ? c : 0;
+        const uint32_t cb = 4 * (c < dk ? c : 0);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int t = 8 * i + (tid >> 5);
-            r.g[i] = *reinterpret_cast<const float4*>(p.g + base + min(max(t, x.lo), x.n - 1) * rs + cl);
+            const int t = 8 * (tid >> 5) + i;
+            r.g[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                    gb, (uint32_t)(t - x.lo) * rsb * 4 + cb, 0, 0));
         }
     }
+    const __amdgpu_buffer_rsrc_t kb = item_rows(p.k, rlo, p.H, x.h, dk, ES, rows);
+    const __amdgpu_buffer_rsrc_t qb = item_rows(p.q, rlo, p.H, x.h, dk, ES, rows);
     {
         const int c = 8 * (tid & 15);
-        const int cl = c < dk ? c : 0;
+        const uint32_t cb = ES * (c < dk ? c : 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int t = 16 * i + (tid >> 4);
-            r.k[i] = IO::load8(p.k, base + min(max(t, x.lo), x.n - 1) * rs + cl);
+            r.k[i] = IO::bload8(kb, (uint32_t)(t - x.lo) * rsb * ES + cb);
         }
     }
     {
@@ -521,17 +546,21 @@ __device__ __forceinline__ void prep_load(PrepRaw<TIn>& r, const PrepParams& p, 
         for (int u = 0; u < 4; ++u) {
             const int t = 16 * ((u >> 1) ? rb : ra) + (lane & 15);
             const int c = 32 * (2 * (w >> 1) + (u & 1)) + 8 * (lane >> 4);
-            r.qg[u] = IO::load8(p.q, base + min(max(t, x.lo), x.n - 1) * rs + (c < dk ? c : 0));
+            r.qg[u] = IO::bload8(qb, (uint32_t)(t - x.lo) * rsb * ES + ES * (c < dk ? c : 0));
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int idx = tid + NT * u;
             const int ws = idx >> 8, mt = (idx >> 6) & 3, ln = idx & 63;
             const int tt = tok_of(mt, ln & 15), c = SL * ws + 8 * (ln >> 4);
-            r.qd[u] = IO::load8(p.q, base + min(max(tt, x.lo), x.n - 1) * rs + (c < dk ? c : 0));
+            r.qd[u] = IO::bload8(qb, (uint32_t)(tt - x.lo) * rsb * ES + ES * (c < dk ? c : 0));
         }
     }
-    r.beta = p.beta[(x.row0 + min(max(tid & 63, x.lo), x.n - 1)) * p.H + x.h];
+    {
+        const __amdgpu_buffer_rsrc_t bb = item_rows(p.beta, rlo, p.H, x.h, 1, 4, rows);
+        r.beta = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                               bb, (uint32_t)((tid & 63) - x.lo) * (uint32_t)p.H * 4, 0, 0));
+    }
 }
 
 // One workgroup per (chunk, head) item; two are resident per compute unit.
@@ -556,19 +585,44 @@ void prep_kernel(PrepParams p) {
         uint4* __restrict__ dst = p.ops + (x.gc * p.H + x.h) * CHUNK_OPS;
 
         // ---- stage this item's inputs (zero outside rows lo .. n-1 and past
-        // dk); log-decays in
-        // log2 units, so every factor below is a bare exp2 ----
+        // dk); log-decays in log2 units, so every factor below is a bare
+        // exp2.  The cumulative log-decay: each thread sums its 8 rows of 4
+        // channels in registers, the 8-row totals go through LDS, and each
+        // thread adds the totals of the row blocks before its own.  The span
+        // check of the diagonal Gram blocks (first and last row against the
+        // middle row of each 16-row tile) needs only sums inside one 8-row
+        // block: G[16R] - G[16R+7] in the block's first half and
+        // G[16R+7] - G[16R+15] (minus the second half's total) ----
+        int extreme = 0;
+        float4 gr[8];
+        const int gblk = tid >> 5, gc = 4 * (tid & 31);
         {
-            const int c = 4 * (tid & 31);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const int t = 8 * i + (tid >> 5);
-                // rows outside lo .. n-1 and channels past dk were read from
-                // valid (finite) entries: a zero factor clears them without a branch
+                const int t = 8 * gblk + i;
+                // rows outside lo .. n-1 read as zero and channels past dk
+                // from valid (finite) entries: a zero factor clears them
+                // without a branch
                 const float4 gv = raw.g[i];
-                const float f = (t >= lo && t < n && c < dk) ? LOG2E : 0.f;
-                *reinterpret_cast<float4*>(&sm.u.G[t][c]) = make_float4(gv.x * f, gv.y * f, gv.z * f, gv.w * f);
+                const float f = (t >= lo && t < n && gc < dk) ? LOG2E : 0.f;
+                gr[i] = make_float4(gv.x * f, gv.y * f, gv.z * f, gv.w * f);
             }
+#pragma unroll
+            for (int i = 1; i < 8; ++i) {
+                gr[i].x += gr[i - 1].x;
+                gr[i].y += gr[i - 1].y;
+                gr[i].z += gr[i - 1].z;
+                gr[i].w += gr[i - 1].w;
+            }
+            if (gblk & 1) {
+                extreme = (-gr[7].x > SPAN_LIMIT) | (-gr[7].y > SPAN_LIMIT) | (-gr[7].z > SPAN_LIMIT) |
+                          (-gr[7].w > SPAN_LIMIT);
+            } else {
+                extreme = (gr[0].x - gr[7].x > SPAN_LIMIT) | (gr[0].y - gr[7].y > SPAN_LIMIT) |
+                          (gr[0].z - gr[7].z > SPAN_LIMIT) | (gr[0].w - gr[7].w > SPAN_LIMIT);
+            }
+            // 8-row totals, in the A/B area (unused until the Gram exchange)
+            reinterpret_cast<float4*>(&sm.ab.A[0][0])[gblk * 32 + (tid & 31)] = gr[7];
         }
         {
             const int c = 8 * (tid & 15);
@@ -581,30 +635,26 @@ void prep_kernel(PrepParams p) {
         }
         if (tid < C) sm.beta[tid] = (tid >= lo && tid < n) ? raw.beta : 0.f;
         __syncthreads();
-
-        // ---- cumulative log-decay per channel; the span check of the
-        // diagonal Gram blocks (first and last row against the middle row of
-        // each 16-row tile) is independent of the running offset ----
-        int extreme = 0;
         {
-            const int c = tid & 127, half = tid >> 7;
-            float run = 0.f, g0 = 0.f, g7 = 0.f;
+            // every total is read and the earlier blocks' are selected (a
+            // read under a condition becomes a branch and a wait)
+            float4 base = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-            for (int r = 0; r < 32; ++r) {
-                run += sm.u.G[half * 32 + r][c];
-                sm.u.G[half * 32 + r][c] = run;
-                if ((r & 15) == 0) g0 = run;
-                if ((r & 15) == 7) g7 = run;
-                if ((r & 15) == 15) extreme |= (g0 - g7 > SPAN_LIMIT) | (g7 - run > SPAN_LIMIT);
+            for (int b2 = 0; b2 < 7; ++b2) {
+                const float4 tb = reinterpret_cast<const float4*>(&sm.ab.A[0][0])[b2 * 32 + (tid & 31)];
+                if (b2 < gblk) {
+                    base.x += tb.x;
+                    base.y += tb.y;
+                    base.z += tb.z;
+                    base.w += tb.w;
+                }
             }
-            __syncthreads();
-            if (half == 1) {
-                const float base = sm.u.G[31][c];
-#pragma unroll 8
-                for (int r = 32; r < 64; ++r) sm.u.G[r][c] += base;
-            }
-            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                *reinterpret_cast<float4*>(&sm.u.G[8 * gblk + i][gc]) =
+                    make_float4(gr[i].x + base.x, gr[i].y + base.y, gr[i].z + base.z, gr[i].w + base.w);
         }
+        __syncthreads();
 
         // ---- Gram matrices A and B, 16 x 16 blocks (row tile R, column tile ts <= R) ----
         // Off-diagonal blocks use the reference r = G at row 16R - 1, so both
@@ -765,13 +815,14 @@ void prep_kernel(PrepParams p) {
         // and staged as V^T after the diagonal blocks of T are solved
         typename IO::V8 vr[4];
         {
+            constexpr int ES = (int)sizeof(TIn);
             const int c = 8 * (tid & 15);
-            const int64_t vs = (int64_t)p.H * p.dv;
-            const int64_t vb = (x.row0 * p.H + x.h) * (int64_t)p.dv + (c < p.dv ? c : 0);
+            const __amdgpu_buffer_rsrc_t vbuf = item_rows(p.v, x.row0 + lo, p.H, x.h, p.dv, ES, n - lo);
+            const uint32_t rsb = (uint32_t)(p.H * p.dv) * ES, cb = ES * (c < p.dv ? c : 0);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = 2 * (tid >> 4) + (i & 1) + 32 * (i >> 1);
-                vr[i] = IO::load8(p.v, vb + min(max(t, lo), n - 1) * vs);
+                vr[i] = IO::bload8(vbuf, (uint32_t)(t - lo) * rsb + cb);
             }
         }
 
