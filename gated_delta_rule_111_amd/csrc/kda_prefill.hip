@@ -1308,7 +1308,7 @@ void scan_kernel(ScanParams p) {
     // pair of tiles, so the same for a tile at either width
     const int rot = (tile0 >> 1) & 3;
     const uint32_t rsh = 8 * rot;
-    auto rot_bytes = [rsh](uint32_t x) { return (x >> rsh) | (x << ((32 - rsh) & 31)); };
+    auto rot_bytes = [rsh](uint32_t x) { return (uint32_t)((((uint64_t)x << 32) | x) >> rsh); };
     const int64_t seq0 = p.cu[b];
     const int len = p.cu[b + 1] - p.cu[b];
     // chunks sit at absolute multiples of C (see plan_kernel): pad leading
@@ -1427,6 +1427,17 @@ void scan_kernel(ScanParams p) {
         if constexpr (DB) scan_load1(nx, nblk, w, tile0, vo, rot);
         lds_barrier();
 
+        // the state rows of every block, then the exponent bytes, as one
+        // batch of LDS reads (one round trip)
+        uint4 Sh[TPW][4], Sl[TPW][4];
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                Sh[t][r] = sm.sx[t][(r + rot) & 3][lane][0];
+                Sl[t][r] = sm.sx[t][(r + rot) & 3][lane][1];
+            }
+
         // exponents of this chunk (scalar): the state-row blocks of each tile,
         // and the bound of U over each pair of token tiles (a K-step of the
         // state update): |U| <= |U~| + 128 max|W| max|S| < 2^bu[t][ks]
@@ -1446,28 +1457,29 @@ void scan_kernel(ScanParams p) {
                                     7 + max(byte_exp(xm, 2 * ks), byte_exp(xm, 2 * ks + 1)) + esmax);
         }
 
-        // ---- this wave's token tile: U = U~ - W S, then Q' S on the matrix
-        // unit while U is formed and published ----
+        // ---- this wave's token tile: U = U~ - W S, formed and published
+        // first; Q' S (this wave's output products) goes on the matrix unit
+        // after it -- with one value tile after barrier 2, while the reads of
+        // U are in flight ----
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
         f32x4 pq[TPW][4];
+        auto qs_products = [&]() {
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) pq[t][r] = mfma_h(o.q[r], Sh[t][r], z);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) pq[t][r] = mfma_h(o.q[r], Sl[t][r], pq[t][r]);
+            }
+        };
         if (ci > 0) store_out();
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
-            uint4 Sh[4], Sl[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                Sh[r] = sm.sx[t][(r + rot) & 3][lane][0];
-                Sl[r] = sm.sx[t][(r + rot) & 3][lane][1];
-            }
             f32x4 y[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) y[r] = mfma_h(o.w[r], Sh[r], z);
+            for (int r = 0; r < 4; ++r) y[r] = mfma_h(o.w[r], Sh[t][r], z);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) y[r] = mfma_h(o.w[r], Sl[r], y[r]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) pq[t][r] = mfma_h(o.q[r], Sh[r], z);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) pq[t][r] = mfma_h(o.q[r], Sl[r], pq[t][r]);
+            for (int r = 0; r < 4; ++r) y[r] = mfma_h(o.w[r], Sl[t][r], y[r]);
             f32x4 ws = y[0] * pow2f(byte_exp(xw, 0) + es[t][0] - 2 * F16_TOP);
 #pragma unroll
             for (int r = 1; r < 4; ++r) {
@@ -1482,30 +1494,37 @@ void scan_kernel(ScanParams p) {
             sm.ux[t][w >> 1][lane].h[w & 1] = uh;
             sm.ux[t][w >> 1][lane].l[w & 1] = ul;
         }
+        // two value tiles: the state operands of both are not kept across
+        // barrier 2 (register budget)
+        if constexpr (TPW != 1) qs_products();
         if constexpr (DB) scan_load2(nx, nblk, w, tile0, vo, rot);
         else scan_load1(nx, nblk, w, tile0, vo, rot);  // W, U~ and the exponents are consumed
         lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
 
         // ---- the whole U: this wave's state rows, and this wave's output
         // tiles O = scale (Q' S + O~) while the products run ----
         f32x4 a[TPW][2][2];
+        uint4 Uh[TPW][2], Ul[TPW][2];
 #pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-            uint4 Uh[2], Ul[2];
+        for (int t = 0; t < TPW; ++t)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
                 const typename ScanSmem<TPW>::Ux x = sm.ux[t][ks][lane];
-                Uh[ks] = make_uint4(x.h[0].x, x.h[0].y, x.h[1].x, x.h[1].y);
-                Ul[ks] = make_uint4(x.l[0].x, x.l[0].y, x.l[1].x, x.l[1].y);
+                Uh[t][ks] = make_uint4(x.h[0].x, x.h[0].y, x.h[1].x, x.h[1].y);
+                Ul[t][ks] = make_uint4(x.l[0].x, x.l[0].y, x.l[1].x, x.l[1].y);
             }
+        if constexpr (TPW == 1) qs_products();
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
 #pragma unroll
             for (int m = 0; m < 2; ++m)
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) a[t][m][ks] = mfma_h(o.kd[m][ks], Uh[ks], z);
+                for (int ks = 0; ks < 2; ++ks) a[t][m][ks] = mfma_h(o.kd[m][ks], Uh[t][ks], z);
 #pragma unroll
             for (int m = 0; m < 2; ++m)
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) a[t][m][ks] = mfma_h(o.kd[m][ks], Ul[ks], a[t][m][ks]);
+                for (int ks = 0; ks < 2; ++ks) a[t][m][ks] = mfma_h(o.kd[m][ks], Ul[t][ks], a[t][m][ks]);
         }
         if constexpr (DB) scan_load3(nx, nblk, w, vo, vd);
 
