@@ -1394,7 +1394,15 @@ void scan_kernel(ScanParams p) {
                                                           ooff[e] - oshift, 16 * t * OB, 0);
             }
     };
-    auto chunk = [&](const int ci, ScanOps<TPW>& o, ScanOps<TPW>& nx) {
+    // One value tile per workgroup (few, long recurrences): each chunk also
+    // touches the operand block two chunks ahead, so that the register
+    // prefetch one chunk ahead finds it in L2.  The head's 4 * tiles waves
+    // each load one dword of every (4 * tiles)-th 128-byte line; the value is
+    // consumed (by an empty asm statement) only a chunk later, after the next
+    // such load was issued, so no wait is spent on it.  The two unrolled
+    // chunk instances keep it in registers of their own (a copy would wait).
+    uint32_t pfA = 0, pfB = 0;
+    auto chunk = [&](const int ci, ScanOps<TPW>& o, ScanOps<TPW>& nx, uint32_t& pfo, uint32_t& pfn) {
         // chunk rows lo .. n-1 are tokens row0 + lo .. row0 + n - 1
         const int64_t row0 = seq0 - pad + (int64_t)ci * C;
         const int n = min(C, pad + len - ci * C);
@@ -1527,6 +1535,13 @@ void scan_kernel(ScanParams p) {
                 for (int ks = 0; ks < 2; ++ks) a[t][m][ks] = mfma_h(o.kd[m][ks], Ul[t][ks], a[t][m][ks]);
         }
         if constexpr (DB) scan_load3(nx, nblk, w, vo, vd);
+        if constexpr (TPW == 1) {
+            const int ns = 4 * p.ngroups, si = (pos % p.ngroups) * 4 + w;
+            const __amdgpu_buffer_rsrc_t pb = scan_block(p, cbase + min(ci + 2, nch - 1), h);
+            const int line = min(si + lane * ns, (CHUNK_OPS * 16 - 1) / 128);
+            pfn = __builtin_amdgcn_raw_buffer_load_b32(pb, line * 128, 0, 0);
+            asm volatile("" :: "v"(pfo));
+        }
 
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
@@ -1589,14 +1604,15 @@ void scan_kernel(ScanParams p) {
     int ci = 0;
     if constexpr (DB) {
         for (; ci + 1 < nch; ci += 2) {
-            chunk(ci, opA, opB);
-            chunk(ci + 1, opB, opA);
+            chunk(ci, opA, opB, pfA, pfB);
+            chunk(ci + 1, opB, opA, pfB, pfA);
         }
-        if (ci < nch) chunk(ci, opA, opB);
+        if (ci < nch) chunk(ci, opA, opB, pfA, pfB);
     } else {
         (void)opB;
-        for (; ci < nch; ++ci) chunk(ci, opA, opA);
+        for (; ci < nch; ++ci) chunk(ci, opA, opA, pfA, pfA);
     }
+    if constexpr (TPW == 1) asm volatile("" :: "v"(pfA), "v"(pfB));
     if (nch > 0) store_out();
 
 #pragma unroll
