@@ -63,6 +63,8 @@
 #include "kda_common.h"
 #include "kda_internal.h"
 
+#include <type_traits>
+
 namespace kda {
 namespace {
 
@@ -676,12 +678,17 @@ void prep_kernel(PrepParams p) {
                     pB[sl][ts] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
             const int hh = w >> 1;
+            // instantiated per pair of row tiles (waves 0 and 3: tiles 0 and 3;
+            // waves 1 and 2: tiles 1 and 2), so that every block choice below
+            // is known at compile time and no LDS read waits behind a branch
+            auto gram_blocks = [&](auto ra_c) {
+            constexpr int RA = decltype(ra_c)::value;
 #pragma unroll 1
             for (int kk = 0; kk < 2; ++kk) {
                 const int c0 = 32 * (2 * hh + kk) + 8 * g4;
 #pragma unroll
                 for (int sl = 0; sl < 2; ++sl) {
-                    const int R = gram_row(w, sl);
+                    const int R = sl ? 3 - RA : RA;
                     const int t = 16 * R + i16;
                     float kt[8], qt[8];
                     IO::f32x8(*reinterpret_cast<const typename IO::V8*>(&sm.k.kS[t][c0]), kt);
@@ -751,6 +758,9 @@ void prep_kernel(PrepParams p) {
                     }
                 }
             }
+            };
+            if (w == 0 || w == 3) gram_blocks(std::integral_constant<int, 0>{});
+            else gram_blocks(std::integral_constant<int, 1>{});
             // exchange: the slot this wave does not own goes to its partner
             const int own = (gram_row(w, 0) == w) ? 0 : 1;
             f32x4 accA[4];
