@@ -190,8 +190,9 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // -126 for zero and subnormals), and the same as a byte e + 126
 __device__ __forceinline__ int bound_exp(uint32_t b) { return (int)(b >> 23) - 126; }
 __device__ __forceinline__ uint8_t exp_byte(uint32_t b) { return (uint8_t)(b >> 23); }
-// exponent byte i of a packed word
+// exponent byte i of a packed word, and the raw byte (exponent + 126)
 __device__ __forceinline__ int byte_exp(uint32_t packed, int i) { return (int)((packed >> (8 * i)) & 0xffu) - 126; }
+__device__ __forceinline__ int byte_raw(uint32_t packed, int i) { return (int)((packed >> (8 * i)) & 0xffu); }
 // 2^e as a float: exact down to 2^-149 (subnormal), 0 below; e is capped at
 // 127 so that a zero accumulator never meets an infinite factor (a product
 // that needs a larger factor overflows fp32 anyway)
@@ -1461,18 +1462,22 @@ void scan_kernel(ScanParams p) {
         // state update): |U| <= |U~| + 128 max|W| max|S| < 2^bu[t][ks]
         const uint32_t xw = rot_bytes(uni(o.ex.x)), xq = rot_bytes(uni(o.ex.y)), xk = uni(o.ex.z),
                        xu = uni(o.ex4.x), xm = uni(o.ex4.y);
-        int es[TPW][4], bu[TPW][2];
+        // (esb and bub: the state-block and U exponents less 2 F16_TOP and the
+        // byte bias, so that a factor's exponent is one raw byte plus one of them)
+        int esb[TPW][4], bu[TPW][2], bub[TPW][2];
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
             const uint32_t sp = uni(sm.se[t]), spr = rot_bytes(sp);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) es[t][r] = byte_exp(spr, r);
+            for (int r = 0; r < 4; ++r) esb[t][r] = byte_exp(spr, r) - 2 * F16_TOP - 126;
             const int esmax = bound_exp(max(max(sp & 0xffu, (sp >> 8) & 0xffu),
                                             max((sp >> 16) & 0xffu, sp >> 24)) << 23);
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
+            for (int ks = 0; ks < 2; ++ks) {
                 bu[t][ks] = 1 + max(max(byte_exp(xu, 2 * ks), byte_exp(xu, 2 * ks + 1)),
                                     7 + max(byte_exp(xm, 2 * ks), byte_exp(xm, 2 * ks + 1)) + esmax);
+                bub[t][ks] = bu[t][ks] - 2 * F16_TOP - 126;
+            }
         }
 
         // ---- this wave's token tile: U = U~ - W S, formed and published
@@ -1498,10 +1503,10 @@ void scan_kernel(ScanParams p) {
             for (int r = 0; r < 4; ++r) y[r] = mfma_h(o.w[r], Sh[t][r], z);
 #pragma unroll
             for (int r = 0; r < 4; ++r) y[r] = mfma_h(o.w[r], Sl[t][r], y[r]);
-            f32x4 ws = y[0] * pow2f(byte_exp(xw, 0) + es[t][0] - 2 * F16_TOP);
+            f32x4 ws = y[0] * pow2f(byte_raw(xw, 0) + esb[t][0]);
 #pragma unroll
             for (int r = 1; r < 4; ++r) {
-                const float f = pow2f(byte_exp(xw, r) + es[t][r] - 2 * F16_TOP);
+                const float f = pow2f(byte_raw(xw, r) + esb[t][r]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) ws[e] = __builtin_fmaf(y[r][e], f, ws[e]);
             }
@@ -1555,10 +1560,10 @@ void scan_kernel(ScanParams p) {
 
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
-            f32x4 po = pq[t][0] * pow2f(byte_exp(xq, 0) + es[t][0] - 2 * F16_TOP);
+            f32x4 po = pq[t][0] * pow2f(byte_raw(xq, 0) + esb[t][0]);
 #pragma unroll
             for (int r = 1; r < 4; ++r) {
-                const float f = pow2f(byte_exp(xq, r) + es[t][r] - 2 * F16_TOP);
+                const float f = pow2f(byte_raw(xq, r) + esb[t][r]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) po[e] = __builtin_fmaf(pq[t][r][e], f, po[e]);
             }
@@ -1580,7 +1585,7 @@ void scan_kernel(ScanParams p) {
                 f32x4 sv = S[t][m] * f32x4{d.x, d.y, d.z, d.w};
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
-                    const float f = pow2f(byte_exp(xk, 2 * m + ks) + bu[t][ks] - 2 * F16_TOP);
+                    const float f = pow2f(byte_raw(xk, 2 * m + ks) + bub[t][ks]);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) sv[e] = __builtin_fmaf(a[t][m][ks][e], f, sv[e]);
                 }
