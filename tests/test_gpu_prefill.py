@@ -270,6 +270,31 @@ def test_resume_bit_exact_and_tiling_independent():
     assert torch.equal(f3, fin[1:3]), "resumed varlen final states differ"
 
 
+def test_chained_segments_bit_exact():
+    """One sequence prefilled as three calls on chunk-aligned segments, each
+    starting from the previous call's final state, reproduces the single call
+    bit for bit: outputs, snapshots (each segment's own, at the same
+    positions) and the final state."""
+    from gated_delta_rule_111_amd import kda
+    from gated_delta_rule_111_amd.inputs import prefill_inputs
+    T, iv = 2560, 256
+    inp = prefill_inputs([T], H=4, dk=128, dv=128, seed=43, state_std=0.05, device=DEV)
+    out, fin, snaps = _gpu(inp, interval=iv)
+    state = inp.initial_state
+    outs, segsnaps = [], []
+    for a, b in ((0, 512), (512, 2048), (2048, T)):
+        cu = torch.tensor([0, b - a], dtype=torch.int32, device=DEV)
+        o, state, sn = kda.prefill(inp.q[a:b], inp.k[a:b], inp.v[a:b], inp.g[a:b],
+                                   inp.beta[a:b], cu, initial_state=state,
+                                   snapshot_interval=iv)
+        outs.append(o)
+        segsnaps.append(sn)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat(outs), out), "segmented outputs differ"
+    assert torch.equal(torch.cat(segsnaps), snaps), "segmented snapshots differ"
+    assert torch.equal(state, fin), "segmented final state differs"
+
+
 def test_decode_chain_matches_prefill():
     """T chained kda_decode steps against one kda_prefill of the same tokens."""
     from gated_delta_rule_111_amd import kda
