@@ -1316,7 +1316,10 @@ void scan_kernel(ScanParams p) {
     const int dk = p.dk, dv = p.dv;
     const int j0 = 16 * tile0 + i16;  // value column of this lane in tile t: j0 + 16 t
     // the order of the state-row blocks (see scan_load1): a function of the
-    // pair of tiles, so the same for a tile at either width
+    // pair of tiles.  The blocks are loaded in the order of the workgroup's
+    // first pair; tile t sums its four block products starting at block
+    // (t / 2) of that order, which is its own pair's order, so every tile
+    // sums in the same order at any width
     const int rot = (tile0 >> 1) & 3;
     const uint32_t rsh = 8 * rot;
     auto rot_bytes = [rsh](uint32_t x) { return (uint32_t)((((uint64_t)x << 32) | x) >> rsh); };
@@ -1503,9 +1506,11 @@ void scan_kernel(ScanParams p) {
             for (int r = 0; r < 4; ++r) y[r] = mfma_h(o.w[r], Sh[t][r], z);
 #pragma unroll
             for (int r = 0; r < 4; ++r) y[r] = mfma_h(o.w[r], Sl[t][r], y[r]);
-            f32x4 ws = y[0] * pow2f(byte_raw(xw, 0) + esb[t][0]);
+            const int sh = t >> 1;  // this tile's pair: its block order (see rot)
+            f32x4 ws = y[sh & 3] * pow2f(byte_raw(xw, sh & 3) + esb[t][sh & 3]);
 #pragma unroll
-            for (int r = 1; r < 4; ++r) {
+            for (int r0 = 1; r0 < 4; ++r0) {
+                const int r = (r0 + sh) & 3;
                 const float f = pow2f(byte_raw(xw, r) + esb[t][r]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) ws[e] = __builtin_fmaf(y[r][e], f, ws[e]);
@@ -1560,9 +1565,11 @@ void scan_kernel(ScanParams p) {
 
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
-            f32x4 po = pq[t][0] * pow2f(byte_raw(xq, 0) + esb[t][0]);
+            const int sh = t >> 1;
+            f32x4 po = pq[t][sh & 3] * pow2f(byte_raw(xq, sh & 3) + esb[t][sh & 3]);
 #pragma unroll
-            for (int r = 1; r < 4; ++r) {
+            for (int r0 = 1; r0 < 4; ++r0) {
+                const int r = (r0 + sh) & 3;
                 const float f = pow2f(byte_raw(xq, r) + esb[t][r]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) po[e] = __builtin_fmaf(pq[t][r][e], f, po[e]);
@@ -1716,25 +1723,28 @@ hipError_t launch_t(const PrefillArgs& a) {
     sp.scale = a.scale;
     sp.nchains = a.num_seqs * a.H;
     // the value-tile width: one 16-column tile per workgroup while that
-    // leaves at most two chains' worth of workgroups per compute unit (few,
-    // long recurrences: every unit runs one latency-bound chain and the
+    // leaves fewer than two workgroups per compute unit (few, long
+    // recurrences: every unit runs one latency-bound chain and the
     // double-buffered prefetch hides the loads); with more chains, two tiles
-    // per workgroup (W, Q', Kd loaded once for 32 columns), the loads being
-    // what bounds the scan then
+    // per workgroup, and four once that still leaves two workgroups per unit
+    // (W, Q' and Kd loaded once for 32 or 64 columns)
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) == hipSuccess)
         (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     const int tiles = a.dv / 16;
-    const bool wide = tiles % 2 == 0 && ((int64_t)sp.nchains + 7) / 8 * 8 * tiles >= 2 * (int64_t)cus;
-    const int tpw = wide ? 2 : 1;
+    const int64_t ntile = ((int64_t)sp.nchains + 7) / 8 * 8 * tiles;
+    const int tpw = (tiles % 4 == 0 && ntile >= 8 * (int64_t)cus) ? 4
+                    : (tiles % 2 == 0 && ntile >= 2 * (int64_t)cus) ? 2 : 1;
     sp.ngroups = tiles / tpw;
     const int64_t nwg = ((int64_t)sp.nchains + 7) / 8 * 8 * sp.ngroups;
     auto go = [&](auto kern) { hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(NT), 0, a.stream, sp); };
     if (a.out_bf16) {
-        if (wide) go(scan_kernel<true, true, 2>);
+        if (tpw == 4) go(scan_kernel<true, true, 4>);
+        else if (tpw == 2) go(scan_kernel<true, true, 2>);
         else go(scan_kernel<true, true, 1>);
     } else {
-        if (wide) go(scan_kernel<false, true, 2>);
+        if (tpw == 4) go(scan_kernel<false, true, 4>);
+        else if (tpw == 2) go(scan_kernel<false, true, 2>);
         else go(scan_kernel<false, true, 1>);
     }
     return hipGetLastError();

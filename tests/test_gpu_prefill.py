@@ -270,6 +270,31 @@ def test_resume_bit_exact_and_tiling_independent():
     assert torch.equal(f3, fin[1:3]), "resumed varlen final states differ"
 
 
+def test_value_tile_widths_bit_identical():
+    """The scan's width follows the chain count: 16 sequences x 32 heads take
+    four 16-column value tiles per workgroup, 4 sequences two, one sequence
+    one.  The sequences shared by the three calls must come out bit for bit
+    the same (outputs, snapshots, final states)."""
+    from gated_delta_rule_111_amd import kda
+    from gated_delta_rule_111_amd.inputs import prefill_inputs
+    lens = [384, 130, 257, 320, 200, 64, 401, 333, 150, 256, 99, 380, 275, 190, 300, 128]
+    iv = 128
+    inp = prefill_inputs(lens, H=32, dk=128, dv=128, seed=47, state_std=0.05, device=DEV)
+    out, fin, snaps = _gpu(inp, interval=iv)
+    cu = inp.cu_seqlens.cpu().tolist()
+    nsn = [l // iv for l in lens]
+    for nseq in (4, 1):
+        e = cu[nseq]
+        cu_s = torch.tensor(cu[:nseq + 1], dtype=torch.int32, device=DEV)
+        o2, f2, s2 = kda.prefill(inp.q[:e], inp.k[:e], inp.v[:e], inp.g[:e], inp.beta[:e], cu_s,
+                                 initial_state=inp.initial_state[:nseq].contiguous(),
+                                 snapshot_interval=iv)
+        torch.cuda.synchronize()
+        assert torch.equal(o2, out[:e]), f"outputs differ with {nseq} sequences"
+        assert torch.equal(f2, fin[:nseq]), f"final states differ with {nseq} sequences"
+        assert torch.equal(s2, snaps[:sum(nsn[:nseq])]), f"snapshots differ with {nseq} sequences"
+
+
 def test_chained_segments_bit_exact():
     """One sequence prefilled as three calls on chunk-aligned segments, each
     starting from the previous call's final state, reproduces the single call
