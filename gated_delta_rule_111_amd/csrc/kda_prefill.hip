@@ -212,6 +212,16 @@ __device__ __forceinline__ int vt_group(int j, int g) { return g ^ ((j ^ (j >> 3
 // Storage slot of token group g in row c of (K e^G)^T: rows 8 channels apart
 // (the transposing writes of one instruction) land in different slots.
 __device__ __forceinline__ int kg_group(int c, int g) { return g ^ ((c >> 3) & 7); }
+// Token order of the prep's token-contracted operands (TB, V^T, (K e^G)^T and
+// M): within each 32-token K-step, slot 8g + e holds token 4g + e (e < 4) or
+// 16 + 4g + e - 4 (e >= 4), the order in which an MFMA accumulator of M^T
+// (two 16-token tiles) leaves a lane's values, so M needs no LDS transpose.
+__device__ __forceinline__ int kslot(int t) {
+    return (t & ~31) + (((t & 15) >> 2) << 3) + (t & 3) + ((t & 16) ? 4 : 0);
+}
+__device__ __forceinline__ int kslot_tok(int q) {
+    return (q & ~31) + ((q & 4) ? 16 : 0) + (((q & 31) >> 3) << 2) + (q & 3);
+}
 
 // eight consecutive fp32 of an LDS row (16-byte aligned) as two 128-bit reads
 __device__ __forceinline__ void lds8(const float* p, float (&x)[8]) {
@@ -422,7 +432,6 @@ struct PrepSmem {
     union {
         float A[C][C + 4];     // strictly lower b_t sum_c k_t k_s e^{G_t - G_s}
         float B[C][C + 4];     // lower sum_c q_t k_s e^{G_t - G_s}, once T is formed
-        float M[C][C + 4];     // B TB, once every wave holds its rows of B
     } ab;
     union {
         TIn kS[C][KP];             // the chunk's keys (zero past n and dk)
@@ -897,7 +906,10 @@ void prep_kernel(PrepParams p) {
         for (int r = 0; r < 4; ++r) {
             const int t = tok_of(w, i16), c0 = SL * r + 8 * g4;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sm.k.KgT[c0 + e][kg_group(c0 + e, t >> 3) * 8 + (t & 7)] = kg[r][e];
+            for (int e = 0; e < 8; ++e) {
+                const int q = kslot(t);
+                sm.k.KgT[c0 + e][kg_group(c0 + e, q >> 3) * 8 + (q & 7)] = kg[r][e];
+            }
         }
         // ---- T = (I + A)^-1 by block forward substitution ----
         if (lane < 16) {
@@ -933,7 +945,8 @@ void prep_kernel(PrepParams p) {
                         const int j = c + e;
                         const uint32_t wd = __builtin_amdgcn_perm(r1[e >> 1], r0[e >> 1],
                                                                   (e & 1) ? 0x07060302u : 0x05040100u);
-                        *reinterpret_cast<uint32_t*>(&sm.u.tv.VT[0][j][vt_group(j, t >> 3) * 8 + (t & 7)]) =
+                        const int q = kslot(t);  // t even: t + 1 sits in slot q + 1
+                        *reinterpret_cast<uint32_t*>(&sm.u.tv.VT[0][j][vt_group(j, q >> 3) * 8 + (q & 7)]) =
                             wd & keep;
                     }
                 }
@@ -948,7 +961,8 @@ void prep_kernel(PrepParams p) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
                         const int j = c + e;
-                        const int off = vt_group(j, t >> 3) * 8 + (t & 7);
+                        const int q = kslot(t);
+                        const int off = vt_group(j, q >> 3) * 8 + (q & 7);
                         uint16_t hi, lo;
                         split(live ? xv[e] : 0.f, hi, lo);
                         sm.u.tv.VT[0][j][off] = hi;
@@ -1005,9 +1019,10 @@ void prep_kernel(PrepParams p) {
             }
         __syncthreads();
 
-        // ---- wave w from here on: token tile w.  Rows of TB and B as MFMA
-        // operands, then M = B TB (blocks that vanish by triangularity are
-        // skipped) ----
+        // ---- wave w from here on: token tile w.  Rows of TB (in slot order,
+        // see kslot) and of B as MFMA operands, then M = B TB formed as M^T
+        // (blocks that vanish by triangularity are skipped), whose
+        // accumulators hold the wave's rows of M in slot order ----
         bf16x8_t TBh[2], TBl[2], Mh[2], Ml[2];
         {
             const int t = tok_of(w, i16);
@@ -1018,9 +1033,9 @@ void prep_kernel(PrepParams p) {
                 float tv[8], bv[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const int s = s0 + e;
-                    const float x = sm.u.tv.t.TT[s][t] * sm.beta[s];
-                    tv[e] = (s <= t) ? x : 0.f;
+                    const int s = s0 + e, sq = kslot_tok(s);
+                    const float x = sm.u.tv.t.TT[sq][t] * sm.beta[sq];
+                    tv[e] = (sq <= t) ? x : 0.f;
                     bv[e] = sm.ab.B[t][s];
                 }
                 uint4 th, tl, bh, bl;
@@ -1052,42 +1067,37 @@ void prep_kernel(PrepParams p) {
                     uint4 ch, cl;
                     split8(cv, ch, cl);
                     const bf16x8_t CH = as_op(ch), CL = as_op(cl);
-                    acc[nt] = mfma(Bh[ks], CH, acc[nt]);
-                    acc[nt] = mfma(Bh[ks], CL, acc[nt]);
-                    acc[nt] = mfma(Bl[ks], CH, acc[nt]);
+                    acc[nt] = mfma(CH, Bh[ks], acc[nt]);
+                    acc[nt] = mfma(CL, Bh[ks], acc[nt]);
+                    acc[nt] = mfma(CH, Bl[ks], acc[nt]);
                 }
             }
-            __syncthreads();  // every row of B and of T is read: their storage becomes M
-                              // and the low half of (K e^G)^T
+            __syncthreads();  // every row of T is read: its storage becomes the low
+                              // half of (K e^G)^T
+            // M^T tiles 2 ks and 2 ks + 1 are M's K-step ks in slot order
 #pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sm.ab.M[tok_of(w, 4 * g4 + e)][16 * nt + i16] = acc[nt][e];
+            for (int ks = 0; ks < 2; ++ks) {
+                const float mv[8] = {acc[2 * ks][0], acc[2 * ks][1], acc[2 * ks][2], acc[2 * ks][3],
+                                     acc[2 * ks + 1][0], acc[2 * ks + 1][1], acc[2 * ks + 1][2],
+                                     acc[2 * ks + 1][3]};
+                uint4 mh, ml;
+                split8(mv, mh, ml);
+                Mh[ks] = as_op(mh);
+                Ml[ks] = as_op(ml);
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int c0 = SL * r + 8 * g4;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const uint32_t x = kgl[r][e >> 1];
-                    sm.u.tv.t.KgL[c0 + e][vt_group(c0 + e, t >> 3) * 8 + (t & 7)] =
+                    const int q = kslot(t);
+                    sm.u.tv.t.KgL[c0 + e][vt_group(c0 + e, q >> 3) * 8 + (q & 7)] =
                         (uint16_t)((e & 1) ? (x >> 16) : (x & 0xffffu));
                 }
             }
         }
         __syncthreads();
-        {
-            const int t = tok_of(w, i16);
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                float mv[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) mv[e] = sm.ab.M[t][32 * ks + 8 * g4 + e];
-                uint4 mh, ml;
-                split8(mv, mh, ml);
-                Mh[ks] = as_op(mh);
-                Ml[ks] = as_op(ml);
-            }
-        }
 
         // ---- W = TB (K e^G) and Q' = Q e^G - M (K e^G) for token tile w,
         // formed transposed: accumulator rows are channels 32r + chan_of(m, .),
