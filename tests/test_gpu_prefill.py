@@ -270,16 +270,18 @@ def test_resume_bit_exact_and_tiling_independent():
     assert torch.equal(f3, fin[1:3]), "resumed varlen final states differ"
 
 
-def test_value_tile_widths_bit_identical():
-    """The scan's width follows the chain count: 16 sequences x 32 heads take
-    four 16-column value tiles per workgroup, 4 sequences two, one sequence
-    one.  The sequences shared by the three calls must come out bit for bit
-    the same (outputs, snapshots, final states)."""
+@pytest.mark.parametrize("d", [128, 64, 32])
+def test_value_tile_widths_bit_identical(d):
+    """The scan's width follows the chain count: at d = 128, 16 sequences x 32
+    heads take four 16-column value tiles per workgroup, 4 sequences two, one
+    sequence one (d = 64: four, two, one; d = 32: at most two).  The
+    sequences shared by the three calls must come out bit for bit the same
+    (outputs, snapshots, final states)."""
     from gated_delta_rule_111_amd import kda
     from gated_delta_rule_111_amd.inputs import prefill_inputs
     lens = [384, 130, 257, 320, 200, 64, 401, 333, 150, 256, 99, 380, 275, 190, 300, 128]
     iv = 128
-    inp = prefill_inputs(lens, H=32, dk=128, dv=128, seed=47, state_std=0.05, device=DEV)
+    inp = prefill_inputs(lens, H=32, dk=d, dv=d, seed=47, state_std=0.05, device=DEV)
     out, fin, snaps = _gpu(inp, interval=iv)
     cu = inp.cu_seqlens.cpu().tolist()
     nsn = [l // iv for l in lens]
