@@ -407,51 +407,57 @@ __global__ __launch_bounds__(64 * FE_WAVES) void frontend_kernel(FeParams p) {
 // state slice is read and written by the one wave that owns the token, reads
 // first, so the state may be updated in place.  (256 sequences x 4096
 // channels: 9.5 us with the general kernel, one token per wave; 7.2 us with
-// 2 or 4 tokens per wave; 8 tokens per wave leave too few waves.)
+// 2 or 4 tokens per wave; 8 tokens per wave leave too few waves; 6.8 us with
+// the parameters read at once and the inputs and taps requested before the
+// slot lookups.)
 constexpr int FE_UNIT = 4;
 
 template <int W, typename TIn, typename TOut>
 __global__ __launch_bounds__(64 * FE_WAVES) void frontend_unit_kernel(FeParams p) {
     constexpr int NW = W > 1 ? W - 1 : 1;
+    // Every parameter is read here, before the first branch, and held by the
+    // empty asm statements below (which the compiler cannot move), so the
+    // kernel-argument loads leave together and are waited for once; the
+    // pointers of q and k are then selected, not loaded by index.
+    const int nwg = p.nwg, ngroups = p.ngroups, nslab = p.nslab, T = p.T, dk = p.dk;
+    const float eps2 = p.eps2;
+    const int64_t C = p.C;
+    const int32_t* __restrict__ slots = p.slots;
+    const TIn* x0 = static_cast<const TIn*>(p.x[0]); const TIn* x1 = static_cast<const TIn*>(p.x[1]);
+    const float* w0 = p.w[0]; const float* w1 = p.w[1];
+    const TIn* si0 = static_cast<const TIn*>(p.sin[0]); const TIn* si1 = static_cast<const TIn*>(p.sin[1]);
+    TIn* so0 = static_cast<TIn*>(p.sout[0]); TIn* so1 = static_cast<TIn*>(p.sout[1]);
+    TOut* y0 = static_cast<TOut*>(p.y[0]); TOut* y1 = static_cast<TOut*>(p.y[1]);
+    asm volatile("" :: "s"(nwg), "s"(ngroups), "s"(nslab), "s"(T), "s"(dk), "s"(eps2), "s"(C), "s"(slots));
+    asm volatile("" :: "s"(x0), "s"(x1), "s"(w0), "s"(w1), "s"(y0), "s"(y1));
+    asm volatile("" :: "s"(si0), "s"(si1), "s"(so0), "s"(so1));
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int L = blockIdx.x;
-    if ((p.nwg & 7) == 0) L = (blockIdx.x & 7) * (p.nwg >> 3) + (blockIdx.x >> 3);
-    const int grp = L % p.ngroups;
-    const int rest = L / p.ngroups;
-    const int slab = rest % p.nslab;
-    const int tsel = rest / p.nslab;
+    if ((nwg & 7) == 0) L = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
+    const int grp = L % ngroups;
+    const int rest = L / ngroups;
+    const int slab = rest % nslab;
+    const int tsel = rest / nslab;
     const int t0 = (grp * FE_WAVES + wv) * FE_UNIT;
-    if (t0 >= p.T) return;
-    const int T = p.T;
+    if (t0 >= T) return;
     const int ch0 = slab * FE_SLAB + lane * FE_LANE_CH;
-    const bool live = ch0 < p.C;
+    const bool live = ch0 < C;
     const int ch = live ? ch0 : 0;
-    const int64_t C = p.C;
-    const TIn* __restrict__ x = static_cast<const TIn*>(p.x[tsel]) + ch;
-    TOut* __restrict__ y = static_cast<TOut*>(p.y[tsel]) + ch;
-    const TIn* sin = static_cast<const TIn*>(p.sin[tsel]);   // may alias sout
-    TIn* sout = static_cast<TIn*>(p.sout[tsel]);
+    const TIn* __restrict__ x = (tsel ? x1 : x0) + ch;
+    TOut* __restrict__ y = (tsel ? y1 : y0) + ch;
+    const TIn* sin = tsel ? si1 : si0;   // may alias sout
+    TIn* sout = tsel ? so1 : so0;
+    const float* wsel = tsel ? w1 : w0;
 
-    int64_t slot[FE_UNIT];
-#pragma unroll
-    for (int u = 0; u < FE_UNIT; ++u) {
-        const int t = min(t0 + u, T - 1);
-        slot[u] = p.slots ? p.slots[t] : t;
-    }
+    // the inputs and the taps are requested before the slot lookups, whose
+    // state rows wait for them
     Raw8<TIn> xr[FE_UNIT];
 #pragma unroll
     for (int u = 0; u < FE_UNIT; ++u) xr[u] = load_raw(x + (int64_t)min(t0 + u, T - 1) * C);
-    Raw8<TIn> hr[FE_UNIT][NW];
-    if (W > 1 && sin) {
-#pragma unroll
-        for (int u = 0; u < FE_UNIT; ++u)
-#pragma unroll
-            for (int j = 0; j < W - 1; ++j) hr[u][j] = load_raw(sin + (slot[u] * (W - 1) + j) * C + ch);
-    }
     float wt[W][8];  // -log2(e) w[ch + i][j], as in frontend_kernel
     {
-        const float4* wp = reinterpret_cast<const float4*>(p.w[tsel] + (int64_t)ch * W);
+        const float4* wp = reinterpret_cast<const float4*>(wsel + (int64_t)ch * W);
         float buf[8 * W];
 #pragma unroll
         for (int i = 0; i < 2 * W; ++i) {
@@ -463,7 +469,20 @@ __global__ __launch_bounds__(64 * FE_WAVES) void frontend_unit_kernel(FeParams p
 #pragma unroll
             for (int i = 0; i < 8; ++i) wt[j][i] = buf[i * W + j] * -1.4426950408889634f;
     }
-    const int head_lanes = p.dk / FE_LANE_CH;
+    int64_t slot[FE_UNIT];
+#pragma unroll
+    for (int u = 0; u < FE_UNIT; ++u) {
+        const int t = min(t0 + u, T - 1);
+        slot[u] = slots ? slots[t] : t;
+    }
+    Raw8<TIn> hr[FE_UNIT][NW];
+    if (W > 1 && sin) {
+#pragma unroll
+        for (int u = 0; u < FE_UNIT; ++u)
+#pragma unroll
+            for (int j = 0; j < W - 1; ++j) hr[u][j] = load_raw(sin + (slot[u] * (W - 1) + j) * C + ch);
+    }
+    const int head_lanes = dk / FE_LANE_CH;
 #pragma unroll
     for (int u = 0; u < FE_UNIT; ++u) {
         if (t0 + u >= T) break;
@@ -489,7 +508,7 @@ __global__ __launch_bounds__(64 * FE_WAVES) void frontend_unit_kernel(FeParams p
             ss = fmaf(a[i], a[i], ss);
         }
         ss = head_sum(ss, head_lanes);
-        const float inv = -__builtin_amdgcn_rsqf(ss + p.eps2);
+        const float inv = -__builtin_amdgcn_rsqf(ss + eps2);
 #pragma unroll
         for (int i = 0; i < 8; ++i) a[i] *= inv;
         if (live) {
