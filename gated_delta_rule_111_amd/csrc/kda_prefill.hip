@@ -318,11 +318,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t item_rows(const void* base, in
 // ---------------------------------------------------------------------------
 constexpr int LPT_MAX = 512;
 
-__device__ __forceinline__ int seq_chunks(const int32_t* cu, const int32_t* start, int b) {
-    const int L = cu[b + 1] - cu[b];
-    const int s0 = start ? start[b] : 0;
-    return L > 0 ? (s0 % C + L + C - 1) / C : 0;
-}
 
 __global__ __launch_bounds__(NT) void plan_kernel(const int32_t* __restrict__ cu,
                                                   const int32_t* __restrict__ start, int num_seqs,
@@ -332,17 +327,23 @@ __global__ __launch_bounds__(NT) void plan_kernel(const int32_t* __restrict__ cu
     __shared__ int32_t wtot[2][4];
     __shared__ int32_t carry[2];
     __shared__ int32_t keys[LPT_MAX];
+    // the arguments are held here so that their loads leave together (the
+    // compiler cannot move an asm statement)
+    asm volatile("" :: "s"(cu), "s"(start), "s"(num_seqs), "s"(interval), "s"(chunk_start),
+                 "s"(snap_base), "s"(order));
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (tid == 0) carry[0] = carry[1] = 0;
     __syncthreads();
+    const int32_t* sp = start ? start : cu;  // read unconditionally, used only with start
     for (int base = 0; base <= num_seqs; base += NT) {
         const int b = base + tid;
         int vc = 0, vs = 0;
         if (b < num_seqs) {
             const int L = cu[b + 1] - cu[b];
-            const int s0 = start ? start[b] : 0;
-            vc = seq_chunks(cu, start, b);
+            const int s0 = start ? sp[b] : 0;
+            vc = L > 0 ? (s0 % C + L + C - 1) / C : 0;
             vs = interval > 0 ? (s0 + L) / interval - s0 / interval : 0;
+            if (num_seqs <= LPT_MAX) keys[b] = vc;  // the sort below reuses the counts
         }
         int ic = vc, is = vs;
 #pragma unroll
@@ -368,8 +369,6 @@ __global__ __launch_bounds__(NT) void plan_kernel(const int32_t* __restrict__ cu
         for (int b = tid; b < num_seqs; b += NT) order[b] = b;
         return;
     }
-    for (int b = tid; b < num_seqs; b += NT) keys[b] = seq_chunks(cu, start, b);
-    __syncthreads();
     for (int b = tid; b < num_seqs; b += NT) {
         const int key = keys[b];
         int rank = 0;
@@ -1317,13 +1316,21 @@ void scan_kernel(ScanParams p) {
     // Workgroups are dealt round-robin over the 8 XCDs: chain rho goes to XCD
     // rho mod 8, where its groups follow each other in dispatch order, so the
     // tiles of one head share an L2 and the chains start in order of length.
+    // The start of a workgroup is a chain of dependent loads (arguments, the
+    // chain's sequence, its offsets, its initial state): null index arrays
+    // are replaced by a valid one whose values are then ignored, so no load
+    // waits behind a branch, and the initial state is requested at once.
+    const int ngroups = p.ngroups, nchains = p.nchains, H = p.H, dk = p.dk, dv = p.dv;
+    const int32_t* const order = p.order;
+    const int32_t* const cu = p.cu;
+    const int32_t* const start = p.start;
+    const int32_t* const slots = p.slots;
     const int pos = blockIdx.x >> 3;
-    const int chain = (pos / p.ngroups) * 8 + (blockIdx.x & 7);
-    if (chain >= p.nchains) return;
-    const int tile0 = (pos % p.ngroups) * TPW;
-    const int rk = chain / p.H, h = chain - rk * p.H;
-    const int b = p.order[rk];
-    const int dk = p.dk, dv = p.dv;
+    const int chain = (pos / ngroups) * 8 + (blockIdx.x & 7);
+    if (chain >= nchains) return;
+    const int tile0 = (pos % ngroups) * TPW;
+    const int rk = chain / H, h = chain - rk * H;
+    const int b = order[rk];
     const int j0 = 16 * tile0 + i16;  // value column of this lane in tile t: j0 + 16 t
     // the order of the state-row blocks (see scan_load1): a function of the
     // pair of tiles.  The blocks are loaded in the order of the workgroup's
@@ -1333,33 +1340,49 @@ void scan_kernel(ScanParams p) {
     const int rot = (tile0 >> 1) & 3;
     const uint32_t rsh = 8 * rot;
     auto rot_bytes = [rsh](uint32_t x) { return (uint32_t)((((uint64_t)x << 32) | x) >> rsh); };
-    const int64_t seq0 = p.cu[b];
-    const int len = p.cu[b + 1] - p.cu[b];
-    // chunks sit at absolute multiples of C (see plan_kernel): pad leading
-    // rows of the first chunk precede the sequence's first token
-    const int spos = p.start ? p.start[b] : 0;
-    const int pad = spos % C;
-    const int nch = len > 0 ? (pad + len + C - 1) / C : 0;
+    const int32_t c0v = cu[b], c1v = cu[b + 1];
+    const int32_t startv = (start ? start : cu)[b];
+    const int32_t slotv = (slots ? slots : cu)[b];
     const int64_t cbase = p.chunk_start[b];
     const int64_t sbase = p.snap_base[b];
+    const int64_t seq0 = c0v;
+    const int len = c1v - c0v;
+    // chunks sit at absolute multiples of C (see plan_kernel): pad leading
+    // rows of the first chunk precede the sequence's first token
+    const int spos = start ? startv : 0;
+    const int pad = spos % C;
+    const int nch = len > 0 ? (pad + len + C - 1) / C : 0;
 
     // state rows of this lane: 32w + chan_of(m, 4*g4 + e) = 32w + 8*g4 + 4m + e
     f32x4 S[TPW][2];
-    const int64_t srow = ((p.slots ? (int64_t)p.slots[b] : (int64_t)b) * p.H + h) * dk;
+    const int64_t srow = ((slots ? (int64_t)slotv : (int64_t)b) * H + h) * dk;
     const bool has_init = p.init && (!p.init_if_started || spos > 0);
+    if (has_init) {
+        float xi[TPW][2][4];  // every load first, then the masking
 #pragma unroll
-    for (int t = 0; t < TPW; ++t)
+        for (int t = 0; t < TPW; ++t)
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
+            for (int m = 0; m < 2; ++m)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int c = SL * w + 8 * g4 + 4 * m + e;
-                S[t][m][e] = 0.f;
-                if (has_init) {
-                    const float x = p.init[(srow + (c < dk ? c : 0)) * dv + j0 + 16 * t];
-                    S[t][m][e] = c < dk ? x : 0.f;
+                for (int e = 0; e < 4; ++e) {
+                    const int c = SL * w + 8 * g4 + 4 * m + e;
+                    xi[t][m][e] = p.init[(srow + (c < dk ? c : 0)) * dv + j0 + 16 * t];
                 }
-            }
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int c = SL * w + 8 * g4 + 4 * m + e;
+                    S[t][m][e] = c < dk ? xi[t][m][e] : 0.f;
+                }
+    } else {
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+#pragma unroll
+            for (int m = 0; m < 2; ++m) S[t][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
     // Operands are prefetched into two register sets used in turn (DB: the
     // loop body is instantiated twice with the roles swapped, so no loaded
@@ -1377,7 +1400,7 @@ void scan_kernel(ScanParams p) {
     // sequence's last row: stores past it fall outside and are dropped.
     // Tile t's columns sit 16 t elements after tile 0's (a scalar offset).
     constexpr int OB = OUT_BF16 ? 2 : 4;
-    const int64_t orow = (int64_t)p.H * dv;  // elements per token row
+    const int64_t orow = (int64_t)H * dv;  // elements per token row
     uint32_t ooff[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -1388,13 +1411,13 @@ void scan_kernel(ScanParams p) {
     // instead of dividing per chunk.  snap_off: element offset of the next
     // snapshot's block for this head.
     int64_t snap_next = p.interval > 0 ? ((int64_t)spos / p.interval + 1) * p.interval : -1;
-    int64_t snap_off = (sbase * p.H + h) * (int64_t)dk * dv;
-    const int64_t snap_step = (int64_t)p.H * dk * dv;
+    int64_t snap_off = (sbase * H + h) * (int64_t)dk * dv;
+    const int64_t snap_step = (int64_t)H * dk * dv;
     // operand block of the chunk after the current one (the last chunk
     // reloads itself, so the same loads are issued on every path; that data
     // is unused)
-    const int64_t blk_step = (int64_t)p.H * CHUNK_OPS;
-    const uint4* nptr = p.ops + ((cbase + min(1, nch - 1)) * p.H + h) * CHUNK_OPS;
+    const int64_t blk_step = (int64_t)H * CHUNK_OPS;
+    const uint4* nptr = p.ops + ((cbase + min(1, nch - 1)) * H + h) * CHUNK_OPS;
 
     // A chunk's output tiles are stored during the next chunk, while that
     // chunk waits for its state rows from LDS (the last ones after the loop).
@@ -1566,7 +1589,7 @@ void scan_kernel(ScanParams p) {
         }
         if constexpr (DB) scan_load3(nx, nblk, w, vo, vd);
         if constexpr (TPW == 1) {
-            const int ns = 4 * p.ngroups, si = (pos % p.ngroups) * 4 + w;
+            const int ns = 4 * ngroups, si = (pos % ngroups) * 4 + w;
             const __amdgpu_buffer_rsrc_t pb = scan_block(p, cbase + min(ci + 2, nch - 1), h);
             const int line = min(si + lane * ns, (CHUNK_OPS * 16 - 1) / 128);
             pfn = __builtin_amdgcn_raw_buffer_load_b32(pb, line * 128, 0, 0);
