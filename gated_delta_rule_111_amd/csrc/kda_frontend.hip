@@ -415,10 +415,10 @@ constexpr int FE_UNIT = 4;
 template <int W, typename TIn, typename TOut>
 __global__ __launch_bounds__(64 * FE_WAVES) void frontend_unit_kernel(FeParams p) {
     constexpr int NW = W > 1 ? W - 1 : 1;
-    // Every parameter is read here, before the first branch, and held by the
-    // empty asm statements below (which the compiler cannot move), so the
-    // kernel-argument loads leave together and are waited for once; the
-    // pointers of q and k are then selected, not loaded by index.
+    // Every parameter is read up front and there is no branch before the
+    // loads (a wave past the last token clamps its rows and stores nothing),
+    // so the kernel-argument loads leave together and are waited for once;
+    // the pointers of q or k are selected, not loaded by index.
     const int nwg = p.nwg, ngroups = p.ngroups, nslab = p.nslab, T = p.T, dk = p.dk;
     const float eps2 = p.eps2;
     const int64_t C = p.C;
@@ -428,19 +428,14 @@ __global__ __launch_bounds__(64 * FE_WAVES) void frontend_unit_kernel(FeParams p
     const TIn* si0 = static_cast<const TIn*>(p.sin[0]); const TIn* si1 = static_cast<const TIn*>(p.sin[1]);
     TIn* so0 = static_cast<TIn*>(p.sout[0]); TIn* so1 = static_cast<TIn*>(p.sout[1]);
     TOut* y0 = static_cast<TOut*>(p.y[0]); TOut* y1 = static_cast<TOut*>(p.y[1]);
-    asm volatile("" :: "s"(nwg), "s"(ngroups), "s"(nslab), "s"(T), "s"(dk), "s"(eps2), "s"(C), "s"(slots));
-    asm volatile("" :: "s"(x0), "s"(x1), "s"(w0), "s"(w1), "s"(y0), "s"(y1));
-    asm volatile("" :: "s"(si0), "s"(si1), "s"(so0), "s"(so1));
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    int L = blockIdx.x;
-    if ((nwg & 7) == 0) L = (blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3);
+    const int L = (nwg & 7) == 0 ? (int)((blockIdx.x & 7) * (nwg >> 3) + (blockIdx.x >> 3)) : (int)blockIdx.x;
     const int grp = L % ngroups;
     const int rest = L / ngroups;
     const int slab = rest % nslab;
     const int tsel = rest / nslab;
     const int t0 = (grp * FE_WAVES + wv) * FE_UNIT;
-    if (t0 >= T) return;
     const int ch0 = slab * FE_SLAB + lane * FE_LANE_CH;
     const bool live = ch0 < C;
     const int ch = live ? ch0 : 0;

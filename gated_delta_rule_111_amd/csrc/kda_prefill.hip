@@ -327,10 +327,6 @@ __global__ __launch_bounds__(NT) void plan_kernel(const int32_t* __restrict__ cu
     __shared__ int32_t wtot[2][4];
     __shared__ int32_t carry[2];
     __shared__ int32_t keys[LPT_MAX];
-    // the arguments are held here so that their loads leave together (the
-    // compiler cannot move an asm statement)
-    asm volatile("" :: "s"(cu), "s"(start), "s"(num_seqs), "s"(interval), "s"(chunk_start),
-                 "s"(snap_base), "s"(order));
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (tid == 0) carry[0] = carry[1] = 0;
     __syncthreads();
